@@ -1,0 +1,265 @@
+/*
+ * CPU oracle for the int4 routed-expert MoE layer. TEST INFRASTRUCTURE ONLY:
+ * see oracle.h for the pages followed and the readings taken where they are
+ * silent. Scalar C99, double accumulation, no blocking, fusion or reordering
+ * beyond what each step's definition states.
+ */
+#include "oracle.h"
+
+#include <fenv.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------- quantiser
+ * [HF] container: each quantised weight is a U8 tensor of packed int4 nibbles
+ * plus an F32 scale per row; the conversion rounds with np.rint, matching the
+ * engine's lrintf (round half to even). [P5] section 三: gs64 group scales.
+ * Scale max|w|/7 and the clamp to [-8, 7] are the stated reading. */
+
+static int8_t quant_one(float w, float scale) {
+    if (scale == 0.0f) return 0;
+    float v = rintf(w / scale);          /* float division, nearest-even */
+    if (v > 7.0f) v = 7.0f;
+    if (v < -8.0f) v = -8.0f;
+    return (int8_t)v;
+}
+
+int oracle_quantize_int4(const float* w, int64_t rows, int64_t cols, int32_t group,
+                         uint8_t* q, float* s) {
+    if (rows < 0 || cols <= 0 || (cols & 1)) return -1;
+    if (group != 0 && group != 64) return -1;
+    if (group == 64 && cols % 64) return -1;
+    if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+    int64_t span = group ? group : cols;          /* columns sharing one scale */
+    int64_t per_row = cols / span;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* wr = w + r * cols;
+        uint8_t* qr = q + r * (cols / 2);
+        for (int64_t g = 0; g < per_row; ++g) {
+            float m = 0.0f;
+            for (int64_t c = g * span; c < (g + 1) * span; ++c) {
+                float a = fabsf(wr[c]);
+                if (a > m) m = a;
+            }
+            float scale = m / 7.0f;
+            s[r * per_row + g] = scale;
+            for (int64_t c = g * span; c < (g + 1) * span; c += 2) {
+                int8_t lo = quant_one(wr[c], scale);
+                int8_t hi = quant_one(wr[c + 1], scale);
+                qr[c / 2] = (uint8_t)(((uint8_t)lo & 0x0F) | (((uint8_t)hi & 0x0F) << 4));
+            }
+        }
+    }
+    return 0;
+}
+
+/* Signed value of nibble c of a packed row (two's complement, low nibble first). */
+static int nibble(const uint8_t* row, int64_t c) {
+    int v = (c & 1) ? (row[c >> 1] >> 4) : (row[c >> 1] & 0x0F);
+    return v >= 8 ? v - 16 : v;
+}
+
+static double scale_of(const float* s, int64_t r, int64_t c, int64_t cols, int32_t group) {
+    if (group == 0) return (double)s[r];
+    return (double)s[r * (cols / group) + c / group];
+}
+
+void oracle_dequantize_int4(const uint8_t* q, const float* s, int64_t rows, int64_t cols,
+                            int32_t group, double* out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = (double)nibble(q + r * (cols / 2), c) * scale_of(s, r, c, cols, group);
+}
+
+/* ---------------------------------------------------------------- router
+ * [P5] section 一/二 and [HF]: the router stays F32. Logits accumulate in
+ * double and are rounded once. */
+void oracle_router_logits(const float* wr, const float* x, int32_t T, int32_t H, int32_t E,
+                          float* logits) {
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < H; ++j) acc += (double)wr[(int64_t)e * H + j] * (double)x[(int64_t)t * H + j];
+            logits[(int64_t)t * E + e] = (float)acc;
+        }
+}
+
+/* [P4] section 三 item 1: a DeepSeek-V3-style sigmoid router picks 8 of 256
+ * experts per token. [P4] section 四 item 3: the aux-loss-free bias adjusts
+ * selection; routing, selection and scaling are reproduced exactly. [P2]:
+ * scoring_func sigmoid, norm_topk_prob true. */
+int oracle_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                 int32_t* idx, float* w) {
+    if (T < 0 || E <= 0 || k <= 0 || k > E) return -1;
+    float* score = (float*)malloc(sizeof(float) * (size_t)E);
+    float* key = (float*)malloc(sizeof(float) * (size_t)E);
+    unsigned char* used = (unsigned char*)malloc((size_t)E);
+    if (!score || !key || !used) { free(score); free(key); free(used); return -1; }
+    for (int32_t t = 0; t < T; ++t) {
+        const float* l = logits + (int64_t)t * E;
+        for (int32_t e = 0; e < E; ++e) {
+            score[e] = (float)(1.0 / (1.0 + exp(-(double)l[e])));   /* sigmoid, one rounding */
+            key[e] = score[e] + (bias ? bias[e] : 0.0f);            /* float add */
+            used[e] = 0;
+        }
+        /* selection: k passes, each taking the largest remaining key; the
+         * strict > keeps the lowest index among equal keys */
+        int32_t* it = idx + (int64_t)t * k;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (used[e]) continue;
+                if (best < 0 || key[e] > key[best]) best = e;
+            }
+            used[best] = 1;
+            it[j] = best;
+        }
+        /* normalised weights from the unbiased scores, sum in slot order */
+        double sum = 0.0;
+        for (int32_t j = 0; j < k; ++j) sum += (double)score[it[j]];
+        for (int32_t j = 0; j < k; ++j)
+            w[(int64_t)t * k + j] = (sum == 0.0) ? (float)(1.0 / k) : (float)((double)score[it[j]] / sum);
+    }
+    free(score); free(key); free(used);
+    return 0;
+}
+
+/* ----------------------------------------------------------------- union
+ * [P4] section 三 item 4 and [P5] section 二: positions of a batch that hit
+ * the same expert are merged, so each unique expert is read once and applied
+ * to all of its positions. */
+int oracle_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* unique, int32_t* n_unique) {
+    if (T < 0 || k <= 0 || E <= 0) return -1;
+    int64_t n = (int64_t)T * k;
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < n; ++a) {
+        if (idx[a] < 0 || idx[a] >= E) return -1;
+        counts[idx[a]] += 1;
+    }
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    if (!fill) return -1;
+    for (int64_t a = 0; a < n; ++a) {
+        int32_t e = idx[a];
+        perm[offsets[e] + fill[e]] = (int32_t)a;
+        fill[e] += 1;
+    }
+    free(fill);
+    int32_t u = 0;
+    for (int32_t e = 0; e < E; ++e)
+        if (counts[e] > 0) unique[u++] = e;
+    *n_unique = u;
+    return 0;
+}
+
+/* ------------------------------------------------------------ expert FFN
+ * [P5] section 二: an expert is three matrices (gate, up, down) stored
+ * adjacently. SwiGLU: h_r = silu(g_r) * u_r with g = gate x, u = up x; then
+ * y = down h. Each product term is dequantised (nibble * scale) in double. */
+void oracle_expert_ffn(const oracle_expert* ex, int32_t H, int32_t I, int32_t group,
+                       const float* x, double* y) {
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < I; ++r) {
+        const uint8_t* gr = ex->gate_q + (int64_t)r * (H / 2);
+        const uint8_t* ur = ex->up_q + (int64_t)r * (H / 2);
+        double g = 0.0, u = 0.0;
+        for (int32_t c = 0; c < H; ++c) {
+            g += (double)nibble(gr, c) * scale_of(ex->gate_s, r, c, H, group) * (double)x[c];
+            u += (double)nibble(ur, c) * scale_of(ex->up_s, r, c, H, group) * (double)x[c];
+        }
+        h[r] = g / (1.0 + exp(-g)) * u;
+    }
+#pragma omp parallel for schedule(static)
+    for (int32_t c = 0; c < H; ++c) {
+        const uint8_t* dr = ex->down_q + (int64_t)c * (I / 2);
+        double acc = 0.0;
+        for (int32_t r = 0; r < I; ++r)
+            acc += (double)nibble(dr, r) * scale_of(ex->down_s, c, r, I, group) * h[r];
+        y[c] = acc;
+    }
+    free(h);
+}
+
+int oracle_expert_ffn_union(const oracle_expert* experts, int32_t H, int32_t I, int32_t group,
+                            const float* x, int32_t T, int32_t k, const int32_t* offsets,
+                            const int32_t* perm, const int32_t* unique, int32_t n_unique,
+                            double* y_assign) {
+    if (H <= 0 || I <= 0 || T < 0 || k <= 0) return -1;
+    for (int32_t i = 0; i < n_unique; ++i) {
+        int32_t e = unique[i];
+        for (int32_t p = offsets[e]; p < offsets[e + 1]; ++p) {
+            int32_t a = perm[p];
+            oracle_expert_ffn(&experts[e], H, I, group, x + (int64_t)(a / k) * H,
+                              y_assign + (int64_t)a * H);
+        }
+    }
+    return 0;
+}
+
+/* ----------------------------------------------------------------- layer
+ * [P5] section 二: per token and layer, route -> union -> (placement) ->
+ * execute. The combine sums the routed outputs in slot order weighted by
+ * the normalised weights, scales that sum by rs, and adds the shared expert
+ * (weight 1) — [P4] section 四 item 3 asks for the scaling semantics to be
+ * reproduced; rs defaults to 1. */
+int oracle_layer(int32_t H, int32_t I, int32_t E, int32_t k, int32_t group, float routed_scale,
+                 const float* x, int32_t T, const float* logits, const float* wr,
+                 const float* bias, const oracle_expert* experts, const oracle_expert* shared,
+                 float* y, double* y64, int32_t* idx_out, float* w_out) {
+    if (H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E || T < 0) return -1;
+    if ((logits == NULL) == (wr == NULL)) return -1;
+    int rc = -1;
+    int64_t n = (int64_t)T * k;
+    float* lg = (float*)malloc(sizeof(float) * ((size_t)T * E + 1));
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * ((size_t)n + 1));
+    float* w = (float*)malloc(sizeof(float) * ((size_t)n + 1));
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * ((size_t)E + 1));
+    int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * ((size_t)n + 1));
+    int32_t* unique = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    double* ya = (double*)malloc(sizeof(double) * ((size_t)n * H + 1));
+    double* ys = (double*)malloc(sizeof(double) * (size_t)H);
+    int32_t n_unique = 0;
+    if (!lg || !idx || !w || !counts || !offsets || !perm || !unique || !ya || !ys) goto done;
+
+    if (logits) memcpy(lg, logits, sizeof(float) * (size_t)T * E);
+    else oracle_router_logits(wr, x, T, H, E, lg);
+    if (oracle_route(lg, bias, T, E, k, idx, w)) goto done;
+    if (oracle_union(idx, T, k, E, counts, offsets, perm, unique, &n_unique)) goto done;
+    if (oracle_expert_ffn_union(experts, H, I, group, x, T, k, offsets, perm, unique, n_unique, ya))
+        goto done;
+    for (int32_t t = 0; t < T; ++t) {
+        if (shared) oracle_expert_ffn(shared, H, I, group, x + (int64_t)t * H, ys);
+        for (int32_t c = 0; c < H; ++c) {
+            double routed = 0.0;
+            for (int32_t j = 0; j < k; ++j)
+                routed += (double)w[(int64_t)t * k + j] * ya[((int64_t)t * k + j) * H + c];
+            double v = (shared ? ys[c] : 0.0) + (double)routed_scale * routed;
+            y[(int64_t)t * H + c] = (float)v;
+            if (y64) y64[(int64_t)t * H + c] = v;
+        }
+    }
+    if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)n);
+    if (w_out) memcpy(w_out, w, sizeof(float) * (size_t)n);
+    rc = 0;
+done:
+    free(lg); free(idx); free(w); free(counts); free(offsets); free(perm); free(unique);
+    free(ya); free(ys);
+    return rc;
+}
