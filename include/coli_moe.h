@@ -1,0 +1,248 @@
+/*
+ * libcoli_moe: one int4 routed-expert MoE layer with a sigmoid router, for
+ * MI355X (gfx950). C ABI: plain pointers and sizes, no C++ or torch types.
+ *
+ * The layer, per token (practical guide "colibrì 實戰指南：以純 C 引擎在消費級
+ * 硬體上串流運行 744B MoE 模型", section 二: route -> union -> place ->
+ * overlapped execute -> learn):
+ *   1. route: sigmoid scores of the router logits, a per-expert bias added for
+ *      selection only, the top-k experts by biased key, weights = unbiased
+ *      scores normalised over the k selected (lbrq.cn article "github一周涨
+ *      11k⭐️！25GB 内存跑 744B GLM-5.2 模型！", section 三 item 1 and section 四
+ *      item 3; config.json values sigmoid / norm_topk_prob quoted by the
+ *      int8-MTP page "解密GLM-5.2-colibri-int4-with-int8-mtp…").
+ *   2. union: the T*k (token, slot) assignments grouped by expert, so each
+ *      unique expert's weights are read once for all of its tokens (lbrq.cn
+ *      article section 三 item 4; practical guide section 二).
+ *   3. place: an HBM cache of expert blobs in front of pinned host memory
+ *      (practical guide section 二: per-layer LRU, one read per expert,
+ *      misses loaded while resident experts compute).
+ *   4. execute: each selected expert and the shared expert is an int4 SwiGLU
+ *      FFN, y_e = down(silu(gate x) * (up x)); the layer output is
+ *      y = shared(x) + routed_scale * sum_j w_j y_{e_j}, summed in slot order.
+ *
+ * Quantised format (model card "jlnsrk/GLM-5.2-colibri-int4": U8 packed int4
+ * nibbles plus F32 scales, rounded with np.rint / lrintf; gs64 groups from
+ * the practical guide section 三): scale = max|w|/7 per row (group 0) or per
+ * 64 consecutive inputs of a row (group 64); q = rint(w/scale) in float,
+ * half-to-even, clamped to [-8, 7]; two's-complement nibbles, column 2i in
+ * bits 0-3 and 2i+1 in bits 4-7 of byte i; rows are row-major.
+ *
+ * Expert blob: one contiguous device buffer per expert holding, in order,
+ * gate_q [I][H/2], up_q [I][H/2], down_q [H][I/2] (u8), gate_s, up_s
+ * ([I] or [I][H/64] f32) and down_s ([H] or [H][I/64] f32); every part starts
+ * on a 256-byte boundary (coli_expert_blob_layout gives the offsets). A miss
+ * of the expert cache is therefore one copy.
+ *
+ * Conventions for every call:
+ *  - d_* pointers are device memory, h_* pointers host memory. The caller owns
+ *    all of them; the library keeps none after a call returns (the expert
+ *    cache handle aside).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on it and return, unless stated otherwise.
+ *  - Return value: COLI_OK, or a negative code with a message readable via
+ *    coli_last_error() (thread-local, valid until the next call on the same
+ *    thread). Argument errors are found before anything is enqueued. Faults
+ *    inside kernels surface at the caller's next synchronisation, as for any
+ *    HIP stream work.
+ *  - Floating-point inputs must be finite.
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define COLI_API __attribute__((visibility("default")))
+#else
+#define COLI_API
+#endif
+
+typedef int32_t coli_status;
+#define COLI_OK 0
+#define COLI_EINVAL (-1)        /* null pointer, bad size or shape */
+#define COLI_EUNSUPPORTED (-2)  /* valid but outside the supported ranges */
+#define COLI_EHIP (-3)          /* a HIP call failed; message has hipGetErrorString */
+#define COLI_ENOMEM (-4)        /* workspace too small or host allocation failed */
+#define COLI_EBUSY (-5)         /* every cache slot of the layer is pinned by this call */
+
+COLI_API const char* coli_last_error(void);
+COLI_API const char* coli_version(void);
+
+/* Layer shape. Supported: hidden and inter positive multiples of 32 (and of
+ * 64 when group == 64); 1 <= n_routed <= 1024; n_shared 0 or 1;
+ * 1 <= top_k <= min(32, n_routed); group 0 or 64; routed_scale finite. */
+typedef struct coli_moe_shape {
+    int32_t hidden;       /* H: model width, input and output of the layer */
+    int32_t inter;        /* I: intermediate width of one expert */
+    int32_t n_routed;     /* E: routed experts */
+    int32_t n_shared;     /* 0 or 1 shared expert, weight 1, always applied */
+    int32_t top_k;        /* k: experts per token */
+    int32_t group;        /* 0: one scale per row; 64: one scale per 64 inputs */
+    float routed_scale;   /* multiplies the routed sum at the combine (1.0 = none) */
+} coli_moe_shape;
+
+/* Offsets (bytes) of gate_q, up_q, down_q, gate_s, up_s, down_s inside one
+ * expert blob, and the blob size. Host-only arithmetic. */
+COLI_API coli_status coli_expert_blob_layout(const coli_moe_shape* shape, size_t off[6], size_t* blob_bytes);
+
+/* Quantise d_w [rows][cols] (f32) to d_q [rows][cols/2] (u8) and d_s ([rows]
+ * or [rows][cols/64] f32) by the rule above. Bit-identical to the CPU
+ * reference for finite input. cols even (multiple of 64 for group 64). */
+COLI_API coli_status coli_quantize_int4(const float* d_w, int64_t rows, int64_t cols, int32_t group,
+                               uint8_t* d_q, float* d_s, void* stream);
+
+/* Quantise one expert's three f32 matrices (gate/up [I][H], down [H][I]) into
+ * the blob d_blob (coli_expert_blob_layout bytes). */
+COLI_API coli_status coli_quantize_expert(const coli_moe_shape* shape, const float* d_gate,
+                                 const float* d_up, const float* d_down, void* d_blob,
+                                 void* stream);
+
+/* Router logits d_logits [T][E] = d_x [T][H] . d_wr [E][H]^T: f32 inputs,
+ * products and sum in double, one rounding to f32 (the router stays F32 in
+ * the container, model card file table). */
+COLI_API coli_status coli_moe_router_logits(const float* d_wr, const float* d_x, int32_t T, int32_t H,
+                                   int32_t E, float* d_logits, void* stream);
+
+/* Sigmoid top-k routing of T tokens over E experts (E <= 1024, k <= 32).
+ * score = sigmoid(logit) computed in double and rounded once to f32;
+ * key = score + bias (f32; d_bias NULL means zero); the k largest keys in
+ * descending order, equal keys to the lower expert index, into d_idx [T][k];
+ * d_w [T][k] = score / (sum of the k selected scores, in slot order, double),
+ * rounded to f32 (1/k if that sum is 0). */
+COLI_API coli_status coli_moe_route(const float* d_logits, const float* d_bias, int32_t T, int32_t E,
+                           int32_t k, int32_t* d_idx, float* d_w, void* stream);
+
+/* Workspace bytes coli_moe_union needs for T tokens, k slots, E experts. */
+COLI_API coli_status coli_moe_union_workspace_size(int32_t T, int32_t k, int32_t E, size_t* bytes);
+
+/* Batch union of the T*k assignments a = t*k + j of d_idx [T][k]:
+ * d_counts [E]; d_offsets [E+1] (exclusive prefix sum, offsets[E] = T*k);
+ * d_perm [T*k]: assignments grouped by expert, ascending within a group;
+ * d_unique [E]: the experts with count > 0, ascending, first *d_n_unique
+ * entries valid. Deterministic (no atomics decide any order). Entries outside
+ * [0, E) belong to no expert: they are left out of counts and perm, so
+ * offsets[E] is then the number of valid entries. */
+COLI_API coli_status coli_moe_union(const int32_t* d_idx, int32_t T, int32_t k, int32_t E,
+                           int32_t* d_counts, int32_t* d_offsets, int32_t* d_perm,
+                           int32_t* d_unique, int32_t* d_n_unique, void* d_ws, size_t ws_bytes,
+                           void* stream);
+
+#define COLI_PATH_AUTO 0   /* GEMV family for small per-expert counts, MFMA otherwise */
+#define COLI_PATH_GEMV 1   /* int4 dequant GEMV family (f32-accurate) */
+#define COLI_PATH_MFMA 2   /* bf16 MFMA grouped GEMM on dequantised tiles */
+
+/* Workspace bytes for coli_moe_expert_ffn / coli_moe_layer_fwd with T tokens. */
+COLI_API coli_status coli_moe_workspace_size(const coli_moe_shape* shape, int32_t T, int32_t path,
+                                    size_t* bytes);
+
+/* Unweighted expert outputs for a union: for every unique expert e (first
+ * *d_n_unique entries of d_unique) and every assignment a in d_perm
+ * [d_offsets[e], d_offsets[e+1]), d_y_assign [a][H] = FFN_e(d_x [a / k]).
+ * Rows of assignments of no listed expert are left untouched.
+ * d_blob_table: device array [E] of device pointers to expert blobs. */
+COLI_API coli_status coli_moe_expert_ffn(const coli_moe_shape* shape, const void* const* d_blob_table,
+                                const float* d_x, int32_t T, const int32_t* d_offsets,
+                                const int32_t* d_perm, const int32_t* d_unique,
+                                const int32_t* d_n_unique, float* d_y_assign, int32_t path,
+                                void* d_ws, size_t ws_bytes, void* stream);
+
+struct coli_expert_cache;
+
+/* One whole layer for T tokens: route, union, expert FFNs (routed + shared),
+ * combine. Exactly one of d_logits [T][E] and d_router_w [E][H] is given.
+ * d_bias [E] may be NULL. d_shared_blob is required iff shape->n_shared == 1.
+ * Without a cache, d_blob_table [E] (device) gives the routed blobs. With a
+ * cache, d_blob_table is ignored: the call copies the routing to the host
+ * (one blocking 4*T*k-byte read), makes the selected experts of `layer`
+ * resident, runs the resident ones while the misses are copied, then the
+ * misses. d_idx_out [T][k] and d_w_out [T][k] (nullable) receive the routing.
+ * d_y [T][H] f32. */
+COLI_API coli_status coli_moe_layer_fwd(const coli_moe_shape* shape, const float* d_x, int32_t T,
+                               const float* d_logits, const float* d_router_w,
+                               const float* d_bias, const void* const* d_blob_table,
+                               const void* d_shared_blob, struct coli_expert_cache* cache,
+                               int32_t layer, float* d_y, int32_t* d_idx_out, float* d_w_out,
+                               int32_t path, void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ expert cache
+ * Per-layer LRU of expert blobs in an HBM arena, filled from pinned host
+ * memory (practical guide section 二: per-layer LRU; a miss is one read of the
+ * whole expert; a read in flight is never issued twice; misses load while
+ * resident experts compute; placement changes speed, never the result). */
+typedef struct coli_cache_cfg {
+    int32_t n_layers;
+    int32_t n_experts;          /* routed experts per layer */
+    int32_t slots_per_layer;    /* HBM slots per layer, >= top_k of the calls */
+    size_t blob_bytes;          /* bytes per expert blob */
+    void* d_arena;              /* device, n_layers * slots_per_layer * blob_bytes */
+    const void* h_pool;         /* pinned host, n_layers * n_experts * blob_bytes,
+                                   blob of (layer, e) at (layer*n_experts + e)*blob_bytes */
+    void* copy_stream;          /* hipStream_t for the host-to-device copies */
+} coli_cache_cfg;
+
+typedef struct coli_cache_stats {
+    uint64_t hits;
+    uint64_t misses;
+    uint64_t evictions;
+    uint64_t bytes_h2d;
+    uint64_t copy_ns;           /* sum of the copies' event-measured durations */
+    uint64_t lookups;
+} coli_cache_stats;
+
+/* Creates the handle and its per-layer device pointer tables (n_layers *
+ * n_experts pointers; entries of non-resident experts are NULL). */
+COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct coli_expert_cache** out);
+COLI_API coli_status coli_expert_cache_destroy(struct coli_expert_cache* cache);
+
+/* Make experts h_ids[0..n) of `layer` resident. Hits refresh their LRU age;
+ * each miss evicts the least recently used slot not named in this call
+ * (waiting, on the copy stream, for the compute that last read it) and
+ * enqueues one host-to-device copy on the copy stream. h_miss_mask[i]
+ * (nullable) is set to 1 for a miss. Duplicate ids count once. COLI_EBUSY if
+ * n exceeds the layer's slots. Host-side bookkeeping only; never blocks on
+ * the GPU. */
+COLI_API coli_status coli_expert_cache_ensure(struct coli_expert_cache* cache, int32_t layer,
+                                     const int32_t* h_ids, int32_t n, int32_t* h_miss_mask);
+
+/* Make `compute_stream` wait for the copies enqueued by the last ensure on
+ * `layer` (and for its pointer-table update). */
+COLI_API coli_status coli_expert_cache_wait(struct coli_expert_cache* cache, int32_t layer,
+                                   void* compute_stream);
+
+/* Record that the slots used by the last ensure on `layer` are read by work
+ * already enqueued on `compute_stream`; a later eviction waits for it. */
+COLI_API coli_status coli_expert_cache_release(struct coli_expert_cache* cache, int32_t layer,
+                                      void* compute_stream);
+
+/* Device pointer table [n_experts] of `layer` (valid for resident experts
+ * once coli_expert_cache_wait has been called on the stream that reads it). */
+COLI_API coli_status coli_expert_cache_table(struct coli_expert_cache* cache, int32_t layer,
+                                    const void* const** d_table);
+
+COLI_API coli_status coli_expert_cache_stats(struct coli_expert_cache* cache, coli_cache_stats* out);
+
+/* Forget every resident expert (the next lookups all miss); stats zeroed. */
+COLI_API coli_status coli_expert_cache_reset(struct coli_expert_cache* cache);
+
+/* ---------------------------------------------------------- kernel timing
+ * Optional HIP-event timing of the library's main kernels, recorded on the
+ * stream each kernel runs on. coli_profile_enable(n) pre-creates n event
+ * pairs (0 turns timing off and frees them); each timed launch takes the next
+ * pair until they run out. coli_profile_summary(name) waits for the recorded
+ * events of kernel `name` ("gemv_gateup", "gemv_down", "gemm_gateup",
+ * "gemm_down") and returns how many were timed and their total milliseconds.
+ * coli_profile_clear() forgets the records and reuses the pairs. */
+COLI_API coli_status coli_profile_enable(int32_t max_records);
+COLI_API coli_status coli_profile_clear(void);
+COLI_API coli_status coli_profile_summary(const char* name, int64_t* count, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

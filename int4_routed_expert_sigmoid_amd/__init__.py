@@ -1,0 +1,298 @@
+"""Python binding of libcoli_moe (one int4 routed-expert MoE layer, MI355X).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels (``csrc/``); this module turns torch tensors into device pointers and
+the current torch stream into a ``hipStream_t``. The names follow the C ABI in
+``include/coli_moe.h``. There is no CPU fallback: if the library is missing,
+``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SO_PATH = os.path.join(HERE, "libcoli_moe.so")
+
+COLI_OK, COLI_EINVAL, COLI_EUNSUPPORTED, COLI_EHIP, COLI_ENOMEM, COLI_EBUSY = 0, -1, -2, -3, -4, -5
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+
+EXPORTED = [
+    "coli_last_error", "coli_version", "coli_expert_blob_layout", "coli_quantize_int4",
+    "coli_quantize_expert", "coli_moe_router_logits", "coli_moe_route",
+    "coli_moe_union_workspace_size", "coli_moe_union", "coli_moe_workspace_size",
+    "coli_moe_expert_ffn", "coli_moe_layer_fwd", "coli_expert_cache_create",
+    "coli_expert_cache_destroy", "coli_expert_cache_ensure", "coli_expert_cache_wait",
+    "coli_expert_cache_release", "coli_expert_cache_table", "coli_expert_cache_stats",
+    "coli_expert_cache_reset", "coli_profile_enable", "coli_profile_clear",
+    "coli_profile_summary",
+]
+
+
+class ColiError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"coli status {code}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float)]
+
+
+class CacheCfg(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("slots_per_layer", ctypes.c_int32), ("blob_bytes", ctypes.c_size_t),
+                ("d_arena", ctypes.c_void_p), ("h_pool", ctypes.c_void_p),
+                ("copy_stream", ctypes.c_void_p)]
+
+
+class CacheStats(ctypes.Structure):
+    _fields_ = [("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
+                ("evictions", ctypes.c_uint64), ("bytes_h2d", ctypes.c_uint64),
+                ("copy_ns", ctypes.c_uint64), ("lookups", ctypes.c_uint64)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """Load libcoli_moe.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(SO_PATH):
+                raise ImportError(f"{SO_PATH} is missing: run __graft_entry__.build() first")
+            L = ctypes.CDLL(SO_PATH)
+            vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+            f32 = ctypes.c_float
+            P = ctypes.POINTER
+            for name in EXPORTED:
+                getattr(L, name).restype = ctypes.c_int32
+            L.coli_last_error.restype = ctypes.c_char_p
+            L.coli_version.restype = ctypes.c_char_p
+            L.coli_expert_blob_layout.argtypes = [P(Shape), P(sz), P(sz)]
+            L.coli_quantize_int4.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+            L.coli_quantize_expert.argtypes = [P(Shape), vp, vp, vp, vp, vp]
+            L.coli_moe_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+            L.coli_moe_route.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+            L.coli_moe_union_workspace_size.argtypes = [i32, i32, i32, P(sz)]
+            L.coli_moe_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+            L.coli_moe_workspace_size.argtypes = [P(Shape), i32, i32, P(sz)]
+            L.coli_moe_expert_ffn.argtypes = [P(Shape), vp, vp, i32, vp, vp, vp, vp, vp, i32, vp,
+                                              sz, vp]
+            L.coli_moe_layer_fwd.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, vp, i32, vp,
+                                             vp, vp, i32, vp, sz, vp]
+            L.coli_expert_cache_create.argtypes = [P(CacheCfg), P(vp)]
+            L.coli_expert_cache_destroy.argtypes = [vp]
+            L.coli_expert_cache_ensure.argtypes = [vp, i32, vp, i32, vp]
+            L.coli_expert_cache_wait.argtypes = [vp, i32, vp]
+            L.coli_expert_cache_release.argtypes = [vp, i32, vp]
+            L.coli_expert_cache_table.argtypes = [vp, i32, P(vp)]
+            L.coli_expert_cache_stats.argtypes = [vp, P(CacheStats)]
+            L.coli_expert_cache_reset.argtypes = [vp]
+            L.coli_profile_enable.argtypes = [i32]
+            L.coli_profile_clear.argtypes = []
+            L.coli_profile_summary.argtypes = [ctypes.c_char_p, P(i64), P(ctypes.c_double)]
+            _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != COLI_OK:
+        raise ColiError(rc, lib().coli_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name):
+    import torch
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class MoEShape:
+    hidden: int
+    inter: int
+    n_routed: int
+    n_shared: int = 1
+    top_k: int = 8
+    group: int = 0
+    routed_scale: float = 1.0
+
+    def c(self) -> Shape:
+        return Shape(self.hidden, self.inter, self.n_routed, self.n_shared, self.top_k, self.group,
+                     self.routed_scale)
+
+
+def version() -> str:
+    return lib().coli_version().decode()
+
+
+def blob_layout(shape: MoEShape):
+    """(offsets of gate_q, up_q, down_q, gate_s, up_s, down_s; blob bytes)."""
+    off = (ctypes.c_size_t * 6)()
+    nb = ctypes.c_size_t()
+    _check(lib().coli_expert_blob_layout(ctypes.byref(shape.c()), off, ctypes.byref(nb)))
+    return list(off), nb.value
+
+
+def quantize_int4(w, group=0, q=None, s=None, stream=None):
+    import torch
+    _need(w, torch.float32, "w")
+    rows, cols = w.shape
+    if q is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty((rows,) if group == 0 else (rows, cols // 64), dtype=torch.float32,
+                        device=w.device)
+    _check(lib().coli_quantize_int4(_ptr(w), rows, cols, group, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def quantize_expert(shape: MoEShape, gate, up, down, blob=None, stream=None):
+    import torch
+    for t, n in ((gate, "gate"), (up, "up"), (down, "down")):
+        _need(t, torch.float32, n)
+    if blob is None:
+        blob = torch.empty(blob_layout(shape)[1], dtype=torch.uint8, device=gate.device)
+    _check(lib().coli_quantize_expert(ctypes.byref(shape.c()), _ptr(gate), _ptr(up), _ptr(down),
+                                      _ptr(blob), _stream(stream)))
+    return blob
+
+
+def router_logits(wr, x, out=None, stream=None):
+    import torch
+    _need(wr, torch.float32, "wr")
+    _need(x, torch.float32, "x")
+    E, H = wr.shape
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().coli_moe_router_logits(_ptr(wr), _ptr(x), T, H, E, _ptr(out), _stream(stream)))
+    return out
+
+
+def route(logits, bias, k, idx=None, w=None, stream=None):
+    import torch
+    _need(logits, torch.float32, "logits")
+    _need(bias, torch.float32, "bias")
+    T, E = logits.shape
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().coli_moe_route(_ptr(logits), _ptr(bias), T, E, k, _ptr(idx), _ptr(w),
+                                _stream(stream)))
+    return idx, w
+
+
+def union(idx, E, stream=None):
+    import torch
+    _need(idx, torch.int32, "idx")
+    T, k = idx.shape
+    dev = idx.device
+    nb = ctypes.c_size_t()
+    _check(lib().coli_moe_union_workspace_size(T, k, E, ctypes.byref(nb)))
+    ws = torch.empty(max(1, nb.value), dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(1, T * k), dtype=torch.int32, device=dev)
+    unique = torch.empty(E, dtype=torch.int32, device=dev)
+    n_unique = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().coli_moe_union(_ptr(idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm),
+                                _ptr(unique), _ptr(n_unique), _ptr(ws), nb.value, _stream(stream)))
+    return counts, offsets, perm[: T * k], unique, n_unique
+
+
+def workspace_size(shape: MoEShape, T: int, path: int = PATH_AUTO) -> int:
+    nb = ctypes.c_size_t()
+    _check(lib().coli_moe_workspace_size(ctypes.byref(shape.c()), T, path, ctypes.byref(nb)))
+    return nb.value
+
+
+def workspace(shape: MoEShape, T: int, path: int = PATH_AUTO, device="cuda"):
+    import torch
+    return torch.empty(max(1, workspace_size(shape, T, path)), dtype=torch.uint8, device=device)
+
+
+def blob_table(blobs, device="cuda"):
+    """Device array of blob pointers from a list of device tensors (or ints)."""
+    import torch
+    ptrs = [b if isinstance(b, int) else b.data_ptr() for b in blobs]
+    return torch.tensor(ptrs, dtype=torch.int64, device=device)
+
+
+def expert_ffn(shape: MoEShape, table, x, offsets, perm, unique, n_unique, y_assign=None,
+               path=PATH_AUTO, ws=None, stream=None):
+    import torch
+    _need(x, torch.float32, "x")
+    T = x.shape[0]
+    if y_assign is None:
+        y_assign = torch.zeros((T * shape.top_k, shape.hidden), dtype=torch.float32,
+                               device=x.device)
+    if ws is None:
+        ws = workspace(shape, T, path, x.device)
+    _check(lib().coli_moe_expert_ffn(ctypes.byref(shape.c()), _ptr(table), _ptr(x), T,
+                                     _ptr(offsets), _ptr(perm), _ptr(unique), _ptr(n_unique),
+                                     _ptr(y_assign), path, _ptr(ws), ws.numel(), _stream(stream)))
+    return y_assign
+
+
+def layer_fwd(shape: MoEShape, x, table=None, shared_blob=None, logits=None, router_w=None,
+              bias=None, cache=None, layer=0, y=None, idx_out=None, w_out=None, path=PATH_AUTO,
+              ws=None, stream=None):
+    import torch
+    _need(x, torch.float32, "x")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, shape.hidden), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(shape, T, path, x.device)
+    _check(lib().coli_moe_layer_fwd(ctypes.byref(shape.c()), _ptr(x), T, _ptr(logits),
+                                    _ptr(router_w), _ptr(bias), _ptr(table), _ptr(shared_blob),
+                                    _ptr(cache.handle if cache is not None else None), layer,
+                                    _ptr(y), _ptr(idx_out), _ptr(w_out), path, _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+    return y
+
+
+def profile_enable(max_records: int):
+    _check(lib().coli_profile_enable(max_records))
+
+
+def profile_clear():
+    _check(lib().coli_profile_clear())
+
+
+def profile_summary(name: str):
+    """(launches timed, total milliseconds) for kernel `name`."""
+    n = ctypes.c_int64()
+    ms = ctypes.c_double()
+    _check(lib().coli_profile_summary(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

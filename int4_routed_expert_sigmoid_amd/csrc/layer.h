@@ -1,0 +1,31 @@
+// Internal: workspace layout and the launch sequences behind the C ABI.
+#pragma once
+
+#include "common.h"
+
+namespace coli {
+
+struct WsLayout {
+    size_t logits, idx, w, counts, offsets, perm, unique, n_unique, n_items, union_ws, items,
+        rows_tok, rows_out, xplanes, xscale, hplanes, hscale, y_rows, phase, bytes;
+};
+
+coli_status check_shape(const coli_moe_shape* s);
+WsLayout ws_layout(const coli_moe_shape* s, int32_t T, int32_t path);
+
+coli_status run_expert_ffn(const coli_moe_shape* shape, const void* const* table, const float* x,
+                           int32_t T, const int32_t* offsets, const int32_t* perm,
+                           const int32_t* unique, const int32_t* n_unique, float* y_assign,
+                           int32_t path, uint8_t* ws, const WsLayout& W, hipStream_t stream);
+
+coli_status run_layer(const coli_moe_shape* shape, const float* x, int32_t T, const float* logits,
+                      const float* router_w, const float* bias, const void* const* table,
+                      const void* shared_blob, struct coli_expert_cache* cache, int32_t layer,
+                      float* y, int32_t* idx_out, float* w_out, int32_t path, uint8_t* ws,
+                      const WsLayout& W, hipStream_t stream);
+
+// Expert-cache hooks used by run_layer (cache.hip).
+coli_status cache_layer_table(struct coli_expert_cache* cache, int32_t layer, int32_t n_experts,
+                              const void* const** table);
+
+}  // namespace coli

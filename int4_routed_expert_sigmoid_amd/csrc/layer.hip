@@ -1,0 +1,79 @@
+// Launch sequences of coli_moe_expert_ffn and coli_moe_layer_fwd.
+//
+// Practical guide section 二: per token and layer, route -> union -> place ->
+// execute (-> learn). Everything below is enqueued on the caller's stream;
+// nothing waits on the host except the cached layer, which must read the
+// routing back to decide placement.
+#include <algorithm>
+#include <vector>
+
+#include "layer.h"
+
+namespace coli {
+
+template <typename T>
+static T* at(uint8_t* ws, size_t off) { return reinterpret_cast<T*>(ws + off); }
+
+coli_status run_expert_ffn(const coli_moe_shape* s, const void* const* table, const float* x,
+                           int32_t T, const int32_t* offsets, const int32_t* perm,
+                           const int32_t* unique, const int32_t* n_unique, float* y_assign,
+                           int32_t path, uint8_t* ws, const WsLayout& W, hipStream_t stream) {
+    (void)path;
+    const int32_t H = s->hidden, I = s->inter, E = s->n_routed, k = s->top_k;
+    coli_status st = launch_plan(offsets, perm, unique, n_unique, table, nullptr, T, k, E, nullptr,
+                                 0, at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items),
+                                 at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
+    if (st) return st;
+    st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
+    if (st) return st;
+    const int32_t max_items = std::min<int64_t>(E, (int64_t)T * k);
+    return launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
+                           at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
+                           at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
+                           at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_assign, H, I,
+                           s->group, stream);
+}
+
+coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const float* logits,
+                      const float* router_w, const float* bias, const void* const* table,
+                      const void* shared_blob, struct coli_expert_cache* cache, int32_t layer,
+                      float* y, int32_t* idx_out, float* w_out, int32_t path, uint8_t* ws,
+                      const WsLayout& W, hipStream_t stream) {
+    (void)path;
+    const int32_t H = s->hidden, I = s->inter, E = s->n_routed, k = s->top_k;
+    if (cache) return fail(COLI_EUNSUPPORTED, "layer_fwd: expert cache not available yet");
+    (void)layer;
+    coli_status st;
+    const float* lg = logits;
+    if (!lg) {
+        st = launch_router_logits(router_w, x, T, H, E, at<float>(ws, W.logits), stream);
+        if (st) return st;
+        lg = at<float>(ws, W.logits);
+    }
+    int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, W.idx);
+    float* w = w_out ? w_out : at<float>(ws, W.w);
+    st = launch_route(lg, bias, T, E, k, idx, w, stream);
+    if (st) return st;
+    st = launch_union(idx, T, k, E, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
+                      at<int32_t>(ws, W.perm), at<int32_t>(ws, W.unique), at<int32_t>(ws, W.n_unique),
+                      ws + W.union_ws, stream);
+    if (st) return st;
+    st = launch_plan(at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.perm), at<int32_t>(ws, W.unique),
+                     at<int32_t>(ws, W.n_unique), table, shared_blob, T, k, E, nullptr, 0,
+                     at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items),
+                     at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
+    if (st) return st;
+    st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
+    if (st) return st;
+    const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
+    st = launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
+                         at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
+                         at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
+                         at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale),
+                         at<float>(ws, W.y_rows), H, I, s->group, stream);
+    if (st) return st;
+    return launch_combine(at<float>(ws, W.y_rows), w, T, k, H, shared_blob ? 1 : 0,
+                          s->routed_scale, y, stream);
+}
+
+}  // namespace coli

@@ -1,0 +1,211 @@
+"""GPU path vs the CPU oracle, element by element on the same seeded inputs.
+
+Bar: quantiser bytes/scales, routing indices, union arrays bit-exact; routing
+weights exact (same double arithmetic); expert/layer outputs max per-row
+relative L2 <= 1e-3 on the GEMV path."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import ExpertSet, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def coli():
+    import torch
+    import int4_routed_expert_sigmoid_amd as c
+    c.lib()
+    assert torch.cuda.is_available()
+    return c
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+# ------------------------------------------------------------------ quantiser
+@pytest.mark.parametrize("rows,cols,group", [
+    (1, 4, 0), (3, 6, 0), (7, 250, 0), (64, 256, 0), (33, 6144, 0), (2048, 2048, 0),
+    (5, 64, 64), (17, 192, 64), (129, 6144, 64), (2048, 2048, 64), (0, 64, 0),
+])
+def test_quantize_bit_exact(coli, rows, cols, group):
+    import torch
+    w = synth.normal(1, synth.TAG_WEIGHT, rows, cols, rows * cols, 0.0, 0.02).reshape(rows, cols)
+    if rows >= 3:
+        w[1] = 0.0                                   # all-zero row
+        w[2, ::3] *= 100.0                           # a wide row
+    q, s = coli.quantize_int4(_dev(w), group)
+    torch.cuda.synchronize()
+    if rows == 0:
+        return
+    q_ref, s_ref = oracle.quantize_int4(w, group)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_quantize_expert_layout(coli):
+    import torch
+    shape = coli.MoEShape(256, 128, 8, 1, 2, 64)
+    off, nbytes = coli.blob_layout(shape)
+    g, u, d = synth.expert_weights(3, 0, 1, 256, 128)
+    blob = coli.quantize_expert(shape, _dev(g), _dev(u), _dev(d)).cpu().numpy()
+    qe = oracle.QExpert.quantize(g, u, d, 64)
+    parts = qe.parts
+    for i, p in enumerate(parts):
+        raw = blob[off[i]:off[i] + p.nbytes]
+        assert np.array_equal(raw, p.reshape(-1).view(np.uint8)), f"part {i}"
+
+
+# --------------------------------------------------------------------- router
+@pytest.mark.parametrize("T,E,H", [(4, 8, 256), (1, 256, 6144), (33, 64, 512)])
+def test_router_logits(coli, T, E, H):
+    import torch
+    wr = synth.router_weights(2, 0, E, H)
+    x = synth.activations(2, 0, 0, T, H)
+    lg = coli.router_logits(_dev(wr), _dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(wr, x)
+    got = lg.cpu().numpy()
+    # double accumulation in another order: equal after the rounding to float
+    # except where the double sums straddle a float rounding boundary (1 ulp)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    assert (ulps > 0).mean() < 1e-3
+
+
+@pytest.mark.parametrize("T,E,k,kind", [
+    (4, 8, 2, "router"), (1, 256, 8, "router"), (8, 256, 8, "zipf"), (2048, 256, 8, "zipf_mix"),
+    (37, 1024, 32, "zipf"), (5, 64, 1, "zipf"), (16, 256, 8, "ties"), (3, 8, 8, "zipf"),
+])
+def test_route_bit_exact(coli, T, E, k, kind):
+    import torch
+    if kind == "router":
+        H = 256 if E == 8 else 6144
+        lg = oracle.router_logits(synth.router_weights(0, 0, E, H), synth.activations(0, 0, 0, T, H))
+        b = synth.bias(0, 0, E)
+    elif kind == "ties":
+        lg = np.round(synth.zipf_logits(9, 0, 0, T, E), 1).astype(np.float32)
+        b = np.zeros(E, np.float32)
+        b[::7] = 0.125
+    else:
+        lg = synth.zipf_logits(9, 0, 0, T, E, s=1.1, mix=0.1 if kind == "zipf_mix" else 0.0)
+        b = synth.bias(9, 0, E)
+    idx, w = coli.route(_dev(lg), _dev(b), k)
+    torch.cuda.synchronize()
+    idx_ref, w_ref = oracle.route(lg, b, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.array_equal(w.cpu().numpy(), w_ref)
+
+
+def test_route_no_bias(coli):
+    import torch
+    lg = synth.zipf_logits(4, 0, 0, 64, 256)
+    idx, w = coli.route(_dev(lg), None, 8)
+    torch.cuda.synchronize()
+    idx_ref, w_ref = oracle.route(lg, None, 8)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.array_equal(w.cpu().numpy(), w_ref)
+
+
+# ---------------------------------------------------------------------- union
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (8, 8, 256), (4, 2, 8), (2048, 8, 256),
+                                   (1000, 3, 1024), (7, 1, 5), (0, 8, 256), (130, 8, 16)])
+def test_union_bit_exact(coli, T, k, E):
+    import torch
+    if T > 0:
+        idx_np, _ = oracle.route(synth.zipf_logits(6, 0, 0, T, E, s=1.1), None, k)
+    else:
+        idx_np = np.zeros((0, k), np.int32)
+    idx = _dev(idx_np) if T > 0 else torch.zeros((0, k), dtype=torch.int32, device="cuda")
+    counts, offsets, perm, unique, n_unique = coli.union(idx, E)
+    torch.cuda.synchronize()
+    c, o, p, u = oracle.union(idx_np, E)
+    nu = int(n_unique.cpu()[0])
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(perm.cpu().numpy(), p)
+    assert nu == len(u) and np.array_equal(unique.cpu().numpy()[:nu], u)
+
+
+# ----------------------------------------------------------------- expert FFN
+@pytest.mark.parametrize("H,I,group,T,k,E", [
+    (256, 128, 0, 4, 2, 8), (256, 128, 64, 4, 2, 8), (512, 256, 0, 1, 8, 16),
+    (192, 320, 64, 9, 3, 6), (6144, 2048, 0, 1, 8, 256), (6144, 2048, 64, 8, 8, 256),
+    (2048, 512, 0, 17, 4, 8),
+])
+def test_expert_ffn(coli, H, I, group, T, k, E):
+    import torch
+    shape = coli.MoEShape(H, I, E, 0, k, group)
+    lg = synth.zipf_logits(8, 0, 0, T, E, s=1.1)
+    idx_np, _ = oracle.route(lg, None, k)
+    c, o, p, u = oracle.union(idx_np, E)
+    ex = ExpertSet(coli, shape, seed=8, which=u, shared=False)
+    x = synth.activations(8, 0, 0, T, H)
+    offsets, perm = _dev(o), _dev(p)
+    uu = np.zeros(E, np.int32)
+    uu[:len(u)] = u
+    y = coli.expert_ffn(shape, ex.table, _dev(x), offsets, perm, _dev(uu),
+                        _dev(np.array([len(u)], np.int32)), path=coli.PATH_GEMV)
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn_union(ex.oracle_list(), x, k, o, p, u, H, I, group)
+    err = rel_l2_rows(y.cpu().numpy(), ref)
+    assert err.max() <= TOL, f"max rel L2 {err.max():.3e}"
+
+
+# ---------------------------------------------------------------------- layer
+def _layer_case(coli, H, I, E, k, group, T, seed, routing, rs=1.0, n_shared=1):
+    import torch
+    shape = coli.MoEShape(H, I, E, n_shared, k, group, rs)
+    x = synth.activations(seed, 0, 0, T, H)
+    wr = b = lg = None
+    if routing == "router":
+        wr = synth.router_weights(seed, 0, E, H)
+        b = synth.bias(seed, 0, E)
+        lg_sel = oracle.router_logits(wr, x)
+    else:
+        lg = synth.zipf_logits(seed, 0, 0, T, E, s=1.1, mix=0.1 if routing == "zipf_mix" else 0.0)
+        lg_sel = lg
+    idx_sel, _ = oracle.route(lg_sel, b, k)
+    ex = ExpertSet(coli, shape, seed=seed, which=np.unique(idx_sel), shared=n_shared == 1)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = coli.layer_fwd(shape, _dev(x), table=ex.table, shared_blob=ex.shared_blob,
+                       logits=None if lg is None else _dev(lg),
+                       router_w=None if wr is None else _dev(wr),
+                       bias=None if b is None else _dev(b), idx_out=idx, w_out=w,
+                       path=coli.PATH_GEMV)
+    torch.cuda.synchronize()
+    y_ref, y64, idx_ref, w_ref = oracle.layer(x, ex.oracle_list(), ex.shared_oracle, k, group, rs,
+                                              logits=lg, wr=wr, bias=b)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.array_equal(w.cpu().numpy(), w_ref)
+    err = rel_l2_rows(y.cpu().numpy(), y64)
+    assert err.max() <= TOL, f"max rel L2 {err.max():.3e}"
+    return err
+
+
+@pytest.mark.parametrize("group", [0, 64])
+def test_layer_tiny(coli, group):
+    _layer_case(coli, 256, 128, 8, 2, group, 4, 0, "router")
+
+
+def test_layer_decode_glm_shape(coli):
+    # decode launch configuration: hidden 6144, inter 2048, 256 + 1 experts, top-8, T = 1,
+    # per-row scales, logits from the f32 router; several tokens one call at a time
+    for t in range(3):
+        _layer_case(coli, 6144, 2048, 256, 8, 0, 1, 100 + t, "router")
+
+
+def test_layer_mtp_verify_glm_shape(coli):
+    # MTP-verify launch configuration: gs64, T = 8, Zipf(1.1) routing
+    _layer_case(coli, 6144, 2048, 256, 8, 64, 8, 7, "zipf")
+
+
+def test_layer_routed_scale_no_shared(coli):
+    _layer_case(coli, 512, 256, 16, 4, 0, 5, 3, "zipf", rs=2.5, n_shared=0)
