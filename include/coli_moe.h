@@ -74,7 +74,7 @@ typedef int32_t coli_status;
 COLI_API const char* coli_last_error(void);
 COLI_API const char* coli_version(void);
 
-/* Layer shape. Supported: hidden and inter positive multiples of 32 (and of
+/* Layer shape. Supported: hidden <= 16384 and inter <= 4096, positive multiples of 32 (and of
  * 64 when group == 64); 1 <= n_routed <= 1024; n_shared 0 or 1;
  * 1 <= top_k <= min(32, n_routed); group 0 or 64; routed_scale finite. */
 typedef struct coli_moe_shape {
@@ -137,7 +137,11 @@ COLI_API coli_status coli_moe_union(const int32_t* d_idx, int32_t T, int32_t k, 
 #define COLI_PATH_GEMV 1   /* int4 dequant GEMV family (f32-accurate) */
 #define COLI_PATH_MFMA 2   /* bf16 MFMA grouped GEMM on dequantised tiles */
 
-/* Workspace bytes for coli_moe_expert_ffn / coli_moe_layer_fwd with T tokens. */
+/* Workspace bytes for coli_moe_expert_ffn / coli_moe_layer_fwd with T tokens.
+ * The workspace (device memory, owned by the caller) must be zero-filled once
+ * before its first use: it holds arrival counters that every call leaves at
+ * zero again. A workspace serves one call at a time: calls that share one
+ * must be ordered on a stream. */
 COLI_API coli_status coli_moe_workspace_size(const coli_moe_shape* shape, int32_t T, int32_t path,
                                     size_t* bytes);
 

@@ -237,8 +237,9 @@ def workspace_size(shape: MoEShape, T: int, path: int = PATH_AUTO) -> int:
 
 
 def workspace(shape: MoEShape, T: int, path: int = PATH_AUTO, device="cuda"):
+    """Zero-filled workspace (its arrival counters must start at zero)."""
     import torch
-    return torch.empty(max(1, workspace_size(shape, T, path)), dtype=torch.uint8, device=device)
+    return torch.zeros(max(1, workspace_size(shape, T, path)), dtype=torch.uint8, device=device)
 
 
 def blob_table(blobs, device="cuda"):

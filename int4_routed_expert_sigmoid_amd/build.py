@@ -14,7 +14,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "layer.hip", "quant.hip", "route.hip", "union.hip", "gemv.hip", "gemm.hip",
-           "cache.hip", "profile.hip"]
+           "cache.hip", "profile.hip", "gemv_gateup.hip", "gemv_down.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

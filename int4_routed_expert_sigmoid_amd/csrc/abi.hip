@@ -34,8 +34,8 @@ coli_status check_shape(const coli_moe_shape* s) {
     if (s->n_shared != 0 && s->n_shared != 1) return fail(COLI_EUNSUPPORTED, "n_shared must be 0 or 1");
     if (s->top_k < 1 || s->top_k > 32 || s->top_k > s->n_routed)
         return fail(COLI_EUNSUPPORTED, "top_k must be in [1, min(32, n_routed)]");
-    if (s->hidden > 32768) return fail(COLI_EUNSUPPORTED, "hidden must be <= 32768");
-    if (s->inter > 8192) return fail(COLI_EUNSUPPORTED, "inter must be <= 8192");
+    if (s->hidden > 16384) return fail(COLI_EUNSUPPORTED, "hidden must be <= 16384");
+    if (s->inter > 4096) return fail(COLI_EUNSUPPORTED, "inter must be <= 4096");
     if (!(s->routed_scale == s->routed_scale) || s->routed_scale > 3.4e38f || s->routed_scale < -3.4e38f)
         return fail(COLI_EINVAL, "routed_scale must be finite");
     return COLI_OK;

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "../../include/coli_moe.h"
+#include "profile.h"
 
 namespace coli {
 
@@ -61,16 +62,35 @@ struct WorkItem {
 };
 
 // ------------------------------------------------------ activation digits
-// The GEMV family multiplies int4 weights by activations held as five planes
+// The GEMV family multiplies int4 weights by activations held as four planes
 // of signed base-16 digits per 32-element block: x_c ~= scale_b * X_c with
-// scale_b a power of two chosen so that |X_c| <= 2^18, and
-// X_c = sum_{p<5} 16^p d_{p,c}, d in [-8, 7]. Every nibble product
-// q * d is then exact in a v_dot8_i32_i4 and the per-block integer sum
-// sum_c q_c X_c is exact in int32; the only rounding is X_c = rint(x_c/scale_b)
-// (relative error <= 2^-18 of the block's largest |x|).
-constexpr int kPlanes = 5;
+// scale_b = max_c |x_c| / kDigitMax and X_c = rint(x_c / scale_b) written as
+// sum_{p<4} 16^p d_{p,c}, d in [-8, 7]. Four such digits cover every integer
+// in [-34952, 30583], so |X_c| <= kDigitMax = 30583 always decomposes. Every
+// nibble product q * d is then exact in a v_dot8_i32_i4 and the per-block
+// integer sum sum_c q_c X_c is exact in int32; the only rounding is that of
+// X_c (at most half a step, step = max|x| / 30583 of the block).
+constexpr int kPlanes = 4;
+constexpr int kDigitMax = 30583;     // 7 * (16^4 - 1) / 15
 constexpr int kBlock = 32;                 // elements per block (= one 16-byte nibble load)
 constexpr int kWordsPerBlock = kPlanes * 4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+typedef __attribute__((address_space(1))) const float global_f32;
+
+// Streaming 128-bit load of weight nibbles (read once: non-temporal). The
+// pointer is cast to the global address space: blob pointers come from
+// tables in memory, and a generic (FLAT) load would also count against the
+// LDS wait counter and serialise the prefetching.
+__device__ __forceinline__ uint4 ldg128(const uint8_t* p) {
+    const u32x4 v = __builtin_nontemporal_load((global_u32x4*)(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Plain global load of one float through a global-address-space pointer.
+__device__ __forceinline__ float ldg_f32(const float* p) { return *(global_f32*)(p); }
 
 __device__ __forceinline__ int dot8(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
@@ -88,7 +108,7 @@ __device__ __forceinline__ int block_dot(const uint4& w, const uint4* p) {
         acc = dot8(w.w, p[i].w, acc);
         a[i] = acc;
     }
-    return a[0] + a[1] * 16 + a[2] * 256 + a[3] * 4096 + a[4] * 65536;
+    return a[0] + a[1] * 16 + a[2] * 256 + a[3] * 4096;
 }
 
 // Encode 8 consecutive elements (this thread's quarter of a 32-element block;
@@ -103,12 +123,11 @@ __device__ __forceinline__ float encode_quarter(const float v[8], uint32_t words
 #pragma unroll
     for (int p = 0; p < kPlanes; ++p) words[p] = 0u;
     if (m == 0.f) return 0.f;
-    int ex;
-    frexpf(m, &ex);                         // m < 2^ex
-    int s = ex - 18;                        // |x| * 2^-s < 2^18
+    const float inv = (float)kDigitMax / m;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        int X = (int)rintf(ldexpf(v[i], -s));
+        int X = (int)rintf(v[i] * inv);
+        X = min(max(X, -kDigitMax), kDigitMax);
 #pragma unroll
         for (int p = 0; p < kPlanes; ++p) {
             int d = ((X + 8) & 15) - 8;
@@ -116,7 +135,7 @@ __device__ __forceinline__ float encode_quarter(const float v[8], uint32_t words
             words[p] |= (uint32_t)(d & 15) << (4 * i);
         }
     }
-    return ldexpf(1.0f, s);
+    return m / (float)kDigitMax;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -125,12 +144,125 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// ------------------------------------------------- wave transpose-reduce
+// Sums N partials (N a power of two <= 64) over the 64 lanes of a wave in
+// one pass: every stage pairs each lane with a partner in the other half of
+// its lane group, keeps half of the values and adds the partner's copy of
+// them. Stage partners: lane^32 and lane^16 via v_permlane32/16_swap,
+// lane^8 (DPP row_ror:8), lane^7 (DPP row_half_mirror), lane^2 and lane^1
+// (DPP quad_perm). Afterwards lane l holds the wave-wide sum of value
+// l >> (6 - log2 N).
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
+    const int i = __float_as_int(v);
+    int r;
+    switch (ctrl_sel) {
+        case 8: r = __builtin_amdgcn_update_dpp(0, i, 0x128, 0xF, 0xF, false); break;  // row_ror:8
+        case 4: r = __builtin_amdgcn_update_dpp(0, i, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+        case 2: r = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+        default: r = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false); break;  // quad_perm 1,0,3,2
+    }
+    return __int_as_float(r);
+}
+
+// Value of lane partner(l) for the butterfly partners used in this file:
+// S = 1, 2 (lane^S, DPP quad_perm), 4 (lane^7, DPP row_half_mirror),
+// 8 (lane^8, DPP row_ror:8), 16 (lane^16), 32 (lane^32) via permlane swaps.
+// The six partners generate all 64 lanes, so a butterfly over them is a
+// full all-reduce.
+template <int S>
+__device__ __forceinline__ int lane_xchg(int v) {
+    if constexpr (S == 32 || S == 16) {
+        const auto r = (S == 32) ? __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false)
+                                 : __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+        const int lane = threadIdx.x & 63;
+        return (int)((lane & S) ? r[0] : r[1]);
+    } else {
+        return __float_as_int(dpp_f(__int_as_float(v), S));
+    }
+}
+
+template <int S, int N>
+__device__ __forceinline__ void transpose_stage(float* v, int lane) {
+    constexpr int h = N / 2;
+    if constexpr (S >= 16) {
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const auto r = (S == 32)
+                ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + h]), false, false)
+                : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + h]), false, false);
+            v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    } else {
+        const int bit = (S == 4) ? ((lane >> 2) & 1) : ((lane & S) ? 1 : 0);
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const float keep = bit ? v[i + h] : v[i];
+            const float give = bit ? v[i] : v[i + h];
+            v[i] = keep + dpp_f(give, S);
+        }
+    }
+}
+
+template <int S>
+__device__ __forceinline__ float plain_stage(float v) {
+    if constexpr (S >= 16) {
+        const auto r = (S == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                                 : __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        return v + dpp_f(v, S);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[N]) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+    const int lane = threadIdx.x & 63;
+    if constexpr (N >= 2) transpose_stage<32, N>(v, lane); else v[0] = plain_stage<32>(v[0]);
+    if constexpr (N >= 4) transpose_stage<16, N / 2>(v, lane); else v[0] = plain_stage<16>(v[0]);
+    if constexpr (N >= 8) transpose_stage<8, N / 4>(v, lane); else v[0] = plain_stage<8>(v[0]);
+    if constexpr (N >= 16) transpose_stage<4, N / 8>(v, lane); else v[0] = plain_stage<4>(v[0]);
+    if constexpr (N >= 32) transpose_stage<2, N / 16>(v, lane); else v[0] = plain_stage<2>(v[0]);
+    if constexpr (N >= 64) transpose_stage<1, N / 32>(v, lane); else v[0] = plain_stage<1>(v[0]);
+    return v[0];
+}
+
+template <int N>
+__device__ __forceinline__ constexpr int transpose_shift() {
+    return N == 64 ? 0 : N == 32 ? 1 : N == 16 ? 2 : N == 8 ? 3 : N == 4 ? 4 : N == 2 ? 5 : 6;
+}
+
 // ------------------------------------------------- launch entry points
 // (host functions implemented in the .hip files; all enqueue on `stream`)
 coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t group,
                             uint8_t* q, float* s, hipStream_t stream);
 coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int32_t H,
                                  int32_t E, float* logits, hipStream_t stream);
+// Router for small batches (T <= kSmallT): logits (when router_w is given)
+// and activation encoding, then routing, union and FFN work list.
+constexpr int kSmallT = 16;
+struct SmallRouterArgs {
+    const float* x;            // [T][H]
+    const float* router_w;     // [E][H] or NULL
+    const float* logits_in;    // [T][E] when router_w is NULL
+    const float* bias;         // [E] or NULL
+    float* logits_out;         // [T][E] scratch (router_w given)
+    int32_t* idx;              // [T][k]
+    float* w;                  // [T][k]
+    int32_t *counts, *offsets, *perm, *unique, *n_unique;
+    WorkItem* items;
+    int32_t* n_items;
+    int32_t *rows_tok, *rows_out;
+    uint32_t* xplanes;
+    float* xscale;
+    const void* const* table;
+    const void* shared_blob;
+    const uint8_t* phase_mask; // [E] or NULL: keep only experts whose mask equals `phase`
+    int32_t phase;
+    int32_t T, E, k, H;
+};
+coli_status launch_router_small(const SmallRouterArgs& a, hipStream_t stream);
+
 coli_status launch_route(const float* logits, const float* bias, int32_t T, int32_t E,
                          int32_t k, int32_t* idx, float* w, hipStream_t stream);
 size_t union_ws_bytes(int32_t T, int32_t k, int32_t E);
@@ -149,6 +281,7 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
                         hipStream_t stream);
 coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* planes, float* scales,
                           hipStream_t stream);
+// gate/up then down GEMV over a work list.
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
                             int32_t max_count, const int32_t* rows_tok, const int32_t* rows_out,
                             const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <vector>
 
+#include "gemv.h"
 #include "layer.h"
 
 namespace coli {
@@ -44,14 +45,41 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
     if (cache) return fail(COLI_EUNSUPPORTED, "layer_fwd: expert cache not available yet");
     (void)layer;
     coli_status st;
+    int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, W.idx);
+    float* w = w_out ? w_out : at<float>(ws, W.w);
+    if (T <= kSmallT && path != COLI_PATH_MFMA) {
+        // three launches: fused router, gate/up GEMV, down GEMV with the combine
+        SmallRouterArgs ra;
+        ra.x = x; ra.router_w = router_w; ra.logits_in = logits; ra.bias = bias;
+        ra.logits_out = at<float>(ws, W.logits);
+        ra.idx = idx; ra.w = w;
+        ra.counts = at<int32_t>(ws, W.counts); ra.offsets = at<int32_t>(ws, W.offsets);
+        ra.perm = at<int32_t>(ws, W.perm); ra.unique = at<int32_t>(ws, W.unique);
+        ra.n_unique = at<int32_t>(ws, W.n_unique);
+        ra.items = at<WorkItem>(ws, W.items); ra.n_items = at<int32_t>(ws, W.n_items);
+        ra.rows_tok = at<int32_t>(ws, W.rows_tok); ra.rows_out = at<int32_t>(ws, W.rows_out);
+        ra.xplanes = at<uint32_t>(ws, W.xplanes); ra.xscale = at<float>(ws, W.xscale);
+        ra.table = table; ra.shared_blob = shared_blob;
+        ra.phase_mask = nullptr; ra.phase = 0;
+        ra.T = T; ra.E = E; ra.k = k; ra.H = H;
+        st = launch_router_small(ra, stream);
+        if (st) return st;
+        const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
+        st = launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
+                             at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
+                             at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
+                             at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale),
+                             at<float>(ws, W.y_rows), H, I, s->group, stream);
+        if (st) return st;
+        return launch_combine(at<float>(ws, W.y_rows), w, T, k, H, shared_blob ? 1 : 0,
+                              s->routed_scale, y, stream);
+    }
     const float* lg = logits;
     if (!lg) {
         st = launch_router_logits(router_w, x, T, H, E, at<float>(ws, W.logits), stream);
         if (st) return st;
         lg = at<float>(ws, W.logits);
     }
-    int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, W.idx);
-    float* w = w_out ? w_out : at<float>(ws, W.w);
     st = launch_route(lg, bias, T, E, k, idx, w, stream);
     if (st) return st;
     st = launch_union(idx, T, k, E, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),

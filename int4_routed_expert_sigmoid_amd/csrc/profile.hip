@@ -1,14 +1,13 @@
-// Optional kernel timing with HIP events, recorded on the stream each kernel
-// is launched on. Off unless coli_profile_enable() pre-allocates a pool;
-// every profiled launch then takes the next (start, stop) pair, so a captured
-// graph gets distinct events per kernel instance.
+// Optional kernel timing: HIP events attached to the dispatch of tagged
+// kernels (hipExtLaunchKernel start/stop events). Off unless
+// coli_profile_enable() pre-allocates a pool; every timed launch takes the
+// next (start, stop) pair.
 #include <map>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "common.h"
-#include "profile.h"
 
 namespace coli {
 namespace {
@@ -32,23 +31,21 @@ ProfState& state() {
 
 }  // namespace
 
-int prof_start(hipStream_t stream) {
-    ProfState& P = state();
-    std::lock_guard<std::mutex> g(P.mu);
-    if (P.capacity == 0 || P.recs.size() >= P.capacity) return -1;
-    const size_t i = P.recs.size();
-    Record r{nullptr, P.pool[2 * i], P.pool[2 * i + 1]};
-    if (hipEventRecord(r.start, stream) != hipSuccess) return -1;
-    P.recs.push_back(r);
-    return (int)i;
-}
+static thread_local const char* t_pending = nullptr;
 
-void prof_stop(int slot, const char* name, hipStream_t stream) {
-    if (slot < 0) return;
+void prof_tag(const char* name) { t_pending = name; }
+const char* prof_pending() { return t_pending; }
+
+bool prof_take(const char* name, hipEvent_t* start, hipEvent_t* stop) {
     ProfState& P = state();
     std::lock_guard<std::mutex> g(P.mu);
-    P.recs[(size_t)slot].name = name;
-    (void)hipEventRecord(P.recs[(size_t)slot].stop, stream);
+    if (P.capacity == 0 || P.recs.size() >= P.capacity) return false;
+    const size_t i = P.recs.size();
+    Record r{name, P.pool[2 * i], P.pool[2 * i + 1]};
+    P.recs.push_back(r);
+    *start = r.start;
+    *stop = r.stop;
+    return true;
 }
 
 }  // namespace coli

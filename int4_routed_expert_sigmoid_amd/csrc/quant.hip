@@ -117,14 +117,14 @@ coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t 
                         (cols % 8 == 0) ? 1 : 0;
     if (group == 0) {
         if (rows > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: too many rows");
-        hipLaunchKernelGGL(quant_row_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, rows,
+        launch(quant_row_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, rows,
                            cols, q, s, aligned);
     } else {
         // the group of 8 lanes must not straddle rows: cols % 64 == 0 is required
         const int64_t total = rows * (cols / 8);
         const int64_t blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: tensor too large");
-        hipLaunchKernelGGL(quant_g64_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, rows,
+        launch(quant_g64_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, rows,
                            cols, q, s, aligned);
     }
     COLI_CHECK_LAUNCH("quantize kernel launch");

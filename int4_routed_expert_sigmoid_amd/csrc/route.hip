@@ -7,6 +7,8 @@
 // adjusts the selection, and routing, selection and scaling semantics must be
 // reproduced exactly. config.json values quoted by the int8-MTP page:
 // scoring_func sigmoid, norm_topk_prob true.
+#include <algorithm>
+
 #include "common.h"
 
 namespace coli {
@@ -32,17 +34,25 @@ __global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ w
 
 constexpr int kMaxExpertsPerLane = 16;   // E <= 1024
 
-// One wave per token. Lane l holds experts l, l+64, ... . k rounds of a wave
-// arg-max over (key descending, index ascending) pick the experts in slot
-// order; the weights are normalised in double in slot order.
+template <int S>
+__device__ __forceinline__ void argmax_step(float& bk, int& bi) {
+    const float ok = __int_as_float(lane_xchg<S>(__float_as_int(bk)));
+    const int oi = lane_xchg<S>(bi);
+    if (oi != 0x7fffffff && (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi))) {
+        bk = ok;
+        bi = oi;
+    }
+}
+
+// Route one token with one wave. Lane l holds experts l, l+64, ... . k rounds
+// of a wave arg-max over (key descending, index ascending) pick the experts
+// in slot order; the weights are normalised in double in slot order.
 template <int EPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
-                                                    const float* __restrict__ bias, int T, int E,
-                                                    int k, int* __restrict__ idx,
-                                                    float* __restrict__ w) {
+__device__ __forceinline__ void route_token(const float* __restrict__ lrow,
+                                            const float* __restrict__ bias, int E, int k,
+                                            int* __restrict__ idx_row, float* __restrict__ w_row,
+                                            int* lds_idx = nullptr) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
     float score[EPL], key[EPL];
     bool avail[EPL];
 #pragma unroll
@@ -52,7 +62,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         score[i] = 0.f;
         key[i] = 0.f;
         if (avail[i]) {
-            const double l = (double)logits[(int64_t)t * E + e];
+            const double l = (double)lrow[e];
             score[i] = (float)(1.0 / (1.0 + exp(-l)));
             key[i] = score[i] + (bias ? bias[e] : 0.f);
         }
@@ -61,7 +71,6 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     float my_sel = 0.f;      // lane j (< k) keeps the score of slot j
     int my_idx = 0;
     for (int j = 0; j < k; ++j) {
-        // best candidate of this lane
         float bk = 0.f;
         int bi = 0x7fffffff;
 #pragma unroll
@@ -70,28 +79,219 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
             const int e = lane + 64 * i;
             if (bi == 0x7fffffff || key[i] > bk) { bk = key[i]; bi = e; }
         }
-        // wave arg-max: larger key wins, equal keys go to the lower index
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ok = __shfl_xor(bk, o);
-            const int oi = __shfl_xor(bi, o);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi))) {
-                bk = ok;
-                bi = oi;
-            }
-        }
-        const int owner = bi & 63, slot = bi >> 6;
+        // wave arg-max (all lanes get the winner): larger key wins, equal
+        // keys go to the lower index; partners exchanged with DPP/permlane
+        argmax_step<1>(bk, bi);
+        argmax_step<2>(bk, bi);
+        argmax_step<4>(bk, bi);
+        argmax_step<8>(bk, bi);
+        argmax_step<16>(bk, bi);
+        argmax_step<32>(bk, bi);
+        const int owner = __builtin_amdgcn_readfirstlane(bi & 63), slot = bi >> 6;
         float s_sel = 0.f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             if (i == slot && lane == owner) { avail[i] = false; s_sel = score[i]; }
-        s_sel = __shfl(s_sel, owner);
+        s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_sel), owner));
         sum += (double)s_sel;
         if (lane == j) { my_sel = s_sel; my_idx = bi; }
     }
     if (lane < k) {
-        idx[(int64_t)t * k + lane] = my_idx;
-        w[(int64_t)t * k + lane] = (sum == 0.0) ? (float)(1.0 / k) : (float)((double)my_sel / sum);
+        idx_row[lane] = my_idx;
+        w_row[lane] = (sum == 0.0) ? (float)(1.0 / k) : (float)((double)my_sel / sum);
+        if (lds_idx) lds_idx[lane] = my_idx;
+    }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int T, int E,
+                                                    int k, int* __restrict__ idx,
+                                                    float* __restrict__ w) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    route_token<EPL>(logits + (int64_t)t * E, bias, E, k, idx + (int64_t)t * k, w + (int64_t)t * k);
+}
+
+// ----------------------------------------------------- router, small T
+// Two launches for batches of up to kSmallT tokens. The first spreads over
+// many workgroups: each computes the logits of one expert (f32 router rows,
+// double sums) and encodes a share of the activations into digit planes.
+// The second is one workgroup: it routes the tokens, forms the batch union
+// (stable counting sort) and writes the FFN work list.
+constexpr int kRouterThreads = 256;
+
+__device__ __forceinline__ double block_sum_f64(double v, double* sh) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    return sh[0] + sh[1] + sh[2] + sh[3];
+}
+
+__global__ __launch_bounds__(kRouterThreads) void router_prep_kernel(SmallRouterArgs a) {
+    __shared__ double shd[4];
+    const int tid = threadIdx.x;
+    const int T = a.T, E = a.E, H = a.H;
+    if (a.router_w && (int)blockIdx.x < E) {
+        const int e = blockIdx.x;
+        const float* wrow = a.router_w + (int64_t)e * H;
+        for (int t = 0; t < T; ++t) {
+            const float* xrow = a.x + (int64_t)t * H;
+            double acc = 0.0;
+            for (int j = tid * 4; j < H; j += kRouterThreads * 4) {
+                const float4 wv = *reinterpret_cast<const float4*>(wrow + j);
+                const float4 xv = *reinterpret_cast<const float4*>(xrow + j);
+                acc = fma((double)wv.x, (double)xv.x, acc);
+                acc = fma((double)wv.y, (double)xv.y, acc);
+                acc = fma((double)wv.z, (double)xv.z, acc);
+                acc = fma((double)wv.w, (double)xv.w, acc);
+            }
+            acc = block_sum_f64(acc, shd);
+            if (tid == 0) a.logits_out[(int64_t)t * E + e] = (float)acc;
+        }
+    }
+    // digit-plane encoding of x: one quarter block per thread
+    const int C = H / kBlock;
+    const int64_t g = (int64_t)blockIdx.x * kRouterThreads + tid;
+    const int q = (int)(g & 3);
+    const int64_t blk = g >> 2;
+    const int64_t row = blk / C;
+    const int b = (int)(blk % C);
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const bool ok = row < T;
+    if (ok) {
+        const float* p = a.x + row * H + b * kBlock + q * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = p[i];
+    }
+    uint32_t words[kPlanes];
+    const float sc = encode_quarter(v, words);
+    if (ok) {
+        uint32_t* out = a.xplanes + (row * C + b) * kWordsPerBlock;
+#pragma unroll
+        for (int p = 0; p < kPlanes; ++p) out[p * 4 + q] = words[p];
+        if (q == 0) a.xscale[row * C + b] = sc;
+    }
+}
+
+// Exclusive prefix sum over the 256 threads of the block (v >= 0); *total
+// receives the sum. Wave scans by shuffles, then one pass over wave totals.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += sh[w];
+    *total = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return base + incl - v;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouterArgs a) {
+    constexpr int EPT = 4;                  // experts per thread (E <= 1024)
+    __shared__ int s_idx[kSmallT * 32];
+    __shared__ int s_cnt[1024];
+    __shared__ int s_off[1024];
+    __shared__ int s_uniq[1024];
+    __shared__ int s_scan[4];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int T = a.T, E = a.E, k = a.k;
+    const float* lg = a.router_w ? a.logits_out : a.logits_in;
+    for (int t = wave; t < T; t += kRouterThreads / 64)
+        route_token<EPL>(lg + (int64_t)t * E, a.bias, E, k, a.idx + (int64_t)t * k,
+                         a.w + (int64_t)t * k, s_idx + t * k);
+    for (int e = tid; e < E; e += kRouterThreads) s_cnt[e] = 0;
+    __syncthreads();
+    // batch union of the n = T*k assignments (stable counting sort)
+    const int n = T * k;
+    for (int i = tid; i < n; i += kRouterThreads) atomicAdd(&s_cnt[s_idx[i]], 1);
+    __syncthreads();
+    // offsets and unique list: thread tid owns experts tid*EPT .. tid*EPT+3
+    int c[EPT], sum = 0, nz = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        c[i] = e < E ? s_cnt[e] : 0;
+        sum += c[i];
+        nz += c[i] > 0 ? 1 : 0;
+    }
+    int total = 0, nu = 0;
+    int off = block_excl_scan(sum, s_scan, &total);
+    int upos = block_excl_scan(nz, s_scan, &nu);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        if (e < E) {
+            a.counts[e] = c[i];
+            a.offsets[e] = off;
+            s_off[e] = off;
+            if (c[i] > 0) { a.unique[upos] = e; s_uniq[upos] = e; ++upos; }
+            off += c[i];
+        }
+    }
+    if (tid == 0) {
+        a.offsets[E] = total;
+        *a.n_unique = nu;
+    }
+    __syncthreads();
+    // work items: the shared expert first, then the unique experts (of one phase)
+    const int base = a.shared_blob ? 1 : 0;
+    if (tid == 0 && a.shared_blob) {
+        WorkItem it;
+        it.blob = (const uint8_t*)a.shared_blob;
+        it.begin = n;
+        it.count = T;
+        a.items[0] = it;
+    }
+    int keep[EPT], nk = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int u = tid * EPT + i;
+        keep[i] = 0;
+        if (u < nu) {
+            const int e = s_uniq[u];
+            keep[i] = (a.phase_mask == nullptr || a.phase_mask[e] == a.phase) ? 1 : 0;
+        }
+        nk += keep[i];
+    }
+    int nkeep = 0;
+    int kpos = block_excl_scan(nk, s_scan, &nkeep);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int u = tid * EPT + i;
+        if (keep[i]) {
+            const int e = s_uniq[u];
+            WorkItem it;
+            it.blob = (const uint8_t*)a.table[e];
+            it.begin = s_off[e];
+            it.count = s_cnt[e];
+            a.items[base + kpos++] = it;
+        }
+    }
+    if (tid == 0) *a.n_items = base + nkeep;
+    // stable positions: rank of assignment i among earlier equal experts
+    for (int i = tid; i < n; i += kRouterThreads) {
+        const int e = s_idx[i];
+        int r = 0;
+        for (int j = 0; j < i; ++j) r += (s_idx[j] == e) ? 1 : 0;
+        const int p = s_off[e] + r;
+        a.perm[p] = i;
+        a.rows_tok[p] = i / k;
+        a.rows_out[p] = i;
+    }
+    for (int t = tid; t < T; t += kRouterThreads) {
+        a.rows_tok[n + t] = t;
+        a.rows_out[n + t] = n + t;
     }
 }
 
@@ -101,9 +301,26 @@ coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int
                                  float* logits, hipStream_t stream) {
     const int64_t pairs = (int64_t)T * E;
     if (pairs == 0) return COLI_OK;
-    hipLaunchKernelGGL(logits_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, wr,
+    launch(logits_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, wr,
                        x, T, H, E, logits);
     COLI_CHECK_LAUNCH("router logits kernel launch");
+    return COLI_OK;
+}
+
+coli_status launch_router_small(const SmallRouterArgs& a, hipStream_t stream) {
+    const int C = a.H / kBlock;
+    const int enc_blocks = (int)(((int64_t)a.T * C * 4 + kRouterThreads - 1) / kRouterThreads);
+    const int grid = std::max(a.router_w ? a.E : 1, enc_blocks);
+    launch(router_prep_kernel, dim3(grid), dim3(kRouterThreads), 0, stream, a);
+    COLI_CHECK_LAUNCH("router prep kernel launch");
+    const int epl = (a.E + 63) / 64;
+    const dim3 one(1), blk(kRouterThreads);
+    if (epl <= 1) launch(router_plan_kernel<1>, one, blk, 0, stream, a);
+    else if (epl <= 2) launch(router_plan_kernel<2>, one, blk, 0, stream, a);
+    else if (epl <= 4) launch(router_plan_kernel<4>, one, blk, 0, stream, a);
+    else if (epl <= 8) launch(router_plan_kernel<8>, one, blk, 0, stream, a);
+    else launch(router_plan_kernel<16>, one, blk, 0, stream, a);
+    COLI_CHECK_LAUNCH("router plan kernel launch");
     return COLI_OK;
 }
 
@@ -112,11 +329,11 @@ coli_status launch_route(const float* logits, const float* bias, int32_t T, int3
     if (T == 0) return COLI_OK;
     const dim3 grid((T + 3) / 4), block(256);
     const int epl = (E + 63) / 64;
-    if (epl <= 1) hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= 2) hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= 4) hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= 8) hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= kMaxExpertsPerLane) hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
+    if (epl <= 1) launch(route_kernel<1>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
+    else if (epl <= 2) launch(route_kernel<2>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
+    else if (epl <= 4) launch(route_kernel<4>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
+    else if (epl <= 8) launch(route_kernel<8>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
+    else if (epl <= kMaxExpertsPerLane) launch(route_kernel<16>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
     else return fail(COLI_EUNSUPPORTED, "route: more than 1024 experts");
     COLI_CHECK_LAUNCH("route kernel launch");
     return COLI_OK;

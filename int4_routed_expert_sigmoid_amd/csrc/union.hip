@@ -173,7 +173,7 @@ coli_status launch_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, in
     const size_t C = ((size_t)n + 63) / 64;
     int32_t* chunk_cnt = (int32_t*)ws;
     int32_t* rank = (int32_t*)((char*)ws + align256(C * (size_t)E * 4));
-    hipLaunchKernelGGL(union_kernel, dim3(1), dim3(kUnionThreads), 0, stream, idx, n, E, counts,
+    launch(union_kernel, dim3(1), dim3(kUnionThreads), 0, stream, idx, n, E, counts,
                        offsets, perm, unique, n_unique, chunk_cnt, rank);
     COLI_CHECK_LAUNCH("union kernel launch");
     return COLI_OK;
@@ -185,7 +185,7 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
                         int32_t k, int32_t E, const uint8_t* phase_mask, int32_t phase,
                         WorkItem* items, int32_t* n_items, int32_t* rows_tok, int32_t* rows_out,
                         hipStream_t stream) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, offsets, perm, unique,
+    launch(plan_kernel, dim3(1), dim3(256), 0, stream, offsets, perm, unique,
                        n_unique, blob_table, shared_blob, T, k, E, phase_mask, phase, items,
                        n_items, rows_tok, rows_out);
     COLI_CHECK_LAUNCH("plan kernel launch");

@@ -1,0 +1,78 @@
+"""Properties of the GEMV path that hold at any size.
+
+- Batch invariance: a token's layer output does not depend on the batch it
+  is computed in (the draft/verify lesson of the practical guide, section 二:
+  both must compute the same function). Per token, the integer block sums are
+  exact and the float reductions run in the same order for any batch, so the
+  outputs must be bit-identical.
+- Reuse: the same workspace serves consecutive calls (its counters return to
+  zero), and repeated calls give identical bits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import ExpertSet, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def coli():
+    import int4_routed_expert_sigmoid_amd as c
+    c.lib()
+    return c
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+@pytest.fixture(scope="module")
+def layer_setup(coli):
+    H, I, E, k, T = 2048, 512, 64, 8, 17
+    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0)
+    ex = ExpertSet(coli, shape, seed=21)
+    x = synth.activations(21, 0, 0, T, H)
+    lg = synth.zipf_logits(21, 0, 0, T, E, s=1.1)
+    b = synth.bias(21, 0, E)
+    return shape, ex, x, lg, b
+
+
+@pytest.mark.parametrize("batch", [8, 17])
+def test_batch_invariance(coli, layer_setup, batch):
+    import torch
+    shape, ex, x, lg, b = layer_setup
+    ws = coli.workspace(shape, 17, coli.PATH_GEMV)
+    singles = []
+    for t in range(batch):
+        y = coli.layer_fwd(shape, _dev(x[t:t + 1]), table=ex.table, shared_blob=ex.shared_blob,
+                           logits=_dev(lg[t:t + 1]), bias=_dev(b), path=coli.PATH_GEMV, ws=ws)
+        singles.append(y)
+    yb = coli.layer_fwd(shape, _dev(x[:batch]), table=ex.table, shared_blob=ex.shared_blob,
+                        logits=_dev(lg[:batch]), bias=_dev(b), path=coli.PATH_GEMV, ws=ws)
+    torch.cuda.synchronize()
+    ys = torch.cat(singles).cpu().numpy()
+    assert np.array_equal(yb.cpu().numpy(), ys)
+    _, y64, _, _ = oracle.layer(x[:batch], ex.oracle_list(), ex.shared_oracle, shape.top_k, 0, 1.0,
+                                logits=lg[:batch], bias=b)
+    assert rel_l2_rows(ys, y64).max() <= 1e-3
+
+
+def test_workspace_reuse_and_repeatability(coli, layer_setup):
+    import torch
+    shape, ex, x, lg, b = layer_setup
+    ws = coli.workspace(shape, 8, coli.PATH_GEMV)
+    outs = []
+    for _ in range(3):
+        y = coli.layer_fwd(shape, _dev(x[:8]), table=ex.table, shared_blob=ex.shared_blob,
+                           logits=_dev(lg[:8]), bias=_dev(b), path=coli.PATH_GEMV, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    # a stale arrival counter would skip the fused combine and leave y unwritten
+    _, y64, _, _ = oracle.layer(x[:8], ex.oracle_list(), ex.shared_oracle, shape.top_k, 0, 1.0,
+                                logits=lg[:8], bias=b)
+    assert rel_l2_rows(outs[2], y64).max() <= 1e-3
