@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="replay the timed tokens from a HIP graph")
     ap.add_argument("--cpu-sample", type=int, default=8, help="tokens of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
     return ap.parse_args()
 
 
@@ -99,6 +100,55 @@ def cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept):
             "sample": f"first {sample} tokens of the decode workload, whole layer (router logits, "
                       f"route, union, 9 expert FFNs, combine), scalar C, f64 accumulation, "
                       f"OpenMP over output rows; {dt:.2f} s"}
+
+
+def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
+    """2048-token prefill through the same layer: Zipf(1.1) + 10% uniform
+    routing (router logits with that popularity), bf16 MFMA grouped GEMM."""
+    import torch
+    import synth
+    H, I, E, k, T = shape.hidden, shape.inter, shape.n_routed, shape.top_k, 2048
+    lg = torch.from_numpy(synth.zipf_logits(seed, 1, 0, T, E, s=1.1, mix=0.1)).to(dev)
+    x = torch.from_numpy(synth.activations(seed, 1, 0, T, H)).to(dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = coli.workspace(shape, T, coli.PATH_MFMA, dev)
+
+    def call():
+        coli.layer_fwd(shape, x, table=table, shared_blob=shared, logits=lg, y=y, idx_out=idx,
+                       path=coli.PATH_MFMA, ws=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    coli.profile_enable(2 * calls + 8)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / calls
+    n_gu, ms_gu = coli.profile_summary("gemm_gateup")
+    n_dn, ms_dn = coli.profile_summary("gemm_down")
+    coli.profile_enable(0)
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=E)
+    flops_gu = 2.0 * 2 * H * I * (T * k + T)
+    flops_dn = 2.0 * H * I * (T * k + T)
+    gu_s, dn_s = ms_gu / max(1, n_gu) / 1e3, ms_dn / max(1, n_dn) / 1e3
+    return {
+        "workload": "prefill, 2048 tokens, Zipf(1.1) + 10% uniform routing, same layer",
+        "tokens_per_s": round(T / dt, 1),
+        "ms_per_call": round(dt * 1e3, 4),
+        "tflops_layer": round((flops_gu + flops_dn) / dt / 1e12, 2),
+        "gemm_gateup_us": round(gu_s * 1e6, 2),
+        "gemm_down_us": round(dn_s * 1e6, 2),
+        "gemm_tflops": round((flops_gu + flops_dn) / (gu_s + dn_s) / 1e12, 2) if n_gu else None,
+        "gemm_frac_of_bf16_peak": round((flops_gu + flops_dn) / (gu_s + dn_s) / 1e12 / BF16_PEAK_TFLOPS, 4) if n_gu else None,
+        "algorithmic_tflop": round((flops_gu + flops_dn) / 1e12, 4),
+        "experts_used": int((counts > 0).sum()),
+        "tokens_per_expert_max": int(counts.max()),
+        "tokens_per_expert_median": float(np.median(counts[counts > 0])),
+        "tokens_per_expert_min": int(counts[counts > 0].min()),
+    }
 
 
 def main():
@@ -190,6 +240,11 @@ def main():
     gemv_gbps = (gu_bytes + dn_bytes) / (gu_avg_s + dn_avg_s) / 1e9 if n_gu and n_dn else None
     tok_s = args.steps / elapsed
 
+    prefill = None
+    if not args.no_prefill:
+        log("prefill: 2048 tokens through the same layer (bf16 MFMA)")
+        prefill = run_prefill(coli, shape, table, shared, seed, dev)
+
     cpu = None
     if sample:
         cpu = cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept)
@@ -222,6 +277,7 @@ def main():
                         "down_GBps": dn_gbps and round(dn_gbps, 1),
                         "both_GBps": gemv_gbps and round(gemv_gbps, 1),
                         "down_avg_us": round(dn_avg_s * 1e6, 3)},
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

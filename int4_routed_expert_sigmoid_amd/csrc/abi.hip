@@ -1,10 +1,12 @@
 // C ABI of libcoli_moe: argument checks, workspace carving and the launch
 // sequence of each call (include/coli_moe.h documents every entry point).
+#include <algorithm>
 #include <exception>
 #include <new>
 #include <string>
 
 #include "common.h"
+#include "gemm.h"
 #include "layer.h"
 
 namespace coli {
@@ -68,6 +70,15 @@ WsLayout ws_layout(const coli_moe_shape* s, int32_t T, int32_t path) {
     W.hscale = take(R * (I / kBlock) * 4);
     W.y_rows = take(R * H * 4);
     W.phase = take(E);
+    // bf16 MFMA path
+    const size_t max_items = std::min<size_t>(E, n) + 1;
+    W.max_tiles = gemm_tiles_max((int32_t)R, (int32_t)max_items);
+    W.tiles = take(W.max_tiles * 8);
+    W.n_tiles = take(4);
+    W.xb = take((size_t)T * H * 2);
+    W.sx = take((size_t)T * (H / 64) * 4);
+    W.hb = take(R * I * 2);
+    W.sh = take(R * (I / 64) * 4);
     W.bytes = o;
     return W;
 }

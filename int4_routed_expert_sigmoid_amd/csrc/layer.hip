@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <vector>
 
+#include "gemm.h"
 #include "gemv.h"
 #include "layer.h"
 
@@ -15,24 +16,69 @@ namespace coli {
 template <typename T>
 static T* at(uint8_t* ws, size_t off) { return reinterpret_cast<T*>(ws + off); }
 
+// Decide the FFN path: the GEMV family for small batches, the bf16 MFMA
+// grouped GEMM for large ones (auto), or the caller's choice.
+static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, bool* mfma) {
+    const bool shape_ok = s->hidden % 64 == 0 && s->inter % 64 == 0;
+    if (path == COLI_PATH_MFMA) {
+        if (!shape_ok) return fail(COLI_EUNSUPPORTED, "mfma path: hidden and inter must be multiples of 64");
+        *mfma = true;
+    } else if (path == COLI_PATH_GEMV) {
+        *mfma = false;
+    } else {
+        *mfma = shape_ok && T > kSmallT;
+    }
+    return COLI_OK;
+}
+
+static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, int32_t T,
+                           int32_t max_items, float* y_rows, uint8_t* ws, const WsLayout& W,
+                           bool x_encoded, hipStream_t stream) {
+    const int32_t H = s->hidden, I = s->inter;
+    if (mfma) {
+        GemmArgs g;
+        g.items = at<WorkItem>(ws, W.items);
+        g.n_items = at<int32_t>(ws, W.n_items);
+        g.rows_tok = at<int32_t>(ws, W.rows_tok);
+        g.rows_out = at<int32_t>(ws, W.rows_out);
+        g.tiles = at<int2>(ws, W.tiles);
+        g.n_tiles = at<int32_t>(ws, W.n_tiles);
+        g.xb = at<uint16_t>(ws, W.xb);
+        g.sx = at<float>(ws, W.sx);
+        g.hb = at<uint16_t>(ws, W.hb);
+        g.sh = at<float>(ws, W.sh);
+        g.y_rows = y_rows;
+        g.L = blob_layout(H, I, s->group);
+        g.H = H; g.I = I; g.group = s->group;
+        const int32_t max_tiles = (int32_t)gemm_tiles_max(
+            (int32_t)((int64_t)T * s->top_k + T), max_items);
+        return launch_mfma_ffn(g, x, T, max_tiles, stream);
+    }
+    if (!x_encoded) {
+        coli_status st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
+        if (st) return st;
+    }
+    return launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
+                           at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
+                           at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
+                           at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_rows, H, I,
+                           s->group, stream);
+}
+
 coli_status run_expert_ffn(const coli_moe_shape* s, const void* const* table, const float* x,
                            int32_t T, const int32_t* offsets, const int32_t* perm,
                            const int32_t* unique, const int32_t* n_unique, float* y_assign,
                            int32_t path, uint8_t* ws, const WsLayout& W, hipStream_t stream) {
-    (void)path;
-    const int32_t H = s->hidden, I = s->inter, E = s->n_routed, k = s->top_k;
-    coli_status st = launch_plan(offsets, perm, unique, n_unique, table, nullptr, T, k, E, nullptr,
-                                 0, at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items),
-                                 at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
+    const int32_t E = s->n_routed, k = s->top_k;
+    bool mfma = false;
+    coli_status st = pick_mfma(s, T, path, &mfma);
     if (st) return st;
-    st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
+    st = launch_plan(offsets, perm, unique, n_unique, table, nullptr, T, k, E, nullptr, 0,
+                     at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items),
+                     at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
     if (st) return st;
-    const int32_t max_items = std::min<int64_t>(E, (int64_t)T * k);
-    return launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
-                           at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
-                           at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
-                           at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_assign, H, I,
-                           s->group, stream);
+    const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k);
+    return run_ffn(s, mfma, x, T, max_items, y_assign, ws, W, false, stream);
 }
 
 coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const float* logits,
@@ -40,15 +86,17 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
                       const void* shared_blob, struct coli_expert_cache* cache, int32_t layer,
                       float* y, int32_t* idx_out, float* w_out, int32_t path, uint8_t* ws,
                       const WsLayout& W, hipStream_t stream) {
-    (void)path;
-    const int32_t H = s->hidden, I = s->inter, E = s->n_routed, k = s->top_k;
+    const int32_t H = s->hidden, E = s->n_routed, k = s->top_k;
     if (cache) return fail(COLI_EUNSUPPORTED, "layer_fwd: expert cache not available yet");
     (void)layer;
-    coli_status st;
+    bool mfma = false;
+    coli_status st = pick_mfma(s, T, path, &mfma);
+    if (st) return st;
     int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, W.idx);
     float* w = w_out ? w_out : at<float>(ws, W.w);
-    if (T <= kSmallT && path != COLI_PATH_MFMA) {
-        // three launches: fused router, gate/up GEMV, down GEMV with the combine
+    bool encoded = false;
+    if (T <= kSmallT) {
+        // router: logits + activation encoding, then route / union / work list
         SmallRouterArgs ra;
         ra.x = x; ra.router_w = router_w; ra.logits_in = logits; ra.bias = bias;
         ra.logits_out = at<float>(ws, W.logits);
@@ -64,41 +112,29 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
         ra.T = T; ra.E = E; ra.k = k; ra.H = H;
         st = launch_router_small(ra, stream);
         if (st) return st;
-        const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
-        st = launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
-                             at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
-                             at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
-                             at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale),
-                             at<float>(ws, W.y_rows), H, I, s->group, stream);
+        encoded = true;
+    } else {
+        const float* lg = logits;
+        if (!lg) {
+            st = launch_router_logits(router_w, x, T, H, E, at<float>(ws, W.logits), stream);
+            if (st) return st;
+            lg = at<float>(ws, W.logits);
+        }
+        st = launch_route(lg, bias, T, E, k, idx, w, stream);
         if (st) return st;
-        return launch_combine(at<float>(ws, W.y_rows), w, T, k, H, shared_blob ? 1 : 0,
-                              s->routed_scale, y, stream);
-    }
-    const float* lg = logits;
-    if (!lg) {
-        st = launch_router_logits(router_w, x, T, H, E, at<float>(ws, W.logits), stream);
+        st = launch_union(idx, T, k, E, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
+                          at<int32_t>(ws, W.perm), at<int32_t>(ws, W.unique),
+                          at<int32_t>(ws, W.n_unique), ws + W.union_ws, stream);
         if (st) return st;
-        lg = at<float>(ws, W.logits);
+        st = launch_plan(at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.perm),
+                         at<int32_t>(ws, W.unique), at<int32_t>(ws, W.n_unique), table,
+                         shared_blob, T, k, E, nullptr, 0, at<WorkItem>(ws, W.items),
+                         at<int32_t>(ws, W.n_items), at<int32_t>(ws, W.rows_tok),
+                         at<int32_t>(ws, W.rows_out), stream);
+        if (st) return st;
     }
-    st = launch_route(lg, bias, T, E, k, idx, w, stream);
-    if (st) return st;
-    st = launch_union(idx, T, k, E, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
-                      at<int32_t>(ws, W.perm), at<int32_t>(ws, W.unique), at<int32_t>(ws, W.n_unique),
-                      ws + W.union_ws, stream);
-    if (st) return st;
-    st = launch_plan(at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.perm), at<int32_t>(ws, W.unique),
-                     at<int32_t>(ws, W.n_unique), table, shared_blob, T, k, E, nullptr, 0,
-                     at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items),
-                     at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
-    if (st) return st;
-    st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
-    if (st) return st;
     const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
-    st = launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
-                         at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
-                         at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
-                         at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale),
-                         at<float>(ws, W.y_rows), H, I, s->group, stream);
+    st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W, encoded, stream);
     if (st) return st;
     return launch_combine(at<float>(ws, W.y_rows), w, T, k, H, shared_blob ? 1 : 0,
                           s->routed_scale, y, stream);

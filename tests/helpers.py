@@ -18,9 +18,11 @@ class ExpertSet:
     """Experts of one layer on both sides: oracle copies (host, quantised by the
     oracle) and device blobs (quantised by coli_quantize_expert from the same
     f32 weights). `which` limits generation to some experts; the others share
-    one zero blob on the device and have no oracle copy."""
+    one zero blob on the device and have no oracle copy. `keep_oracle` (set)
+    limits the oracle copies further, for large layers checked on samples."""
 
-    def __init__(self, coli, shape, seed=0, layer=0, which=None, dev="cuda", shared=True):
+    def __init__(self, coli, shape, seed=0, layer=0, which=None, dev="cuda", shared=True,
+                 keep_oracle=None):
         import torch
 
         import oracle
@@ -38,7 +40,8 @@ class ExpertSet:
         self.shared_oracle = None
         for e in ids:
             g, u, d = synth.expert_weights(seed, layer, e, H, I)
-            qe = oracle.QExpert.quantize(g, u, d, G)
+            host = keep_oracle is None or e in keep_oracle or e == E
+            qe = oracle.QExpert.quantize(g, u, d, G) if host else None
             blob = coli.quantize_expert(shape, torch.from_numpy(g).to(dev),
                                         torch.from_numpy(u).to(dev), torch.from_numpy(d).to(dev))
             if e == E:
