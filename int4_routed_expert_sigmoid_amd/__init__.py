@@ -277,7 +277,7 @@ def layer_fwd(shape: MoEShape, x, table=None, shared_blob=None, logits=None, rou
         ws = workspace(shape, T, path, x.device)
     _check(lib().coli_moe_layer_fwd(ctypes.byref(shape.c()), _ptr(x), T, _ptr(logits),
                                     _ptr(router_w), _ptr(bias), _ptr(table), _ptr(shared_blob),
-                                    _ptr(cache.handle if cache is not None else None), layer,
+                                    None if cache is None else ctypes.c_void_p(cache.handle), layer,
                                     _ptr(y), _ptr(idx_out), _ptr(w_out), path, _ptr(ws), ws.numel(),
                                     _stream(stream)))
     return y
@@ -297,3 +297,61 @@ def profile_summary(name: str):
     ms = ctypes.c_double()
     _check(lib().coli_profile_summary(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+class ExpertCache:
+    """Per-layer LRU of expert blobs in an HBM arena in front of pinned host
+    memory (coli_expert_cache_*). With arena and pool both None the cache only
+    keeps the books (policy simulation, no GPU needed)."""
+
+    def __init__(self, n_layers, n_experts, slots_per_layer, blob_bytes, arena=None, pool=None,
+                 copy_stream=None):
+        self.cfg = CacheCfg(n_layers, n_experts, slots_per_layer, blob_bytes,
+                            None if arena is None else arena.data_ptr(),
+                            None if pool is None else pool.data_ptr(),
+                            None if copy_stream is None else copy_stream.cuda_stream)
+        self._keep = (arena, pool, copy_stream)
+        h = ctypes.c_void_p()
+        _check(lib().coli_expert_cache_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self.handle = h.value
+        self.n_experts = n_experts
+
+    def close(self):
+        if self.handle:
+            lib().coli_expert_cache_destroy(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def ensure(self, layer, ids):
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        miss = np.zeros(len(ids), dtype=np.int32)
+        _check(lib().coli_expert_cache_ensure(ctypes.c_void_p(self.handle), layer,
+                                              ids.ctypes.data_as(ctypes.c_void_p), len(ids),
+                                              miss.ctypes.data_as(ctypes.c_void_p)))
+        return miss
+
+    def wait(self, layer, stream=None):
+        _check(lib().coli_expert_cache_wait(ctypes.c_void_p(self.handle), layer, _stream(stream)))
+
+    def release(self, layer, stream=None):
+        _check(lib().coli_expert_cache_release(ctypes.c_void_p(self.handle), layer,
+                                               _stream(stream)))
+
+    def table_ptr(self, layer) -> int:
+        p = ctypes.c_void_p()
+        _check(lib().coli_expert_cache_table(ctypes.c_void_p(self.handle), layer, ctypes.byref(p)))
+        return p.value
+
+    def stats(self) -> dict:
+        s = CacheStats()
+        _check(lib().coli_expert_cache_stats(ctypes.c_void_p(self.handle), ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in CacheStats._fields_}
+
+    def reset(self):
+        _check(lib().coli_expert_cache_reset(ctypes.c_void_p(self.handle)))

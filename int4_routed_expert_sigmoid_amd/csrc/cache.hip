@@ -1,27 +1,328 @@
-// Expert cache (placeholder entry points until the cache lands).
+// HBM expert cache: a per-layer LRU of expert blobs in a device arena, filled
+// from pinned host memory (practical guide section 二: per-layer LRU cache;
+// each expert's three matrices are adjacent so a miss is one read; missing
+// experts load while resident ones compute; a read in flight is never issued
+// twice; placement changes speed only, never routing or results).
+//
+// Host-side bookkeeping plus HIP copies and events:
+//  - ensure(): hits refresh their age; each miss takes the least recently used
+//    slot that this call does not use, makes the copy stream wait for the
+//    compute that last read that slot (its release event), and enqueues one
+//    host-to-device copy of the whole blob, followed by the slot's ready event.
+//  - wait(): the compute stream waits for the ready events of every slot the
+//    last ensure() named (completed events cost nothing).
+//  - release(): records, on the compute stream, the release event of those
+//    slots; a later eviction of any of them waits for it.
+// With a NULL arena and pool the cache only keeps the books (no copies, no
+// events): the policy can be simulated without a GPU.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
 #include "layer.h"
 
+struct coli_expert_cache {
+    coli_cache_cfg cfg;
+    bool dry = false;
+    struct Slot {
+        int32_t expert = -1;
+        uint64_t last_use = 0;
+        hipEvent_t ready = nullptr;       // after the copy that filled it
+        hipEvent_t release = nullptr;     // after the compute that last read it
+        bool release_recorded = false;
+    };
+    std::vector<std::vector<Slot>> slots;          // [layer][slot]
+    std::vector<std::vector<int32_t>> where;       // [layer][expert] -> slot or -1
+    std::vector<std::vector<int32_t>> used;        // [layer] slots named by the last ensure
+    void** d_tables = nullptr;                     // device [layer][expert]
+    uint8_t* h_slot_ptrs = nullptr;                // pinned: device address of every slot
+    uint64_t clock = 0;
+    coli_cache_stats st{};
+    // copy timing: ring of (start, stop) pairs, summed as they complete
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> timers;
+    std::vector<bool> timer_live;
+    size_t timer_next = 0;
+    // pinned staging of the cached layer call: routing read back, phase per expert
+    int32_t* h_idx = nullptr;
+    size_t h_idx_cap = 0;
+    uint8_t* h_phase = nullptr;        // [layer][expert]
+};
+
+namespace coli {
+
+static coli_status harvest_timer(coli_expert_cache* c, size_t i, bool wait) {
+    if (!c->timer_live[i]) return COLI_OK;
+    if (wait) COLI_CHECK_HIP(hipEventSynchronize(c->timers[i].second));
+    else if (hipEventQuery(c->timers[i].second) != hipSuccess) return COLI_OK;
+    float ms = 0.f;
+    COLI_CHECK_HIP(hipEventElapsedTime(&ms, c->timers[i].first, c->timers[i].second));
+    c->st.copy_ns += (uint64_t)(ms * 1e6);
+    c->timer_live[i] = false;
+    return COLI_OK;
+}
+
+coli_status cache_layer_table(coli_expert_cache* c, int32_t layer, int32_t n_experts,
+                              const void* const** table) {
+    if (!c || layer < 0 || layer >= c->cfg.n_layers) return fail(COLI_EINVAL, "cache: bad layer");
+    if (n_experts != c->cfg.n_experts) return fail(COLI_EINVAL, "cache: expert count differs from the layer shape");
+    if (c->dry) return fail(COLI_EINVAL, "cache: a bookkeeping-only cache has no device table");
+    *table = (const void* const*)(c->d_tables + (size_t)layer * c->cfg.n_experts);
+    return COLI_OK;
+}
+
+// Placement step of a cached layer call: read the routing back (blocking),
+// make the selected experts of `layer` resident, and upload the phase of each
+// selected expert (0: resident before the call, 1: copied by it) to d_phase.
+coli_status cache_place(coli_expert_cache* c, int32_t layer, const int32_t* d_idx, int32_t n,
+                        uint8_t* d_phase, int32_t* n_miss, hipStream_t stream) {
+    if (c->dry) return fail(COLI_EINVAL, "cache: a bookkeeping-only cache cannot serve layer calls");
+    if ((size_t)n > c->h_idx_cap) {
+        if (c->h_idx) COLI_CHECK_HIP(hipHostFree(c->h_idx));
+        c->h_idx = nullptr;
+        c->h_idx_cap = 0;
+        COLI_CHECK_HIP(hipHostMalloc((void**)&c->h_idx, sizeof(int32_t) * (size_t)n * 2, hipHostMallocDefault));
+        c->h_idx_cap = (size_t)n * 2;
+    }
+    COLI_CHECK_HIP(hipMemcpyAsync(c->h_idx, d_idx, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
+    COLI_CHECK_HIP(hipStreamSynchronize(stream));
+    std::vector<int32_t> miss((size_t)n);
+    coli_status st = coli_expert_cache_ensure(c, layer, c->h_idx, n, miss.data());
+    if (st) return st;
+    uint8_t* ph = c->h_phase + (size_t)layer * c->cfg.n_experts;
+    int32_t nm = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        ph[c->h_idx[i]] = miss[i] ? 1 : 0;
+        nm += miss[i];
+    }
+    *n_miss = nm;
+    // the previous upload from this layer's staging row finished before the
+    // synchronisation above
+    COLI_CHECK_HIP(hipMemcpyAsync(d_phase, ph, (size_t)c->cfg.n_experts, hipMemcpyHostToDevice, stream));
+    return COLI_OK;
+}
+
+}  // namespace coli
+
+using namespace coli;
+
 extern "C" {
-coli_status coli_expert_cache_create(const coli_cache_cfg*, struct coli_expert_cache**) {
-    return coli::fail(COLI_EUNSUPPORTED, "expert cache not available yet");
+
+COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct coli_expert_cache** out) {
+    try {
+        if (!cfg || !out) return fail(COLI_EINVAL, "cache_create: NULL argument");
+        if (cfg->n_layers <= 0 || cfg->n_experts <= 0 || cfg->n_experts > 1024 ||
+            cfg->slots_per_layer <= 0 || cfg->blob_bytes == 0)
+            return fail(COLI_EINVAL, "cache_create: bad sizes");
+        const bool dry = cfg->d_arena == nullptr && cfg->h_pool == nullptr;
+        if (!dry && (!cfg->d_arena || !cfg->h_pool))
+            return fail(COLI_EINVAL, "cache_create: give both arena and pool, or neither");
+        auto* c = new coli_expert_cache();
+        c->cfg = *cfg;
+        c->dry = dry;
+        const int L = cfg->n_layers, S = cfg->slots_per_layer, E = cfg->n_experts;
+        c->slots.assign(L, std::vector<coli_expert_cache::Slot>(S));
+        c->where.assign(L, std::vector<int32_t>(E, -1));
+        c->used.assign(L, {});
+        if (!dry) {
+            auto cleanup = [&](coli_status code, const char* what) {
+                coli_expert_cache_destroy(c);
+                return fail(code, what);
+            };
+            if (hipMalloc((void**)&c->d_tables, sizeof(void*) * (size_t)L * E) != hipSuccess)
+                return cleanup(COLI_EHIP, "cache_create: device table allocation failed");
+            if (hipMemset(c->d_tables, 0, sizeof(void*) * (size_t)L * E) != hipSuccess)
+                return cleanup(COLI_EHIP, "cache_create: device table clear failed");
+            if (hipHostMalloc((void**)&c->h_slot_ptrs, sizeof(void*) * (size_t)L * S, hipHostMallocDefault) != hipSuccess)
+                return cleanup(COLI_EHIP, "cache_create: pinned slot table allocation failed");
+            for (int l = 0; l < L; ++l)
+                for (int s = 0; s < S; ++s) {
+                    void* p = (uint8_t*)cfg->d_arena + ((size_t)l * S + s) * cfg->blob_bytes;
+                    std::memcpy(c->h_slot_ptrs + ((size_t)l * S + s) * sizeof(void*), &p, sizeof(void*));
+                    auto& sl = c->slots[l][s];
+                    if (hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming) != hipSuccess ||
+                        hipEventCreateWithFlags(&sl.release, hipEventDisableTiming) != hipSuccess)
+                        return cleanup(COLI_EHIP, "cache_create: event creation failed");
+                }
+            if (hipHostMalloc((void**)&c->h_phase, (size_t)L * E, hipHostMallocDefault) != hipSuccess)
+                return cleanup(COLI_EHIP, "cache_create: pinned phase table allocation failed");
+            std::memset(c->h_phase, 0, (size_t)L * E);
+            c->timers.resize(64);
+            c->timer_live.assign(64, false);
+            for (auto& t : c->timers)
+                if (hipEventCreate(&t.first) != hipSuccess || hipEventCreate(&t.second) != hipSuccess)
+                    return cleanup(COLI_EHIP, "cache_create: event creation failed");
+        }
+        *out = c;
+        return COLI_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(COLI_ENOMEM, "cache_create: host allocation failed");
+    }
 }
-coli_status coli_expert_cache_destroy(struct coli_expert_cache*) { return COLI_OK; }
-coli_status coli_expert_cache_ensure(struct coli_expert_cache*, int32_t, const int32_t*, int32_t, int32_t*) {
-    return coli::fail(COLI_EUNSUPPORTED, "expert cache not available yet");
+
+COLI_API coli_status coli_expert_cache_destroy(struct coli_expert_cache* c) {
+    if (!c) return COLI_OK;
+    if (!c->dry) (void)hipDeviceSynchronize();
+    for (auto& layer : c->slots)
+        for (auto& s : layer) {
+            if (s.ready) (void)hipEventDestroy(s.ready);
+            if (s.release) (void)hipEventDestroy(s.release);
+        }
+    for (auto& t : c->timers) {
+        if (t.first) (void)hipEventDestroy(t.first);
+        if (t.second) (void)hipEventDestroy(t.second);
+    }
+    if (c->d_tables) (void)hipFree(c->d_tables);
+    if (c->h_slot_ptrs) (void)hipHostFree(c->h_slot_ptrs);
+    if (c->h_idx) (void)hipHostFree(c->h_idx);
+    if (c->h_phase) (void)hipHostFree(c->h_phase);
+    delete c;
+    return COLI_OK;
 }
-coli_status coli_expert_cache_wait(struct coli_expert_cache*, int32_t, void*) {
-    return coli::fail(COLI_EUNSUPPORTED, "expert cache not available yet");
+
+COLI_API coli_status coli_expert_cache_ensure(struct coli_expert_cache* c, int32_t layer,
+                                              const int32_t* h_ids, int32_t n, int32_t* h_miss_mask) {
+    try {
+        if (!c || layer < 0 || layer >= c->cfg.n_layers || n < 0 || (n > 0 && !h_ids))
+            return fail(COLI_EINVAL, "cache_ensure: bad arguments");
+        const int S = c->cfg.slots_per_layer, E = c->cfg.n_experts;
+        auto& slots = c->slots[layer];
+        auto& where = c->where[layer];
+        // distinct ids of this call, in first-appearance order
+        std::vector<int32_t> ids;
+        ids.reserve(n);
+        std::vector<char> seen(E, 0);
+        for (int32_t i = 0; i < n; ++i) {
+            const int32_t e = h_ids[i];
+            if (e < 0 || e >= E) return fail(COLI_EINVAL, "cache_ensure: expert id out of range");
+            if (!seen[e]) { seen[e] = 1; ids.push_back(e); }
+        }
+        if ((int)ids.size() > S) return fail(COLI_EBUSY, "cache_ensure: more distinct experts than slots");
+        const uint64_t now = ++c->clock;
+        std::vector<char> pinned(S, 0);
+        std::vector<int32_t> misses;
+        for (int32_t e : ids) {
+            if (where[e] >= 0) {
+                pinned[where[e]] = 1;
+                slots[where[e]].last_use = now;
+                c->st.hits++;
+            } else {
+                misses.push_back(e);
+            }
+        }
+        c->st.lookups += ids.size();
+        std::vector<int32_t> used;
+        for (int32_t e : ids)
+            if (where[e] >= 0) used.push_back(where[e]);
+        hipStream_t cs = (hipStream_t)c->cfg.copy_stream;
+        for (int32_t e : misses) {
+            // victim: the first empty slot, else the least recently used slot
+            // not named by this call (equal ages: the lowest expert id)
+            int victim = -1;
+            for (int s = 0; s < S; ++s) {
+                if (pinned[s]) continue;
+                if (victim < 0) { victim = s; continue; }
+                const auto& a = slots[s];
+                const auto& b = slots[victim];
+                if (b.expert < 0) continue;
+                if (a.expert < 0 || a.last_use < b.last_use ||
+                    (a.last_use == b.last_use && a.expert < b.expert))
+                    victim = s;
+            }
+            auto& sl = slots[victim];
+            if (sl.expert >= 0) {
+                where[sl.expert] = -1;
+                c->st.evictions++;
+            }
+            sl.expert = e;
+            sl.last_use = now;
+            where[e] = victim;
+            pinned[victim] = 1;
+            used.push_back(victim);
+            c->st.misses++;
+            c->st.bytes_h2d += c->cfg.blob_bytes;
+            if (!c->dry) {
+                const size_t bb = c->cfg.blob_bytes;
+                uint8_t* dst = (uint8_t*)c->cfg.d_arena + ((size_t)layer * S + victim) * bb;
+                const uint8_t* src = (const uint8_t*)c->cfg.h_pool + ((size_t)layer * E + e) * bb;
+                if (sl.release_recorded) COLI_CHECK_HIP(hipStreamWaitEvent(cs, sl.release, 0));
+                const size_t ti = c->timer_next;
+                c->timer_next = (ti + 1) % c->timers.size();
+                coli_status hs = harvest_timer(c, ti, true);
+                if (hs) return hs;
+                COLI_CHECK_HIP(hipEventRecord(c->timers[ti].first, cs));
+                COLI_CHECK_HIP(hipMemcpyAsync(dst, src, bb, hipMemcpyHostToDevice, cs));
+                COLI_CHECK_HIP(hipEventRecord(c->timers[ti].second, cs));
+                c->timer_live[ti] = true;
+                // pointer of the expert in the device table: a constant pinned source
+                COLI_CHECK_HIP(hipMemcpyAsync(
+                    c->d_tables + (size_t)layer * E + e,
+                    c->h_slot_ptrs + ((size_t)layer * S + victim) * sizeof(void*), sizeof(void*),
+                    hipMemcpyHostToDevice, cs));
+                COLI_CHECK_HIP(hipEventRecord(sl.ready, cs));
+            }
+        }
+        c->used[layer] = used;
+        if (h_miss_mask)
+            for (int32_t i = 0; i < n; ++i) {
+                h_miss_mask[i] = 0;
+                for (int32_t e : misses)
+                    if (e == h_ids[i]) h_miss_mask[i] = 1;
+            }
+        return COLI_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(COLI_ENOMEM, "cache_ensure: host allocation failed");
+    }
 }
-coli_status coli_expert_cache_release(struct coli_expert_cache*, int32_t, void*) {
-    return coli::fail(COLI_EUNSUPPORTED, "expert cache not available yet");
+
+COLI_API coli_status coli_expert_cache_wait(struct coli_expert_cache* c, int32_t layer, void* stream) {
+    if (!c || layer < 0 || layer >= c->cfg.n_layers) return fail(COLI_EINVAL, "cache_wait: bad arguments");
+    if (c->dry) return COLI_OK;
+    for (int32_t s : c->used[layer])
+        COLI_CHECK_HIP(hipStreamWaitEvent((hipStream_t)stream, c->slots[layer][s].ready, 0));
+    return COLI_OK;
 }
-coli_status coli_expert_cache_table(struct coli_expert_cache*, int32_t, const void* const**) {
-    return coli::fail(COLI_EUNSUPPORTED, "expert cache not available yet");
+
+COLI_API coli_status coli_expert_cache_release(struct coli_expert_cache* c, int32_t layer, void* stream) {
+    if (!c || layer < 0 || layer >= c->cfg.n_layers) return fail(COLI_EINVAL, "cache_release: bad arguments");
+    if (c->dry) return COLI_OK;
+    for (int32_t s : c->used[layer]) {
+        auto& sl = c->slots[layer][s];
+        COLI_CHECK_HIP(hipEventRecord(sl.release, (hipStream_t)stream));
+        sl.release_recorded = true;
+    }
+    return COLI_OK;
 }
-coli_status coli_expert_cache_stats(struct coli_expert_cache*, coli_cache_stats*) {
-    return coli::fail(COLI_EUNSUPPORTED, "expert cache not available yet");
+
+COLI_API coli_status coli_expert_cache_table(struct coli_expert_cache* c, int32_t layer,
+                                             const void* const** d_table) {
+    if (!c || !d_table) return fail(COLI_EINVAL, "cache_table: NULL argument");
+    return cache_layer_table(c, layer, c->cfg.n_experts, d_table);
 }
-coli_status coli_expert_cache_reset(struct coli_expert_cache*) {
-    return coli::fail(COLI_EUNSUPPORTED, "expert cache not available yet");
+
+COLI_API coli_status coli_expert_cache_stats(struct coli_expert_cache* c, coli_cache_stats* out) {
+    if (!c || !out) return fail(COLI_EINVAL, "cache_stats: NULL argument");
+    for (size_t i = 0; i < c->timers.size(); ++i) {
+        coli_status s = harvest_timer(c, i, true);
+        if (s) return s;
+    }
+    *out = c->st;
+    return COLI_OK;
 }
+
+COLI_API coli_status coli_expert_cache_reset(struct coli_expert_cache* c) {
+    if (!c) return fail(COLI_EINVAL, "cache_reset: NULL argument");
+    if (!c->dry) COLI_CHECK_HIP(hipStreamSynchronize((hipStream_t)c->cfg.copy_stream));
+    for (auto& layer : c->slots)
+        for (auto& s : layer) {
+            s.expert = -1;
+            s.last_use = 0;
+        }
+    for (auto& w : c->where) std::fill(w.begin(), w.end(), -1);
+    for (auto& u : c->used) u.clear();
+    for (size_t i = 0; i < c->timer_live.size(); ++i) c->timer_live[i] = false;
+    c->st = coli_cache_stats{};
+    return COLI_OK;
 }
+
+}  // extern "C"

@@ -28,5 +28,7 @@ coli_status run_layer(const coli_moe_shape* shape, const float* x, int32_t T, co
 // Expert-cache hooks used by run_layer (cache.hip).
 coli_status cache_layer_table(struct coli_expert_cache* cache, int32_t layer, int32_t n_experts,
                               const void* const** table);
+coli_status cache_place(struct coli_expert_cache* cache, int32_t layer, const int32_t* d_idx,
+                        int32_t n, uint8_t* d_phase, int32_t* n_miss, hipStream_t stream);
 
 }  // namespace coli

@@ -87,8 +87,12 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
                       float* y, int32_t* idx_out, float* w_out, int32_t path, uint8_t* ws,
                       const WsLayout& W, hipStream_t stream) {
     const int32_t H = s->hidden, E = s->n_routed, k = s->top_k;
-    if (cache) return fail(COLI_EUNSUPPORTED, "layer_fwd: expert cache not available yet");
-    (void)layer;
+    if (cache) {
+        coli_status cs = cache_layer_table(cache, layer, E, &table);
+        if (cs) return cs;
+    }
+    // with a cache the work items are formed after placement (table unused here)
+    const void* const* route_table = cache ? nullptr : table;
     bool mfma = false;
     coli_status st = pick_mfma(s, T, path, &mfma);
     if (st) return st;
@@ -107,7 +111,7 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
         ra.items = at<WorkItem>(ws, W.items); ra.n_items = at<int32_t>(ws, W.n_items);
         ra.rows_tok = at<int32_t>(ws, W.rows_tok); ra.rows_out = at<int32_t>(ws, W.rows_out);
         ra.xplanes = at<uint32_t>(ws, W.xplanes); ra.xscale = at<float>(ws, W.xscale);
-        ra.table = table; ra.shared_blob = shared_blob;
+        ra.table = route_table; ra.shared_blob = shared_blob;
         ra.phase_mask = nullptr; ra.phase = 0;
         ra.T = T; ra.E = E; ra.k = k; ra.H = H;
         st = launch_router_small(ra, stream);
@@ -126,16 +130,46 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
                           at<int32_t>(ws, W.perm), at<int32_t>(ws, W.unique),
                           at<int32_t>(ws, W.n_unique), ws + W.union_ws, stream);
         if (st) return st;
-        st = launch_plan(at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.perm),
-                         at<int32_t>(ws, W.unique), at<int32_t>(ws, W.n_unique), table,
-                         shared_blob, T, k, E, nullptr, 0, at<WorkItem>(ws, W.items),
-                         at<int32_t>(ws, W.n_items), at<int32_t>(ws, W.rows_tok),
-                         at<int32_t>(ws, W.rows_out), stream);
-        if (st) return st;
+        if (!cache) {
+            st = launch_plan(at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.perm),
+                             at<int32_t>(ws, W.unique), at<int32_t>(ws, W.n_unique), table,
+                             shared_blob, T, k, E, nullptr, 0, at<WorkItem>(ws, W.items),
+                             at<int32_t>(ws, W.n_items), at<int32_t>(ws, W.rows_tok),
+                             at<int32_t>(ws, W.rows_out), stream);
+            if (st) return st;
+        }
     }
     const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
-    st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W, encoded, stream);
-    if (st) return st;
+    if (!cache) {
+        st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W, encoded, stream);
+        if (st) return st;
+    } else {
+        // place: read the routing back, make the experts resident (misses are
+        // copied on the cache's copy stream), upload each expert's phase
+        uint8_t* d_phase = at<uint8_t>(ws, W.phase);
+        int32_t n_miss = 0;
+        st = cache_place(cache, layer, idx, T * k, d_phase, &n_miss, stream);
+        if (st) return st;
+        // execute the experts that were resident (and the shared one) while the
+        // misses copy, then wait for the copies and execute the misses
+        for (int phase = 0; phase < (n_miss > 0 ? 2 : 1); ++phase) {
+            if (phase == 1) {
+                st = coli_expert_cache_wait(cache, layer, (void*)stream);
+                if (st) return st;
+            }
+            st = launch_plan(at<int32_t>(ws, W.offsets), at<int32_t>(ws, W.perm),
+                             at<int32_t>(ws, W.unique), at<int32_t>(ws, W.n_unique), table,
+                             phase == 0 ? shared_blob : nullptr, T, k, E, d_phase, phase,
+                             at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items),
+                             at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
+            if (st) return st;
+            st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W,
+                         encoded || phase == 1, stream);
+            if (st) return st;
+        }
+        st = coli_expert_cache_release(cache, layer, (void*)stream);
+        if (st) return st;
+    }
     return launch_combine(at<float>(ws, W.y_rows), w, T, k, H, shared_blob ? 1 : 0,
                           s->routed_scale, y, stream);
 }

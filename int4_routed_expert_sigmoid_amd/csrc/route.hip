@@ -244,9 +244,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
         *a.n_unique = nu;
     }
     __syncthreads();
-    // work items: the shared expert first, then the unique experts (of one phase)
+    // work items: the shared expert first, then the unique experts (of one
+    // phase); without a table (cached calls) the items are formed later
+    if (a.table == nullptr) {
+        if (tid == 0) *a.n_items = 0;
+    }
     const int base = a.shared_blob ? 1 : 0;
-    if (tid == 0 && a.shared_blob) {
+    if (tid == 0 && a.shared_blob && a.table) {
         WorkItem it;
         it.blob = (const uint8_t*)a.shared_blob;
         it.begin = n;
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     for (int i = 0; i < EPT; ++i) {
         const int u = tid * EPT + i;
         keep[i] = 0;
-        if (u < nu) {
+        if (u < nu && a.table) {
             const int e = s_uniq[u];
             keep[i] = (a.phase_mask == nullptr || a.phase_mask[e] == a.phase) ? 1 : 0;
         }
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
             a.items[base + kpos++] = it;
         }
     }
-    if (tid == 0) *a.n_items = base + nkeep;
+    if (tid == 0 && a.table) *a.n_items = base + nkeep;
     // stable positions: rank of assignment i among earlier equal experts
     for (int i = tid; i < n; i += kRouterThreads) {
         const int e = s_idx[i];

@@ -1,0 +1,91 @@
+"""Cached layer calls vs resident ones (practical guide section 二: placement
+decides speed only, never routing or precision). Experts of several layers
+live in pinned host memory; a small HBM cache per layer holds the resident
+ones; the outputs must be bit-identical to calls with every expert resident."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import ExpertSet, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def coli():
+    import int4_routed_expert_sigmoid_amd as c
+    c.lib()
+    return c
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _setup(coli, L, H, I, E, k, group, slots):
+    import torch
+    shape = coli.MoEShape(H, I, E, 1, k, group)
+    _, nbytes = coli.blob_layout(shape)
+    sets = [ExpertSet(coli, shape, seed=40 + l, layer=l) for l in range(L)]
+    pool = torch.empty(L * E * nbytes, dtype=torch.uint8).pin_memory()
+    for l, s in enumerate(sets):
+        for e in range(E):
+            pool[(l * E + e) * nbytes:(l * E + e + 1) * nbytes].copy_(s.blobs[e].cpu())
+    arena = torch.zeros(L * slots * nbytes, dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    cache = coli.ExpertCache(L, E, slots, nbytes, arena=arena, pool=pool, copy_stream=copy_stream)
+    return shape, sets, cache
+
+
+@pytest.mark.parametrize("T,group", [(1, 0), (8, 64), (20, 0)])
+def test_cached_equals_resident(coli, T, group):
+    import torch
+    L, H, I, k, steps = 3, 512, 256, 4, 12
+    E = 32 if T == 1 else 64
+    slots = max(10, min(E, T * k))        # a call may name up to T*k distinct experts
+    shape, sets, cache = _setup(coli, L, H, I, E, k, group, slots)
+    ws_c = coli.workspace(shape, T)
+    ws_r = coli.workspace(shape, T)
+    for step in range(steps):
+        for l in range(L):
+            lg, _ = synth.locality_logits(50 + l, l, steps * T, E, k, keep_p=0.6)
+            lgs = lg[step * T:(step + 1) * T]
+            x = synth.activations(50, l, step * T, T, H)
+            yc = coli.layer_fwd(shape, _dev(x), shared_blob=sets[l].shared_blob, logits=_dev(lgs),
+                                cache=cache, layer=l, ws=ws_c)
+            yr = coli.layer_fwd(shape, _dev(x), table=sets[l].table, shared_blob=sets[l].shared_blob,
+                                logits=_dev(lgs), ws=ws_r)
+            torch.cuda.synchronize()
+            assert np.array_equal(yc.cpu().numpy(), yr.cpu().numpy()), (step, l)
+    st = cache.stats()
+    assert st["misses"] > 0 and st["hits"] > 0
+    assert st["bytes_h2d"] == st["misses"] * coli.blob_layout(shape)[1]
+    assert st["copy_ns"] > 0
+    # and the cached result is the layer: spot-check the last call against the oracle
+    _, y64, _, _ = oracle.layer(x, sets[L - 1].oracle_list(), sets[L - 1].shared_oracle, k, group,
+                                1.0, logits=lgs)
+    tol = 1e-3 if T <= 16 else 2e-2
+    assert rel_l2_rows(yc.cpu().numpy(), y64).max() <= tol
+    cache.close()
+
+
+def test_slots_equal_top_k(coli):
+    """Every new expert evicts: the smallest legal cache."""
+    import torch
+    L, H, I, E, k = 1, 256, 128, 16, 4
+    shape, sets, cache = _setup(coli, L, H, I, E, k, 0, k)
+    ws = coli.workspace(shape, 1)
+    lg = synth.zipf_logits(60, 0, 0, 30, E, s=0.5)
+    x = synth.activations(60, 0, 0, 30, H)
+    for t in range(30):
+        yc = coli.layer_fwd(shape, _dev(x[t:t + 1]), shared_blob=sets[0].shared_blob,
+                            logits=_dev(lg[t:t + 1]), cache=cache, layer=0, ws=ws)
+        yr = coli.layer_fwd(shape, _dev(x[t:t + 1]), table=sets[0].table,
+                            shared_blob=sets[0].shared_blob, logits=_dev(lg[t:t + 1]))
+        torch.cuda.synchronize()
+        assert np.array_equal(yc.cpu().numpy(), yr.cpu().numpy()), t
+    st = cache.stats()
+    assert st["evictions"] > 0
+    cache.close()
