@@ -36,19 +36,26 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed tokens (default 1000; 512 for the stream workload)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--graph", type=int, default=1, help="replay the timed tokens from a HIP graph")
     ap.add_argument("--cpu-sample", type=int, default=8, help="tokens of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
+    ap.add_argument("--pinned-layers", type=int, default=13,
+                    help="stream workload: distinct pinned layer pools (the rest reuse them)")
+    ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "stream"],
+                    help="decode (headline, with the prefill line), mtp (gs64, 8-token verify "
+                         "batches), stream (16 layers from pinned host through an HBM cache)")
     return ap.parse_args()
 
 
-def build_experts(coli, shape, seed, dev, keep_host=()):
-    """All routed + shared experts quantised on the GPU from seeded f32 weights.
-    Returns (arena, table, shared_blob, host f32 copies of `keep_host`)."""
+def build_experts(coli, shape, seed, dev, keep_host=(), layer=0):
+    """All routed + shared experts of `layer` quantised on the GPU from seeded
+    f32 weights. Returns (arena, table, shared_blob, host f32 copies of
+    `keep_host`)."""
     import torch
     import synth
     H, I, E = shape.hidden, shape.inter, shape.n_routed
@@ -62,9 +69,9 @@ def build_experts(coli, shape, seed, dev, keep_host=()):
     d_h = torch.empty((H, I), dtype=torch.float32).pin_memory()
     kept = {}
     for e in range(E + 1):
-        synth.expert_matrix(seed, 0, e, synth.MAT_GATE, I, H, out=g_h.numpy())
-        synth.expert_matrix(seed, 0, e, synth.MAT_UP, I, H, out=u_h.numpy())
-        synth.expert_matrix(seed, 0, e, synth.MAT_DOWN, H, I, out=d_h.numpy())
+        synth.expert_matrix(seed, layer, e, synth.MAT_GATE, I, H, out=g_h.numpy())
+        synth.expert_matrix(seed, layer, e, synth.MAT_UP, I, H, out=u_h.numpy())
+        synth.expert_matrix(seed, layer, e, synth.MAT_DOWN, H, I, out=d_h.numpy())
         if e in keep_host:
             kept[e] = (g_h.numpy().copy(), u_h.numpy().copy(), d_h.numpy().copy())
         g_d.copy_(g_h, non_blocking=True)
@@ -151,8 +158,196 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
     }
 
 
+def run_mtp(args, coli, dev):
+    """MTP-verify batches: gs64 scales, 8 tokens per call, router logits with
+    Zipf(1.1) popularity (Gumbel top-k), bias 0, 125 calls = 1,000 tokens."""
+    import torch
+    import synth
+    H, I, E, k, T = 6144, 2048, 256, 8, 8
+    shape = coli.MoEShape(H, I, E, 1, k, 64, 1.0)
+    steps = max(1, args.steps // T)
+    warm = max(1, args.warmup // T + 1)
+    n = steps + warm
+    t0 = time.perf_counter()
+    arena, table, shared, _ = build_experts(coli, shape, args.seed, dev)
+    log(f"gs64 experts ready in {time.perf_counter() - t0:.1f} s")
+    lg = torch.from_numpy(synth.zipf_logits(args.seed, 0, 0, n * T, E, s=1.1)).to(dev)
+    x = torch.from_numpy(synth.activations(args.seed, 0, 0, n * T, H)).to(dev)
+    y = torch.empty((n * T, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((n * T, k), dtype=torch.int32, device=dev)
+    ws = coli.workspace(shape, T, coli.PATH_GEMV, dev)
+    stream = torch.cuda.Stream()
+
+    def call(i):
+        sl = slice(i * T, (i + 1) * T)
+        coli.layer_fwd(shape, x[sl], table=table, shared_blob=shared, logits=lg[sl], y=y[sl],
+                       idx_out=idx[sl], path=coli.PATH_GEMV, ws=ws)
+
+    with torch.cuda.stream(stream):
+        for i in range(warm):
+            call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(warm, n):
+            call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    coli.profile_enable(2 * steps + 8)
+    with torch.cuda.stream(stream):
+        for i in range(warm, n):
+            call(i)
+    torch.cuda.synchronize()
+    n_gu, ms_gu = coli.profile_summary("gemv_gateup")
+    n_dn, ms_dn = coli.profile_summary("gemv_down")
+    coli.profile_enable(0)
+    ids = idx[warm * T:].cpu().numpy().reshape(steps, T * k)
+    uniq = np.array([len(np.unique(r)) for r in ids])
+    blob = coli.blob_layout(shape)[1]
+    off, _ = coli.blob_layout(shape)
+    gu_bytes = (uniq + 1) * (off[2] - off[0] + (off[5] - off[3]))      # gate/up nibbles + scales
+    dn_bytes = (uniq + 1) * (off[3] - off[2] + (blob - off[5]))        # down nibbles + scales
+    gu_s = ms_gu / max(1, n_gu) / 1e3
+    dn_s = ms_dn / max(1, n_dn) / 1e3
+    gbps = float((gu_bytes + dn_bytes).mean()) / (gu_s + dn_s) / 1e9
+    tok_s = steps * T / elapsed
+    return {
+        "metric": "MTP-verify tokens/s (gs64, 8-token batches; weight GB/s vs HBM peak)",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(1e3 * elapsed / steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 weights (gs64) x f32 activations (exact int32 nibble products), f32 accumulate",
+        "data": "synthetic (seeded Philox N(0,0.02) weights, N(0,1) activations, Zipf(1.1) logits)",
+        "config": {"workload": "MTP-verify batches of 8 tokens, GLM-5.2-shaped layer, gs64",
+                   "hidden": H, "inter": I, "n_routed": E, "top_k": k, "group": 64,
+                   "tokens": steps * T, "graph": True},
+        "unique_experts_per_token": round(float(uniq.mean()) / T, 3),
+        "unique_experts_per_step_mean": round(float(uniq.mean()), 2),
+        "unique_experts_per_step_range": [int(uniq.min()), int(uniq.max())],
+        "roofline": {"bound": "hbm", "kernel": "gemv_gateup + gemv_down",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_gateup_us": round(gu_s * 1e6, 2), "avg_down_us": round(dn_s * 1e6, 2)},
+    }
+
+
+def run_stream(args, coli, dev):
+    """Streaming decode across 16 layers: 16 x 256 expert blobs (77.5 GB) in
+    pinned host memory, an HBM LRU cache of 64 experts per layer, routing with
+    temporal locality (each of the previous token's experts kept with p = 0.6,
+    the rest drawn by Zipf(1.1) popularity), batch 1, 512 tokens."""
+    import torch
+    import synth
+    H, I, E, k, L, S = 6144, 2048, 256, 8, 16, 64
+    n_tok = max(1, args.steps)
+    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0)
+    blob = coli.blob_layout(shape)[1]
+    t0 = time.perf_counter()
+    arena0, _, shared0, _ = build_experts(coli, shape, args.seed, dev)
+    # one pinned pool per layer; the box caps pinned memory per process at
+    # 64 GiB (13 layer pools of 4.84 GB fit with headroom), so the last layers
+    # stream from the pools of the first ones (same copies, same traffic)
+    n_pools = min(L, args.pinned_layers)
+    log(f"layer-0 experts ready in {time.perf_counter() - t0:.1f} s; pinning {n_pools} x {E * blob / 1e9:.2f} GB")
+    t0 = time.perf_counter()
+    pools = []
+    for l in range(n_pools):
+        p = pinned_bytes(E * blob)
+        # layer l holds the layer-0 experts in a seeded order of its own
+        order = synth.permutation(args.seed, synth.TAG_PERM, 1000 + l, 0, E)
+        for e in range(E):
+            src = int(order[e])
+            p[e * blob:(e + 1) * blob].copy_(arena0[src * blob:(src + 1) * blob])
+        pools.append(p)
+        log(f"host pool: layer {l + 1}/{n_pools} filled")
+    layer_pools = [pools[l % n_pools] for l in range(L)]
+    log(f"host pool filled in {time.perf_counter() - t0:.1f} s")
+    shared = [shared0.clone() for _ in range(L)]
+    del arena0
+    arena = torch.empty(L * S * blob, dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+    cache = coli.ExpertCache(L, E, S, blob, arena=arena, pools=layer_pools, copy_stream=copy_stream)
+    lg = [torch.from_numpy(synth.locality_logits(args.seed, l, n_tok, E, k, keep_p=0.6)[0]).to(dev)
+          for l in range(L)]
+    xs = [torch.from_numpy(synth.activations(args.seed, l, 0, n_tok, H)).to(dev) for l in range(L)]
+    y = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ws = coli.workspace(shape, 1, coli.PATH_GEMV, dev)
+    cold = min(16, n_tok)
+    torch.cuda.synchronize()
+    coli.profile_enable(2 * L * n_tok + 8)
+    t_start = time.perf_counter()
+    t_cold = None
+    for t in range(n_tok):
+        for l in range(L):
+            coli.layer_fwd(shape, xs[l][t:t + 1], shared_blob=shared[l], logits=lg[l][t:t + 1],
+                           cache=cache, layer=l, y=y, path=coli.PATH_GEMV, ws=ws)
+        if t + 1 == cold:
+            torch.cuda.synchronize()
+            t_cold = time.perf_counter()
+            st_cold = cache.stats()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    n_gu, ms_gu = coli.profile_summary("gemv_gateup")
+    n_dn, ms_dn = coli.profile_summary("gemv_down")
+    coli.profile_enable(0)
+    st = cache.stats()
+    warm_tok = n_tok - cold
+    hits_w = st["hits"] - st_cold["hits"]
+    miss_w = st["misses"] - st_cold["misses"]
+    pcie = st["bytes_h2d"] / max(1, st["copy_ns"])         # bytes per ns = GB/s
+    # 9 blobs per layer call, over the GEMV kernels' summed time (a cached call
+    # launches each GEMV twice: resident experts, then the copied ones)
+    ffn_bytes = 9 * blob * L * n_tok
+    hbm = ffn_bytes / ((ms_gu + ms_dn) / 1e3) / 1e9 if n_gu else None
+    cache.close()
+    warm_s = t_end - t_cold if warm_tok else None
+    return {
+        "metric": "streaming decode tokens/s, 16 layers, experts streamed from pinned host (hit rate, PCIe and HBM GB/s)",
+        "value": round(warm_tok / warm_s, 3) if warm_tok else None, "unit": "tokens/s",
+        "n_gpus": 1, "steps": warm_tok, "warmup": cold,
+        "ms_per_step": round(1e3 * warm_s / warm_tok, 4) if warm_tok else None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 weights x f32 activations (exact int32 nibble products), f32 accumulate",
+        "data": "synthetic (seeded Philox weights; layer l holds the layer-0 experts in a seeded order; locality routing)",
+        "config": {"workload": "streaming decode, 16 GLM-5.2-shaped layers, 64-slot HBM LRU per layer",
+                   "hidden": H, "inter": I, "n_routed": E, "top_k": k, "layers": L, "slots": S,
+                   "host_pool_GB": round(L * E * blob / 1e9, 2),
+                   "distinct_pinned_pools": n_pools, "tokens": n_tok},
+        "cold_tokens": cold, "cold_tokens_per_s": round(cold / (t_cold - t_start), 3),
+        "hit_rate_warm": round(hits_w / max(1, hits_w + miss_w), 4),
+        "misses_per_token_per_layer_warm": round(miss_w / max(1, warm_tok * L), 3),
+        "pcie_GBps": round(pcie, 2), "h2d_GB": round(st["bytes_h2d"] / 1e9, 2),
+        "copy_s": round(st["copy_ns"] / 1e9, 3),
+        "hbm_GBps_ffn_kernels": round(hbm, 1) if hbm else None,
+        "cache": st,
+    }
+
+
+def pinned_bytes(nbytes):
+    """Exactly `nbytes` of pinned host memory (hipHostMalloc) as a uint8 tensor;
+    torch's pinned allocator would round a 77.5 GB request up to a power of two."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    ptr = ctypes.c_void_p()
+    rc = hip.hipHostMalloc(ctypes.byref(ptr), ctypes.c_size_t(nbytes), ctypes.c_uint(0))
+    if rc != 0 or not ptr.value:
+        raise RuntimeError(f"hipHostMalloc of {nbytes} bytes failed ({rc})")
+    buf = (ctypes.c_uint8 * nbytes).from_address(ptr.value)
+    t = torch.frombuffer(buf, dtype=torch.uint8)
+    t._coli_keep = (hip, ptr, buf)
+    return t
+
+
 def main():
     args = parse()
+    if args.steps is None:
+        args.steps = 512 if args.workload == "stream" else 1000
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -164,6 +359,10 @@ def main():
     import oracle
 
     dev = torch.device("cuda:0")
+    if args.workload != "decode":
+        line = run_mtp(args, coli, dev) if args.workload == "mtp" else run_stream(args, coli, dev)
+        print(json.dumps(line), flush=True)
+        return
     H, I, E, k = 6144, 2048, 256, 8
     shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0)
     seed = args.seed

@@ -185,8 +185,9 @@ typedef struct coli_cache_cfg {
     int32_t slots_per_layer;    /* HBM slots per layer, >= top_k of the calls */
     size_t blob_bytes;          /* bytes per expert blob */
     void* d_arena;              /* device, n_layers * slots_per_layer * blob_bytes */
-    const void* h_pool;         /* pinned host, n_layers * n_experts * blob_bytes,
-                                   blob of (layer, e) at (layer*n_experts + e)*blob_bytes */
+    const void* const* h_pools; /* host array [n_layers] of pinned host pointers, each to
+                                   n_experts * blob_bytes; blob e of layer l at
+                                   h_pools[l] + e * blob_bytes (layers may share a pool) */
     void* copy_stream;          /* hipStream_t for the host-to-device copies */
 } coli_cache_cfg;
 
@@ -200,7 +201,10 @@ typedef struct coli_cache_stats {
 } coli_cache_stats;
 
 /* Creates the handle and its per-layer device pointer tables (n_layers *
- * n_experts pointers; entries of non-resident experts are NULL). */
+ * n_experts pointers; entries of non-resident experts are unspecified). The
+ * pool pointer array is copied; the pools themselves must outlive the handle.
+ * With d_arena and h_pools both NULL the handle only keeps the books (no
+ * copies, no events): the placement policy can be simulated without a GPU. */
 COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct coli_expert_cache** out);
 COLI_API coli_status coli_expert_cache_destroy(struct coli_expert_cache* cache);
 

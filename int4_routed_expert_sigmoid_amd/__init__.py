@@ -47,7 +47,7 @@ class Shape(ctypes.Structure):
 class CacheCfg(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("slots_per_layer", ctypes.c_int32), ("blob_bytes", ctypes.c_size_t),
-                ("d_arena", ctypes.c_void_p), ("h_pool", ctypes.c_void_p),
+                ("d_arena", ctypes.c_void_p), ("h_pools", ctypes.c_void_p),
                 ("copy_stream", ctypes.c_void_p)]
 
 
@@ -304,13 +304,24 @@ class ExpertCache:
     memory (coli_expert_cache_*). With arena and pool both None the cache only
     keeps the books (policy simulation, no GPU needed)."""
 
-    def __init__(self, n_layers, n_experts, slots_per_layer, blob_bytes, arena=None, pool=None,
+    def __init__(self, n_layers, n_experts, slots_per_layer, blob_bytes, arena=None, pools=None,
                  copy_stream=None):
+        """pools: one pinned host tensor (n_experts * blob_bytes bytes) per layer, or
+        one tensor holding all layers back to back."""
+        ptrs = None
+        if pools is not None:
+            if not isinstance(pools, (list, tuple)):
+                base = pools.data_ptr()
+                layer_bytes = n_experts * blob_bytes
+                pools_list = [base + l * layer_bytes for l in range(n_layers)]
+            else:
+                pools_list = [p if isinstance(p, int) else p.data_ptr() for p in pools]
+            ptrs = (ctypes.c_void_p * n_layers)(*pools_list)
         self.cfg = CacheCfg(n_layers, n_experts, slots_per_layer, blob_bytes,
                             None if arena is None else arena.data_ptr(),
-                            None if pool is None else pool.data_ptr(),
+                            None if ptrs is None else ctypes.cast(ptrs, ctypes.c_void_p).value,
                             None if copy_stream is None else copy_stream.cuda_stream)
-        self._keep = (arena, pool, copy_stream)
+        self._keep = (arena, pools, copy_stream, ptrs)
         h = ctypes.c_void_p()
         _check(lib().coli_expert_cache_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self.handle = h.value

@@ -25,6 +25,7 @@
 struct coli_expert_cache {
     coli_cache_cfg cfg;
     bool dry = false;
+    std::vector<const uint8_t*> pools;             // [layer] host pool
     struct Slot {
         int32_t expert = -1;
         uint64_t last_use = 0;
@@ -114,12 +115,18 @@ COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct 
         if (cfg->n_layers <= 0 || cfg->n_experts <= 0 || cfg->n_experts > 1024 ||
             cfg->slots_per_layer <= 0 || cfg->blob_bytes == 0)
             return fail(COLI_EINVAL, "cache_create: bad sizes");
-        const bool dry = cfg->d_arena == nullptr && cfg->h_pool == nullptr;
-        if (!dry && (!cfg->d_arena || !cfg->h_pool))
-            return fail(COLI_EINVAL, "cache_create: give both arena and pool, or neither");
+        const bool dry = cfg->d_arena == nullptr && cfg->h_pools == nullptr;
+        if (!dry && (!cfg->d_arena || !cfg->h_pools))
+            return fail(COLI_EINVAL, "cache_create: give both arena and pools, or neither");
+        if (!dry)
+            for (int l = 0; l < cfg->n_layers; ++l)
+                if (!cfg->h_pools[l]) return fail(COLI_EINVAL, "cache_create: NULL pool pointer");
         auto* c = new coli_expert_cache();
         c->cfg = *cfg;
+        c->cfg.h_pools = nullptr;
         c->dry = dry;
+        if (!dry)
+            for (int l = 0; l < cfg->n_layers; ++l) c->pools.push_back((const uint8_t*)cfg->h_pools[l]);
         const int L = cfg->n_layers, S = cfg->slots_per_layer, E = cfg->n_experts;
         c->slots.assign(L, std::vector<coli_expert_cache::Slot>(S));
         c->where.assign(L, std::vector<int32_t>(E, -1));
@@ -244,7 +251,7 @@ COLI_API coli_status coli_expert_cache_ensure(struct coli_expert_cache* c, int32
             if (!c->dry) {
                 const size_t bb = c->cfg.blob_bytes;
                 uint8_t* dst = (uint8_t*)c->cfg.d_arena + ((size_t)layer * S + victim) * bb;
-                const uint8_t* src = (const uint8_t*)c->cfg.h_pool + ((size_t)layer * E + e) * bb;
+                const uint8_t* src = c->pools[layer] + (size_t)e * bb;
                 if (sl.release_recorded) COLI_CHECK_HIP(hipStreamWaitEvent(cs, sl.release, 0));
                 const size_t ti = c->timer_next;
                 c->timer_next = (ti + 1) % c->timers.size();

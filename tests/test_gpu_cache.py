@@ -35,7 +35,7 @@ def _setup(coli, L, H, I, E, k, group, slots):
             pool[(l * E + e) * nbytes:(l * E + e + 1) * nbytes].copy_(s.blobs[e].cpu())
     arena = torch.zeros(L * slots * nbytes, dtype=torch.uint8, device="cuda")
     copy_stream = torch.cuda.Stream()
-    cache = coli.ExpertCache(L, E, slots, nbytes, arena=arena, pool=pool, copy_stream=copy_stream)
+    cache = coli.ExpertCache(L, E, slots, nbytes, arena=arena, pools=pool, copy_stream=copy_stream)
     return shape, sets, cache
 
 
