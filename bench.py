@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
     ap.add_argument("--pinned-layers", type=int, default=13,
                     help="stream workload: distinct pinned layer pools (the rest reuse them)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "stream"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "stream", "copy"],
                     help="decode (headline, with the prefill line), mtp (gs64, 8-token verify "
-                         "batches), stream (16 layers from pinned host through an HBM cache)")
+                         "batches), stream (16 layers from pinned host through an HBM cache), "
+                         "copy (plain 1 GiB device copy: bandwidth and counter calibration)")
     return ap.parse_args()
 
 
@@ -107,6 +108,23 @@ def cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept):
             "sample": f"first {sample} tokens of the decode workload, whole layer (router logits, "
                       f"route, union, 9 expert FFNs, combine), scalar C, f64 accumulation, "
                       f"OpenMP over output rows; {dt:.2f} s"}
+
+
+def measured_traffic(kernel_json):
+    """HBM bytes per launch from the committed counter profile, if the kernel's
+    sources are unchanged since the counters were taken (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", kernel_json)
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for f in rec["source_files"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["traffic_bytes_per_dispatch"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
@@ -328,6 +346,28 @@ def run_stream(args, coli, dev):
     }
 
 
+def run_copy(args, dev):
+    """A plain device-to-device copy of 1 GiB, 20 times: the achievable
+    read+write bandwidth, and the reference for scaling HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(20):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    s = a.elapsed_time(b) / 1e3 / 20
+    return {"metric": "device copy GB/s (read + write)", "value": round(2 * n / s / 1e9, 1),
+            "unit": "GB/s", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+            "us_per_copy": round(s * 1e6, 2), "n_gpus": 1}
+
+
 def pinned_bytes(nbytes):
     """Exactly `nbytes` of pinned host memory (hipHostMalloc) as a uint8 tensor;
     torch's pinned allocator would round a 77.5 GB request up to a power of two."""
@@ -360,7 +400,12 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.workload != "decode":
-        line = run_mtp(args, coli, dev) if args.workload == "mtp" else run_stream(args, coli, dev)
+        if args.workload == "copy":
+            line = run_copy(args, dev)
+        elif args.workload == "mtp":
+            line = run_mtp(args, coli, dev)
+        else:
+            line = run_stream(args, coli, dev)
         print(json.dumps(line), flush=True)
         return
     H, I, E, k = 6144, 2048, 256, 8
@@ -469,7 +514,7 @@ def main():
                      "achieved": round(gu_gbps, 1) if gu_gbps else None,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4) if gu_gbps else None,
-                     "traffic": None,
+                     "traffic": measured_traffic("gemv_gateup_decode_traffic.json"),
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
                      "launches_timed": n_gu},
         "expert_gemv": {"gateup_GBps": gu_gbps and round(gu_gbps, 1),
