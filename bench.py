@@ -267,9 +267,9 @@ def run_stream(args, coli, dev):
     blob = coli.blob_layout(shape)[1]
     t0 = time.perf_counter()
     arena0, _, shared0, _ = build_experts(coli, shape, args.seed, dev)
-    # one pinned pool per layer; the box caps pinned memory per process at
-    # 64 GiB (13 layer pools of 4.84 GB fit with headroom), so the last layers
-    # stream from the pools of the first ones (same copies, same traffic)
+    # one pinned pool per layer; pinned host memory per process is capped (near
+    # 64 GiB where measured: 13 layer pools of 4.84 GB fit with headroom), so the
+    # last layers stream from the pools of the first ones (same copies, same traffic)
     n_pools = min(L, args.pinned_layers)
     log(f"layer-0 experts ready in {time.perf_counter() - t0:.1f} s; pinning {n_pools} x {E * blob / 1e9:.2f} GB")
     t0 = time.perf_counter()
