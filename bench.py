@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
     ap.add_argument("--pinned-layers", type=int, default=13,
                     help="stream workload: distinct pinned layer pools (the rest reuse them)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "stream", "copy"],
-                    help="decode (headline, with the prefill line), mtp (gs64, 8-token verify "
-                         "batches), stream (16 layers from pinned host through an HBM cache), "
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "mtp", "stream", "copy"],
+                    help="decode (headline, with the prefill line), prefill (that line alone), "
+                         "mtp (gs64, 8-token verify batches), stream (16 layers from pinned host through an HBM cache), "
                          "copy (plain 1 GiB device copy: bandwidth and counter calibration)")
     return ap.parse_args()
 
@@ -402,6 +403,13 @@ def main():
     if args.workload != "decode":
         if args.workload == "copy":
             line = run_copy(args, dev)
+        elif args.workload == "prefill":
+            shape = coli.MoEShape(6144, 2048, 256, 1, 8, 0, 1.0)
+            arena, table, shared, _ = build_experts(coli, shape, args.seed, dev)
+            line = run_prefill(coli, shape, table, shared, args.seed, dev,
+                               calls=max(1, min(args.steps, 50)), warmup=max(1, args.warmup))
+            line = {"metric": "prefill TFLOP/s (2048 tokens, bf16 MFMA)", "value": line["tflops_layer"],
+                    "unit": "TFLOP/s", "n_gpus": 1, **line}
         elif args.workload == "mtp":
             line = run_mtp(args, coli, dev)
         else:

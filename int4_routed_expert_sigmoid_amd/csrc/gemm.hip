@@ -3,8 +3,8 @@
 // Batch union (lbrq.cn article section 三 item 4; practical guide section 二):
 // every unique expert's weights are applied to all of its tokens as one
 // grouped GEMM: h = silu(Xe Wg^T) * (Xe Wu^T), ye = h Wd^T, where Xe holds the
-// rows of the expert's tokens. Tiles of 64 tokens x 64 rows (x gate and up)
-// or 64 tokens x 128 rows (down); a device-built list of 64-token tiles per
+// rows of the expert's tokens. Tiles of 64 tokens x 128 rows of gate and of
+// up, or x 256 columns of down; a device-built list of 64-token tiles per
 // work item lets one launch cover every expert whatever its token count.
 //
 // Operands. A (activations) is bf16: x rounded once to bf16 by a prep pass,
@@ -18,9 +18,10 @@
 //
 // MFMA operand layout used here (32x32x16): lane l supplies A[m][k] and
 // B[k][n] for m = n = l % 32 and the 8 k-values of half l / 32. K-step s of a
-// 64-wide k block maps half h, element j to k = 32h + 8s + j, so one 16-byte
-// load per lane covers 32 consecutive k of one weight row (4 K-steps) and
-// 64 bytes of its activation row. Accumulator element j of lane l is
+// 64-wide k block maps half h, element j to k = 32h + 8s + kSlot[j] (kSlot
+// below), so one 16-byte load per lane covers 32 consecutive k of one weight
+// row (4 K-steps) and 64 bytes of its activation row, which is stored in
+// slot order. Accumulator element j of lane l is
 // C[8(j/4) + 4(l/32) + j%4][l % 32].
 #include <algorithm>
 
@@ -43,19 +44,25 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
 }
 
 // 8 nibbles (two's complement, column order) -> 8 bf16 values q + 136 in
-// MFMA operand order (element j <-> column j).
+// operand slot order kSlot: slot j holds column kSlot[j] = 0 2 4 6 1 3 5 7, so
+// each output word is one byte permute of the even or the odd nibbles with
+// the constant exponent byte 0x43.
 __device__ __forceinline__ bf16x8 nib8_to_bf16(uint32_t w) {
-    const uint32_t u = w ^ 0x88888888u;                 // q + 8 in every nibble
-    const uint32_t lo = u & 0x0F0F0F0Fu;                // columns 0, 2, 4, 6
-    const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;         // columns 1, 3, 5, 7
-    const uint32_t p01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // u0 u1 u2 u3
-    const uint32_t p23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // u4 u5 u6 u7
+    const uint32_t lo = (w ^ 0x88888888u) & 0x0F0F0F0Fu;          // q + 8 of columns 0, 2, 4, 6
+    const uint32_t hi = ((w >> 4) ^ 0x08888888u) & 0x0F0F0F0Fu;   // q + 8 of columns 1, 3, 5, 7
     uint4 r;
-    r.x = __builtin_amdgcn_perm(0x43434343u, p01, 0x05010400u);        // 128+u0, 128+u1
-    r.y = __builtin_amdgcn_perm(0x43434343u, p01, 0x05030402u);
-    r.z = __builtin_amdgcn_perm(0x43434343u, p23, 0x05010400u);
-    r.w = __builtin_amdgcn_perm(0x43434343u, p23, 0x05030402u);
+    r.x = __builtin_amdgcn_perm(0x43434343u, lo, 0x05010400u);         // 128+u0, 128+u2
+    r.y = __builtin_amdgcn_perm(0x43434343u, lo, 0x05030402u);         // 128+u4, 128+u6
+    r.z = __builtin_amdgcn_perm(0x43434343u, hi, 0x05010400u);         // 128+u1, 128+u3
+    r.w = __builtin_amdgcn_perm(0x43434343u, hi, 0x05030402u);         // 128+u5, 128+u7
     return __builtin_bit_cast(bf16x8, r);
+}
+
+// The bf16 activations (x and h) are stored in the same slot order inside
+// every aligned group of 8 columns, so an operand is one plain 16-byte load:
+// column c lives at position slot_pos(c).
+__device__ __forceinline__ int slot_pos(int c) {
+    return (c & ~7) + ((c & 7) >> 1) + 4 * (c & 1);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
@@ -86,11 +93,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ x, 
         const float4 a = *reinterpret_cast<const float4*>(src + j);
         const float4 b = *reinterpret_cast<const float4*>(src + j + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        // slot order: positions 0..7 hold columns 0 2 4 6 1 3 5 7
         uint32_t pk[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint16_t l = bf16_bits(v[2 * i]), h = bf16_bits(v[2 * i + 1]);
-            pk[i] = (uint32_t)l | ((uint32_t)h << 16);
+            const int c0 = 4 * (i & 1) + (i >> 1), c1 = c0 + 2;     // (0,2) (4,6) (1,3) (5,7)
+            pk[i] = (uint32_t)bf16_bits(v[c0]) | ((uint32_t)bf16_bits(v[c1]) << 16);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) s += bf16_round(v[i]);
@@ -128,234 +136,324 @@ __global__ __launch_bounds__(256) void tiles_kernel(const WorkItem* __restrict__
     if (t == 0) *n_tiles = base;
 }
 
+constexpr int kCsChunk = 64;        // 64-column groups staged in LDS at a time (gs64)
+
+// Stage 136 * sums[row(m0 + t)][q] for the 64 tile rows t and the groups
+// q = q0 .. q0 + 63 (clamped to n_groups) as s[t * 64 + q - q0]. Called by the
+// whole workgroup at the same k block; the barriers fence the previous chunk's
+// readers and publish the new one.
+__device__ __forceinline__ void stage_group_sums(float* s, const float* sums, const int* rows,
+                                                 const WorkItem& it, int m0, int n_groups, int q0) {
+    __syncthreads();
+    const int nq = min(kCsChunk, n_groups - q0);
+    for (int i = threadIdx.x; i < kTileM * kCsChunk; i += blockDim.x) {
+        const int t = i / kCsChunk, q = i % kCsChunk;
+        if (q < nq) {
+            const int r = rows[it.begin + min(m0 + t, it.count - 1)];
+            s[i] = kOffset * sums[(size_t)r * n_groups + q0 + q];
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------ work order
+// Work unit = (64-token tile, block of weight rows). Units are taken in a
+// grouped order: kGroupTiles consecutive tiles (usually of one expert, or of a
+// few small ones) times every row block, so that the units of a group share
+// activation rows and weight rows. Workgroup L runs on XCD L % 8, and each XCD
+// takes one contiguous eighth of the units, so a group's reuse stays inside
+// one XCD's L2. Returns false for units past the device-side tile count.
+constexpr int kGroupTiles = 4;
+
+__device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& rb) {
+    const int n = n_tiles * n_rb;
+    const int per = (n + 7) / 8;
+    const int local = blockIdx.x >> 3;
+    if (local >= per) return false;
+    const int w = (int)(blockIdx.x & 7) * per + local;
+    if (w >= n) return false;
+    const int gsz = kGroupTiles * n_rb;
+    const int grp = w / gsz, r = w % gsz;
+    const int gt = min(kGroupTiles, n_tiles - grp * kGroupTiles);
+    rb = r / gt;
+    tile = grp * kGroupTiles + r % gt;
+    return true;
+}
+
+// ------------------------------------------------------------- main loop
+// One wave computes a 64-token x (2 x 32)-row block of sums
+//   acc[b][half][j] = sum_k (136 + q_b[n][k]) * A[m][k]
+// for its two 32-row weight blocks b (gate and up rows, or two column blocks
+// of down) and the tile's token halves (the second only when TWO). The 64 x 64
+// activation block of each k step is staged once per workgroup in LDS (double
+// buffered, one barrier per k step) and shared by the 4 waves; weight nibbles
+// go straight from HBM to registers, two k steps ahead. With GS, every k step
+// is one 64-column scale group, folded into `out` with its scale and its
+// 136 * S correction; otherwise `out` holds the raw sums.
+constexpr int kLdsRow = 72;          // bf16 per LDS activation row (64 + 8 pad: conflict-free 16-B reads)
+
+template <bool GS, bool TWO>
+__device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int nk,
+                                         const uint8_t* __restrict__ b0, const uint8_t* __restrict__ b1,
+                                         const float* __restrict__ gs0, const float* __restrict__ gs1,
+                                         const float* __restrict__ sums, const int32_t* __restrict__ rows,
+                                         const WorkItem& it, int m0,
+                                         uint16_t (*sA)[kTileM][kLdsRow], float* s_cs,
+                                         f32x16 (&out)[2][2]) {
+    const int lane = threadIdx.x & 63, ln = lane & 31, lh = lane >> 5;
+    const int ar = threadIdx.x >> 2, aq = threadIdx.x & 3;     // staging: row, 16-column quarter
+    const bool aload = TWO || ar < 32;                         // wave-uniform
+    // per-row scales: accumulate straight into `out`; gs64: per-group sums in `part`
+    f32x16 part[2][2];
+    f32x16 (&acc)[2][2] = GS ? part : out;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = out[b][0] = out[b][1] = f32x16{};
+    uint4 P0[2], P1[2], Ar0 = {}, Ar1 = {};
+    float F0[2] = {}, F1[2] = {};                              // gs64: scales of the staged k step
+    auto ldA = [&](int kb) {
+        if (aload) {
+            Ar0 = ldg16(arow + kb * 64);
+            Ar1 = ldg16(arow + kb * 64 + 8);
+        }
+    };
+    auto stA = [&](int buf) {
+        if (aload) {
+            *reinterpret_cast<uint4*>(&sA[buf][ar][aq * 16]) = Ar0;
+            *reinterpret_cast<uint4*>(&sA[buf][ar][aq * 16 + 8]) = Ar1;
+        }
+    };
+    auto ldB = [&](uint4 (&P)[2], float (&F)[2], int kb) {
+        P[0] = ldg16(b0 + kb * 32);
+        P[1] = ldg16(b1 + kb * 32);
+        if (GS) {
+            F[0] = gs0[kb];
+            F[1] = gs1[kb];
+        }
+    };
+    auto mma = [&](int buf, const uint4 (&P)[2]) {
+        const uint4* r0 = reinterpret_cast<const uint4*>(&sA[buf][ln][lh * 32]);
+        const uint4* r1 = reinterpret_cast<const uint4*>(&sA[buf][32 + ln][lh * 32]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 a0 = r0[s];
+            uint4 a1;
+            if (TWO) a1 = r1[s];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const uint32_t w = s == 0 ? P[b].x : s == 1 ? P[b].y : s == 2 ? P[b].z : P[b].w;
+                const bf16x8 bb = nib8_to_bf16(w);
+                acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bb, acc[b][0], 0, 0, 0);
+                if (TWO) acc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bb, acc[b][1], 0, 0, 0);
+            }
+        }
+    };
+    auto fold = [&](int kb, const float (&f)[2]) {
+        const float* cs_k = s_cs + kb % kCsChunk;
+#pragma unroll
+        for (int mb = 0; mb < (TWO ? 2 : 1); ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float cs = cs_k[(mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)) * kCsChunk];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    out[b][mb][j] = fmaf(f[b], acc[b][mb][j] - cs, out[b][mb][j]);
+                    acc[b][mb][j] = 0.f;
+                }
+            }
+    };
+    const int last = nk - 1;
+    ldA(0);
+    stA(0);
+    ldB(P0, F0, 0);
+    ldB(P1, F1, min(1, last));
+    __syncthreads();
+    // pairs of k steps (buffer 0 then 1) with no exit in between, so the
+    // accumulators stay in place across iterations; then the odd last step
+    int kb = 0;
+    for (; kb + 1 < nk; kb += 2) {
+        if (GS && kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
+        ldA(kb + 1);
+        mma(0, P0);
+        if (GS) fold(kb, F0);
+        ldB(P0, F0, min(kb + 2, last));
+        stA(1);
+        __syncthreads();
+        ldA(min(kb + 2, last));
+        mma(1, P1);
+        if (GS) fold(kb + 1, F1);
+        ldB(P1, F1, min(kb + 3, last));
+        stA(0);
+        __syncthreads();
+    }
+    if (kb < nk) {
+        if (GS && kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
+        mma(0, P0);
+        if (GS) fold(kb, F0);
+    }
+}
+
 // ----------------------------------------------------------------- gate/up
-// Workgroup: 64 tokens of one item x 64 intermediate rows of gate and up.
-// Wave (wm, wi): tokens 32wm.., rows 32wi.., one 32x32 accumulator per matrix.
+// Workgroup: 64 tokens of one item x 128 intermediate rows of gate and up.
+// Wave w owns rows 32w..32w+31 of both matrices; epilogue h = silu(g) * u,
+// stored as bf16 by output row, plus the per-64-row sums of the stored bf16
+// values that the down GEMM's correction needs.
+template <bool GS, bool TWO>
+__device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& it, int m0, int rb,
+                                            uint16_t (*sA)[kTileM][kLdsRow], float* s_cs,
+                                            const float* s_tot, const int* s_out,
+                                            float (*s_part)[kTileM]) {
+    const int H = a.H, I = a.I, G = H / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ln = lane & 31, lh = lane >> 5;
+    const BlobLayout& L = a.L;
+    const int wrow = rb * 128 + wave * 32;                    // this wave's first weight row
+    const bool wlive = wrow < I;                              // false in the last block when I % 128 == 64
+    const int irow = min(wrow, I - 32) + ln;                  // this lane's weight row (clamped when dead)
+    const size_t boff = (size_t)irow * (H / 2) + lh * 16;
+    const float* gsc = reinterpret_cast<const float*>(it.blob + L.gate_s);
+    const float* usc = reinterpret_cast<const float*>(it.blob + L.up_s);
+    const int atok = a.rows_tok[it.begin + min(m0 + (int)(threadIdx.x >> 2), it.count - 1)];
+    const uint16_t* arow = a.xb + (size_t)atok * H + (threadIdx.x & 3) * 16;
+
+    // per-row scales are read before the main loop: in the epilogue a late
+    // load would make every store wait for the stores before it
+    const float fg = GS ? 1.f : gsc[irow], fu = GS ? 1.f : usc[irow];
+    f32x16 out[2][2];
+    mainloop<GS, TWO>(arow, G, it.blob + L.gate_q + boff, it.blob + L.up_q + boff,
+                      gsc + (size_t)irow * G, usc + (size_t)irow * G, a.sx, a.rows_tok, it, m0,
+                      sA, s_cs, out);
+
+#pragma unroll
+    for (int mb = 0; mb < (TWO ? 2 : 1); ++mb) {
+        float rsum[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int mi = mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);     // token in the tile
+            const float g = GS ? out[0][mb][j] : fg * (out[0][mb][j] - kOffset * s_tot[mi]);
+            const float u = GS ? out[1][mb][j] : fu * (out[1][mb][j] - kOffset * s_tot[mi]);
+            const float h = g / (1.f + expf(-g)) * u;
+            rsum[j] = bf16_round(h);
+            const int o = s_out[mi];
+            if (o >= 0 && wlive) a.hb[(size_t)o * I + slot_pos(irow)] = bf16_bits(h);
+        }
+        // sum over the 32 rows of this wave (lanes sharing lh), fixed butterfly order
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            float v = rsum[j];
+            v += __int_as_float(lane_xchg<1>(__float_as_int(v)));
+            v += __int_as_float(lane_xchg<2>(__float_as_int(v)));
+            v += __int_as_float(lane_xchg<4>(__float_as_int(v)));
+            v += __int_as_float(lane_xchg<8>(__float_as_int(v)));
+            v += __int_as_float(lane_xchg<16>(__float_as_int(v)));
+            rsum[j] = v;
+        }
+        if (ln == 0) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s_part[wave][mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)] = rsum[j];
+        }
+    }
+    __syncthreads();
+    // group sums: waves (0, 1) cover one 64-row group of h, waves (2, 3) the next
+    if (threadIdx.x < 2 * kTileM) {
+        const int t = threadIdx.x & (kTileM - 1), grp = threadIdx.x >> 6;
+        const int o = s_out[t], q = rb * 2 + grp;
+        if (o >= 0 && q * 64 < I) a.sh[(size_t)o * (I / 64) + q] = s_part[2 * grp][t] + s_part[2 * grp + 1][t];
+    }
+}
+
 template <bool GS>
 __global__ __launch_bounds__(256) void gemm_gateup_kernel(GemmArgs a) {
-    __shared__ float s_part[2][kTileM];          // per-wave row sums of bf16(h)
+    __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
+    __shared__ float s_part[4][kTileM];          // per-wave token sums of bf16(h)
     __shared__ float s_tot[kTileM];              // per-token sum of the bf16 x row
-    const int tile = blockIdx.x;
-    if (tile >= *a.n_tiles) return;
+    __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
+    __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: 136 * group sums, [token][group]
+    int tile, rb;
+    if (!unit_of(*a.n_tiles, (a.I + 127) / 128, tile, rb)) return;
     const int2 td = a.tiles[tile];
     const WorkItem it = a.items[td.x];
     const int m0 = td.y;
+    if (threadIdx.x < kTileM) {
+        const int m = m0 + (int)threadIdx.x;
+        s_out[threadIdx.x] = m < it.count ? a.rows_out[it.begin + m] : -1;
+    }
     if (!GS && threadIdx.x < kTileM) {
-        const int tok = a.rows_tok[it.begin + min(m0 + (int)threadIdx.x, it.count - 1)];
         const int G = a.H / 64;
+        const int tok = a.rows_tok[it.begin + min(m0 + (int)threadIdx.x, it.count - 1)];
         float s = 0.f;
         for (int q = 0; q < G; ++q) s += a.sx[(size_t)tok * G + q];
         s_tot[threadIdx.x] = s;
     }
-    __syncthreads();
-    const int nt = blockIdx.y;                   // 64-row block of the intermediate axis
-    const int H = a.H, I = a.I;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wi = wave >> 1;
-    const int ln = lane & 31, lh = lane >> 5;
-    const BlobLayout& L = a.L;
-    const uint8_t* gq = it.blob + L.gate_q;
-    const uint8_t* uq = it.blob + L.up_q;
-    const float* gsc = reinterpret_cast<const float*>(it.blob + L.gate_s);
-    const float* usc = reinterpret_cast<const float*>(it.blob + L.up_s);
-    const int G = H / 64;
-
-    // this lane's A row (token) and B rows (intermediate index)
-    const int pm = m0 + wm * 32 + ln;                        // token position in the item
-    const int arow = a.rows_tok[it.begin + min(pm, it.count - 1)];
-    const uint16_t* ap = a.xb + (size_t)arow * H + lh * 32;
-    const int irow = nt * 64 + wi * 32 + ln;
-    const uint8_t* gp = gq + (size_t)irow * (H / 2) + lh * 16;
-    const uint8_t* up = uq + (size_t)irow * (H / 2) + lh * 16;
-
-    f32x16 accg = {}, accu = {};
-    f32x16 totg = {}, totu = {};                 // gs64: scaled sum over groups
-    uint4 A[4], Bg, Bu, An[4], Bgn, Bun;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) A[s] = ldg16(ap + 8 * s);
-    Bg = ldg16(gp);
-    Bu = ldg16(up);
-    for (int kb = 0; kb < G; ++kb) {
-        const bool more = kb + 1 < G;
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) An[s] = ldg16(ap + (kb + 1) * 64 + 8 * s);
-            Bgn = ldg16(gp + (kb + 1) * 32);
-            Bun = ldg16(up + (kb + 1) * 32);
-        }
-        const uint32_t wg[4] = {Bg.x, Bg.y, Bg.z, Bg.w};
-        const uint32_t wu[4] = {Bu.x, Bu.y, Bu.z, Bu.w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bf16x8 av = as_bf16x8(A[s]);
-            accg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, nib8_to_bf16(wg[s]), accg, 0, 0, 0);
-            accu = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, nib8_to_bf16(wu[s]), accu, 0, 0, 0);
-        }
-        if (GS) {
-            // one 64-column group per k block: scale it and start a new sum
-            const float fg = gsc[(size_t)irow * G + kb], fu = usc[(size_t)irow * G + kb];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int m = m0 + wm * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-                const int tok = a.rows_tok[it.begin + min(m, it.count - 1)];
-                const float cs = kOffset * a.sx[(size_t)tok * G + kb];
-                totg[j] = fmaf(fg, accg[j] - cs, totg[j]);
-                totu[j] = fmaf(fu, accu[j] - cs, totu[j]);
-                accg[j] = 0.f;
-                accu[j] = 0.f;
-            }
-        }
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) A[s] = An[s];
-            Bg = Bgn;
-            Bu = Bun;
-        }
-    }
-    // epilogue: h = silu(g) * u -> bf16, and per-token sums of the bf16 h
-    const float fg = GS ? 1.f : gsc[irow], fu = GS ? 1.f : usc[irow];
-    float rsum[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-        float g, u;
-        if (GS) {
-            g = totg[j];
-            u = totu[j];
-        } else {
-            const float sxt = s_tot[m - m0 < kTileM ? m - m0 : 0];
-            g = fg * (accg[j] - kOffset * sxt);
-            u = fu * (accu[j] - kOffset * sxt);
-        }
-        const float h = g / (1.f + expf(-g)) * u;
-        const uint16_t hb = bf16_bits(h);
-        rsum[j] = bf16_round(h);
-        if (m < it.count) {
-            const int out = a.rows_out[it.begin + m];
-            a.hb[(size_t)out * I + irow] = hb;
-        }
-    }
-    // sum over the 32 rows of this wave (lanes sharing lh), fixed butterfly order
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        float v = rsum[j];
-        v += __int_as_float(lane_xchg<1>(__float_as_int(v)));
-        v += __int_as_float(lane_xchg<2>(__float_as_int(v)));
-        v += __int_as_float(lane_xchg<4>(__float_as_int(v)));
-        v += __int_as_float(lane_xchg<8>(__float_as_int(v)));
-        v += __int_as_float(lane_xchg<16>(__float_as_int(v)));
-        rsum[j] = v;
-    }
-    if (ln == 0) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s_part[wi][wm * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)] = rsum[j];
-    }
-    __syncthreads();
-    if (threadIdx.x < kTileM) {
-        const int m = m0 + threadIdx.x;
-        if (m < it.count) {
-            const int out = a.rows_out[it.begin + m];
-            a.sh[(size_t)out * (I / 64) + nt] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x];
-        }
-    }
+    // (the main loop's first barrier publishes s_tot)
+    if (it.count - m0 > 32) gateup_tile<GS, true>(a, it, m0, rb, sA, s_cs, s_tot, s_out, s_part);
+    else gateup_tile<GS, false>(a, it, m0, rb, sA, s_cs, s_tot, s_out, s_part);
 }
 
 // -------------------------------------------------------------------- down
-// Workgroup: 64 tokens of one item x 128 output columns. Wave (wm, wn):
-// tokens 32wm.., columns 64wn.. (two 32x32 accumulators).
-template <bool GS>
-__global__ __launch_bounds__(256) void gemm_down_kernel(GemmArgs a) {
-    __shared__ float s_tot[kTileM];              // per-row sum of the bf16 h row
-    const int tile = blockIdx.x;
-    if (tile >= *a.n_tiles) return;
-    const int2 td = a.tiles[tile];
-    const WorkItem it = a.items[td.x];
-    const int m0 = td.y;
-    if (!GS && threadIdx.x < kTileM) {
-        const int out = a.rows_out[it.begin + min(m0 + (int)threadIdx.x, it.count - 1)];
-        const int GI = a.I / 64;
-        float s = 0.f;
-        for (int q = 0; q < GI; ++q) s += a.sh[(size_t)out * GI + q];
-        s_tot[threadIdx.x] = s;
-    }
-    __syncthreads();
-    const int H = a.H, I = a.I;
+// Workgroup: 64 tokens of one item x 256 output columns. Wave w owns columns
+// 64w..64w+63 as two 32-column blocks.
+template <bool GS, bool TWO>
+__device__ __forceinline__ void down_tile(const GemmArgs& a, const WorkItem& it, int m0, int rb,
+                                          uint16_t (*sA)[kTileM][kLdsRow], float* s_cs,
+                                          const float* s_tot, const int* s_out) {
+    const int H = a.H, I = a.I, GI = I / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
     const int ln = lane & 31, lh = lane >> 5;
     const BlobLayout& L = a.L;
     const uint8_t* dq = it.blob + L.down_q;
     const float* dsc = reinterpret_cast<const float*>(it.blob + L.down_s);
-    const int GI = I / 64;
+    const int c0 = rb * 256 + wave * 64 + ln, c1 = c0 + 32;   // this lane's two output columns
+    const int cc0 = min(c0, H - 1), cc1 = min(c1, H - 1);
+    const int arw = a.rows_out[it.begin + min(m0 + (int)(threadIdx.x >> 2), it.count - 1)];
+    const uint16_t* arow = a.hb + (size_t)arw * I + (threadIdx.x & 3) * 16;
 
-    const int pm = m0 + wm * 32 + ln;
-    const int arow = a.rows_out[it.begin + min(pm, it.count - 1)];
-    const uint16_t* ap = a.hb + (size_t)arow * I + lh * 32;
-    const int c0 = blockIdx.y * 128 + wn * 64 + ln;          // first of this lane's 2 columns
-    const uint8_t* bp0 = dq + (size_t)min(c0, H - 1) * (I / 2) + lh * 16;
-    const uint8_t* bp1 = dq + (size_t)min(c0 + 32, H - 1) * (I / 2) + lh * 16;
+    const float f[2] = {GS ? 1.f : dsc[cc0], GS ? 1.f : dsc[cc1]};   // before the loop, as in gate/up
+    f32x16 out[2][2];
+    mainloop<GS, TWO>(arow, GI, dq + (size_t)cc0 * (I / 2) + lh * 16, dq + (size_t)cc1 * (I / 2) + lh * 16,
+                      dsc + (size_t)cc0 * GI, dsc + (size_t)cc1 * GI, a.sh, a.rows_out, it, m0,
+                      sA, s_cs, out);
 
-    f32x16 acc0 = {}, acc1 = {}, tot0 = {}, tot1 = {};
-    uint4 A[4], B0, B1, An[4], B0n, B1n;
+    const int cols[2] = {c0, c1};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) A[s] = ldg16(ap + 8 * s);
-    B0 = ldg16(bp0);
-    B1 = ldg16(bp1);
-    for (int kb = 0; kb < GI; ++kb) {
-        const bool more = kb + 1 < GI;
-        if (more) {
+    for (int mb = 0; mb < (TWO ? 2 : 1); ++mb)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) An[s] = ldg16(ap + (kb + 1) * 64 + 8 * s);
-            B0n = ldg16(bp0 + (kb + 1) * 32);
-            B1n = ldg16(bp1 + (kb + 1) * 32);
-        }
-        const uint32_t w0[4] = {B0.x, B0.y, B0.z, B0.w};
-        const uint32_t w1[4] = {B1.x, B1.y, B1.z, B1.w};
+        for (int j = 0; j < 16; ++j) {
+            const int mi = mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+            const int o = s_out[mi];
+            if (o < 0) continue;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bf16x8 av = as_bf16x8(A[s]);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, nib8_to_bf16(w0[s]), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, nib8_to_bf16(w1[s]), acc1, 0, 0, 0);
-        }
-        if (GS) {
-            const float f0 = dsc[(size_t)min(c0, H - 1) * GI + kb];
-            const float f1 = dsc[(size_t)min(c0 + 32, H - 1) * GI + kb];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int m = m0 + wm * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-                const int out = a.rows_out[it.begin + min(m, it.count - 1)];
-                const float cs = kOffset * a.sh[(size_t)out * GI + kb];
-                tot0[j] = fmaf(f0, acc0[j] - cs, tot0[j]);
-                tot1[j] = fmaf(f1, acc1[j] - cs, tot1[j]);
-                acc0[j] = 0.f;
-                acc1[j] = 0.f;
+            for (int b = 0; b < 2; ++b) {
+                if (cols[b] >= H) continue;
+                const float y = GS ? out[b][mb][j] : f[b] * (out[b][mb][j] - kOffset * s_tot[mi]);
+                a.y_rows[(size_t)o * H + cols[b]] = y;
             }
         }
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) A[s] = An[s];
-            B0 = B0n;
-            B1 = B1n;
-        }
+}
+
+template <bool GS>
+__global__ __launch_bounds__(256) void gemm_down_kernel(GemmArgs a) {
+    __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
+    __shared__ float s_tot[kTileM];              // per-row sum of the bf16 h row
+    __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
+    __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: 136 * group sums, [row][group]
+    int tile, rb;
+    if (!unit_of(*a.n_tiles, (a.H + 255) / 256, tile, rb)) return;
+    const int2 td = a.tiles[tile];
+    const WorkItem it = a.items[td.x];
+    const int m0 = td.y;
+    if (threadIdx.x < kTileM) {
+        const int m = m0 + (int)threadIdx.x;
+        s_out[threadIdx.x] = m < it.count ? a.rows_out[it.begin + m] : -1;
     }
-    const float f0 = GS ? 1.f : dsc[min(c0, H - 1)], f1 = GS ? 1.f : dsc[min(c0 + 32, H - 1)];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-        if (m >= it.count) continue;
-        const int out = a.rows_out[it.begin + m];
-        float y0, y1;
-        if (GS) {
-            y0 = tot0[j];
-            y1 = tot1[j];
-        } else {
-            const float s = s_tot[m - m0];
-            y0 = f0 * (acc0[j] - kOffset * s);
-            y1 = f1 * (acc1[j] - kOffset * s);
-        }
-        if (c0 < H) a.y_rows[(size_t)out * H + c0] = y0;
-        if (c0 + 32 < H) a.y_rows[(size_t)out * H + c0 + 32] = y1;
+    if (!GS && threadIdx.x < kTileM) {
+        const int GI = a.I / 64;
+        const int o = a.rows_out[it.begin + min(m0 + (int)threadIdx.x, it.count - 1)];
+        float s = 0.f;
+        for (int q = 0; q < GI; ++q) s += a.sh[(size_t)o * GI + q];
+        s_tot[threadIdx.x] = s;
     }
+    if (it.count - m0 > 32) down_tile<GS, true>(a, it, m0, rb, sA, s_cs, s_tot, s_out);
+    else down_tile<GS, false>(a, it, m0, rb, sA, s_cs, s_tot, s_out);
 }
 
 }  // namespace
@@ -376,14 +474,14 @@ coli_status launch_mfma_ffn(const GemmArgs& a, const float* x, int32_t T, int32_
     COLI_CHECK_LAUNCH("tile list kernel launch");
     {
         ProfTag prof("gemm_gateup");
-        const dim3 grid(max_tiles, a.I / 64);
+        const dim3 grid((unsigned)(8 * (((size_t)max_tiles * ((a.I + 127) / 128) + 7) / 8)));
         if (a.group) launch(gemm_gateup_kernel<true>, grid, dim3(256), 0, stream, a);
         else launch(gemm_gateup_kernel<false>, grid, dim3(256), 0, stream, a);
     }
     COLI_CHECK_LAUNCH("gate/up GEMM launch");
     {
         ProfTag prof("gemm_down");
-        const dim3 grid(max_tiles, (a.H + 127) / 128);
+        const dim3 grid((unsigned)(8 * (((size_t)max_tiles * ((a.H + 255) / 256) + 7) / 8)));
         if (a.group) launch(gemm_down_kernel<true>, grid, dim3(256), 0, stream, a);
         else launch(gemm_down_kernel<false>, grid, dim3(256), 0, stream, a);
     }
