@@ -2,21 +2,27 @@
 // the T*k (token, slot) assignments are grouped by expert so that each
 // unique expert's weights are read once for all of its tokens.
 //
-// One workgroup of 1024 threads, deterministic throughout:
-//  1. every wave takes 64-assignment chunks; inside a chunk, lanes holding the
-//     same expert are found with ballots (one round per distinct expert), which
-//     gives each assignment its rank among equal experts of its chunk and the
-//     chunk's per-expert count;
-//  2. per expert, an exclusive scan over the chunks (in chunk order);
-//  3. counts -> offsets (exclusive scan over experts) and the unique list;
-//  4. scatter: perm[offsets[e] + chunk_prefix[c][e] + rank] = a.
+// Three passes over slabs of 1024 assignments, deterministic throughout:
+//  1. per slab (one workgroup, 16 waves of 64): lanes holding the same expert
+//     are found with ballots (one round per distinct expert in the wave),
+//     which gives each assignment its rank among equal experts of its wave and
+//     the wave's per-expert count; an exclusive scan over the 16 waves (in
+//     order) turns that into the rank inside the slab and the slab's count;
+//  2. one workgroup: per expert, an exclusive scan of the slab counts (in slab
+//     order), the expert's total, then offsets (exclusive scan over experts)
+//     and the unique list;
+//  3. per slab: perm[offsets[e] + slab_prefix[s][e] + rank] = a.
 // The result is the stable counting sort of the assignments by expert.
+#include <algorithm>
+
 #include "common.h"
 
 namespace coli {
 namespace {
 
 constexpr int kUnionThreads = 1024;
+constexpr int kSlab = kUnionThreads;           // assignments per slab
+constexpr int kSlabWaves = kSlab / 64;
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
     // Hillis-Steele over 1024 threads; sh has 1024 ints.
@@ -35,47 +41,72 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
     return incl - v;
 }
 
-__global__ __launch_bounds__(kUnionThreads) void union_kernel(
-    const int32_t* __restrict__ idx, int n, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ unique,
-    int32_t* __restrict__ n_unique, int32_t* __restrict__ chunk_cnt /* [C][E] */,
+__device__ __forceinline__ int valid_expert(const int32_t* idx, int a, int n, int E) {
+    const int e = a < n ? idx[a] : -1;
+    return (e >= 0 && e < E) ? e : -1;           // out-of-range entries are skipped
+}
+
+// Pass 1. Dynamic LDS: kSlabWaves * E ints.
+__global__ __launch_bounds__(kUnionThreads) void union_count_kernel(
+    const int32_t* __restrict__ idx, int n, int E, int32_t* __restrict__ slab_cnt /* [S][E] */,
     int32_t* __restrict__ rank /* [n] */) {
-    __shared__ int sh[kUnionThreads];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nwaves = kUnionThreads / 64;
-    const int C = (n + 63) / 64;
-    for (int i = t; i < C * E; i += kUnionThreads) chunk_cnt[i] = 0;
+    extern __shared__ int s_cnt[];               // [wave][E]: counts, then exclusive prefixes
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    for (int i = t; i < kSlabWaves * E; i += kUnionThreads) s_cnt[i] = 0;
     __syncthreads();
-    // 1. ranks inside each chunk
-    for (int c = wave; c < C; c += nwaves) {
-        const int a = c * 64 + lane;
-        int e = (a < n) ? idx[a] : -1;
-        if (e >= E) e = -1;                       // out-of-range entries are skipped
-        unsigned long long active = __ballot(e >= 0);
-        while (active) {
-            const int leader = __ffsll((long long)active) - 1;
-            const int v = __shfl(e, leader);
-            const unsigned long long m = __ballot(e == v) & active;
-            if (e == v) {
-                const unsigned long long below = (lane == 0) ? 0ull : (m & ((1ull << lane) - 1ull));
-                rank[a] = __popcll(below);
-            }
-            if (lane == leader) chunk_cnt[(int64_t)c * E + v] = __popcll(m);
-            active &= ~m;
-        }
+    const int a = blockIdx.x * kSlab + t;
+    const int e = valid_expert(idx, a, n, E);
+    int r = 0;
+    unsigned long long active = __ballot(e >= 0);
+    while (active) {
+        const int leader = __ffsll((long long)active) - 1;
+        const int v = __shfl(e, leader);
+        const unsigned long long m = __ballot(e == v) & active;
+        if (e == v) r = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == leader) s_cnt[wave * E + v] = __popcll(m);
+        active &= ~m;
     }
     __syncthreads();
-    // 2. per-expert exclusive scan over chunks, in chunk order
+    for (int x = t; x < E; x += kUnionThreads) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kSlabWaves; ++w) {
+            const int v = s_cnt[w * E + x];
+            s_cnt[w * E + x] = c;
+            c += v;
+        }
+        slab_cnt[(int64_t)blockIdx.x * E + x] = c;
+    }
+    __syncthreads();
+    if (e >= 0) rank[a] = s_cnt[wave * E + e] + r;
+}
+
+// Pass 2: one workgroup.
+__global__ __launch_bounds__(kUnionThreads) void union_scan_kernel(
+    int S, int E, int32_t* __restrict__ slab_cnt, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ unique, int32_t* __restrict__ n_unique) {
+    __shared__ int sh[kUnionThreads];
+    const int t = threadIdx.x;
     int cnt = 0;
     if (t < E) {
-        for (int c = 0; c < C; ++c) {
-            const int v = chunk_cnt[(int64_t)c * E + t];
-            chunk_cnt[(int64_t)c * E + t] = cnt;
+        int s = 0;
+        for (; s + 8 <= S; s += 8) {             // independent loads, then the serial sum
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = slab_cnt[(int64_t)(s + j) * E + t];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                slab_cnt[(int64_t)(s + j) * E + t] = cnt;
+                cnt += v[j];
+            }
+        }
+        for (; s < S; ++s) {
+            const int v = slab_cnt[(int64_t)s * E + t];
+            slab_cnt[(int64_t)s * E + t] = cnt;
             cnt += v;
         }
         counts[t] = cnt;
     }
-    __syncthreads();
-    // 3. offsets and the unique list
     int total = 0;
     const int off = block_exclusive_scan(t < E ? cnt : 0, sh, &total);
     if (t < E) offsets[t] = off;
@@ -84,21 +115,22 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(
     const int upos = block_exclusive_scan((t < E && cnt > 0) ? 1 : 0, sh, &nu);
     if (t < E && cnt > 0) unique[upos] = t;
     if (t == 0) *n_unique = nu;
-    // offsets[] of other threads are needed below: keep them in shared memory
-    __syncthreads();
-    sh[t] = off;
-    __syncthreads();
-    // 4. scatter
-    for (int a = t; a < n; a += kUnionThreads) {
-        const int e = idx[a];
-        if (e < 0 || e >= E) continue;
-        const int c = a / 64;
-        perm[sh[e] + chunk_cnt[(int64_t)c * E + e] + rank[a]] = a;
-    }
+}
+
+// Pass 3.
+__global__ __launch_bounds__(kUnionThreads) void union_scatter_kernel(
+    const int32_t* __restrict__ idx, int n, int E, const int32_t* __restrict__ slab_cnt,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm) {
+    const int a = blockIdx.x * kSlab + threadIdx.x;
+    const int e = valid_expert(idx, a, n, E);
+    if (e < 0) return;
+    perm[offsets[e] + slab_cnt[(int64_t)blockIdx.x * E + e] + rank[a]] = a;
 }
 
 // Work list for the FFN kernels: optional shared expert first, then the
 // unique experts in ascending order (optionally only those of one phase).
+// Every workgroup fills 256 rows of the slot list; workgroup 0 builds the list.
 __global__ __launch_bounds__(256) void plan_kernel(
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ unique,
@@ -109,15 +141,16 @@ __global__ __launch_bounds__(256) void plan_kernel(
     __shared__ int sh[256];
     const int t = threadIdx.x;
     const int n = T * k;
-    for (int p = t; p < n; p += 256) {
+    const int p = blockIdx.x * 256 + t;          // slot-list rows: one per thread over the grid
+    if (p < n) {
         const int a = perm[p];
         rows_tok[p] = a / k;
         rows_out[p] = a;
+    } else if (p < n + T) {
+        rows_tok[p] = p - n;
+        rows_out[p] = p;
     }
-    for (int s = t; s < T; s += 256) {
-        rows_tok[n + s] = s;
-        rows_out[n + s] = n + s;
-    }
+    if (blockIdx.x != 0) return;
     const int has_shared = shared_blob != nullptr ? 1 : 0;
     if (t == 0 && has_shared) {
         WorkItem it;
@@ -162,20 +195,30 @@ __global__ __launch_bounds__(256) void plan_kernel(
 }  // namespace
 
 size_t union_ws_bytes(int32_t T, int32_t k, int32_t E) {
-    const size_t n = (size_t)T * k, C = (n + 63) / 64;
-    return align256(C * (size_t)E * 4) + align256(n * 4 + 4);
+    const size_t n = (size_t)T * k, S = (n + kSlab - 1) / kSlab;
+    return align256(S * (size_t)E * 4) + align256(n * 4 + 4);
 }
 
 coli_status launch_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
                          int32_t* offsets, int32_t* perm, int32_t* unique, int32_t* n_unique,
                          void* ws, hipStream_t stream) {
     const int n = T * k;
-    const size_t C = ((size_t)n + 63) / 64;
-    int32_t* chunk_cnt = (int32_t*)ws;
-    int32_t* rank = (int32_t*)((char*)ws + align256(C * (size_t)E * 4));
-    launch(union_kernel, dim3(1), dim3(kUnionThreads), 0, stream, idx, n, E, counts,
-                       offsets, perm, unique, n_unique, chunk_cnt, rank);
-    COLI_CHECK_LAUNCH("union kernel launch");
+    const int S = (n + kSlab - 1) / kSlab;
+    int32_t* slab_cnt = (int32_t*)ws;
+    int32_t* rank = (int32_t*)((char*)ws + align256((size_t)S * E * 4));
+    if (S > 0) {
+        launch(union_count_kernel, dim3(S), dim3(kUnionThreads), (size_t)kSlabWaves * E * 4, stream,
+               idx, n, E, slab_cnt, rank);
+        COLI_CHECK_LAUNCH("union count kernel launch");
+    }
+    launch(union_scan_kernel, dim3(1), dim3(kUnionThreads), 0, stream, S, E, slab_cnt, counts,
+           offsets, unique, n_unique);
+    COLI_CHECK_LAUNCH("union scan kernel launch");
+    if (S > 0) {
+        launch(union_scatter_kernel, dim3(S), dim3(kUnionThreads), 0, stream, idx, n, E, slab_cnt,
+               rank, offsets, perm);
+        COLI_CHECK_LAUNCH("union scatter kernel launch");
+    }
     return COLI_OK;
 }
 
@@ -185,7 +228,8 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
                         int32_t k, int32_t E, const uint8_t* phase_mask, int32_t phase,
                         WorkItem* items, int32_t* n_items, int32_t* rows_tok, int32_t* rows_out,
                         hipStream_t stream) {
-    launch(plan_kernel, dim3(1), dim3(256), 0, stream, offsets, perm, unique,
+    const int rows = T * k + T;
+    launch(plan_kernel, dim3(std::max(1, (rows + 255) / 256)), dim3(256), 0, stream, offsets, perm, unique,
                        n_unique, blob_table, shared_blob, T, k, E, phase_mask, phase, items,
                        n_items, rows_tok, rows_out);
     COLI_CHECK_LAUNCH("plan kernel launch");
