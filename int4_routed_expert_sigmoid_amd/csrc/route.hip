@@ -34,67 +34,80 @@ __global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ w
 
 constexpr int kMaxExpertsPerLane = 16;   // E <= 1024
 
-template <int S>
-__device__ __forceinline__ void argmax_step(float& bk, int& bi) {
-    const float ok = __int_as_float(lane_xchg<S>(__float_as_int(bk)));
-    const int oi = lane_xchg<S>(bi);
-    if (oi != 0x7fffffff && (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi))) {
-        bk = ok;
-        bi = oi;
-    }
+// Selection order as one unsigned 64-bit number: the key's bits mapped so
+// that unsigned order is float order (high word), then the complement of the
+// expert id (low word), so a larger key wins and equal keys go to the lower
+// id. A -0.0 key is folded to +0.0 first (they compare equal as floats).
+// Every valid entry is nonzero; 0 marks an empty or taken entry.
+__device__ __forceinline__ uint64_t selection_code(float key, int e) {
+    const uint32_t b = __float_as_uint(key + 0.0f);
+    const uint32_t o = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
 }
 
-// Route one token with one wave. Lane l holds experts l, l+64, ... . k rounds
-// of a wave arg-max over (key descending, index ascending) pick the experts
-// in slot order; the weights are normalised in double in slot order.
+template <int S>
+__device__ __forceinline__ void max_step(uint64_t& v) {
+    const uint32_t hi = (uint32_t)lane_xchg<S>((int)(uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)lane_xchg<S>((int)(uint32_t)v);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+}
+
+// Route one token with one wave. Lane l holds experts l, l+64, ... . Each of
+// the k rounds takes the lane maxima of the selection codes, a wave-wide
+// maximum (butterfly over DPP / permlane partners, no branches), and retires
+// the winner; the picks come out in slot order. The weights are normalised in
+// double in slot order.
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ lrow,
                                             const float* __restrict__ bias, int E, int k,
                                             int* __restrict__ idx_row, float* __restrict__ w_row,
                                             int* lds_idx = nullptr) {
     const int lane = threadIdx.x & 63;
-    float score[EPL], key[EPL];
-    bool avail[EPL];
+    uint64_t code[EPL];
+    float score[EPL], lv[EPL], bv[EPL];
+    // all loads first (clamped ids), then branch-free arithmetic
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+        lv[i] = lrow[e];
+        bv[i] = bias ? bias[e] : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        avail[i] = e < E;
-        score[i] = 0.f;
-        key[i] = 0.f;
-        if (avail[i]) {
-            const double l = (double)lrow[e];
-            score[i] = (float)(1.0 / (1.0 + exp(-l)));
-            key[i] = score[i] + (bias ? bias[e] : 0.f);
-        }
+        const bool valid = e < E;
+        const float s = (float)(1.0 / (1.0 + exp(-(double)lv[i])));
+        score[i] = valid ? s : 0.f;
+        code[i] = valid ? selection_code(s + bv[i], e) : 0;
     }
     double sum = 0.0;
     float my_sel = 0.f;      // lane j (< k) keeps the score of slot j
     int my_idx = 0;
     for (int j = 0; j < k; ++j) {
-        float bk = 0.f;
-        int bi = 0x7fffffff;
+        uint64_t m = code[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) m = code[i] > m ? code[i] : m;
+        max_step<1>(m);
+        max_step<2>(m);
+        max_step<4>(m);
+        max_step<8>(m);
+        max_step<16>(m);
+        max_step<32>(m);
+        const uint32_t wlo = __builtin_amdgcn_readfirstlane((uint32_t)m);
+        const uint32_t whi = __builtin_amdgcn_readfirstlane((uint32_t)(m >> 32));
+        const uint64_t win = ((uint64_t)whi << 32) | wlo;
+        const int e = (int)~wlo;
+        float c = 0.f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            if (!avail[i]) continue;
-            const int e = lane + 64 * i;
-            if (bi == 0x7fffffff || key[i] > bk) { bk = key[i]; bi = e; }
+            const bool hit = code[i] == win;
+            c = hit ? score[i] : c;
+            code[i] = hit ? 0 : code[i];
         }
-        // wave arg-max (all lanes get the winner): larger key wins, equal
-        // keys go to the lower index; partners exchanged with DPP/permlane
-        argmax_step<1>(bk, bi);
-        argmax_step<2>(bk, bi);
-        argmax_step<4>(bk, bi);
-        argmax_step<8>(bk, bi);
-        argmax_step<16>(bk, bi);
-        argmax_step<32>(bk, bi);
-        const int owner = __builtin_amdgcn_readfirstlane(bi & 63), slot = bi >> 6;
-        float s_sel = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (i == slot && lane == owner) { avail[i] = false; s_sel = score[i]; }
-        s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_sel), owner));
+        const float s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), e & 63));
         sum += (double)s_sel;
-        if (lane == j) { my_sel = s_sel; my_idx = bi; }
+        if (lane == j) { my_sel = s_sel; my_idx = e; }
     }
     if (lane < k) {
         idx_row[lane] = my_idx;
@@ -177,19 +190,20 @@ __global__ __launch_bounds__(kRouterThreads) void router_prep_kernel(SmallRouter
     }
 }
 
-// Exclusive prefix sum over the 256 threads of the block (v >= 0); *total
-// receives the sum. Wave scans by shuffles, then one pass over wave totals.
-__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+// Exclusive prefix sum over the 256 threads of the block, modulo 2^32;
+// *total receives the sum. Wave scans by shuffles, then one pass over the
+// wave totals.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
+    uint32_t incl = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, o);
         if (lane >= o) incl += y;
     }
     if (lane == 63) sh[wave] = incl;
     __syncthreads();
-    int base = 0;
+    uint32_t base = 0;
     for (int w = 0; w < wave; ++w) base += sh[w];
     *total = sh[0] + sh[1] + sh[2] + sh[3];
     __syncthreads();
@@ -202,11 +216,19 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     __shared__ int s_idx[kSmallT * 32];
     __shared__ int s_cnt[1024];
     __shared__ int s_off[1024];
-    __shared__ int s_uniq[1024];
-    __shared__ int s_scan[4];
+    __shared__ uint32_t s_scan[4];
     const int tid = threadIdx.x, wave = tid >> 6;
     const int T = a.T, E = a.E, k = a.k;
     const float* lg = a.router_w ? a.logits_out : a.logits_in;
+    // blob pointers of this thread's experts, loaded now so that their latency
+    // hides behind the routing
+    const bool with_items = a.table != nullptr;
+    const void* tptr[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        tptr[i] = (with_items && e < E) ? a.table[e] : nullptr;
+    }
     for (int t = wave; t < T; t += kRouterThreads / 64)
         route_token<EPL>(lg + (int64_t)t * E, a.bias, E, k, a.idx + (int64_t)t * k,
                          a.w + (int64_t)t * k, s_idx + t * k);
@@ -216,18 +238,25 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     const int n = T * k;
     for (int i = tid; i < n; i += kRouterThreads) atomicAdd(&s_cnt[s_idx[i]], 1);
     __syncthreads();
-    // offsets and unique list: thread tid owns experts tid*EPT .. tid*EPT+3
-    int c[EPT], sum = 0, nz = 0;
+    // offsets, the unique list and the kept work items in one scan: thread
+    // tid owns experts tid*EPT .. tid*EPT+3 and scans the packed triple
+    // (assignments << 22 | unique << 11 | kept); the fields cannot carry
+    // (assignments <= 512, experts <= 1024)
+    int c[EPT];
+    uint32_t packed = 0;
+    bool keep[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
         c[i] = e < E ? s_cnt[e] : 0;
-        sum += c[i];
-        nz += c[i] > 0 ? 1 : 0;
+        keep[i] = with_items && c[i] > 0 &&
+                  (a.phase_mask == nullptr || a.phase_mask[e] == a.phase);
+        packed += ((uint32_t)c[i] << 22) + ((uint32_t)(c[i] > 0) << 11) + (uint32_t)keep[i];
     }
-    int total = 0, nu = 0;
-    int off = block_excl_scan(sum, s_scan, &total);
-    int upos = block_excl_scan(nz, s_scan, &nu);
+    uint32_t total = 0;
+    const uint32_t pre = block_excl_scan(packed, s_scan, &total);
+    int off = (int)(pre >> 22), upos = (int)((pre >> 11) & 0x7FF), kpos = (int)(pre & 0x7FF);
+    const int base = a.shared_blob ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
@@ -235,54 +264,32 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
             a.counts[e] = c[i];
             a.offsets[e] = off;
             s_off[e] = off;
-            if (c[i] > 0) { a.unique[upos] = e; s_uniq[upos] = e; ++upos; }
+            if (c[i] > 0) a.unique[upos++] = e;
+            if (keep[i]) {
+                WorkItem it;
+                it.blob = (const uint8_t*)tptr[i];
+                it.begin = off;
+                it.count = c[i];
+                a.items[base + kpos++] = it;
+            }
             off += c[i];
         }
     }
     if (tid == 0) {
-        a.offsets[E] = total;
-        *a.n_unique = nu;
+        a.offsets[E] = (int)(total >> 22);
+        *a.n_unique = (int)((total >> 11) & 0x7FF);
+        // work items: the shared expert first, then the kept unique experts;
+        // without a table (cached calls) the items are formed later
+        if (with_items && a.shared_blob) {
+            WorkItem it;
+            it.blob = (const uint8_t*)a.shared_blob;
+            it.begin = n;
+            it.count = T;
+            a.items[0] = it;
+        }
+        *a.n_items = with_items ? base + (int)(total & 0x7FF) : 0;
     }
     __syncthreads();
-    // work items: the shared expert first, then the unique experts (of one
-    // phase); without a table (cached calls) the items are formed later
-    if (a.table == nullptr) {
-        if (tid == 0) *a.n_items = 0;
-    }
-    const int base = a.shared_blob ? 1 : 0;
-    if (tid == 0 && a.shared_blob && a.table) {
-        WorkItem it;
-        it.blob = (const uint8_t*)a.shared_blob;
-        it.begin = n;
-        it.count = T;
-        a.items[0] = it;
-    }
-    int keep[EPT], nk = 0;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int u = tid * EPT + i;
-        keep[i] = 0;
-        if (u < nu && a.table) {
-            const int e = s_uniq[u];
-            keep[i] = (a.phase_mask == nullptr || a.phase_mask[e] == a.phase) ? 1 : 0;
-        }
-        nk += keep[i];
-    }
-    int nkeep = 0;
-    int kpos = block_excl_scan(nk, s_scan, &nkeep);
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const int u = tid * EPT + i;
-        if (keep[i]) {
-            const int e = s_uniq[u];
-            WorkItem it;
-            it.blob = (const uint8_t*)a.table[e];
-            it.begin = s_off[e];
-            it.count = s_cnt[e];
-            a.items[base + kpos++] = it;
-        }
-    }
-    if (tid == 0 && a.table) *a.n_items = base + nkeep;
     // stable positions: rank of assignment i among earlier equal experts
     for (int i = tid; i < n; i += kRouterThreads) {
         const int e = s_idx[i];
