@@ -66,6 +66,7 @@ WsLayout ws_layout(const coli_moe_shape* s, int32_t T, int32_t path) {
     W.rows_out = take(R * 4);
     W.xplanes = take((size_t)T * (H / kBlock) * kWordsPerBlock * 4);
     W.xscale = take((size_t)T * (H / kBlock) * 4);
+    W.gu = take(R * 2 * I * 4);
     W.hplanes = take(R * (I / kBlock) * kWordsPerBlock * 4);
     W.hscale = take(R * (I / kBlock) * 4);
     W.y_rows = take(R * H * 4);

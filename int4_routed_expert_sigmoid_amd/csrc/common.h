@@ -282,11 +282,14 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
 coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* planes, float* scales,
                           hipStream_t stream);
 // gate/up then down GEMV over a work list.
+// gu [rows][2][I] f32 holds g and u between the two passes; for batches
+// (max_count > 1) an activation pass encodes h = silu(g) * u of all `rows`
+// rows into hplanes [rows][I/32][16] / hscale [rows][I/32].
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
-                            int32_t max_count, const int32_t* rows_tok, const int32_t* rows_out,
-                            const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
-                            float* hscale, float* y_rows, int32_t H, int32_t I, int32_t group,
-                            hipStream_t stream);
+                            int32_t max_count, int32_t rows, const int32_t* rows_tok,
+                            const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
+                            float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
+                            int32_t I, int32_t group, hipStream_t stream);
 coli_status launch_combine(const float* y_rows, const float* w, int32_t T, int32_t k, int32_t H,
                            int32_t has_shared, float routed_scale, float* y, hipStream_t stream);
 

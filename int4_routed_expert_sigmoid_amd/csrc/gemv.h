@@ -5,20 +5,24 @@
 
 namespace coli {
 
-// Launch the gate/up kernel on grid (I/32, max_items); false if H is outside
-// the instantiated range.
+// Launch the gate/up kernel on grid (2*I/32 for mt == 1, else I/32;
+// max_items): g and u, f32, into gu [rows][2][I]; false if H is outside the
+// instantiated range.
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
-                     const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
-                     float* hscale, int H, int I, const BlobLayout& L);
+                     const uint32_t* xplanes, const float* xscale, float* gu, int H, int I,
+                     const BlobLayout& L);
 
 constexpr int kDownRowsPerWave = 16;
 constexpr int kDownRowsPerBlock = 4 * kDownRowsPerWave;
 
-// Launch the down kernel on grid (ceil(H/64), max_items); false if I is
-// outside the instantiated range.
+// Launch the down kernel on grid (ceil(H/64), max_items) into y_rows. mt == 1
+// forms h = silu(g) * u from gu itself; larger mt reads the digit blocks of h
+// (hplanes, hscale) written by the activation pass. False if I is outside the
+// instantiated range.
 bool dispatch_down(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
-                   const int32_t* n_items, const int32_t* rows_out, const uint32_t* hplanes,
-                   const float* hscale, float* y_rows, int H, int I, const BlobLayout& L);
+                   const int32_t* n_items, const int32_t* rows_out, const float* gu,
+                   const uint32_t* hplanes, const float* hscale, float* y_rows, int H, int I,
+                   const BlobLayout& L);
 
 }  // namespace coli

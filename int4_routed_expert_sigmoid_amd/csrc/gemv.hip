@@ -6,6 +6,8 @@
 // SwiGLU): h = silu(gate x) * (up x), y = down h, for every (expert, token)
 // pair of a work list, each expert's weights streamed once per pass of up to
 // MT tokens.
+#include <algorithm>
+
 #include "gemv.h"
 
 namespace coli {
@@ -38,20 +40,65 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
     }
 }
 
+// ------------------------------------------------------------- activation
+// h = silu(g) * u for rows [0, R) of gu [R][2][I], each 32-element block
+// encoded into digit planes: planes [R][I/32][4][4] u32, scales [R][I/32].
+// One 8-element quarter per thread; the quarters of a block sit in 4 adjacent
+// lanes and every lane runs the encoder (its shuffles need them all).
+__global__ __launch_bounds__(256) void act_encode_kernel(const float* __restrict__ gu, int R, int I,
+                                                         uint32_t* __restrict__ hplanes,
+                                                         float* __restrict__ hscale) {
+    const int CI = I / kBlock;
+    const int64_t nq = (int64_t)R * CI * 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t ic = i < nq ? i : nq - 1;
+    const int row = (int)(ic / (CI * 4)), rem = (int)(ic % (CI * 4)), blk = rem >> 2, q = rem & 3;
+    const float* gp = gu + (size_t)row * 2 * I + blk * kBlock + q * 8;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float g = gp[e], u = gp[I + e];
+        v[e] = g / (1.f + expf(-g)) * u;
+    }
+    uint32_t words[kPlanes];
+    const float sc = encode_quarter(v, words);
+    if (i < nq) {
+        uint32_t* dst = hplanes + ((size_t)row * CI + blk) * kWordsPerBlock;
+#pragma unroll
+        for (int p = 0; p < kPlanes; ++p) dst[p * 4 + q] = words[p];
+        if (q == 0) hscale[(size_t)row * CI + blk] = sc;
+    }
+}
+
 // ----------------------------------------------------------------- combine
 // y[t][c] = shared[t][c] + rs * sum_j w[t][j] * y_rows[t*k + j][c], slot order.
+// Grid: (column blocks of 256, tokens); the slot loads are issued in groups of
+// 8 before their multiply-adds, which keep the slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_rows,
                                                       const float* __restrict__ w, int T, int k,
                                                       int H, int has_shared, float rs,
                                                       float* __restrict__ y) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)T * H) return;
-    const int t = (int)(i / H), c = (int)(i % H);
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j)
-        acc = fmaf(w[(int64_t)t * k + j], y_rows[((int64_t)t * k + j) * H + c], acc);
-    const float sh = has_shared ? y_rows[((int64_t)T * k + t) * H + c] : 0.f;
-    y[i] = fmaf(rs, acc, sh);
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= H) return;
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        const float* wt = w + (int64_t)t * k;
+        const float* yr = y_rows + (int64_t)t * k * H + c;
+        const float sh = has_shared ? y_rows[((int64_t)T * k + t) * H + c] : 0.f;
+        float acc = 0.f;
+        int j = 0;
+        for (; j + 8 <= k; j += 8) {
+            float wv[8], yv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                wv[q] = wt[j + q];
+                yv[q] = yr[(int64_t)(j + q) * H];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc = fmaf(wv[q], yv[q], acc);
+        }
+        for (; j < k; ++j) acc = fmaf(wt[j], yr[(int64_t)j * H], acc);
+        y[(int64_t)t * H + c] = fmaf(rs, acc, sh);
+    }
 }
 
 }  // namespace
@@ -67,27 +114,33 @@ coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* pla
 }
 
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
-                            int32_t max_count, const int32_t* rows_tok, const int32_t* rows_out,
-                            const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
-                            float* hscale, float* y_rows, int32_t H, int32_t I, int32_t group,
-                            hipStream_t stream) {
+                            int32_t max_count, int32_t rows, const int32_t* rows_tok,
+                            const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
+                            float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
+                            int32_t I, int32_t group, hipStream_t stream) {
     if (max_items == 0) return COLI_OK;
     const BlobLayout L = blob_layout(H, I, group);
     const int mt = max_count <= 1 ? 1 : max_count <= 2 ? 2 : max_count <= 4 ? 4 : 8;
-    const dim3 g1(I / kBlock, max_items);
+    const dim3 g1((mt == 1 ? 2 : 1) * (I / kBlock), max_items);   // one token: gate and up apart
     bool ok;
     {
         ProfTag prof("gemv_gateup");
         ok = dispatch_gateup(mt, group, g1, stream, items, n_items, rows_tok, rows_out, xplanes,
-                             xscale, hplanes, hscale, H, I, L);
+                             xscale, gu, H, I, L);
     }
     if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: hidden too large (max 16384)");
     COLI_CHECK_LAUNCH("gate/up GEMV launch");
+    if (mt > 1) {
+        const int64_t threads = (int64_t)rows * (I / kBlock) * 4;
+        launch(act_encode_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, gu,
+               rows, I, hplanes, hscale);
+        COLI_CHECK_LAUNCH("activation kernel launch");
+    }
     const dim3 g2((H + kDownRowsPerBlock - 1) / kDownRowsPerBlock, max_items);
     {
         ProfTag prof("gemv_down");
-        ok = dispatch_down(mt, group, g2, stream, items, n_items, rows_out, hplanes, hscale, y_rows,
-                           H, I, L);
+        ok = dispatch_down(mt, group, g2, stream, items, n_items, rows_out, gu, hplanes, hscale,
+                           y_rows, H, I, L);
     }
     if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: inter too large (max 4096)");
     COLI_CHECK_LAUNCH("down GEMV launch");
@@ -96,10 +149,10 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
 
 coli_status launch_combine(const float* y_rows, const float* w, int32_t T, int32_t k, int32_t H,
                            int32_t has_shared, float routed_scale, float* y, hipStream_t stream) {
-    const int64_t n = (int64_t)T * H;
-    if (n == 0) return COLI_OK;
-    launch(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       y_rows, w, T, k, H, has_shared, routed_scale, y);
+    if ((int64_t)T * H == 0) return COLI_OK;
+    const dim3 grid((unsigned)((H + 255) / 256), (unsigned)std::min(T, 65535));
+    launch(combine_kernel, grid, dim3(256), 0, stream, y_rows, w, T, k, H, has_shared,
+           routed_scale, y);
     COLI_CHECK_LAUNCH("combine kernel launch");
     return COLI_OK;
 }

@@ -1,64 +1,55 @@
-// down half of the int4 GEMV family: y_e = down_e h for every (expert, token)
-// pair of a work list (practical guide section 二: gate, up, down adjacent).
+// down half of the int4 GEMV family: y_e = down_e h, h = silu(g) * u, for
+// every (expert, token) pair of a work list (practical guide section 二:
+// gate, up, down adjacent; SwiGLU).
 //
-// Workgroup: 4 waves x 16 rows of one work item's down matrix. Lane l owns
-// the 32-column blocks l + 64*j of h (the digit blocks written by the gate/up
-// pass) and reads each row's 16 bytes in those blocks with one 128-bit load.
-// Rows go in batches of LB = 4/MT rows whose LB*MT partials per lane are
-// summed over the wave by one transpose-reduction; the next batch's loads are
-// issued before the current batch is computed.
+// Workgroup: 4 waves x 16 rows of one work item's down matrix. For one token
+// it first forms h from the f32 g and u of the gate/up pass and encodes each
+// 32-element block into digit planes (common.h) in LDS, once for the
+// workgroup; for batches the activation pass has encoded the blocks once per
+// row. Lane l owns the 32-column blocks l + 64*j of h and
+// reads each row's 16 bytes in those blocks with one 128-bit load. Rows go in
+// batches of LB = 4/MT rows whose LB*MT partials per lane are summed over the
+// wave by one transpose-reduction; loads run one or two batches ahead of the
+// arithmetic, and the first are requested before h is formed.
+#include <algorithm>
+
 #include "gemv.h"
 
 namespace coli {
 namespace {
 
-template <int NCH, int MT, bool GS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH == 1 && MT <= 4 ? 4 : 2, 8)))
-void down_kernel(
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
-    const int32_t* __restrict__ rows_out, const uint32_t* __restrict__ hplanes,
-    const float* __restrict__ hscale, float* __restrict__ y_rows, int H, int I, BlobLayout L) {
+// One work item's rows of this workgroup for all of its tokens, MT at a time.
+// ENC (one-token launches): h is formed and encoded in LDS (s_h: [CI][16]
+// digit words, [CI] scales); otherwise the blocks come from hplanes/hscale.
+template <int NCH, int MT, bool GS, bool ENC>
+__device__ __forceinline__ void down_body(
+    const WorkItem& it, const int32_t* __restrict__ rows_out, const float* __restrict__ gu,
+    const uint32_t* __restrict__ hplanes, const float* __restrict__ hscale,
+    float* __restrict__ y_rows, int H, int I, const BlobLayout& L, uint32_t* s_h) {
     constexpr int LB = (4 / MT) > 0 ? (4 / MT) : 1;      // rows per batch
     constexpr int NV = LB * MT;                          // partials per batch (4, or 8 for MT 8)
     constexpr int SH = transpose_shift<NV>();
-    constexpr int NBT = kDownRowsPerWave / LB;           // batches per wave (even)
-    static_assert(NBT % 2 == 0, "batch count must be even");
-    const int item = blockIdx.y;
-    if (item >= *n_items) return;
-    const WorkItem it = items[item];
+    constexpr int NBT = kDownRowsPerWave / LB;           // batches per wave
+    constexpr int PD = (NCH == 1 && ENC) ? 3 : 2;        // weight register sets (prefetch depth + 1)
     const int CI = I / kBlock;
+    uint32_t* s_words = s_h;
+    float* s_scale = reinterpret_cast<float*>(s_h + (size_t)MT * CI * kWordsPerBlock);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rbase = blockIdx.x * kDownRowsPerBlock + wave * kDownRowsPerWave;
+    const bool live = rbase < H;                         // wave-uniform
     const uint8_t* dq = it.blob + L.down_q;
     const float* dsc = reinterpret_cast<const float*>(it.blob + L.down_s);
     const size_t rowbytes = (size_t)I / 2;
     const int gpr = GS ? I / 64 : 1;
 
-    for (int m0 = 0; m0 < it.count && rbase < H; m0 += MT) {
+    // the token loop is uniform over the workgroup (it holds barriers); waves
+    // past the last row only help to form h
+    int rowwin = 0;                                      // output rows of a 64-token window, one per lane
+    for (int m0 = 0; m0 < it.count; m0 += MT) {
         const int mc = min(MT, it.count - m0);
-        uint4 hp[MT][NCH][kPlanes];
-        float hs[MT][NCH];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int outr = (m < mc) ? rows_out[it.begin + m0 + m] : 0;
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const int ch = lane + 64 * j;
-                if (m < mc && ch < CI) {
-                    const uint4* src = reinterpret_cast<const uint4*>(
-                        hplanes + ((size_t)outr * CI + ch) * kWordsPerBlock);
-#pragma unroll
-                    for (int p = 0; p < kPlanes; ++p) hp[m][j][p] = src[p];
-                    hs[m][j] = hscale[(size_t)outr * CI + ch];
-                } else {
-#pragma unroll
-                    for (int p = 0; p < kPlanes; ++p) hp[m][j][p] = make_uint4(0, 0, 0, 0);
-                    hs[m][j] = 0.f;
-                }
-            }
-        }
-        uint4 wa[LB][NCH], wb[LB][NCH];
-        float fa[LB][NCH], fb[LB][NCH];
+        if (!ENC && (m0 & 63) == 0) rowwin = rows_out[it.begin + min(m0 + lane, it.count - 1)];
+        uint4 wbuf[PD][LB][NCH];
+        float fbuf[PD][LB][NCH];
         auto load = [&](uint4 (&wv)[LB][NCH], float (&fv)[LB][NCH], int batch) {
 #pragma unroll
             for (int r = 0; r < LB; ++r) {
@@ -66,76 +57,154 @@ void down_kernel(
 #pragma unroll
                 for (int j = 0; j < NCH; ++j) {
                     // unconditional loads: lanes past the row end re-read its last
-                    // block; their digit planes and scales are zero
+                    // block; their activation scales are zero
                     const int ch = min(lane + 64 * j, CI - 1);
                     wv[r][j] = ldg128(dq + row * rowbytes + (size_t)ch * 16);
                     if (GS) fv[r][j] = ldg_f32(dsc + (size_t)row * gpr + (ch >> 1));
                 }
             }
         };
-        auto compute = [&](const uint4 (&wv)[LB][NCH], const float (&fv)[LB][NCH], int batch) {
-            float part[NV];
 #pragma unroll
-            for (int r = 0; r < LB; ++r)
+        for (int b = 0; b < PD - 1; ++b) load(wbuf[b], fbuf[b], b);
+        asm volatile("" ::: "memory");    // keep these loads ahead of the barrier below
+        // one token: h = silu(g) * u, one 8-element quarter of a block per
+        // thread (the quarters of a block sit in 4 adjacent lanes, as the
+        // encoder's shuffles require); every lane runs the encoder. Larger
+        // batches read the blocks that the activation pass encoded once.
+        const int nq = ENC ? CI * 4 : 0;
+        for (int i0 = 0; i0 < nq; i0 += 256) {
+            const int i = i0 + (int)threadIdx.x, ic = min(i, nq - 1);
+            const int m = ic / (CI * 4), rem = ic % (CI * 4), blk = rem >> 2, q = rem & 3;
+            const int outr = rows_out[it.begin + m0 + min(m, mc - 1)];
+            const float* gp = gu + (size_t)outr * 2 * I + blk * kBlock + q * 8;
+            float v[8];
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    float acc = 0.f;
-                    if (m < mc) {
-#pragma unroll
-                        for (int j = 0; j < NCH; ++j) {
-                            const float f = GS ? hs[m][j] * fv[r][j] : hs[m][j];
-                            acc += (float)block_dot(wv[r][j], hp[m][j]) * f;
-                        }
-                    }
-                    part[r * MT + m] = acc;
-                }
-            const float v = wave_transpose_sum<NV>(part);
-            const int vi = lane >> SH;
-            const int r = vi / MT, m = vi % MT;
-            const int row = rbase + batch * LB + r;
-            if ((lane & ((1 << SH) - 1)) == 0 && m < mc && row < H) {
-                const int outr = rows_out[it.begin + m0 + m];
-                y_rows[(size_t)outr * H + row] = v * (GS ? 1.f : ldg_f32(dsc + row));
+            for (int e = 0; e < 8; ++e) {
+                const float g = gp[e], u = gp[I + e];
+                v[e] = g / (1.f + expf(-g)) * u;
             }
-        };
-        load(wa, fa, 0);
-#pragma unroll 1
-        for (int b = 0; b < NBT; b += 2) {
-            load(wb, fb, b + 1);
-            compute(wa, fa, b);
-            if (b + 2 < NBT) load(wa, fa, b + 2);
-            compute(wb, fb, b + 1);
+            uint32_t words[kPlanes];
+            const float sc = encode_quarter(v, words);
+            if (i < nq) {
+#pragma unroll
+                for (int p = 0; p < kPlanes; ++p) s_words[(m * CI + blk) * kWordsPerBlock + p * 4 + q] = words[p];
+                if (q == 0) s_scale[m * CI + blk] = m < mc ? sc : 0.f;
+            }
         }
+        __syncthreads();
+        if (live) {
+            uint4 hp[MT][NCH][kPlanes];
+            float hs[MT][NCH];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int outr = ENC ? 0 : __builtin_amdgcn_readlane(rowwin, (m0 & 63) + min(m, mc - 1));
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) {
+                    // unconditional loads (clamped token and block); tokens and
+                    // blocks past the end are masked where the partials are formed
+                    const int ch = lane + 64 * j, chc = min(ch, CI - 1);
+                    const uint4* src = ENC
+                        ? reinterpret_cast<const uint4*>(s_words + chc * kWordsPerBlock)
+                        : reinterpret_cast<const uint4*>(hplanes + ((size_t)outr * CI + chc) * kWordsPerBlock);
+#pragma unroll
+                    for (int p = 0; p < kPlanes; ++p) hp[m][j][p] = src[p];
+                    hs[m][j] = ENC ? s_scale[chc] : hscale[(size_t)outr * CI + chc];   // validity applied where used
+                }
+            }
+            auto compute = [&](const uint4 (&wv)[LB][NCH], const float (&fv)[LB][NCH], int batch) {
+                float part[NV];
+#pragma unroll
+                for (int r = 0; r < LB; ++r)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        float acc = 0.f;
+                        if (m < mc) {
+#pragma unroll
+                            for (int j = 0; j < NCH; ++j) {
+                                const float x = lane + 64 * j < CI ? hs[m][j] : 0.f;
+                                const float f = GS ? x * fv[r][j] : x;
+                                acc += (float)block_dot(wv[r][j], hp[m][j]) * f;
+                            }
+                        }
+                        part[r * MT + m] = acc;
+                    }
+                const float v = wave_transpose_sum<NV>(part);
+                const int vi = lane >> SH;
+                const int r = vi / MT, m = vi % MT;
+                const int row = rbase + batch * LB + r;
+                if ((lane & ((1 << SH) - 1)) == 0 && m < mc && row < H) {
+                    const int outr = rows_out[it.begin + m0 + m];
+                    y_rows[(size_t)outr * H + row] = v * (GS ? 1.f : ldg_f32(dsc + row));
+                }
+            };
+            if constexpr (PD == 3) {
+#pragma unroll
+                for (int b = 0; b < NBT; ++b) {
+                    if (b + 2 < NBT) load(wbuf[(b + 2) % 3], fbuf[(b + 2) % 3], b + 2);
+                    compute(wbuf[b % 3], fbuf[b % 3], b);
+                }
+            } else {
+                static_assert(NBT % 2 == 0, "batch count must be even");
+#pragma unroll 1
+                for (int b = 0; b < NBT; b += 2) {
+                    load(wbuf[1], fbuf[1], b + 1);
+                    compute(wbuf[0], fbuf[0], b);
+                    if (b + 2 < NBT) load(wbuf[0], fbuf[0], b + 2);
+                    compute(wbuf[1], fbuf[1], b + 1);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+
+// MTK == 1: one token (h formed in LDS); MTK == 4: batches, each work item
+// taking the body that fits its token count (1, 2, or chunks of 4).
+template <int NCH, int MTK, bool GS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH == 1 && MTK == 1 && !GS ? 4 : NCH == 1 ? 3 : 2, 8)))
+void down_kernel(
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
+    const int32_t* __restrict__ rows_out, const float* __restrict__ gu,
+    const uint32_t* __restrict__ hplanes, const float* __restrict__ hscale,
+    float* __restrict__ y_rows, int H, int I, BlobLayout L) {
+    extern __shared__ uint32_t s_h[];
+    const int item = blockIdx.y;
+    if (item >= *n_items) return;
+    const WorkItem it = items[item];
+    if constexpr (MTK == 1) {
+        down_body<NCH, 1, GS, true>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
+    } else {
+        if (it.count == 1) down_body<NCH, 1, GS, false>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
+        else if (it.count == 2) down_body<NCH, 2, GS, false>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
+        else down_body<NCH, 4, GS, false>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
     }
 }
 
 template <int NCH, int MT, bool GS>
 void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
-              const int32_t* rows_out, const uint32_t* hp, const float* hs, float* y, int H,
-              int I, const BlobLayout& L) {
-    launch((down_kernel<NCH, MT, GS>), grid, dim3(256), 0, s, items, n_items, rows_out,
-           hp, hs, y, H, I, L);
+              const int32_t* rows_out, const float* gu, const uint32_t* hp, const float* hs,
+              float* y, int H, int I, const BlobLayout& L) {
+    const size_t lds = MT == 1 ? (size_t)(I / kBlock) * (kWordsPerBlock + 1) * sizeof(uint32_t) : 0;
+    launch((down_kernel<NCH, MT, GS>), grid, dim3(256), lds, s, items, n_items, rows_out, gu, hp,
+           hs, y, H, I, L);
 }
 
 template <int NCH, bool GS>
 void by_mt(int mt, dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
-           const int32_t* rows_out, const uint32_t* hp, const float* hs, float* y, int H, int I,
-           const BlobLayout& L) {
-    switch (mt) {
-        case 1: launch_t<NCH, 1, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L); break;
-        case 2: launch_t<NCH, 2, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L); break;
-        case 4: launch_t<NCH, 4, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L); break;
-        default: launch_t<NCH, 8, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L); break;
-    }
+           const int32_t* rows_out, const float* gu, const uint32_t* hp, const float* hs,
+           float* y, int H, int I, const BlobLayout& L) {
+    if (mt == 1) launch_t<NCH, 1, GS>(grid, s, items, n_items, rows_out, gu, hp, hs, y, H, I, L);
+    else launch_t<NCH, 4, GS>(grid, s, items, n_items, rows_out, gu, hp, hs, y, H, I, L);
 }
 
 template <bool GS>
 bool by_width(int CI, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
-              const int32_t* n_items, const int32_t* rows_out, const uint32_t* hp,
-              const float* hs, float* y, int H, int I, const BlobLayout& L) {
+              const int32_t* n_items, const int32_t* rows_out, const float* gu,
+              const uint32_t* hp, const float* hs, float* y, int H, int I, const BlobLayout& L) {
     const int nch = (CI + 63) / 64;
-    if (nch == 1) by_mt<1, GS>(mt, grid, s, items, n_items, rows_out, hp, hs, y, H, I, L);
-    else if (nch == 2) by_mt<2, GS>(mt, grid, s, items, n_items, rows_out, hp, hs, y, H, I, L);
+    if (nch == 1) by_mt<1, GS>(mt, grid, s, items, n_items, rows_out, gu, hp, hs, y, H, I, L);
+    else if (nch == 2) by_mt<2, GS>(mt, grid, s, items, n_items, rows_out, gu, hp, hs, y, H, I, L);
     else return false;
     return true;
 }
@@ -143,12 +212,13 @@ bool by_width(int CI, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
 }  // namespace
 
 bool dispatch_down(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
-                   const int32_t* n_items, const int32_t* rows_out, const uint32_t* hplanes,
-                   const float* hscale, float* y_rows, int H, int I, const BlobLayout& L) {
+                   const int32_t* n_items, const int32_t* rows_out, const float* gu,
+                   const uint32_t* hplanes, const float* hscale, float* y_rows, int H, int I,
+                   const BlobLayout& L) {
     const int CI = I / kBlock;
-    return group ? by_width<true>(CI, mt, grid, s, items, n_items, rows_out, hplanes, hscale,
+    return group ? by_width<true>(CI, mt, grid, s, items, n_items, rows_out, gu, hplanes, hscale,
                                   y_rows, H, I, L)
-                 : by_width<false>(CI, mt, grid, s, items, n_items, rows_out, hplanes, hscale,
+                 : by_width<false>(CI, mt, grid, s, items, n_items, rows_out, gu, hplanes, hscale,
                                    y_rows, H, I, L);
 }
 

@@ -1,130 +1,121 @@
 // gate/up half of the int4 GEMV family (decode and small per-expert counts).
 //
 // Expert FFN (practical guide section 二: gate, up and down stored adjacently;
-// SwiGLU): h = silu(gate x) * (up x) for every (expert, token) pair of a work
-// list, each expert's gate and up rows streamed once per pass of up to MT
-// tokens.
+// SwiGLU): g = gate x and u = up x for every (expert, token) pair of a work
+// list, each expert's rows streamed once per pass of up to MT tokens; the
+// down pass forms h = silu(g) * u.
 //
-// Workgroup: 32 rows (one h block) of one work item's gate and up matrices.
-// W waves split the reduction axis: thread tid owns the 32-column blocks
-// tid + 64*W*j and reads the 16 bytes of each row that fall in them with
-// one 128-bit load. Each block's nibbles are multiplied by the token's digit
-// planes with v_dot8_i32_i4 (exact int32 per block, common.h) and scaled
-// once into an f32 partial. Rows go in batches of LB = 4/MT rows: a batch
-// yields 2*LB*MT partials per lane, summed over the wave by one
+// Workgroup: 32 rows of one work item's gate or up matrix (one token; grid x
+// interleaves tile and matrix, so a decode token's 9 work items give 1152
+// workgroups) or of both (batches). W waves split the reduction axis: thread tid owns the
+// 32-column blocks tid + 64*W*j and reads the 16 bytes of each row that fall
+// in them with one 128-bit load. Each block's nibbles are multiplied by the
+// token's digit planes with v_dot8_i32_i4 (exact int32 per block, common.h)
+// and scaled once into an f32 partial. Rows go in batches of LB = 4/MT rows:
+// a batch yields LB*NM*MT partials per lane (NM matrices), summed over the wave by one
 // transpose-reduction and over the W waves through LDS; the next batch's
 // loads are issued before the current batch is computed. The workgroup ends
-// by applying SiLU, multiplying, and encoding the 32 h values of each token
-// as one digit block for the down pass.
+// by writing g (or u), with its per-row scale applied, as f32.
 #include "gemv.h"
 
 namespace coli {
 namespace {
 
-// Resident waves per SIMD the register budget must allow: the decode grid
-// (9 work items x 64 tiles) then fits on the chip in one round.
-template <int NCH, int MT, bool GS>
-constexpr int gateup_waves_per_eu() {
-    return NCH == 1 && MT <= 4 && (!GS || MT >= 2) ? 3 : 2;
-}
-
-template <int W, int NCH, int MT, bool GS>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(gateup_waves_per_eu<NCH, MT, GS>(), 8)))
-void gateup_kernel(
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
-    const int32_t* __restrict__ rows_tok, const int32_t* __restrict__ rows_out,
-    const uint32_t* __restrict__ xplanes, const float* __restrict__ xscale,
-    uint32_t* __restrict__ hplanes, float* __restrict__ hscale, int H, int I, BlobLayout L) {
+// One work item's 32-row tile of NM matrices (from mat0) for all of its
+// tokens, MT at a time.
+template <int W, int NCH, int MT, int NM, bool GS>
+__device__ __forceinline__ void gateup_body(
+    const WorkItem& it, int tile, int mat0, const int32_t* __restrict__ rows_tok,
+    const int32_t* __restrict__ rows_out, const uint32_t* __restrict__ xplanes,
+    const float* __restrict__ xscale, float* __restrict__ gu, int H, int I, const BlobLayout& L,
+    float* red_raw) {
     constexpr int LB = (4 / MT) > 0 ? (4 / MT) : 1;   // rows per batch
-    constexpr int NV = 2 * LB * MT;                   // partials per batch (8, or 16 for MT 8)
+    constexpr int NV = LB * NM * MT;                  // partials per batch (4 or 8)
     constexpr int SH = transpose_shift<NV>();
     constexpr int NBT = kBlock / LB;                  // batches per tile (even)
     static_assert(NBT % 2 == 0, "batch count must be even");
-    const int item = blockIdx.y;
-    if (item >= *n_items) return;
-    const WorkItem it = items[item];
-    const int tile = blockIdx.x;
     const int r0 = tile * kBlock;
-    const int C = H / kBlock, CI = I / kBlock;
+    const int C = H / kBlock;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint8_t* gq = it.blob + L.gate_q;
-    const uint8_t* uq = it.blob + L.up_q;
-    const float* gsc = reinterpret_cast<const float*>(it.blob + L.gate_s);
-    const float* usc = reinterpret_cast<const float*>(it.blob + L.up_s);
+    const uint8_t* wq[NM];
+    const float* wsc[NM];
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) {
+        wq[mt] = it.blob + (mat0 + mt ? L.up_q : L.gate_q);
+        wsc[mt] = reinterpret_cast<const float*>(it.blob + (mat0 + mt ? L.up_s : L.gate_s));
+    }
     const size_t rowbytes = (size_t)H / 2;
     const int gpr = GS ? H / 64 : 1;
 
-    __shared__ float red[W][kBlock * 2 * MT];
-    __shared__ float hval[MT][kBlock];
+    float (*red)[kBlock * NM * MT] = reinterpret_cast<float (*)[kBlock * NM * MT]>(red_raw);
 
+    int tokwin = 0;                                   // tokens of a 64-token window, one per lane
     for (int m0 = 0; m0 < it.count; m0 += MT) {
         const int mc = min(MT, it.count - m0);
-        uint4 xp[MT][NCH][kPlanes];
-        float xs[MT][NCH];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int tok = (m < mc) ? rows_tok[it.begin + m0 + m] : 0;
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const int ch = tid + 64 * W * j;
-                if (m < mc && ch < C) {
-                    const uint4* src = reinterpret_cast<const uint4*>(
-                        xplanes + ((size_t)tok * C + ch) * kWordsPerBlock);
-#pragma unroll
-                    for (int p = 0; p < kPlanes; ++p) xp[m][j][p] = src[p];
-                    xs[m][j] = xscale[(size_t)tok * C + ch];
-                } else {
-#pragma unroll
-                    for (int p = 0; p < kPlanes; ++p) xp[m][j][p] = make_uint4(0, 0, 0, 0);
-                    xs[m][j] = 0.f;
-                }
-            }
-        }
-
-        uint4 wa[LB][2][NCH], wb[LB][2][NCH];
-        float fa[LB][2][NCH], fb[LB][2][NCH];
-        auto load = [&](uint4 (&wv)[LB][2][NCH], float (&fv)[LB][2][NCH], int batch) {
+        if ((m0 & 63) == 0) tokwin = rows_tok[it.begin + min(m0 + lane, it.count - 1)];
+        // two register sets of weights; the first batch is requested before
+        // the activation planes
+        uint4 wa[LB][NM][NCH], wb[LB][NM][NCH];
+        float fa[LB][NM][NCH], fb[LB][NM][NCH];
+        auto load = [&](uint4 (&wv)[LB][NM][NCH], float (&fv)[LB][NM][NCH], int batch) {
 #pragma unroll
             for (int r = 0; r < LB; ++r) {
                 const int row = r0 + batch * LB + r;
 #pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    // unconditional loads (no branch for the wait-count pass to
-                    // merge at): threads past the row end re-read its last block,
-                    // and their digit planes and scales are zero
-                    const int ch = min(tid + 64 * W * j, C - 1);
-                    wv[r][0][j] = ldg128(gq + row * rowbytes + (size_t)ch * 16);
-                    wv[r][1][j] = ldg128(uq + row * rowbytes + (size_t)ch * 16);
-                    if (GS) {
-                        fv[r][0][j] = ldg_f32(gsc + (size_t)row * gpr + (ch >> 1));
-                        fv[r][1][j] = ldg_f32(usc + (size_t)row * gpr + (ch >> 1));
+                for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+                    for (int j = 0; j < NCH; ++j) {
+                        // unconditional loads (no branch for the wait-count pass to
+                        // merge at): threads past the row end re-read its last
+                        // block, and their activation scales are zero
+                        const int ch = min(tid + 64 * W * j, C - 1);
+                        wv[r][mt][j] = ldg128(wq[mt] + row * rowbytes + (size_t)ch * 16);
+                        if (GS) fv[r][mt][j] = ldg_f32(wsc[mt] + (size_t)row * gpr + (ch >> 1));
                     }
-                }
             }
         };
-        auto compute = [&](const uint4 (&wv)[LB][2][NCH], const float (&fv)[LB][2][NCH], int batch) {
+        load(wa, fa, 0);
+        uint4 xp[MT][NCH][kPlanes];
+        float xs[MT][NCH];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            // unconditional loads (clamped token and block); tokens and blocks
+            // past the end are masked where the partials are formed
+            const int tok = __builtin_amdgcn_readlane(tokwin, (m0 & 63) + min(m, mc - 1));
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const int ch = tid + 64 * W * j, chc = min(ch, C - 1);
+                const uint4* src = reinterpret_cast<const uint4*>(
+                    xplanes + ((size_t)tok * C + chc) * kWordsPerBlock);
+#pragma unroll
+                for (int p = 0; p < kPlanes; ++p) xp[m][j][p] = src[p];
+                xs[m][j] = xscale[(size_t)tok * C + chc];   // validity applied where it is used
+            }
+        }
+
+        auto compute = [&](const uint4 (&wv)[LB][NM][NCH], const float (&fv)[LB][NM][NCH], int batch) {
             float part[NV];
 #pragma unroll
             for (int r = 0; r < LB; ++r)
 #pragma unroll
-                for (int mat = 0; mat < 2; ++mat)
+                for (int mt = 0; mt < NM; ++mt)
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
                         float acc = 0.f;
                         if (m < mc) {
 #pragma unroll
                             for (int j = 0; j < NCH; ++j) {
-                                const float f = GS ? xs[m][j] * fv[r][mat][j] : xs[m][j];
-                                acc += (float)block_dot(wv[r][mat][j], xp[m][j]) * f;
+                                const float x = tid + 64 * W * j < C ? xs[m][j] : 0.f;
+                                const float f = GS ? x * fv[r][mt][j] : x;
+                                acc += (float)block_dot(wv[r][mt][j], xp[m][j]) * f;
                             }
                         }
-                        part[(r * 2 + mat) * MT + m] = acc;
+                        part[(r * NM + mt) * MT + m] = acc;
                     }
             const float v = wave_transpose_sum<NV>(part);
             if ((lane & ((1 << SH) - 1)) == 0)
                 red[wave][batch * NV + (lane >> SH)] = v;
         };
-        load(wa, fa, 0);
 #pragma unroll 1
         for (int b = 0; b < NBT; b += 2) {
             load(wb, fb, b + 1);
@@ -133,69 +124,87 @@ void gateup_kernel(
             compute(wb, fb, b + 1);
         }
         __syncthreads();
-        for (int i = tid; i < kBlock * MT; i += 64 * W) {
-            const int r = i / MT, m = i % MT;
+        for (int i = tid; i < kBlock * NM * MT; i += 64 * W) {
+            const int m = i % MT, mt = (i / MT) % NM, r = i / (MT * NM);
             if (m < mc) {
-                float g = 0.f, u = 0.f;
+                float v = 0.f;
 #pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    g += red[w][(r * 2 + 0) * MT + m];
-                    u += red[w][(r * 2 + 1) * MT + m];
-                }
-                if (!GS) { g *= ldg_f32(gsc + r0 + r); u *= ldg_f32(usc + r0 + r); }
-                hval[m][r] = g / (1.f + expf(-g)) * u;
-            }
-        }
-        __syncthreads();
-        if (tid < 4 * MT) {
-            const int m = tid >> 2, q = tid & 3;
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (m < mc) ? hval[m][q * 8 + i] : 0.f;
-            uint32_t words[kPlanes];
-            const float sc = encode_quarter(v, words);
-            if (m < mc) {
+                for (int w = 0; w < W; ++w) v += red[w][i];
+                if (!GS) v *= ldg_f32((mt ? wsc[NM - 1] : wsc[0]) + r0 + r);
                 const int out = rows_out[it.begin + m0 + m];
-                uint32_t* dst = hplanes + ((size_t)out * CI + tile) * kWordsPerBlock;
-#pragma unroll
-                for (int p = 0; p < kPlanes; ++p) dst[p * 4 + q] = words[p];
-                if (q == 0) hscale[(size_t)out * CI + tile] = sc;
+                gu[((size_t)out * 2 + mat0 + mt) * I + r0 + r] = v;
             }
         }
         __syncthreads();
     }
 }
 
-template <int W, int NCH, int MT, bool GS>
+
+// Resident waves per SIMD the register budget must allow: the decode grid
+// (9 work items x 64 tiles x 2 matrices, 3 waves each) then fits on the chip
+// in one round.
+template <int NCH, int MTK, bool GS>
+constexpr int gateup_waves_per_eu() {
+    return NCH == 1 && MTK == 1 ? 4 : NCH == 1 && !GS ? 4 : NCH == 1 ? 3 : 2;
+}
+
+// MTK == 1: one token; gate and up in separate workgroups (grid x interleaves
+// tile and matrix: twice the workgroups, half the registers). MTK == 4:
+// batches; both matrices in one workgroup, so that the activation planes are
+// read once for the pair, and each work item takes the body that fits its
+// token count (1, 2, or chunks of 4), which keeps the per-wave batches of
+// weight rows large for the many experts that see one or two tokens.
+template <int W, int NCH, int MTK, bool GS>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(gateup_waves_per_eu<NCH, MTK, GS>(), 8)))
+void gateup_kernel(
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
+    const int32_t* __restrict__ rows_tok, const int32_t* __restrict__ rows_out,
+    const uint32_t* __restrict__ xplanes, const float* __restrict__ xscale,
+    float* __restrict__ gu, int H, int I, BlobLayout L) {
+    __shared__ float red[W * kBlock * (MTK == 1 ? 1 : 2 * 4)];
+    const int item = blockIdx.y;
+    if (item >= *n_items) return;
+    const WorkItem it = items[item];
+    if constexpr (MTK == 1) {
+        gateup_body<W, NCH, 1, 1, GS>(it, (int)blockIdx.x >> 1, (int)blockIdx.x & 1, rows_tok,
+                                      rows_out, xplanes, xscale, gu, H, I, L, red);
+    } else {
+        const int t = blockIdx.x;
+        if (it.count == 1)
+            gateup_body<W, NCH, 1, 2, GS>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+        else if (it.count == 2)
+            gateup_body<W, NCH, 2, 2, GS>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+        else
+            gateup_body<W, NCH, 4, 2, GS>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+    }
+}
+
+template <int W, int NCH, int MTK, bool GS>
 void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
               const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp,
-              const float* xs, uint32_t* hp, float* hs, int H, int I, const BlobLayout& L) {
-    launch((gateup_kernel<W, NCH, MT, GS>), grid, dim3(64 * W), 0, s, items, n_items,
-                       rows_tok, rows_out, xp, xs, hp, hs, H, I, L);
+              const float* xs, float* gu, int H, int I, const BlobLayout& L) {
+    launch((gateup_kernel<W, NCH, MTK, GS>), grid, dim3(64 * W), 0, s, items, n_items,
+                       rows_tok, rows_out, xp, xs, gu, H, I, L);
 }
 
 template <int W, int NCH, bool GS>
 void by_mt(int mt, dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
            const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp, const float* xs,
-           uint32_t* hp, float* hs, int H, int I, const BlobLayout& L) {
-    switch (mt) {
-        case 1: launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L); break;
-        case 2: launch_t<W, NCH, 2, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L); break;
-        case 4: launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L); break;
-        default: launch_t<W, NCH, 8, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L); break;
-    }
+           float* gu, int H, int I, const BlobLayout& L) {
+    if (mt == 1) launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
+    else launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
 }
 
 template <bool GS>
 bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
               const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
-              const uint32_t* xp, const float* xs, uint32_t* hp, float* hs, int H, int I,
+              const uint32_t* xp, const float* xs, float* gu, int H, int I,
               const BlobLayout& L) {
-    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L);
-    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L);
-    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L);
-    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L);
-    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L);
+    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
+    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
+    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
+    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
+    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
     else return false;
     return true;
 }
@@ -204,13 +213,13 @@ bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
 
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
-                     const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
-                     float* hscale, int H, int I, const BlobLayout& L) {
+                     const uint32_t* xplanes, const float* xscale, float* gu, int H, int I,
+                     const BlobLayout& L) {
     const int C = H / kBlock;
     return group ? by_width<true>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                  xscale, hplanes, hscale, H, I, L)
+                                  xscale, gu, H, I, L)
                  : by_width<false>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                   xscale, hplanes, hscale, H, I, L);
+                                   xscale, gu, H, I, L);
 }
 
 }  // namespace coli

@@ -58,11 +58,12 @@ static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, i
         coli_status st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
         if (st) return st;
     }
+    const int32_t rows = (int32_t)((int64_t)T * s->top_k + T);
     return launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
-                           at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
+                           rows, at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
                            at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
-                           at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_rows, H, I,
-                           s->group, stream);
+                           at<float>(ws, W.gu), at<uint32_t>(ws, W.hplanes),
+                           at<float>(ws, W.hscale), y_rows, H, I, s->group, stream);
 }
 
 coli_status run_expert_ffn(const coli_moe_shape* s, const void* const* table, const float* x,
