@@ -55,10 +55,13 @@ inline BlobLayout blob_layout(int64_t H, int64_t I, int32_t group) {
 
 // One unit of GEMV/GEMM work: an expert blob applied to `count` rows of the
 // slot list starting at `begin`.
+// One expert's share of a work list: its blob, its rows begin .. begin+count-1
+// of the slot list (rows_tok / rows_out), and rows_out[begin] (row0).
 struct WorkItem {
     const uint8_t* blob;
     int32_t begin;
     int32_t count;
+    int32_t row0;
 };
 
 // ------------------------------------------------------ activation digits
@@ -282,9 +285,9 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
 coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* planes, float* scales,
                           hipStream_t stream);
 // gate/up then down GEMV over a work list.
-// gu [rows][2][I] f32 holds g and u between the two passes; for batches
-// (max_count > 1) an activation pass encodes h = silu(g) * u of all `rows`
-// rows into hplanes [rows][I/32][16] / hscale [rows][I/32].
+// gu [rows][2][I] f32 holds silu(g) and u between the two passes; for
+// batches (max_count > 1) an activation pass encodes h = silu(g) * u of all
+// `rows` rows into hplanes [rows][I/32][16] / hscale [rows][I/32].
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,

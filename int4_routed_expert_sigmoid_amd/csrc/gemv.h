@@ -6,7 +6,7 @@
 namespace coli {
 
 // Launch the gate/up kernel on grid (2*I/32 for mt == 1, else I/32;
-// max_items): g and u, f32, into gu [rows][2][I]; false if H is outside the
+// max_items): silu(g) and u, f32, into gu [rows][2][I]; false if H is outside the
 // instantiated range.
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
 }
 
 // ------------------------------------------------------------- activation
-// h = silu(g) * u for rows [0, R) of gu [R][2][I], each 32-element block
+// h = silu(g) * u for rows [0, R) of gu [R][2][I] (silu(g), u), each 32-element block
 // encoded into digit planes: planes [R][I/32][4][4] u32, scales [R][I/32].
 // One 8-element quarter per thread; the quarters of a block sit in 4 adjacent
 // lanes and every lane runs the encoder (its shuffles need them all).
@@ -56,10 +56,7 @@ __global__ __launch_bounds__(256) void act_encode_kernel(const float* __restrict
     const float* gp = gu + (size_t)row * 2 * I + blk * kBlock + q * 8;
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float g = gp[e], u = gp[I + e];
-        v[e] = g / (1.f + expf(-g)) * u;
-    }
+    for (int e = 0; e < 8; ++e) v[e] = gp[e] * gp[I + e];                 // silu(g) * u
     uint32_t words[kPlanes];
     const float sc = encode_quarter(v, words);
     if (i < nq) {

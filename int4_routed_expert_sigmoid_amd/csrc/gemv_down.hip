@@ -3,14 +3,14 @@
 // gate, up, down adjacent; SwiGLU).
 //
 // Workgroup: 4 waves x 16 rows of one work item's down matrix. For one token
-// it first forms h from the f32 g and u of the gate/up pass and encodes each
+// it first forms h = silu(g) * u from the f32 silu(g) and u of the gate/up pass and encodes each
 // 32-element block into digit planes (common.h) in LDS, once for the
 // workgroup; for batches the activation pass has encoded the blocks once per
 // row. Lane l owns the 32-column blocks l + 64*j of h and
 // reads each row's 16 bytes in those blocks with one 128-bit load. Rows go in
 // batches of LB = 4/MT rows whose LB*MT partials per lane are summed over the
-// wave by one transpose-reduction; loads run one or two batches ahead of the
-// arithmetic, and the first are requested before h is formed.
+// wave by one transpose-reduction; loads run two batches ahead (one token,
+// the first two requested before h is formed) or one batch ahead (batches).
 #include <algorithm>
 
 #include "gemv.h"
@@ -75,14 +75,11 @@ __device__ __forceinline__ void down_body(
         for (int i0 = 0; i0 < nq; i0 += 256) {
             const int i = i0 + (int)threadIdx.x, ic = min(i, nq - 1);
             const int m = ic / (CI * 4), rem = ic % (CI * 4), blk = rem >> 2, q = rem & 3;
-            const int outr = rows_out[it.begin + m0 + min(m, mc - 1)];
+            const int outr = it.row0;                    // one token per item here
             const float* gp = gu + (size_t)outr * 2 * I + blk * kBlock + q * 8;
             float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float g = gp[e], u = gp[I + e];
-                v[e] = g / (1.f + expf(-g)) * u;
-            }
+            for (int e = 0; e < 8; ++e) v[e] = gp[e] * gp[I + e];          // silu(g) * u
             uint32_t words[kPlanes];
             const float sc = encode_quarter(v, words);
             if (i < nq) {

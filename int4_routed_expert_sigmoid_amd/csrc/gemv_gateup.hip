@@ -15,15 +15,16 @@
 // a batch yields LB*NM*MT partials per lane (NM matrices), summed over the wave by one
 // transpose-reduction and over the W waves through LDS; the next batch's
 // loads are issued before the current batch is computed. The workgroup ends
-// by writing g (or u), with its per-row scale applied, as f32.
+// by writing silu(g) (or u), with the per-row scale applied first, as f32.
 #include "gemv.h"
 
 namespace coli {
 namespace {
 
 // One work item's 32-row tile of NM matrices (from mat0) for all of its
-// tokens, MT at a time.
-template <int W, int NCH, int MT, int NM, bool GS>
+// tokens, MT at a time. ONE: a one-token launch, where every row's token is 0
+// (the activation planes then load without waiting for the token index).
+template <int W, int NCH, int MT, int NM, bool GS, bool ONE>
 __device__ __forceinline__ void gateup_body(
     const WorkItem& it, int tile, int mat0, const int32_t* __restrict__ rows_tok,
     const int32_t* __restrict__ rows_out, const uint32_t* __restrict__ xplanes,
@@ -52,7 +53,7 @@ __device__ __forceinline__ void gateup_body(
     int tokwin = 0;                                   // tokens of a 64-token window, one per lane
     for (int m0 = 0; m0 < it.count; m0 += MT) {
         const int mc = min(MT, it.count - m0);
-        if ((m0 & 63) == 0) tokwin = rows_tok[it.begin + min(m0 + lane, it.count - 1)];
+        if (!ONE && (m0 & 63) == 0) tokwin = rows_tok[it.begin + min(m0 + lane, it.count - 1)];
         // two register sets of weights; the first batch is requested before
         // the activation planes
         uint4 wa[LB][NM][NCH], wb[LB][NM][NCH];
@@ -81,7 +82,7 @@ __device__ __forceinline__ void gateup_body(
         for (int m = 0; m < MT; ++m) {
             // unconditional loads (clamped token and block); tokens and blocks
             // past the end are masked where the partials are formed
-            const int tok = __builtin_amdgcn_readlane(tokwin, (m0 & 63) + min(m, mc - 1));
+            const int tok = ONE ? 0 : __builtin_amdgcn_readlane(tokwin, (m0 & 63) + min(m, mc - 1));
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
                 const int ch = tid + 64 * W * j, chc = min(ch, C - 1);
@@ -131,6 +132,7 @@ __device__ __forceinline__ void gateup_body(
 #pragma unroll
                 for (int w = 0; w < W; ++w) v += red[w][i];
                 if (!GS) v *= ldg_f32((mt ? wsc[NM - 1] : wsc[0]) + r0 + r);
+                if (mat0 + mt == 0) v = v / (1.f + expf(-v));          // gate: store silu(g)
                 const int out = rows_out[it.begin + m0 + m];
                 gu[((size_t)out * 2 + mat0 + mt) * I + r0 + r] = v;
             }
@@ -166,16 +168,16 @@ void gateup_kernel(
     if (item >= *n_items) return;
     const WorkItem it = items[item];
     if constexpr (MTK == 1) {
-        gateup_body<W, NCH, 1, 1, GS>(it, (int)blockIdx.x >> 1, (int)blockIdx.x & 1, rows_tok,
+        gateup_body<W, NCH, 1, 1, GS, true>(it, (int)blockIdx.x >> 1, (int)blockIdx.x & 1, rows_tok,
                                       rows_out, xplanes, xscale, gu, H, I, L, red);
     } else {
         const int t = blockIdx.x;
         if (it.count == 1)
-            gateup_body<W, NCH, 1, 2, GS>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 1, 2, GS, false>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
         else if (it.count == 2)
-            gateup_body<W, NCH, 2, 2, GS>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 2, 2, GS, false>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
         else
-            gateup_body<W, NCH, 4, 2, GS>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 4, 2, GS, false>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
     }
 }
 

@@ -216,6 +216,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     __shared__ int s_idx[kSmallT * 32];
     __shared__ int s_cnt[1024];
     __shared__ int s_off[1024];
+    __shared__ int s_first[1024];
     __shared__ uint32_t s_scan[4];
     const int tid = threadIdx.x, wave = tid >> 6;
     const int T = a.T, E = a.E, k = a.k;
@@ -232,11 +233,73 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     for (int t = wave; t < T; t += kRouterThreads / 64)
         route_token<EPL>(lg + (int64_t)t * E, a.bias, E, k, a.idx + (int64_t)t * k,
                          a.w + (int64_t)t * k, s_idx + t * k);
-    for (int e = tid; e < E; e += kRouterThreads) s_cnt[e] = 0;
+    const int base = a.shared_blob ? 1 : 0;
+    if (T == 1 && a.phase_mask == nullptr) {
+        // one token: the k picks are distinct, so the union is their order by
+        // expert id; every count is 0 or 1 and each offset is the number of
+        // picks below the expert
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = tid * EPT + i;
+            if (e < E) {
+                int c = 0, below = 0, slot = 0;
+                for (int j = 0; j < k; ++j) {
+                    c += s_idx[j] == e;
+                    slot = s_idx[j] == e ? j : slot;
+                    below += s_idx[j] < e;
+                }
+                a.counts[e] = c;
+                a.offsets[e] = below;
+                if (c) {
+                    a.unique[below] = e;
+                    if (with_items) {
+                        WorkItem it;
+                        it.blob = (const uint8_t*)tptr[i];
+                        it.begin = below;
+                        it.count = 1;
+                        it.row0 = slot;
+                        a.items[base + below] = it;
+                    }
+                }
+            }
+        }
+        if (tid < k) {
+            const int e = s_idx[tid];
+            int p = 0;
+            for (int j = 0; j < k; ++j) p += s_idx[j] < e;
+            a.perm[p] = tid;
+            a.rows_tok[p] = 0;
+            a.rows_out[p] = tid;
+        }
+        if (tid == 0) {
+            a.offsets[E] = k;
+            *a.n_unique = k;
+            a.rows_tok[k] = 0;
+            a.rows_out[k] = k;
+            if (with_items && a.shared_blob) {
+                WorkItem it;
+                it.blob = (const uint8_t*)a.shared_blob;
+                it.begin = k;
+                it.count = 1;
+                it.row0 = k;
+                a.items[0] = it;
+            }
+            *a.n_items = with_items ? base + k : 0;
+        }
+        return;
+    }
+    for (int e = tid; e < E; e += kRouterThreads) {
+        s_cnt[e] = 0;
+        s_first[e] = 0x7fffffff;
+    }
     __syncthreads();
     // batch union of the n = T*k assignments (stable counting sort)
     const int n = T * k;
-    for (int i = tid; i < n; i += kRouterThreads) atomicAdd(&s_cnt[s_idx[i]], 1);
+    for (int i = tid; i < n; i += kRouterThreads) {
+        atomicAdd(&s_cnt[s_idx[i]], 1);
+        atomicMin(&s_first[s_idx[i]], i);           // an item's first row is its first assignment
+    }
     __syncthreads();
     // offsets, the unique list and the kept work items in one scan: thread
     // tid owns experts tid*EPT .. tid*EPT+3 and scans the packed triple
@@ -256,7 +319,6 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     uint32_t total = 0;
     const uint32_t pre = block_excl_scan(packed, s_scan, &total);
     int off = (int)(pre >> 22), upos = (int)((pre >> 11) & 0x7FF), kpos = (int)(pre & 0x7FF);
-    const int base = a.shared_blob ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
@@ -270,6 +332,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
                 it.blob = (const uint8_t*)tptr[i];
                 it.begin = off;
                 it.count = c[i];
+                it.row0 = s_first[e];
                 a.items[base + kpos++] = it;
             }
             off += c[i];
@@ -285,6 +348,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
             it.blob = (const uint8_t*)a.shared_blob;
             it.begin = n;
             it.count = T;
+            it.row0 = n;
             a.items[0] = it;
         }
         *a.n_items = with_items ? base + (int)(total & 0x7FF) : 0;

@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256) void plan_kernel(
         it.blob = (const uint8_t*)shared_blob;
         it.begin = n;
         it.count = T;
+        it.row0 = n;
         items[0] = it;
     }
     // compaction of the unique list by phase, in order, 256 at a time
@@ -184,6 +185,7 @@ __global__ __launch_bounds__(256) void plan_kernel(
             it.blob = (const uint8_t*)table[e];
             it.begin = offsets[e];
             it.count = offsets[e + 1] - offsets[e];
+            it.row0 = perm[offsets[e]];
             items[base + pos] = it;
         }
         base += tot;
