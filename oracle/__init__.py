@@ -50,11 +50,12 @@ def lib():
             L.oracle_dequantize_int4.argtypes = [vp, vp, i64, i64, i32, vp]
             L.oracle_router_logits.argtypes = [vp, vp, i32, i32, i32, vp]
             L.oracle_route.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+            L.oracle_route_topp.argtypes = [vp, vp, i32, i32, i32, f32, vp, vp]
             L.oracle_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
             L.oracle_expert_ffn.argtypes = [ctypes.POINTER(Expert), i32, i32, i32, vp, vp]
             L.oracle_expert_ffn_union.argtypes = [ctypes.POINTER(Expert), i32, i32, i32, vp, i32,
                                                   i32, vp, vp, vp, i32, vp]
-            L.oracle_layer.argtypes = [i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, vp,
+            L.oracle_layer.argtypes = [i32, i32, i32, i32, i32, f32, f32, vp, i32, vp, vp, vp,
                                        ctypes.POINTER(Expert), ctypes.POINTER(Expert), vp, vp,
                                        vp, vp]
             L.oracle_num_threads.restype = ctypes.c_int
@@ -108,13 +109,18 @@ def router_logits(wr: np.ndarray, x: np.ndarray) -> np.ndarray:
     return out
 
 
-def route(logits: np.ndarray, bias, k: int):
+def route(logits: np.ndarray, bias, k: int, topp: float = 0.0):
+    """(idx [T][k], w [T][k]); with 0 < topp < 1 dropped slots have idx -1, w 0."""
     logits = _c(logits, np.float32)
     T, E = logits.shape
     b = None if bias is None else _c(bias, np.float32)
     idx = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float32)
-    if lib().oracle_route(_p(logits), _p(b), T, E, k, _p(idx), _p(w)):
+    if topp == 0.0:
+        rc = lib().oracle_route(_p(logits), _p(b), T, E, k, _p(idx), _p(w))
+    else:
+        rc = lib().oracle_route_topp(_p(logits), _p(b), T, E, k, topp, _p(idx), _p(w))
+    if rc:
         raise ValueError("oracle_route: bad arguments")
     return idx, w
 
@@ -179,7 +185,8 @@ def expert_ffn_union(experts, x, k, offsets, perm, unique, H, I, group=0) -> np.
     return y
 
 
-def layer(x, experts, shared, k, group=0, routed_scale=1.0, logits=None, wr=None, bias=None):
+def layer(x, experts, shared, k, group=0, routed_scale=1.0, logits=None, wr=None, bias=None,
+          topp=0.0):
     """Whole layer. Returns (y f32 [T][H], y64 f64 [T][H], idx [T][k], w [T][k])."""
     x = _c(x, np.float32)
     T, H = x.shape
@@ -194,7 +201,7 @@ def layer(x, experts, shared, k, group=0, routed_scale=1.0, logits=None, wr=None
     w = np.empty((T, k), dtype=np.float32)
     arr = _expert_array(experts)
     sh = ctypes.byref(shared.struct) if shared is not None else None
-    rc = lib().oracle_layer(H, I, E, k, group, routed_scale, _p(x), T, _p(lg), _p(wrc), _p(b),
+    rc = lib().oracle_layer(H, I, E, k, group, routed_scale, topp, _p(x), T, _p(lg), _p(wrc), _p(b),
                             arr, sh, _p(y), _p(y64), _p(idx), _p(w))
     if rc:
         raise ValueError("oracle_layer: bad arguments")

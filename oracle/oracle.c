@@ -100,10 +100,24 @@ void oracle_router_logits(const float* wr, const float* x, int32_t T, int32_t H,
 /* [P4] section 三 item 1: a DeepSeek-V3-style sigmoid router picks 8 of 256
  * experts per token. [P4] section 四 item 3: the aux-loss-free bias adjusts
  * selection; routing, selection and scaling are reproduced exactly. [P2]:
- * scoring_func sigmoid, norm_topk_prob true. */
-int oracle_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
-                 int32_t* idx, float* w) {
+ * scoring_func sigmoid, norm_topk_prob true.
+ *
+ * Adaptive expert top-p ([P5] section 三, where it is the recommended setting
+ * for disk-bound machines at 0.7, and the section 五 tuning table: an
+ * adaptive, lossy expert top-p that reads 30-40% fewer expert bytes). The
+ * pages give no formula; the reading taken here: the k experts are selected
+ * as above, then the shortest prefix of them in key (slot) order whose share
+ * of the k selected scores reaches p is kept; its weights are its scores
+ * normalised over the kept prefix (the same rule as for the k, applied to
+ * fewer experts), and the dropped slots get index -1 and weight 0. The share
+ * of the first j+1 slots is (s_0 + ... + s_j) / (s_0 + ... + s_{k-1}), both
+ * sums in double in slot order, compared with p in double; it is (j+1)/k when
+ * every selected score is 0. p = 0 or p >= 1 keeps all k (fixed top-k). */
+int oracle_route_topp(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                      float p, int32_t* idx, float* w) {
     if (T < 0 || E <= 0 || k <= 0 || k > E) return -1;
+    if (!(p >= 0.0f && p <= 1.0f)) return -1;                  /* NaN too */
+    const int adaptive = p > 0.0f && p < 1.0f;
     float* score = (float*)malloc(sizeof(float) * (size_t)E);
     float* key = (float*)malloc(sizeof(float) * (size_t)E);
     unsigned char* used = (unsigned char*)malloc((size_t)E);
@@ -127,14 +141,35 @@ int oracle_route(const float* logits, const float* bias, int32_t T, int32_t E, i
             used[best] = 1;
             it[j] = best;
         }
-        /* normalised weights from the unbiased scores, sum in slot order */
+        /* sum of the k selected unbiased scores, in slot order */
         double sum = 0.0;
         for (int32_t j = 0; j < k; ++j) sum += (double)score[it[j]];
-        for (int32_t j = 0; j < k; ++j)
-            w[(int64_t)t * k + j] = (sum == 0.0) ? (float)(1.0 / k) : (float)((double)score[it[j]] / sum);
+        /* adaptive top-p: the number of slots kept */
+        int32_t kept = k;
+        if (adaptive) {
+            double cum = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                cum += (double)score[it[j]];
+                double share = (sum == 0.0) ? (double)(j + 1) / (double)k : cum / sum;
+                if (share >= (double)p) { kept = j + 1; break; }
+            }
+        }
+        /* normalised weights over the kept slots */
+        double ksum = 0.0;
+        for (int32_t j = 0; j < kept; ++j) ksum += (double)score[it[j]];
+        for (int32_t j = 0; j < k; ++j) {
+            float* wj = &w[(int64_t)t * k + j];
+            if (j >= kept) { it[j] = -1; *wj = 0.0f; continue; }
+            *wj = (ksum == 0.0) ? (float)(1.0 / kept) : (float)((double)score[it[j]] / ksum);
+        }
     }
     free(score); free(key); free(used);
     return 0;
+}
+
+int oracle_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                 int32_t* idx, float* w) {
+    return oracle_route_topp(logits, bias, T, E, k, 0.0f, idx, w);
 }
 
 /* ----------------------------------------------------------------- union
@@ -147,7 +182,8 @@ int oracle_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* c
     int64_t n = (int64_t)T * k;
     for (int32_t e = 0; e < E; ++e) counts[e] = 0;
     for (int64_t a = 0; a < n; ++a) {
-        if (idx[a] < 0 || idx[a] >= E) return -1;
+        if (idx[a] >= E) return -1;
+        if (idx[a] < 0) continue;                 /* a slot dropped by top-p */
         counts[idx[a]] += 1;
     }
     offsets[0] = 0;
@@ -156,6 +192,7 @@ int oracle_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* c
     if (!fill) return -1;
     for (int64_t a = 0; a < n; ++a) {
         int32_t e = idx[a];
+        if (e < 0) continue;
         perm[offsets[e] + fill[e]] = (int32_t)a;
         fill[e] += 1;
     }
@@ -217,9 +254,10 @@ int oracle_expert_ffn_union(const oracle_expert* experts, int32_t H, int32_t I, 
  * execute. The combine sums the routed outputs in slot order weighted by
  * the normalised weights, scales that sum by rs, and adds the shared expert
  * (weight 1) — [P4] section 四 item 3 asks for the scaling semantics to be
- * reproduced; rs defaults to 1. */
+ * reproduced; rs defaults to 1. Slots dropped by the adaptive top-p (index
+ * -1) have no expert and add nothing. */
 int oracle_layer(int32_t H, int32_t I, int32_t E, int32_t k, int32_t group, float routed_scale,
-                 const float* x, int32_t T, const float* logits, const float* wr,
+                 float topp, const float* x, int32_t T, const float* logits, const float* wr,
                  const float* bias, const oracle_expert* experts, const oracle_expert* shared,
                  float* y, double* y64, int32_t* idx_out, float* w_out) {
     if (H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E || T < 0) return -1;
@@ -240,7 +278,7 @@ int oracle_layer(int32_t H, int32_t I, int32_t E, int32_t k, int32_t group, floa
 
     if (logits) memcpy(lg, logits, sizeof(float) * (size_t)T * E);
     else oracle_router_logits(wr, x, T, H, E, lg);
-    if (oracle_route(lg, bias, T, E, k, idx, w)) goto done;
+    if (oracle_route_topp(lg, bias, T, E, k, topp, idx, w)) goto done;
     if (oracle_union(idx, T, k, E, counts, offsets, perm, unique, &n_unique)) goto done;
     if (oracle_expert_ffn_union(experts, H, I, group, x, T, k, offsets, perm, unique, n_unique, ya))
         goto done;
@@ -248,8 +286,10 @@ int oracle_layer(int32_t H, int32_t I, int32_t E, int32_t k, int32_t group, floa
         if (shared) oracle_expert_ffn(shared, H, I, group, x + (int64_t)t * H, ys);
         for (int32_t c = 0; c < H; ++c) {
             double routed = 0.0;
-            for (int32_t j = 0; j < k; ++j)
+            for (int32_t j = 0; j < k; ++j) {
+                if (idx[(int64_t)t * k + j] < 0) continue;      /* dropped by top-p */
                 routed += (double)w[(int64_t)t * k + j] * ya[((int64_t)t * k + j) * H + c];
+            }
             double v = (shared ? ys[c] : 0.0) + (double)routed_scale * routed;
             y[(int64_t)t * H + c] = (float)v;
             if (y64) y64[(int64_t)t * H + c] = v;

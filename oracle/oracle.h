@@ -36,6 +36,8 @@
  *  - activation is SwiGLU: h = silu(gate x) * (up x), y = down h.
  *  - the routed-scale factor rs multiplies the routed sum at the combine; the
  *    shared expert has weight 1.
+ *  - adaptive expert top-p keeps the shortest key-order prefix of the k
+ *    selected whose share of their scores reaches p, renormalised over it.
  */
 #ifndef COLI_ORACLE_H
 #define COLI_ORACLE_H
@@ -77,9 +79,18 @@ void oracle_router_logits(const float* wr, const float* x, int32_t T, int32_t H,
 int oracle_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
                  int32_t* idx, float* w);
 
+/* The same with the adaptive expert top-p p in [0, 1]: for 0 < p < 1 only the
+ * shortest prefix of the k slots whose share of the selected scores reaches p
+ * is kept, renormalised; dropped slots get idx -1 and w 0. p = 0 or 1 is
+ * oracle_route. Returns 0, or -1 for bad arguments (p outside [0, 1]). */
+int oracle_route_topp(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                      float p, int32_t* idx, float* w);
+
 /* Batch union of the T*k assignments a = t*k + j: counts[E], offsets[E+1]
  * (exclusive prefix sum), perm[T*k] (assignments grouped by expert, ascending
- * within each group), unique[n] (experts with counts > 0, ascending). */
+ * within each group), unique[n] (experts with counts > 0, ascending).
+ * Negative entries are slots dropped by top-p: they belong to no expert, and
+ * offsets[E] counts only the others. Entries >= E are an error (-1). */
 int oracle_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* unique, int32_t* n_unique);
 
@@ -94,12 +105,13 @@ int oracle_expert_ffn_union(const oracle_expert* experts, int32_t H, int32_t I, 
                             const int32_t* perm, const int32_t* unique, int32_t n_unique,
                             double* y_assign);
 
-/* Whole layer for T tokens. Exactly one of logits [T][E] and wr [E][H] is
+/* Whole layer for T tokens, with the adaptive expert top-p topp (0 = fixed
+ * top-k, as in oracle_route_topp). Exactly one of logits [T][E] and wr [E][H] is
  * non-NULL. shared may be NULL (no shared expert). y [T][H] float; y64 (nullable)
  * receives the double result before its rounding; idx/w (nullable) receive
  * the routing. Returns 0 or -1. */
 int oracle_layer(int32_t H, int32_t I, int32_t E, int32_t k, int32_t group, float routed_scale,
-                 const float* x, int32_t T, const float* logits, const float* wr,
+                 float topp, const float* x, int32_t T, const float* logits, const float* wr,
                  const float* bias, const oracle_expert* experts, const oracle_expert* shared,
                  float* y, double* y64, int32_t* idx, float* w);
 
