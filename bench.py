@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle sample for about this long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--topp", type=float, default=0.0,
+                    help="decode with the adaptive expert top-p (lossy; 0 = fixed top-8, the headline)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
     ap.add_argument("--pinned-layers", type=int, default=13,
                     help="stream workload: distinct pinned layer pools (the rest reuse them)")
@@ -109,7 +111,7 @@ def cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept, seconds):
     reps, dt = 0, 0.0
     t0 = time.perf_counter()
     while dt < seconds and reps < 1000:
-        oracle.layer(x, experts, shared, k, 0, 1.0, wr=wr, bias=b)
+        oracle.layer(x, experts, shared, k, 0, 1.0, wr=wr, bias=b, topp=shape.topp)
         reps += 1
         dt = time.perf_counter() - t0
     return {"value": reps * sample / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
@@ -425,10 +427,10 @@ def main():
         print(json.dumps(line), flush=True)
         return
     H, I, E, k = 6144, 2048, 256, 8
-    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0)
+    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0, args.topp)
     seed = args.seed
     n_tok = args.warmup + args.steps
-    log(f"decode workload: {n_tok} tokens, H={H} I={I} E={E}+1 k={k}")
+    log(f"decode workload: {n_tok} tokens, H={H} I={I} E={E}+1 k={k} topp={args.topp}")
 
     wr = synth.router_weights(seed, 0, E, H)
     b = synth.bias(seed, 0, E)
@@ -446,11 +448,13 @@ def main():
     b_d = torch.from_numpy(b).to(dev)
     x_d = torch.from_numpy(x_all).to(dev)
     y_d = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
+    idx_d = torch.empty((n_tok, k), dtype=torch.int32, device=dev)
     ws = coli.workspace(shape, 1, coli.PATH_GEMV, dev)
 
     def token(t):
         coli.layer_fwd(shape, x_d[t:t + 1], table=table, shared_blob=shared, router_w=wr_d,
-                       bias=b_d, y=y_d[t:t + 1], path=coli.PATH_GEMV, ws=ws)
+                       bias=b_d, y=y_d[t:t + 1], idx_out=idx_d[t:t + 1], path=coli.PATH_GEMV,
+                       ws=ws)
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -490,9 +494,12 @@ def main():
     coli.profile_enable(0)
     elapsed = elapsed_graph if graph is not None else elapsed_eager
 
-    # algorithmic bytes per token: 9 blobs (8 routed + shared)
-    gu_bytes = 9 * (2 * I * (H // 2) + 2 * I * 4)
-    dn_bytes = 9 * (H * (I // 2) + H * 4)
+    # algorithmic bytes per token: the routed experts the token uses (8, fewer
+    # with top-p: their mean over the timed tokens) and the shared one
+    routed = (idx_d[args.warmup:] >= 0).sum(dim=1).double().mean().item()
+    n_exp = routed + 1.0
+    gu_bytes = n_exp * (2 * I * (H // 2) + 2 * I * 4)
+    dn_bytes = n_exp * (H * (I // 2) + H * 4)
     gu_avg_s = ms_gu / max(1, n_gu) / 1e3
     dn_avg_s = ms_dn / max(1, n_dn) / 1e3
     gu_gbps = gu_bytes / gu_avg_s / 1e9 if n_gu else None
@@ -522,16 +529,20 @@ def main():
         "vs_baseline": None,
         "dtype": "int4 weights x f32 activations (exact int32 nibble products), f32 accumulate",
         "data": "synthetic (seeded Philox N(0,0.02) weights, N(0,1) activations, f32 router)",
-        "config": {"workload": "GLM-5.2-shaped MoE layer, batch-1 decode", "hidden": H,
+        "config": {"workload": "GLM-5.2-shaped MoE layer, batch-1 decode"
+                               + (f", adaptive expert top-p {args.topp}" if args.topp else ""),
+                   "hidden": H,
                    "inter": I, "n_routed": E, "n_shared": 1, "top_k": k, "group": 0,
-                   "tokens": args.steps, "graph": bool(args.graph),
+                   "tokens": args.steps, "graph": bool(args.graph), "topp": args.topp,
+                   "routed_experts_per_token": round(routed, 4),
                    "eager_tokens_per_s": round(args.steps / elapsed_eager, 2)},
         "roofline": {"bound": "hbm", "kernel": "gemv_gateup",
                      "achieved": round(gu_gbps, 1) if gu_gbps else None,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4) if gu_gbps else None,
-                     "traffic": measured_traffic("gemv_gateup_decode_traffic.json"),
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
+                     "traffic": (measured_traffic("gemv_gateup_decode_traffic.json")
+                                 if args.topp == 0.0 else None),
+                     "bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_avg_s * 1e6, 3),
                      "launches_timed": n_gu},
         "expert_gemv": {"gateup_GBps": gu_gbps and round(gu_gbps, 1),
                         "down_GBps": dn_gbps and round(dn_gbps, 1),

@@ -76,7 +76,7 @@ COLI_API const char* coli_version(void);
 
 /* Layer shape. Supported: hidden <= 16384 and inter <= 4096, positive multiples of 32 (and of
  * 64 when group == 64); 1 <= n_routed <= 1024; n_shared 0 or 1;
- * 1 <= top_k <= min(32, n_routed); group 0 or 64; routed_scale finite. */
+ * 1 <= top_k <= min(32, n_routed); group 0 or 64; routed_scale finite; topp in [0, 1]. */
 typedef struct coli_moe_shape {
     int32_t hidden;       /* H: model width, input and output of the layer */
     int32_t inter;        /* I: intermediate width of one expert */
@@ -85,6 +85,8 @@ typedef struct coli_moe_shape {
     int32_t top_k;        /* k: experts per token */
     int32_t group;        /* 0: one scale per row; 64: one scale per 64 inputs */
     float routed_scale;   /* multiplies the routed sum at the combine (1.0 = none) */
+    float topp;           /* adaptive expert top-p, as coli_moe_route_topp: 0 (or 1) keeps
+                             all top_k; in (0, 1) a token may use fewer experts (lossy) */
 } coli_moe_shape;
 
 /* Offsets (bytes) of gate_q, up_q, down_q, gate_s, up_s, down_s inside one
@@ -117,6 +119,22 @@ COLI_API coli_status coli_moe_router_logits(const float* d_wr, const float* d_x,
  * rounded to f32 (1/k if that sum is 0). */
 COLI_API coli_status coli_moe_route(const float* d_logits, const float* d_bias, int32_t T, int32_t E,
                            int32_t k, int32_t* d_idx, float* d_w, void* stream);
+
+/* coli_moe_route with an adaptive expert top-p (practical guide section 三,
+ * where 0.7 is the setting recommended for disk-bound machines, and the
+ * section 五 tuning table: an adaptive expert top-p that reads 30-40% fewer
+ * expert bytes; lossy). The pages give no formula; this call takes the k
+ * experts selected as above, in slot (key) order, and keeps the shortest
+ * prefix whose share of the k selected scores reaches topp: slot j is kept iff
+ * j == 0 or (s_0 + ... + s_{j-1}) / (s_0 + ... + s_{k-1}) < topp, sums in
+ * double in slot order (j / k instead when all k scores are 0). The kept
+ * weights are score / (sum of the kept scores, slot order, double), rounded to
+ * f32 (1/kept if that sum is 0); dropped slots get d_idx -1 and d_w 0, at the
+ * end of each row. topp 0 or 1 is coli_moe_route; outside [0, 1] (or NaN) is
+ * COLI_EINVAL. */
+COLI_API coli_status coli_moe_route_topp(const float* d_logits, const float* d_bias, int32_t T,
+                                int32_t E, int32_t k, float topp, int32_t* d_idx, float* d_w,
+                                void* stream);
 
 /* Workspace bytes coli_moe_union needs for T tokens, k slots, E experts. */
 COLI_API coli_status coli_moe_union_workspace_size(int32_t T, int32_t k, int32_t E, size_t* bytes);
@@ -166,6 +184,8 @@ struct coli_expert_cache;
  * (one blocking 4*T*k-byte read), makes the selected experts of `layer`
  * resident, runs the resident ones while the misses are copied, then the
  * misses. d_idx_out [T][k] and d_w_out [T][k] (nullable) receive the routing.
+ * With shape->topp in (0, 1) the routing is coli_moe_route_topp's: dropped
+ * slots (index -1) are left out of the union and add nothing at the combine.
  * d_y [T][H] f32. */
 COLI_API coli_status coli_moe_layer_fwd(const coli_moe_shape* shape, const float* d_x, int32_t T,
                                const float* d_logits, const float* d_router_w,

@@ -21,7 +21,7 @@ PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 
 EXPORTED = [
     "coli_last_error", "coli_version", "coli_expert_blob_layout", "coli_quantize_int4",
-    "coli_quantize_expert", "coli_moe_router_logits", "coli_moe_route",
+    "coli_quantize_expert", "coli_moe_router_logits", "coli_moe_route", "coli_moe_route_topp",
     "coli_moe_union_workspace_size", "coli_moe_union", "coli_moe_workspace_size",
     "coli_moe_expert_ffn", "coli_moe_layer_fwd", "coli_expert_cache_create",
     "coli_expert_cache_destroy", "coli_expert_cache_ensure", "coli_expert_cache_wait",
@@ -41,7 +41,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("topp", ctypes.c_float)]
 
 
 class CacheCfg(ctypes.Structure):
@@ -81,6 +81,7 @@ def lib():
             L.coli_quantize_expert.argtypes = [P(Shape), vp, vp, vp, vp, vp]
             L.coli_moe_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
             L.coli_moe_route.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+            L.coli_moe_route_topp.argtypes = [vp, vp, i32, i32, i32, f32, vp, vp, vp]
             L.coli_moe_union_workspace_size.argtypes = [i32, i32, i32, P(sz)]
             L.coli_moe_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
             L.coli_moe_workspace_size.argtypes = [P(Shape), i32, i32, P(sz)]
@@ -144,10 +145,11 @@ class MoEShape:
     top_k: int = 8
     group: int = 0
     routed_scale: float = 1.0
+    topp: float = 0.0
 
     def c(self) -> Shape:
         return Shape(self.hidden, self.inter, self.n_routed, self.n_shared, self.top_k, self.group,
-                     self.routed_scale)
+                     self.routed_scale, self.topp)
 
 
 def version() -> str:
@@ -198,7 +200,8 @@ def router_logits(wr, x, out=None, stream=None):
     return out
 
 
-def route(logits, bias, k, idx=None, w=None, stream=None):
+def route(logits, bias, k, idx=None, w=None, stream=None, topp=None):
+    """coli_moe_route, or coli_moe_route_topp when topp is given."""
     import torch
     _need(logits, torch.float32, "logits")
     _need(bias, torch.float32, "bias")
@@ -207,8 +210,12 @@ def route(logits, bias, k, idx=None, w=None, stream=None):
         idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if w is None:
         w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
-    _check(lib().coli_moe_route(_ptr(logits), _ptr(bias), T, E, k, _ptr(idx), _ptr(w),
-                                _stream(stream)))
+    if topp is None:
+        _check(lib().coli_moe_route(_ptr(logits), _ptr(bias), T, E, k, _ptr(idx), _ptr(w),
+                                    _stream(stream)))
+    else:
+        _check(lib().coli_moe_route_topp(_ptr(logits), _ptr(bias), T, E, k, float(topp), _ptr(idx),
+                                         _ptr(w), _stream(stream)))
     return idx, w
 
 

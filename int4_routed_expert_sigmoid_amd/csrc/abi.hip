@@ -40,6 +40,7 @@ coli_status check_shape(const coli_moe_shape* s) {
     if (s->inter > 4096) return fail(COLI_EUNSUPPORTED, "inter must be <= 4096");
     if (!(s->routed_scale == s->routed_scale) || s->routed_scale > 3.4e38f || s->routed_scale < -3.4e38f)
         return fail(COLI_EINVAL, "routed_scale must be finite");
+    if (!(s->topp >= 0.f && s->topp <= 1.f)) return fail(COLI_EINVAL, "topp must be in [0, 1]");
     return COLI_OK;
 }
 
@@ -152,13 +153,26 @@ coli_status coli_moe_router_logits(const float* d_wr, const float* d_x, int32_t 
     COLI_GUARD_END
 }
 
+static coli_status route_call(const float* d_logits, const float* d_bias, int32_t T, int32_t E,
+                              int32_t k, float topp, int32_t* d_idx, float* d_w, void* stream) {
+    if (T < 0 || E <= 0 || k <= 0 || k > E) return fail(COLI_EINVAL, "route: need T >= 0, 1 <= k <= E");
+    if (E > 1024 || k > 32) return fail(COLI_EUNSUPPORTED, "route: E <= 1024 and k <= 32");
+    if (!(topp >= 0.f && topp <= 1.f)) return fail(COLI_EINVAL, "route: topp must be in [0, 1]");
+    if (T > 0 && (!d_logits || !d_idx || !d_w)) return fail(COLI_EINVAL, "route: NULL pointer");
+    return launch_route(d_logits, d_bias, T, E, k, topp, d_idx, d_w, (hipStream_t)stream);
+}
+
 coli_status coli_moe_route(const float* d_logits, const float* d_bias, int32_t T, int32_t E,
                            int32_t k, int32_t* d_idx, float* d_w, void* stream) {
     COLI_GUARD_BEGIN
-    if (T < 0 || E <= 0 || k <= 0 || k > E) return fail(COLI_EINVAL, "route: need T >= 0, 1 <= k <= E");
-    if (E > 1024 || k > 32) return fail(COLI_EUNSUPPORTED, "route: E <= 1024 and k <= 32");
-    if (T > 0 && (!d_logits || !d_idx || !d_w)) return fail(COLI_EINVAL, "route: NULL pointer");
-    return launch_route(d_logits, d_bias, T, E, k, d_idx, d_w, (hipStream_t)stream);
+    return route_call(d_logits, d_bias, T, E, k, 0.f, d_idx, d_w, stream);
+    COLI_GUARD_END
+}
+
+coli_status coli_moe_route_topp(const float* d_logits, const float* d_bias, int32_t T, int32_t E,
+                                int32_t k, float topp, int32_t* d_idx, float* d_w, void* stream) {
+    COLI_GUARD_BEGIN
+    return route_call(d_logits, d_bias, T, E, k, topp, d_idx, d_w, stream);
     COLI_GUARD_END
 }
 

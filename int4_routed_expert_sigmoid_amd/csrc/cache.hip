@@ -87,13 +87,18 @@ coli_status cache_place(coli_expert_cache* c, int32_t layer, const int32_t* d_id
     }
     COLI_CHECK_HIP(hipMemcpyAsync(c->h_idx, d_idx, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
     COLI_CHECK_HIP(hipStreamSynchronize(stream));
-    std::vector<int32_t> miss((size_t)n);
-    coli_status st = coli_expert_cache_ensure(c, layer, c->h_idx, n, miss.data());
+    // slots dropped by the adaptive top-p (index -1) need no expert
+    std::vector<int32_t> ids;
+    ids.reserve((size_t)n);
+    for (int32_t i = 0; i < n; ++i)
+        if (c->h_idx[i] >= 0) ids.push_back(c->h_idx[i]);
+    std::vector<int32_t> miss(ids.size());
+    coli_status st = coli_expert_cache_ensure(c, layer, ids.data(), (int32_t)ids.size(), miss.data());
     if (st) return st;
     uint8_t* ph = c->h_phase + (size_t)layer * c->cfg.n_experts;
     int32_t nm = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        ph[c->h_idx[i]] = miss[i] ? 1 : 0;
+    for (size_t i = 0; i < ids.size(); ++i) {
+        ph[ids[i]] = miss[i] ? 1 : 0;
         nm += miss[i];
     }
     *n_miss = nm;

@@ -263,11 +263,12 @@ struct SmallRouterArgs {
     const uint8_t* phase_mask; // [E] or NULL: keep only experts whose mask equals `phase`
     int32_t phase;
     int32_t T, E, k, H;
+    float topp;                // adaptive expert top-p, active in (0, 1)
 };
 coli_status launch_router_small(const SmallRouterArgs& a, hipStream_t stream);
 
 coli_status launch_route(const float* logits, const float* bias, int32_t T, int32_t E,
-                         int32_t k, int32_t* idx, float* w, hipStream_t stream);
+                         int32_t k, float topp, int32_t* idx, float* w, hipStream_t stream);
 size_t union_ws_bytes(int32_t T, int32_t k, int32_t E);
 coli_status launch_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* counts,
                          int32_t* offsets, int32_t* perm, int32_t* unique, int32_t* n_unique,
@@ -293,7 +294,11 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
                             float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
                             int32_t I, int32_t group, hipStream_t stream);
-coli_status launch_combine(const float* y_rows, const float* w, int32_t T, int32_t k, int32_t H,
-                           int32_t has_shared, float routed_scale, float* y, hipStream_t stream);
+// y [T][H] = shared row + rs * sum_j w[t][j] * y_rows[t*k + j] in slot order;
+// with idx (nullable) given, slots whose index is negative (dropped by top-p)
+// add nothing.
+coli_status launch_combine(const float* y_rows, const float* w, const int32_t* idx, int32_t T,
+                           int32_t k, int32_t H, int32_t has_shared, float routed_scale, float* y,
+                           hipStream_t stream);
 
 }  // namespace coli

@@ -72,13 +72,15 @@ __global__ __launch_bounds__(256) void act_encode_kernel(const float* __restrict
 // Grid: (column blocks of 256, tokens); the slot loads are issued in groups of
 // 8 before their multiply-adds, which keep the slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_rows,
-                                                      const float* __restrict__ w, int T, int k,
-                                                      int H, int has_shared, float rs,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ idx, int T,
+                                                      int k, int H, int has_shared, float rs,
                                                       float* __restrict__ y) {
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= H) return;
     for (int t = blockIdx.y; t < T; t += gridDim.y) {
         const float* wt = w + (int64_t)t * k;
+        const int32_t* it = idx + (int64_t)t * k;
         const float* yr = y_rows + (int64_t)t * k * H + c;
         const float sh = has_shared ? y_rows[((int64_t)T * k + t) * H + c] : 0.f;
         float acc = 0.f;
@@ -90,10 +92,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 wv[q] = wt[j + q];
                 yv[q] = yr[(int64_t)(j + q) * H];
             }
+            if (idx) {
+                // a slot dropped by top-p has no output row: it adds nothing
+#pragma unroll
+                for (int q = 0; q < 8; ++q) yv[q] = it[j + q] < 0 ? 0.f : yv[q];
+            }
 #pragma unroll
             for (int q = 0; q < 8; ++q) acc = fmaf(wv[q], yv[q], acc);
         }
-        for (; j < k; ++j) acc = fmaf(wt[j], yr[(int64_t)j * H], acc);
+        for (; j < k; ++j) {
+            const float yv = (idx && it[j] < 0) ? 0.f : yr[(int64_t)j * H];
+            acc = fmaf(wt[j], yv, acc);
+        }
         y[(int64_t)t * H + c] = fmaf(rs, acc, sh);
     }
 }
@@ -144,11 +154,12 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
     return COLI_OK;
 }
 
-coli_status launch_combine(const float* y_rows, const float* w, int32_t T, int32_t k, int32_t H,
-                           int32_t has_shared, float routed_scale, float* y, hipStream_t stream) {
+coli_status launch_combine(const float* y_rows, const float* w, const int32_t* idx, int32_t T,
+                           int32_t k, int32_t H, int32_t has_shared, float routed_scale, float* y,
+                           hipStream_t stream) {
     if ((int64_t)T * H == 0) return COLI_OK;
     const dim3 grid((unsigned)((H + 255) / 256), (unsigned)std::min(T, 65535));
-    launch(combine_kernel, grid, dim3(256), 0, stream, y_rows, w, T, k, H, has_shared,
+    launch(combine_kernel, grid, dim3(256), 0, stream, y_rows, w, idx, T, k, H, has_shared,
            routed_scale, y);
     COLI_CHECK_LAUNCH("combine kernel launch");
     return COLI_OK;

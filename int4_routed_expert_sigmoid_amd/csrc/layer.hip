@@ -115,6 +115,7 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
         ra.table = route_table; ra.shared_blob = shared_blob;
         ra.phase_mask = nullptr; ra.phase = 0;
         ra.T = T; ra.E = E; ra.k = k; ra.H = H;
+        ra.topp = s->topp;
         st = launch_router_small(ra, stream);
         if (st) return st;
         encoded = true;
@@ -125,7 +126,7 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
             if (st) return st;
             lg = at<float>(ws, W.logits);
         }
-        st = launch_route(lg, bias, T, E, k, idx, w, stream);
+        st = launch_route(lg, bias, T, E, k, s->topp, idx, w, stream);
         if (st) return st;
         st = launch_union(idx, T, k, E, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
                           at<int32_t>(ws, W.perm), at<int32_t>(ws, W.unique),
@@ -171,8 +172,10 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
         st = coli_expert_cache_release(cache, layer, (void*)stream);
         if (st) return st;
     }
-    return launch_combine(at<float>(ws, W.y_rows), w, T, k, H, shared_blob ? 1 : 0,
-                          s->routed_scale, y, stream);
+    // with the adaptive top-p some slots are dropped (index -1, no output row)
+    const bool adaptive = s->topp > 0.f && s->topp < 1.f;
+    return launch_combine(at<float>(ws, W.y_rows), w, adaptive ? idx : nullptr, T, k, H,
+                          shared_blob ? 1 : 0, s->routed_scale, y, stream);
 }
 
 }  // namespace coli

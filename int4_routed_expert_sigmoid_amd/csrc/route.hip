@@ -58,11 +58,19 @@ __device__ __forceinline__ void max_step(uint64_t& v) {
 // maximum (butterfly over DPP / permlane partners, no branches), and retires
 // the winner; the picks come out in slot order. The weights are normalised in
 // double in slot order.
+//
+// Adaptive expert top-p (practical guide "colibrì 實戰指南：以純 C 引擎在消費級
+// 硬體上串流運行 744B MoE 模型", section 三 and the section 五 tuning table; the
+// pages give no formula): with 0 < p < 1 only the shortest slot-order prefix
+// whose share of the k selected scores reaches p is kept. Slot j is kept iff
+// j == 0 or the share of slots 0..j-1 is below p; the shares only grow, so the
+// kept slots are a prefix. The prefix is renormalised over itself; dropped
+// slots get index -1 and weight 0. Shares and sums are double, in slot order.
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ lrow,
                                             const float* __restrict__ bias, int E, int k,
-                                            int* __restrict__ idx_row, float* __restrict__ w_row,
-                                            int* lds_idx = nullptr) {
+                                            float topp, int* __restrict__ idx_row,
+                                            float* __restrict__ w_row, int* lds_idx = nullptr) {
     const int lane = threadIdx.x & 63;
     uint64_t code[EPL];
     float score[EPL], lv[EPL], bv[EPL];
@@ -82,6 +90,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow,
         code[i] = valid ? selection_code(s + bv[i], e) : 0;
     }
     double sum = 0.0;
+    double my_prev = 0.0;    // lane j (< k): sum of slots 0..j-1
     float my_sel = 0.f;      // lane j (< k) keeps the score of slot j
     int my_idx = 0;
     for (int j = 0; j < k; ++j) {
@@ -106,24 +115,40 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow,
             code[i] = hit ? 0 : code[i];
         }
         const float s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), e & 63));
+        if (lane == j) { my_sel = s_sel; my_idx = e; my_prev = sum; }
         sum += (double)s_sel;
-        if (lane == j) { my_sel = s_sel; my_idx = e; }
+    }
+    int kept = k;
+    double ksum = sum;
+    if (topp > 0.f && topp < 1.f) {
+        const double share_before = sum == 0.0 ? (double)lane / (double)k : my_prev / sum;
+        const bool keep = lane < k && (lane == 0 || share_before < (double)topp);
+        kept = __popcll(__ballot(keep));
+        if (kept < k) {
+            // the kept prefix's sum is the running sum before slot `kept`
+            const uint64_t bits = (uint64_t)__double_as_longlong(my_prev);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, kept);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), kept);
+            ksum = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+        }
     }
     if (lane < k) {
-        idx_row[lane] = my_idx;
-        w_row[lane] = (sum == 0.0) ? (float)(1.0 / k) : (float)((double)my_sel / sum);
-        if (lds_idx) lds_idx[lane] = my_idx;
+        const bool kp = lane < kept;
+        idx_row[lane] = kp ? my_idx : -1;
+        w_row[lane] = !kp ? 0.f : (ksum == 0.0) ? (float)(1.0 / kept) : (float)((double)my_sel / ksum);
+        if (lds_idx) lds_idx[lane] = kp ? my_idx : -1;
     }
 }
 
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E,
-                                                    int k, int* __restrict__ idx,
+                                                    int k, float topp, int* __restrict__ idx,
                                                     float* __restrict__ w) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    route_token<EPL>(logits + (int64_t)t * E, bias, E, k, idx + (int64_t)t * k, w + (int64_t)t * k);
+    route_token<EPL>(logits + (int64_t)t * E, bias, E, k, topp, idx + (int64_t)t * k,
+                     w + (int64_t)t * k);
 }
 
 // ----------------------------------------------------- router, small T
@@ -231,7 +256,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
         tptr[i] = (with_items && e < E) ? a.table[e] : nullptr;
     }
     for (int t = wave; t < T; t += kRouterThreads / 64)
-        route_token<EPL>(lg + (int64_t)t * E, a.bias, E, k, a.idx + (int64_t)t * k,
+        route_token<EPL>(lg + (int64_t)t * E, a.bias, E, k, a.topp, a.idx + (int64_t)t * k,
                          a.w + (int64_t)t * k, s_idx + t * k);
     const int base = a.shared_blob ? 1 : 0;
     if (T == 1 && a.phase_mask == nullptr) {
@@ -243,11 +268,12 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
         for (int i = 0; i < EPT; ++i) {
             const int e = tid * EPT + i;
             if (e < E) {
+                // dropped slots hold -1, which is above every id as unsigned
                 int c = 0, below = 0, slot = 0;
                 for (int j = 0; j < k; ++j) {
                     c += s_idx[j] == e;
                     slot = s_idx[j] == e ? j : slot;
-                    below += s_idx[j] < e;
+                    below += (uint32_t)s_idx[j] < (uint32_t)e;
                 }
                 a.counts[e] = c;
                 a.offsets[e] = below;
@@ -264,17 +290,19 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
                 }
             }
         }
-        if (tid < k) {
+        int kept = 0;
+        for (int j = 0; j < k; ++j) kept += s_idx[j] >= 0;
+        if (tid < k && s_idx[tid] >= 0) {
             const int e = s_idx[tid];
             int p = 0;
-            for (int j = 0; j < k; ++j) p += s_idx[j] < e;
+            for (int j = 0; j < k; ++j) p += (uint32_t)s_idx[j] < (uint32_t)e;
             a.perm[p] = tid;
             a.rows_tok[p] = 0;
             a.rows_out[p] = tid;
         }
         if (tid == 0) {
-            a.offsets[E] = k;
-            *a.n_unique = k;
+            a.offsets[E] = kept;
+            *a.n_unique = kept;
             a.rows_tok[k] = 0;
             a.rows_out[k] = k;
             if (with_items && a.shared_blob) {
@@ -285,7 +313,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
                 it.row0 = k;
                 a.items[0] = it;
             }
-            *a.n_items = with_items ? base + k : 0;
+            *a.n_items = with_items ? base + kept : 0;
         }
         return;
     }
@@ -297,8 +325,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     // batch union of the n = T*k assignments (stable counting sort)
     const int n = T * k;
     for (int i = tid; i < n; i += kRouterThreads) {
-        atomicAdd(&s_cnt[s_idx[i]], 1);
-        atomicMin(&s_first[s_idx[i]], i);           // an item's first row is its first assignment
+        const int e = s_idx[i];
+        if (e < 0) continue;                        // dropped by top-p
+        atomicAdd(&s_cnt[e], 1);
+        atomicMin(&s_first[e], i);                  // an item's first row is its first assignment
     }
     __syncthreads();
     // offsets, the unique list and the kept work items in one scan: thread
@@ -357,6 +387,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     // stable positions: rank of assignment i among earlier equal experts
     for (int i = tid; i < n; i += kRouterThreads) {
         const int e = s_idx[i];
+        if (e < 0) continue;
         int r = 0;
         for (int j = 0; j < i; ++j) r += (s_idx[j] == e) ? 1 : 0;
         const int p = s_off[e] + r;
@@ -400,15 +431,15 @@ coli_status launch_router_small(const SmallRouterArgs& a, hipStream_t stream) {
 }
 
 coli_status launch_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
-                         int32_t* idx, float* w, hipStream_t stream) {
+                         float topp, int32_t* idx, float* w, hipStream_t stream) {
     if (T == 0) return COLI_OK;
     const dim3 grid((T + 3) / 4), block(256);
     const int epl = (E + 63) / 64;
-    if (epl <= 1) launch(route_kernel<1>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= 2) launch(route_kernel<2>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= 4) launch(route_kernel<4>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= 8) launch(route_kernel<8>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
-    else if (epl <= kMaxExpertsPerLane) launch(route_kernel<16>, grid, block, 0, stream, logits, bias, T, E, k, idx, w);
+    if (epl <= 1) launch(route_kernel<1>, grid, block, 0, stream, logits, bias, T, E, k, topp, idx, w);
+    else if (epl <= 2) launch(route_kernel<2>, grid, block, 0, stream, logits, bias, T, E, k, topp, idx, w);
+    else if (epl <= 4) launch(route_kernel<4>, grid, block, 0, stream, logits, bias, T, E, k, topp, idx, w);
+    else if (epl <= 8) launch(route_kernel<8>, grid, block, 0, stream, logits, bias, T, E, k, topp, idx, w);
+    else if (epl <= kMaxExpertsPerLane) launch(route_kernel<16>, grid, block, 0, stream, logits, bias, T, E, k, topp, idx, w);
     else return fail(COLI_EUNSUPPORTED, "route: more than 1024 experts");
     COLI_CHECK_LAUNCH("route kernel launch");
     return COLI_OK;
