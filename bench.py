@@ -50,6 +50,15 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
     ap.add_argument("--pinned-layers", type=int, default=13,
                     help="stream workload: distinct pinned layer pools (the rest reuse them)")
+    ap.add_argument("--policies", default="lru",
+                    help="stream workload: comma-separated placement policies, each run on a reset "
+                         "cache: lru; pinN (pin the N hottest experts of each layer from a usage "
+                         "history of later tokens); repinN (pinN, then repin every --repin-every "
+                         "tokens, 4 swaps, 25%% hysteresis, heat decay --repin-decay); lookR "
+                         "(lookahead prefetch of the next layer's experts predicted with recall R); "
+                         "parts combine with +, e.g. pin48+look1.0")
+    ap.add_argument("--repin-every", type=int, default=64)
+    ap.add_argument("--repin-decay", type=float, default=0.9)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "mtp", "stream", "copy"],
                     help="decode (headline, with the prefill line), prefill (that line alone), "
@@ -301,59 +310,120 @@ def run_stream(args, coli, dev):
     arena = torch.empty(L * S * blob, dtype=torch.uint8, device=dev)
     copy_stream = torch.cuda.Stream()
     cache = coli.ExpertCache(L, E, S, blob, arena=arena, pools=layer_pools, copy_stream=copy_stream)
-    lg = [torch.from_numpy(synth.locality_logits(args.seed, l, n_tok, E, k, keep_p=0.6)[0]).to(dev)
-          for l in range(L)]
+    # routing of the timed tokens, plus as many later tokens of the same process
+    # whose picks serve as a usage history from an earlier session
+    loc = [synth.locality_logits(args.seed, l, 2 * n_tok, E, k, keep_p=0.6) for l in range(L)]
+    lg = [torch.from_numpy(np.ascontiguousarray(loc[l][0][:n_tok])).to(dev) for l in range(L)]
+    chosen = [loc[l][1][:n_tok] for l in range(L)]
+    history = np.zeros((L, E), np.uint64)
+    for l in range(L):
+        for row in loc[l][1][n_tok:]:
+            history[l, row] += 1
     xs = [torch.from_numpy(synth.activations(args.seed, l, 0, n_tok, H)).to(dev) for l in range(L)]
     y = torch.empty((1, H), dtype=torch.float32, device=dev)
     ws = coli.workspace(shape, 1, coli.PATH_GEMV, dev)
     cold = min(16, n_tok)
-    torch.cuda.synchronize()
-    coli.profile_enable(2 * L * n_tok + 8)
-    t_start = time.perf_counter()
-    t_cold = None
-    for t in range(n_tok):
+
+    def guesses(recall):
+        """Lookahead predictions of every (layer, token): each true pick kept with
+        probability `recall`, otherwise replaced by an expert outside the set."""
+        rng = np.random.default_rng(args.seed + 7)
+        out = []
         for l in range(L):
-            coli.layer_fwd(shape, xs[l][t:t + 1], shared_blob=shared[l], logits=lg[l][t:t + 1],
-                           cache=cache, layer=l, y=y, path=coli.PATH_GEMV, ws=ws)
-        if t + 1 == cold:
-            torch.cuda.synchronize()
-            t_cold = time.perf_counter()
-            st_cold = cache.stats()
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    n_gu, ms_gu = coli.profile_summary("gemv_gateup")
-    n_dn, ms_dn = coli.profile_summary("gemv_down")
-    coli.profile_enable(0)
-    st = cache.stats()
-    warm_tok = n_tok - cold
-    hits_w = st["hits"] - st_cold["hits"]
-    miss_w = st["misses"] - st_cold["misses"]
-    pcie = st["bytes_h2d"] / max(1, st["copy_ns"])         # bytes per ns = GB/s
-    # 9 blobs per layer call, over the GEMV kernels' summed time (a cached call
-    # launches each GEMV twice: resident experts, then the copied ones)
-    ffn_bytes = 9 * blob * L * n_tok
-    hbm = ffn_bytes / ((ms_gu + ms_dn) / 1e3) / 1e9 if n_gu else None
+            g = chosen[l].copy()
+            for t in range(n_tok):
+                for j in range(k):
+                    if rng.random() >= recall:
+                        while True:
+                            e = int(rng.integers(E))
+                            if e not in chosen[l][t] and e not in g[t]:
+                                break
+                        g[t, j] = e
+            out.append(g)
+        return out
+
+    def run_policy(policy):
+        cache.reset()
+        pin_n, repin, recall = 0, False, None
+        for part in policy.split("+"):
+            if part.startswith("pin"):
+                pin_n = int(part[3:])
+            elif part.startswith("repin"):
+                pin_n, repin = int(part[5:]), True
+            elif part.startswith("look"):
+                recall = float(part[4:])
+            elif part != "lru":
+                raise ValueError(f"unknown placement policy {part}")
+        guess = guesses(recall) if recall is not None else None
+        if pin_n:
+            cache.pin_hot(pin_n, history)
+        torch.cuda.synchronize()
+        st0 = cache.stats()
+        coli.profile_enable(2 * L * n_tok + 8)
+        t_start = time.perf_counter()
+        t_cold, st_cold = None, None
+        for t in range(n_tok):
+            if repin and t > 0 and t % args.repin_every == 0:
+                cache.repin(4, 0.25, args.repin_decay)
+            for l in range(L):
+                coli.layer_fwd(shape, xs[l][t:t + 1], shared_blob=shared[l],
+                               logits=lg[l][t:t + 1], cache=cache, layer=l, y=y,
+                               path=coli.PATH_GEMV, ws=ws)
+                if guess is not None:
+                    # the next layer call's experts, predicted, copied during this one's
+                    nl, nt = (l + 1, t) if l + 1 < L else (0, t + 1)
+                    if nt < n_tok:
+                        cache.prefetch(nl, guess[nl][nt])
+            if t + 1 == cold:
+                torch.cuda.synchronize()
+                t_cold = time.perf_counter()
+                st_cold = cache.stats()
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
+        n_gu, ms_gu = coli.profile_summary("gemv_gateup")
+        n_dn, ms_dn = coli.profile_summary("gemv_down")
+        coli.profile_enable(0)
+        st = cache.stats()
+        warm_tok = n_tok - cold
+        d = {key: st[key] - st_cold[key] for key in st}
+        lookups_w = d["hits"] + d["misses"]
+        pcie = (st["bytes_h2d"] - st0["bytes_h2d"]) / max(1, st["copy_ns"] - st0["copy_ns"])
+        # 9 blobs per layer call, over the GEMV kernels' summed time (a cached call
+        # launches each GEMV twice: resident experts, then the copied ones)
+        ffn_bytes = 9 * blob * L * n_tok
+        hbm = ffn_bytes / ((ms_gu + ms_dn) / 1e3) / 1e9 if n_gu else None
+        warm_s = t_end - t_cold if warm_tok else None
+        log(f"stream policy {policy}: {warm_tok / warm_s if warm_tok else 0:.1f} tokens/s warm")
+        return {
+            "policy": policy,
+            "tokens_per_s_warm": round(warm_tok / warm_s, 3) if warm_tok else None,
+            "ms_per_token_warm": round(1e3 * warm_s / warm_tok, 4) if warm_tok else None,
+            "cold_tokens_per_s": round(cold / (t_cold - t_start), 3),
+            "hit_rate_warm": round(d["hits"] / max(1, lookups_w), 4),
+            "misses_per_token_per_layer_warm": round(d["misses"] / max(1, warm_tok * L), 3),
+            "copies_per_token_per_layer_warm": round(d["bytes_h2d"] / blob / max(1, warm_tok * L), 3),
+            "pcie_GBps": round(pcie, 2), "h2d_GB": round((st["bytes_h2d"] - st0["bytes_h2d"]) / 1e9, 2),
+            "hbm_GBps_ffn_kernels": round(hbm, 1) if hbm else None,
+            "cache": st,
+        }
+
+    results = [run_policy(p) for p in args.policies.split(",")]
     cache.close()
-    warm_s = t_end - t_cold if warm_tok else None
+    main = results[0]
     return {
         "metric": "streaming decode tokens/s, 16 layers, experts streamed from pinned host (hit rate, PCIe and HBM GB/s)",
-        "value": round(warm_tok / warm_s, 3) if warm_tok else None, "unit": "tokens/s",
-        "n_gpus": 1, "steps": warm_tok, "warmup": cold,
-        "ms_per_step": round(1e3 * warm_s / warm_tok, 4) if warm_tok else None,
+        "value": main["tokens_per_s_warm"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": n_tok - cold, "warmup": cold,
+        "ms_per_step": main["ms_per_token_warm"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int4 weights x f32 activations (exact int32 nibble products), f32 accumulate",
         "data": "synthetic (seeded Philox weights; layer l holds the layer-0 experts in a seeded order; locality routing)",
-        "config": {"workload": "streaming decode, 16 GLM-5.2-shaped layers, 64-slot HBM LRU per layer",
+        "config": {"workload": "streaming decode, 16 GLM-5.2-shaped layers, 64-slot HBM cache per layer",
                    "hidden": H, "inter": I, "n_routed": E, "top_k": k, "layers": L, "slots": S,
                    "host_pool_GB": round(L * E * blob / 1e9, 2),
-                   "distinct_pinned_pools": n_pools, "tokens": n_tok},
-        "cold_tokens": cold, "cold_tokens_per_s": round(cold / (t_cold - t_start), 3),
-        "hit_rate_warm": round(hits_w / max(1, hits_w + miss_w), 4),
-        "misses_per_token_per_layer_warm": round(miss_w / max(1, warm_tok * L), 3),
-        "pcie_GBps": round(pcie, 2), "h2d_GB": round(st["bytes_h2d"] / 1e9, 2),
-        "copy_s": round(st["copy_ns"] / 1e9, 3),
-        "hbm_GBps_ffn_kernels": round(hbm, 1) if hbm else None,
-        "cache": st,
+                   "distinct_pinned_pools": n_pools, "tokens": n_tok, "policy": main["policy"]},
+        **{key: v for key, v in main.items() if key != "policy"},
+        "policies": results[1:],
     }
 
 

@@ -212,12 +212,17 @@ typedef struct coli_cache_cfg {
 } coli_cache_cfg;
 
 typedef struct coli_cache_stats {
-    uint64_t hits;
-    uint64_t misses;
+    uint64_t hits;              /* lookups of a resident expert (pinned and prefetched ones too) */
+    uint64_t misses;            /* lookups that copied the expert */
     uint64_t evictions;
-    uint64_t bytes_h2d;
+    uint64_t bytes_h2d;         /* every copy: misses, pins and prefetches */
     uint64_t copy_ns;           /* sum of the copies' event-measured durations */
-    uint64_t lookups;
+    uint64_t lookups;           /* distinct experts named per ensure, summed */
+    uint64_t pin_hits;          /* hits on pinned slots */
+    uint64_t pin_loads;         /* copies made to pin an expert */
+    uint64_t prefetches;        /* copies started by a prefetch */
+    uint64_t prefetch_hits;     /* first lookup of a prefetched expert */
+    uint64_t repin_swaps;
 } coli_cache_stats;
 
 /* Creates the handle and its per-layer device pointer tables (n_layers *
@@ -255,8 +260,76 @@ COLI_API coli_status coli_expert_cache_table(struct coli_expert_cache* cache, in
 
 COLI_API coli_status coli_expert_cache_stats(struct coli_expert_cache* cache, coli_cache_stats* out);
 
-/* Forget every resident expert (the next lookups all miss); stats zeroed. */
+/* Forget every resident expert (the next lookups all miss); pins, usage
+ * history, heat and stats zeroed. */
 COLI_API coli_status coli_expert_cache_reset(struct coli_expert_cache* cache);
+
+/* ------------------------------------------------- learned placement
+ * The practical guide's tuning section (section 五): the engine records which
+ * experts each layer's tokens are routed to (a usage history), pins the
+ * hottest experts so that they are never evicted, lets pinned experts share
+ * one memory budget with the LRU, and can swap cold pinned experts for hot ones
+ * at safe boundaries from a decaying session heat map, with 25% hysteresis and
+ * at most four swaps at a time; and (section 二) a router lookahead applies the
+ * next layer's router early and prefetches what it picks. Here the budget is
+ * the layer's slots: pinned slots are never chosen as victims, and the rest
+ * are the LRU. Placement still changes speed only, never results. */
+
+/* Make h_ids[0..n) the pinned set of `layer` (replacing earlier pins, which
+ * become plain LRU entries); members not resident are copied in on the copy
+ * stream. Distinct ids count once. COLI_EBUSY if they exceed the slots, or
+ * the free slots while a call of the layer is not yet released; nothing
+ * changes then. A later ensure that names more unpinned experts than
+ * unpinned slots returns COLI_EBUSY, so leave room for a call's experts. */
+COLI_API coli_status coli_expert_cache_pin(struct coli_expert_cache* cache, int32_t layer,
+                                  const int32_t* h_ids, int32_t n);
+
+/* Usage history: h_counts [n_layers][n_experts] receives, per expert, how many
+ * ensure calls named it since create or reset. */
+COLI_API coli_status coli_expert_cache_usage(struct coli_expert_cache* cache, uint64_t* h_counts);
+
+/* Pin, in every layer, the `per_layer` experts with the largest counts in
+ * h_counts [n_layers][n_experts] (a saved history; NULL = this cache's own
+ * usage history); equal counts go to the lower id; experts with count 0 are
+ * not pinned. 0 <= per_layer <= slots_per_layer. */
+COLI_API coli_status coli_expert_cache_pin_hot(struct coli_expert_cache* cache,
+                                      const uint64_t* h_counts, int32_t per_layer);
+
+/* Repin at a safe boundary (no layer call in flight on the host side). Heat:
+ * every ensure adds 1 to each expert it names; after the swaps, every heat is
+ * multiplied by `decay` (in [0, 1]). Per layer, up to max_swaps times: the
+ * coldest pinned expert (equal heat: the higher id) is unpinned (it stays
+ * resident as an LRU entry) and the hottest unpinned expert with heat > 0
+ * (equal heat: the lower id) is pinned (copied in if needed), provided its
+ * heat exceeds (1 + hysteresis) times the cold one's; otherwise the layer
+ * stops. The guide's setting is max_swaps 4, hysteresis 0.25. *h_swaps
+ * (nullable) receives the number of swaps over all layers. */
+COLI_API coli_status coli_expert_cache_repin(struct coli_expert_cache* cache, int32_t max_swaps,
+                                    float hysteresis, float decay, int32_t* h_swaps);
+
+/* Prefetch: start copies of the experts h_ids[0..n) of `layer` that are not
+ * resident, in order, each into the LRU victim among slots that are not
+ * pinned, not named by this request and not held by an unreleased call of the
+ * layer; stops when there is none. Experts already resident or in flight are
+ * not read again. A prefetched expert counts as a hit when a call names it;
+ * that call runs it after coli_expert_cache_wait, like a miss, if the copy may
+ * still be in flight. *h_started (nullable) receives the number of copies. */
+COLI_API coli_status coli_expert_cache_prefetch(struct coli_expert_cache* cache, int32_t layer,
+                                       const int32_t* h_ids, int32_t n, int32_t* h_started);
+
+/* Router lookahead into the cache: route d_x [T][H] with `layer`'s router
+ * (d_router_w [E][H], or d_logits [T][E] already computed; d_bias nullable;
+ * shape->topp applies), read the picks back to the host (one blocking
+ * 4*T*k-byte read) and coli_expert_cache_prefetch them into `layer`. Meant to
+ * run with an earlier state of the tokens (the guide applies layer L+1's
+ * router to layer L's post-attention state) so that the copies overlap layer
+ * L's work. Uses the routing regions of d_ws (coli_moe_workspace_size for
+ * shape and T), so it must be ordered with other calls that share d_ws. */
+COLI_API coli_status coli_moe_lookahead(const coli_moe_shape* shape, const float* d_x, int32_t T,
+                               const float* d_logits, const float* d_router_w,
+                               const float* d_bias, struct coli_expert_cache* cache,
+                               int32_t layer, int32_t* h_started, void* d_ws, size_t ws_bytes,
+                               void* stream);
 
 /* ---------------------------------------------------------- kernel timing
  * Optional HIP-event timing of the library's main kernels, recorded on the

@@ -26,8 +26,9 @@ EXPORTED = [
     "coli_moe_expert_ffn", "coli_moe_layer_fwd", "coli_expert_cache_create",
     "coli_expert_cache_destroy", "coli_expert_cache_ensure", "coli_expert_cache_wait",
     "coli_expert_cache_release", "coli_expert_cache_table", "coli_expert_cache_stats",
-    "coli_expert_cache_reset", "coli_profile_enable", "coli_profile_clear",
-    "coli_profile_summary",
+    "coli_expert_cache_reset", "coli_expert_cache_pin", "coli_expert_cache_usage",
+    "coli_expert_cache_pin_hot", "coli_expert_cache_repin", "coli_expert_cache_prefetch",
+    "coli_moe_lookahead", "coli_profile_enable", "coli_profile_clear", "coli_profile_summary",
 ]
 
 
@@ -54,7 +55,10 @@ class CacheCfg(ctypes.Structure):
 class CacheStats(ctypes.Structure):
     _fields_ = [("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
                 ("evictions", ctypes.c_uint64), ("bytes_h2d", ctypes.c_uint64),
-                ("copy_ns", ctypes.c_uint64), ("lookups", ctypes.c_uint64)]
+                ("copy_ns", ctypes.c_uint64), ("lookups", ctypes.c_uint64),
+                ("pin_hits", ctypes.c_uint64), ("pin_loads", ctypes.c_uint64),
+                ("prefetches", ctypes.c_uint64), ("prefetch_hits", ctypes.c_uint64),
+                ("repin_swaps", ctypes.c_uint64)]
 
 
 _lock = threading.Lock()
@@ -97,6 +101,13 @@ def lib():
             L.coli_expert_cache_table.argtypes = [vp, i32, P(vp)]
             L.coli_expert_cache_stats.argtypes = [vp, P(CacheStats)]
             L.coli_expert_cache_reset.argtypes = [vp]
+            L.coli_expert_cache_pin.argtypes = [vp, i32, vp, i32]
+            L.coli_expert_cache_usage.argtypes = [vp, vp]
+            L.coli_expert_cache_pin_hot.argtypes = [vp, vp, i32]
+            L.coli_expert_cache_repin.argtypes = [vp, i32, f32, f32, P(i32)]
+            L.coli_expert_cache_prefetch.argtypes = [vp, i32, vp, i32, P(i32)]
+            L.coli_moe_lookahead.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, i32, P(i32), vp,
+                                             sz, vp]
             L.coli_profile_enable.argtypes = [i32]
             L.coli_profile_clear.argtypes = []
             L.coli_profile_summary.argtypes = [ctypes.c_char_p, P(i64), P(ctypes.c_double)]
@@ -290,6 +301,22 @@ def layer_fwd(shape: MoEShape, x, table=None, shared_blob=None, logits=None, rou
     return y
 
 
+def lookahead(shape: MoEShape, x, cache, layer, logits=None, router_w=None, bias=None, ws=None,
+              stream=None) -> int:
+    """coli_moe_lookahead: route x with `layer`'s router and prefetch its picks;
+    returns the number of copies started."""
+    import torch
+    _need(x, torch.float32, "x")
+    T = x.shape[0]
+    if ws is None:
+        ws = workspace(shape, T, PATH_AUTO, x.device)
+    n = ctypes.c_int32()
+    _check(lib().coli_moe_lookahead(ctypes.byref(shape.c()), _ptr(x), T, _ptr(logits),
+                                    _ptr(router_w), _ptr(bias), ctypes.c_void_p(cache.handle),
+                                    layer, ctypes.byref(n), _ptr(ws), ws.numel(), _stream(stream)))
+    return n.value
+
+
 def profile_enable(max_records: int):
     _check(lib().coli_profile_enable(max_records))
 
@@ -354,12 +381,56 @@ class ExpertCache:
                                               miss.ctypes.data_as(ctypes.c_void_p)))
         return miss
 
+    def _stream_arg(self, stream):
+        # a bookkeeping-only cache records no events: no stream needed
+        return None if self._keep[0] is None else _stream(stream)
+
     def wait(self, layer, stream=None):
-        _check(lib().coli_expert_cache_wait(ctypes.c_void_p(self.handle), layer, _stream(stream)))
+        _check(lib().coli_expert_cache_wait(ctypes.c_void_p(self.handle), layer,
+                                            self._stream_arg(stream)))
 
     def release(self, layer, stream=None):
         _check(lib().coli_expert_cache_release(ctypes.c_void_p(self.handle), layer,
-                                               _stream(stream)))
+                                               self._stream_arg(stream)))
+
+    def pin(self, layer, ids):
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        _check(lib().coli_expert_cache_pin(ctypes.c_void_p(self.handle), layer,
+                                           ids.ctypes.data_as(ctypes.c_void_p), len(ids)))
+
+    def usage(self):
+        """Usage history, uint64 [n_layers][n_experts]."""
+        import numpy as np
+        out = np.zeros((self.cfg.n_layers, self.n_experts), dtype=np.uint64)
+        _check(lib().coli_expert_cache_usage(ctypes.c_void_p(self.handle),
+                                             out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def pin_hot(self, per_layer, counts=None):
+        import numpy as np
+        c = None
+        if counts is not None:
+            c = np.ascontiguousarray(np.asarray(counts, dtype=np.uint64))
+            assert c.shape == (self.cfg.n_layers, self.n_experts)
+        _check(lib().coli_expert_cache_pin_hot(
+            ctypes.c_void_p(self.handle), None if c is None else c.ctypes.data_as(ctypes.c_void_p),
+            per_layer))
+
+    def repin(self, max_swaps=4, hysteresis=0.25, decay=0.5) -> int:
+        n = ctypes.c_int32()
+        _check(lib().coli_expert_cache_repin(ctypes.c_void_p(self.handle), max_swaps, hysteresis,
+                                             decay, ctypes.byref(n)))
+        return n.value
+
+    def prefetch(self, layer, ids) -> int:
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        n = ctypes.c_int32()
+        _check(lib().coli_expert_cache_prefetch(ctypes.c_void_p(self.handle), layer,
+                                                ids.ctypes.data_as(ctypes.c_void_p), len(ids),
+                                                ctypes.byref(n)))
+        return n.value
 
     def table_ptr(self, layer) -> int:
         p = ctypes.c_void_p()

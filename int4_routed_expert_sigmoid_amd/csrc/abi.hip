@@ -254,4 +254,24 @@ coli_status coli_moe_layer_fwd(const coli_moe_shape* shape, const float* d_x, in
     COLI_GUARD_END
 }
 
+coli_status coli_moe_lookahead(const coli_moe_shape* shape, const float* d_x, int32_t T,
+                               const float* d_logits, const float* d_router_w, const float* d_bias,
+                               struct coli_expert_cache* cache, int32_t layer, int32_t* h_started,
+                               void* d_ws, size_t ws_bytes, void* stream) {
+    COLI_GUARD_BEGIN
+    coli_status st = check_shape(shape);
+    if (st) return st;
+    if (T < 0 || !cache) return fail(COLI_EINVAL, "lookahead: T < 0 or no cache");
+    if ((d_logits == nullptr) == (d_router_w == nullptr))
+        return fail(COLI_EINVAL, "lookahead: give exactly one of logits and router_w");
+    if (h_started) *h_started = 0;
+    if (T == 0) return COLI_OK;
+    if (d_router_w && !d_x) return fail(COLI_EINVAL, "lookahead: NULL x");
+    const WsLayout W = ws_layout(shape, T, COLI_PATH_AUTO);
+    if (!d_ws || ws_bytes < W.bytes) return fail(COLI_ENOMEM, "lookahead: workspace too small");
+    return run_lookahead(shape, d_x, T, d_logits, d_router_w, d_bias, cache, layer, h_started,
+                         (uint8_t*)d_ws, W, (hipStream_t)stream);
+    COLI_GUARD_END
+}
+
 }  // extern "C"

@@ -2,17 +2,29 @@
 // from pinned host memory (practical guide section 二: per-layer LRU cache;
 // each expert's three matrices are adjacent so a miss is one read; missing
 // experts load while resident ones compute; a read in flight is never issued
-// twice; placement changes speed only, never routing or results).
+// twice; placement changes speed only, never routing or results), with the
+// learned parts of the same guide's tuning section (section 五): a usage
+// history per (layer, expert), pinned experts that share the layer's slots
+// with the LRU, pinning of the historically hottest experts, a repin step that
+// swaps cold pinned experts for hot ones under hysteresis and a swap limit, and
+// prefetch of the experts a router lookahead predicts (PILOT, section 二).
 //
 // Host-side bookkeeping plus HIP copies and events:
-//  - ensure(): hits refresh their age; each miss takes the least recently used
-//    slot that this call does not use, makes the copy stream wait for the
-//    compute that last read that slot (its release event), and enqueues one
-//    host-to-device copy of the whole blob, followed by the slot's ready event.
+//  - a copy takes the first empty slot, else the least recently used slot that
+//    is not pinned and not otherwise excluded (equal ages: the lowest expert
+//    id), makes the copy stream wait for the compute that last read that slot
+//    (its release event), enqueues one host-to-device copy of the whole blob
+//    and the slot's ready event, and marks the slot pending until a compute
+//    stream has waited for it;
+//  - ensure(): hits refresh their age; each miss is copied into a slot that
+//    this call does not name; a named expert whose copy is still pending (a
+//    prefetch or a pin) is reported like a miss, so its compute runs after
+//    wait();
 //  - wait(): the compute stream waits for the ready events of every slot the
-//    last ensure() named (completed events cost nothing).
+//    last ensure() named (completed events cost nothing);
 //  - release(): records, on the compute stream, the release event of those
-//    slots; a later eviction of any of them waits for it.
+//    slots; a later eviction of any of them waits for it. Until then pin and
+//    prefetch leave those slots alone.
 // With a NULL arena and pool the cache only keeps the books (no copies, no
 // events): the policy can be simulated without a GPU.
 #include <algorithm>
@@ -32,10 +44,16 @@ struct coli_expert_cache {
         hipEvent_t ready = nullptr;       // after the copy that filled it
         hipEvent_t release = nullptr;     // after the compute that last read it
         bool release_recorded = false;
+        bool pinned = false;              // never evicted while pinned
+        bool pending = false;             // copy enqueued, no compute stream has waited for it
+        bool prefetched = false;          // filled by a prefetch, not named by a call since
     };
     std::vector<std::vector<Slot>> slots;          // [layer][slot]
     std::vector<std::vector<int32_t>> where;       // [layer][expert] -> slot or -1
     std::vector<std::vector<int32_t>> used;        // [layer] slots named by the last ensure
+    std::vector<char> open;                        // [layer] last ensure not yet released
+    std::vector<std::vector<uint64_t>> usage;      // [layer][expert] lookups (history)
+    std::vector<std::vector<double>> heat;         // [layer][expert] decaying session heat
     void** d_tables = nullptr;                     // device [layer][expert]
     uint8_t* h_slot_ptrs = nullptr;                // pinned: device address of every slot
     uint64_t clock = 0;
@@ -60,6 +78,112 @@ static coli_status harvest_timer(coli_expert_cache* c, size_t i, bool wait) {
     COLI_CHECK_HIP(hipEventElapsedTime(&ms, c->timers[i].first, c->timers[i].second));
     c->st.copy_ns += (uint64_t)(ms * 1e6);
     c->timer_live[i] = false;
+    return COLI_OK;
+}
+
+// Victim for a copy into `layer`: the first empty slot, else the least
+// recently used slot (equal ages: the lowest expert id) among those that are
+// not pinned and not excluded. -1 if there is none.
+static int pick_victim(coli_expert_cache* c, int32_t layer, const std::vector<char>& excluded) {
+    const auto& slots = c->slots[layer];
+    int victim = -1;
+    for (int s = 0; s < (int)slots.size(); ++s) {
+        if (slots[s].pinned || excluded[s]) continue;
+        if (slots[s].expert < 0) return s;
+        if (victim < 0) { victim = s; continue; }
+        const auto& a = slots[s];
+        const auto& b = slots[victim];
+        if (a.last_use < b.last_use || (a.last_use == b.last_use && a.expert < b.expert)) victim = s;
+    }
+    return victim;
+}
+
+// Slots an asynchronous pin or prefetch must not take: those named by a call
+// that has not been released yet.
+static std::vector<char> open_slots(coli_expert_cache* c, int32_t layer) {
+    std::vector<char> ex(c->cfg.slots_per_layer, 0);
+    if (c->open[layer])
+        for (int32_t s : c->used[layer]) ex[s] = 1;
+    return ex;
+}
+
+// Copy expert e of `layer` into slot `victim` (evicting its occupant).
+static coli_status load_slot(coli_expert_cache* c, int32_t layer, int32_t e, int victim,
+                             uint64_t now) {
+    const int S = c->cfg.slots_per_layer, E = c->cfg.n_experts;
+    auto& sl = c->slots[layer][victim];
+    if (sl.expert >= 0) {
+        c->where[layer][sl.expert] = -1;
+        c->st.evictions++;
+    }
+    sl.expert = e;
+    sl.last_use = now;
+    sl.prefetched = false;
+    c->where[layer][e] = victim;
+    c->st.bytes_h2d += c->cfg.blob_bytes;
+    if (c->dry) return COLI_OK;
+    sl.pending = true;
+    hipStream_t cs = (hipStream_t)c->cfg.copy_stream;
+    const size_t bb = c->cfg.blob_bytes;
+    uint8_t* dst = (uint8_t*)c->cfg.d_arena + ((size_t)layer * S + victim) * bb;
+    const uint8_t* src = c->pools[layer] + (size_t)e * bb;
+    if (sl.release_recorded) COLI_CHECK_HIP(hipStreamWaitEvent(cs, sl.release, 0));
+    const size_t ti = c->timer_next;
+    c->timer_next = (ti + 1) % c->timers.size();
+    coli_status hs = harvest_timer(c, ti, true);
+    if (hs) return hs;
+    COLI_CHECK_HIP(hipEventRecord(c->timers[ti].first, cs));
+    COLI_CHECK_HIP(hipMemcpyAsync(dst, src, bb, hipMemcpyHostToDevice, cs));
+    COLI_CHECK_HIP(hipEventRecord(c->timers[ti].second, cs));
+    c->timer_live[ti] = true;
+    // pointer of the expert in the device table: a constant pinned source
+    COLI_CHECK_HIP(hipMemcpyAsync(c->d_tables + (size_t)layer * E + e,
+                                  c->h_slot_ptrs + ((size_t)layer * S + victim) * sizeof(void*),
+                                  sizeof(void*), hipMemcpyHostToDevice, cs));
+    COLI_CHECK_HIP(hipEventRecord(sl.ready, cs));
+    return COLI_OK;
+}
+
+// Distinct ids of a request in first-appearance order; false if one is out of range.
+static bool distinct_ids(const int32_t* ids, int32_t n, int32_t E, std::vector<int32_t>* out) {
+    std::vector<char> seen(E, 0);
+    out->clear();
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t e = ids[i];
+        if (e < 0 || e >= E) return false;
+        if (!seen[e]) { seen[e] = 1; out->push_back(e); }
+    }
+    return true;
+}
+
+// Make `ids` the pinned set of `layer`: earlier pins not in it become plain
+// LRU entries; members not resident are copied in.
+static coli_status pin_layer(coli_expert_cache* c, int32_t layer, const std::vector<int32_t>& ids) {
+    const int S = c->cfg.slots_per_layer;
+    auto& slots = c->slots[layer];
+    auto& where = c->where[layer];
+    if ((int)ids.size() > S) return fail(COLI_EBUSY, "cache_pin: more experts than slots");
+    std::vector<char> excluded = open_slots(c, layer);
+    std::vector<char> keep(S, 0);
+    int need = 0;
+    for (int32_t e : ids) {
+        if (where[e] >= 0) keep[where[e]] = 1;
+        else ++need;
+    }
+    int avail = 0;
+    for (int s = 0; s < S; ++s) avail += !keep[s] && !excluded[s];
+    if (need > avail) return fail(COLI_EBUSY, "cache_pin: not enough free slots (an unreleased call holds some)");
+    for (int s = 0; s < S; ++s) slots[s].pinned = keep[s] != 0;
+    const uint64_t now = ++c->clock;
+    for (int32_t e : ids) {
+        if (where[e] >= 0) continue;
+        const int v = pick_victim(c, layer, excluded);
+        if (v < 0) return fail(COLI_EBUSY, "cache_pin: no free slot");
+        coli_status st = load_slot(c, layer, e, v, now);
+        if (st) return st;
+        slots[v].pinned = true;
+        c->st.pin_loads++;
+    }
     return COLI_OK;
 }
 
@@ -108,6 +232,27 @@ coli_status cache_place(coli_expert_cache* c, int32_t layer, const int32_t* d_id
     return COLI_OK;
 }
 
+// Lookahead step: read back routing computed for `layer` from an earlier
+// state (blocking) and prefetch the experts it names.
+coli_status cache_prefetch_routed(coli_expert_cache* c, int32_t layer, const int32_t* d_idx,
+                                  int32_t n, int32_t* started, hipStream_t stream) {
+    if (c->dry) return fail(COLI_EINVAL, "cache: a bookkeeping-only cache cannot prefetch routed experts");
+    if ((size_t)n > c->h_idx_cap) {
+        if (c->h_idx) COLI_CHECK_HIP(hipHostFree(c->h_idx));
+        c->h_idx = nullptr;
+        c->h_idx_cap = 0;
+        COLI_CHECK_HIP(hipHostMalloc((void**)&c->h_idx, sizeof(int32_t) * (size_t)n * 2, hipHostMallocDefault));
+        c->h_idx_cap = (size_t)n * 2;
+    }
+    COLI_CHECK_HIP(hipMemcpyAsync(c->h_idx, d_idx, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
+    COLI_CHECK_HIP(hipStreamSynchronize(stream));
+    std::vector<int32_t> ids;
+    ids.reserve((size_t)n);
+    for (int32_t i = 0; i < n; ++i)
+        if (c->h_idx[i] >= 0) ids.push_back(c->h_idx[i]);
+    return coli_expert_cache_prefetch(c, layer, ids.data(), (int32_t)ids.size(), started);
+}
+
 }  // namespace coli
 
 using namespace coli;
@@ -136,6 +281,9 @@ COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct 
         c->slots.assign(L, std::vector<coli_expert_cache::Slot>(S));
         c->where.assign(L, std::vector<int32_t>(E, -1));
         c->used.assign(L, {});
+        c->open.assign(L, 0);
+        c->usage.assign(L, std::vector<uint64_t>(E, 0));
+        c->heat.assign(L, std::vector<double>(E, 0.0));
         if (!dry) {
             auto cleanup = [&](coli_status code, const char* what) {
                 coli_expert_cache_destroy(c);
@@ -202,85 +350,50 @@ COLI_API coli_status coli_expert_cache_ensure(struct coli_expert_cache* c, int32
         auto& where = c->where[layer];
         // distinct ids of this call, in first-appearance order
         std::vector<int32_t> ids;
-        ids.reserve(n);
-        std::vector<char> seen(E, 0);
-        for (int32_t i = 0; i < n; ++i) {
-            const int32_t e = h_ids[i];
-            if (e < 0 || e >= E) return fail(COLI_EINVAL, "cache_ensure: expert id out of range");
-            if (!seen[e]) { seen[e] = 1; ids.push_back(e); }
-        }
+        if (!distinct_ids(h_ids, n, E, &ids)) return fail(COLI_EINVAL, "cache_ensure: expert id out of range");
         if ((int)ids.size() > S) return fail(COLI_EBUSY, "cache_ensure: more distinct experts than slots");
-        const uint64_t now = ++c->clock;
-        std::vector<char> pinned(S, 0);
+        // capacity first, so that a refused call changes nothing
+        std::vector<char> named(S, 0);
         std::vector<int32_t> misses;
         for (int32_t e : ids) {
-            if (where[e] >= 0) {
-                pinned[where[e]] = 1;
-                slots[where[e]].last_use = now;
-                c->st.hits++;
-            } else {
-                misses.push_back(e);
-            }
+            if (where[e] >= 0) named[where[e]] = 1;
+            else misses.push_back(e);
+        }
+        int avail = 0;
+        for (int s = 0; s < S; ++s) avail += !named[s] && !slots[s].pinned;
+        if ((int)misses.size() > avail)
+            return fail(COLI_EBUSY, "cache_ensure: more unpinned experts than unpinned slots");
+        const uint64_t now = ++c->clock;
+        std::vector<char> late(E, 0);          // compute after wait(): copied or still pending
+        std::vector<int32_t> used;
+        for (int32_t e : ids) {
+            c->usage[layer][e] += 1;
+            c->heat[layer][e] += 1.0;
+            const int32_t s = where[e];
+            if (s < 0) continue;
+            auto& sl = slots[s];
+            sl.last_use = now;
+            c->st.hits++;
+            if (sl.pinned) c->st.pin_hits++;
+            if (sl.prefetched) { c->st.prefetch_hits++; sl.prefetched = false; }
+            if (sl.pending) late[e] = 1;
+            used.push_back(s);
         }
         c->st.lookups += ids.size();
-        std::vector<int32_t> used;
-        for (int32_t e : ids)
-            if (where[e] >= 0) used.push_back(where[e]);
-        hipStream_t cs = (hipStream_t)c->cfg.copy_stream;
         for (int32_t e : misses) {
-            // victim: the first empty slot, else the least recently used slot
-            // not named by this call (equal ages: the lowest expert id)
-            int victim = -1;
-            for (int s = 0; s < S; ++s) {
-                if (pinned[s]) continue;
-                if (victim < 0) { victim = s; continue; }
-                const auto& a = slots[s];
-                const auto& b = slots[victim];
-                if (b.expert < 0) continue;
-                if (a.expert < 0 || a.last_use < b.last_use ||
-                    (a.last_use == b.last_use && a.expert < b.expert))
-                    victim = s;
-            }
-            auto& sl = slots[victim];
-            if (sl.expert >= 0) {
-                where[sl.expert] = -1;
-                c->st.evictions++;
-            }
-            sl.expert = e;
-            sl.last_use = now;
-            where[e] = victim;
-            pinned[victim] = 1;
-            used.push_back(victim);
+            const int v = pick_victim(c, layer, named);
+            if (v < 0) return fail(COLI_EBUSY, "cache_ensure: no free slot");
+            coli_status st = load_slot(c, layer, e, v, now);
+            if (st) return st;
+            named[v] = 1;
+            late[e] = 1;
+            used.push_back(v);
             c->st.misses++;
-            c->st.bytes_h2d += c->cfg.blob_bytes;
-            if (!c->dry) {
-                const size_t bb = c->cfg.blob_bytes;
-                uint8_t* dst = (uint8_t*)c->cfg.d_arena + ((size_t)layer * S + victim) * bb;
-                const uint8_t* src = c->pools[layer] + (size_t)e * bb;
-                if (sl.release_recorded) COLI_CHECK_HIP(hipStreamWaitEvent(cs, sl.release, 0));
-                const size_t ti = c->timer_next;
-                c->timer_next = (ti + 1) % c->timers.size();
-                coli_status hs = harvest_timer(c, ti, true);
-                if (hs) return hs;
-                COLI_CHECK_HIP(hipEventRecord(c->timers[ti].first, cs));
-                COLI_CHECK_HIP(hipMemcpyAsync(dst, src, bb, hipMemcpyHostToDevice, cs));
-                COLI_CHECK_HIP(hipEventRecord(c->timers[ti].second, cs));
-                c->timer_live[ti] = true;
-                // pointer of the expert in the device table: a constant pinned source
-                COLI_CHECK_HIP(hipMemcpyAsync(
-                    c->d_tables + (size_t)layer * E + e,
-                    c->h_slot_ptrs + ((size_t)layer * S + victim) * sizeof(void*), sizeof(void*),
-                    hipMemcpyHostToDevice, cs));
-                COLI_CHECK_HIP(hipEventRecord(sl.ready, cs));
-            }
         }
         c->used[layer] = used;
+        c->open[layer] = 1;
         if (h_miss_mask)
-            for (int32_t i = 0; i < n; ++i) {
-                h_miss_mask[i] = 0;
-                for (int32_t e : misses)
-                    if (e == h_ids[i]) h_miss_mask[i] = 1;
-            }
+            for (int32_t i = 0; i < n; ++i) h_miss_mask[i] = late[h_ids[i]];
         return COLI_OK;
     } catch (const std::bad_alloc&) {
         return fail(COLI_ENOMEM, "cache_ensure: host allocation failed");
@@ -290,13 +403,16 @@ COLI_API coli_status coli_expert_cache_ensure(struct coli_expert_cache* c, int32
 COLI_API coli_status coli_expert_cache_wait(struct coli_expert_cache* c, int32_t layer, void* stream) {
     if (!c || layer < 0 || layer >= c->cfg.n_layers) return fail(COLI_EINVAL, "cache_wait: bad arguments");
     if (c->dry) return COLI_OK;
-    for (int32_t s : c->used[layer])
+    for (int32_t s : c->used[layer]) {
         COLI_CHECK_HIP(hipStreamWaitEvent((hipStream_t)stream, c->slots[layer][s].ready, 0));
+        c->slots[layer][s].pending = false;
+    }
     return COLI_OK;
 }
 
 COLI_API coli_status coli_expert_cache_release(struct coli_expert_cache* c, int32_t layer, void* stream) {
     if (!c || layer < 0 || layer >= c->cfg.n_layers) return fail(COLI_EINVAL, "cache_release: bad arguments");
+    c->open[layer] = 0;
     if (c->dry) return COLI_OK;
     for (int32_t s : c->used[layer]) {
         auto& sl = c->slots[layer][s];
@@ -329,12 +445,149 @@ COLI_API coli_status coli_expert_cache_reset(struct coli_expert_cache* c) {
         for (auto& s : layer) {
             s.expert = -1;
             s.last_use = 0;
+            s.pinned = s.pending = s.prefetched = false;
         }
     for (auto& w : c->where) std::fill(w.begin(), w.end(), -1);
     for (auto& u : c->used) u.clear();
+    std::fill(c->open.begin(), c->open.end(), 0);
+    for (auto& u : c->usage) std::fill(u.begin(), u.end(), 0);
+    for (auto& h : c->heat) std::fill(h.begin(), h.end(), 0.0);
+    c->clock = 0;
     for (size_t i = 0; i < c->timer_live.size(); ++i) c->timer_live[i] = false;
     c->st = coli_cache_stats{};
     return COLI_OK;
+}
+
+COLI_API coli_status coli_expert_cache_pin(struct coli_expert_cache* c, int32_t layer,
+                                           const int32_t* h_ids, int32_t n) {
+    try {
+        if (!c || layer < 0 || layer >= c->cfg.n_layers || n < 0 || (n > 0 && !h_ids))
+            return fail(COLI_EINVAL, "cache_pin: bad arguments");
+        std::vector<int32_t> ids;
+        if (!distinct_ids(h_ids, n, c->cfg.n_experts, &ids))
+            return fail(COLI_EINVAL, "cache_pin: expert id out of range");
+        return pin_layer(c, layer, ids);
+    } catch (const std::bad_alloc&) {
+        return fail(COLI_ENOMEM, "cache_pin: host allocation failed");
+    }
+}
+
+COLI_API coli_status coli_expert_cache_usage(struct coli_expert_cache* c, uint64_t* h_counts) {
+    if (!c || !h_counts) return fail(COLI_EINVAL, "cache_usage: NULL argument");
+    const size_t E = (size_t)c->cfg.n_experts;
+    for (size_t l = 0; l < c->usage.size(); ++l)
+        std::memcpy(h_counts + l * E, c->usage[l].data(), E * sizeof(uint64_t));
+    return COLI_OK;
+}
+
+COLI_API coli_status coli_expert_cache_pin_hot(struct coli_expert_cache* c, const uint64_t* h_counts,
+                                               int32_t per_layer) {
+    try {
+        if (!c) return fail(COLI_EINVAL, "cache_pin_hot: NULL cache");
+        if (per_layer < 0 || per_layer > c->cfg.slots_per_layer)
+            return fail(COLI_EINVAL, "cache_pin_hot: per_layer must be in [0, slots_per_layer]");
+        const int L = c->cfg.n_layers, E = c->cfg.n_experts;
+        for (int l = 0; l < L; ++l) {
+            const uint64_t* cnt = h_counts ? h_counts + (size_t)l * E : c->usage[l].data();
+            std::vector<int32_t> order(E);
+            for (int e = 0; e < E; ++e) order[e] = e;
+            std::stable_sort(order.begin(), order.end(),
+                             [cnt](int32_t a, int32_t b) { return cnt[a] > cnt[b]; });
+            std::vector<int32_t> ids;
+            for (int i = 0; i < E && (int)ids.size() < per_layer; ++i)
+                if (cnt[order[i]] > 0) ids.push_back(order[i]);
+            coli_status st = pin_layer(c, l, ids);
+            if (st) return st;
+        }
+        return COLI_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(COLI_ENOMEM, "cache_pin_hot: host allocation failed");
+    }
+}
+
+COLI_API coli_status coli_expert_cache_repin(struct coli_expert_cache* c, int32_t max_swaps,
+                                             float hysteresis, float decay, int32_t* h_swaps) {
+    try {
+        if (!c || max_swaps < 0 || !(hysteresis >= 0.f) || !(decay >= 0.f && decay <= 1.f))
+            return fail(COLI_EINVAL, "cache_repin: bad arguments");
+        const int L = c->cfg.n_layers, E = c->cfg.n_experts;
+        int32_t swaps = 0;
+        for (int l = 0; l < L; ++l) {
+            auto& slots = c->slots[l];
+            auto& where = c->where[l];
+            const auto& heat = c->heat[l];
+            std::vector<char> excluded = open_slots(c, l);
+            for (int n = 0; n < max_swaps; ++n) {
+                // coldest pinned expert (equal heat: the higher id leaves first)
+                int cold = -1;
+                for (const auto& sl : slots)
+                    if (sl.pinned && (cold < 0 || heat[sl.expert] < heat[cold] ||
+                                      (heat[sl.expert] == heat[cold] && sl.expert > cold)))
+                        cold = sl.expert;
+                // hottest expert that is not pinned (equal heat: the lower id)
+                int hot = -1;
+                for (int e = 0; e < E; ++e) {
+                    if (where[e] >= 0 && slots[where[e]].pinned) continue;
+                    if (heat[e] > 0.0 && (hot < 0 || heat[e] > heat[hot])) hot = e;
+                }
+                if (cold < 0 || hot < 0) break;
+                if (!(heat[hot] > (1.0 + (double)hysteresis) * heat[cold])) break;
+                slots[where[cold]].pinned = false;          // stays resident as an LRU entry
+                if (where[hot] >= 0) {
+                    slots[where[hot]].pinned = true;
+                } else {
+                    const int v = pick_victim(c, l, excluded);
+                    if (v < 0) { slots[where[cold]].pinned = true; break; }
+                    coli_status st = load_slot(c, l, hot, v, ++c->clock);
+                    if (st) return st;
+                    slots[v].pinned = true;
+                    c->st.pin_loads++;
+                }
+                ++swaps;
+            }
+        }
+        for (auto& h : c->heat)
+            for (double& v : h) v *= (double)decay;
+        c->st.repin_swaps += (uint64_t)swaps;
+        if (h_swaps) *h_swaps = swaps;
+        return COLI_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(COLI_ENOMEM, "cache_repin: host allocation failed");
+    }
+}
+
+COLI_API coli_status coli_expert_cache_prefetch(struct coli_expert_cache* c, int32_t layer,
+                                                const int32_t* h_ids, int32_t n,
+                                                int32_t* h_started) {
+    try {
+        if (!c || layer < 0 || layer >= c->cfg.n_layers || n < 0 || (n > 0 && !h_ids))
+            return fail(COLI_EINVAL, "cache_prefetch: bad arguments");
+        std::vector<int32_t> ids;
+        if (!distinct_ids(h_ids, n, c->cfg.n_experts, &ids))
+            return fail(COLI_EINVAL, "cache_prefetch: expert id out of range");
+        std::vector<char> excluded = open_slots(c, layer);
+        // experts already resident (or in flight) are not read again and keep
+        // their slots for this request
+        for (int32_t e : ids)
+            if (c->where[layer][e] >= 0) excluded[c->where[layer][e]] = 1;
+        const uint64_t now = ++c->clock;
+        int32_t started = 0;
+        for (int32_t e : ids) {
+            if (c->where[layer][e] >= 0) continue;
+            const int v = pick_victim(c, layer, excluded);
+            if (v < 0) break;
+            coli_status st = load_slot(c, layer, e, v, now);
+            if (st) return st;
+            c->slots[layer][v].prefetched = true;
+            excluded[v] = 1;
+            c->st.prefetches++;
+            ++started;
+        }
+        if (h_started) *h_started = started;
+        return COLI_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(COLI_ENOMEM, "cache_prefetch: host allocation failed");
+    }
 }
 
 }  // extern "C"

@@ -30,5 +30,13 @@ coli_status cache_layer_table(struct coli_expert_cache* cache, int32_t layer, in
                               const void* const** table);
 coli_status cache_place(struct coli_expert_cache* cache, int32_t layer, const int32_t* d_idx,
                         int32_t n, uint8_t* d_phase, int32_t* n_miss, hipStream_t stream);
+coli_status cache_prefetch_routed(struct coli_expert_cache* cache, int32_t layer,
+                                  const int32_t* d_idx, int32_t n, int32_t* started,
+                                  hipStream_t stream);
+
+coli_status run_lookahead(const coli_moe_shape* shape, const float* x, int32_t T,
+                          const float* logits, const float* router_w, const float* bias,
+                          struct coli_expert_cache* cache, int32_t layer, int32_t* started,
+                          uint8_t* ws, const WsLayout& W, hipStream_t stream);
 
 }  // namespace coli

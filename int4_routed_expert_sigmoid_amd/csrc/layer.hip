@@ -178,4 +178,24 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
                           shared_blob ? 1 : 0, s->routed_scale, y, stream);
 }
 
+coli_status run_lookahead(const coli_moe_shape* s, const float* x, int32_t T, const float* logits,
+                          const float* router_w, const float* bias, coli_expert_cache* cache,
+                          int32_t layer, int32_t* started, uint8_t* ws, const WsLayout& W,
+                          hipStream_t stream) {
+    const int32_t H = s->hidden, E = s->n_routed, k = s->top_k;
+    const void* const* table = nullptr;
+    coli_status cs = cache_layer_table(cache, layer, E, &table);   // checks layer and E
+    if (cs) return cs;
+    const float* lg = logits;
+    if (!lg) {
+        coli_status st = launch_router_logits(router_w, x, T, H, E, at<float>(ws, W.logits), stream);
+        if (st) return st;
+        lg = at<float>(ws, W.logits);
+    }
+    coli_status st = launch_route(lg, bias, T, E, k, s->topp, at<int32_t>(ws, W.idx),
+                                  at<float>(ws, W.w), stream);
+    if (st) return st;
+    return cache_prefetch_routed(cache, layer, at<int32_t>(ws, W.idx), T * k, started, stream);
+}
+
 }  // namespace coli

@@ -89,3 +89,69 @@ def test_slots_equal_top_k(coli):
     st = cache.stats()
     assert st["evictions"] > 0
     cache.close()
+
+
+@pytest.mark.parametrize("T", [1, 8, 20])
+def test_learned_placement_equals_resident(coli, T):
+    """Pins (from the cache's own usage history), repins and lookahead prefetches
+    change which experts are resident and when they are copied, never the
+    output: every cached call equals the resident call bit for bit. The
+    lookahead is run right before each call with the call's own routing input,
+    so the call finds its experts prefetched with copies possibly in flight."""
+    import torch
+    L, H, I, k, steps = 2, 512, 256, 4, 10
+    E = 32 if T == 1 else 64
+    # room for the largest call (at most 4, 15 and 23 distinct experts for the
+    # three cases with these seeds) next to 4 pinned experts, with evictions
+    slots = {1: 12, 8: 24, 20: 32}[T]
+    shape, sets, cache = _setup(coli, L, H, I, E, k, 0, slots)
+    ws_c = coli.workspace(shape, T)
+    ws_r = coli.workspace(shape, T)
+    started = 0
+    for step in range(steps):
+        if step == 3:
+            cache.pin_hot(4)
+        if step >= 4 and step % 2 == 0:
+            cache.repin(4, 0.25, 0.5)
+        for l in range(L):
+            lg, _ = synth.locality_logits(90 + l, l, steps * T, E, k, keep_p=0.6)
+            lgs = _dev(lg[step * T:(step + 1) * T])
+            x = _dev(synth.activations(90, l, step * T, T, H))
+            if step % 2 == 1:
+                started += coli.lookahead(shape, x, cache, l, logits=lgs, ws=ws_c)
+            yc = coli.layer_fwd(shape, x, shared_blob=sets[l].shared_blob, logits=lgs,
+                                cache=cache, layer=l, ws=ws_c)
+            yr = coli.layer_fwd(shape, x, table=sets[l].table, shared_blob=sets[l].shared_blob,
+                                logits=lgs, ws=ws_r)
+            torch.cuda.synchronize()
+            assert np.array_equal(yc.cpu().numpy(), yr.cpu().numpy()), (step, l)
+    st = cache.stats()
+    assert started > 0 and st["prefetches"] == started and st["prefetch_hits"] > 0
+    assert st["pin_loads"] + st["pin_hits"] > 0
+    assert st["bytes_h2d"] == (st["misses"] + st["pin_loads"] + st["prefetches"]) * \
+        coli.blob_layout(shape)[1]
+    cache.close()
+
+
+def test_lookahead_with_router(coli):
+    """The lookahead's own routing (router weights applied to a state) prefetches
+    exactly what the layer call with the same state and router then names."""
+    import torch
+    L, H, I, E, k, T = 1, 512, 256, 32, 4, 3
+    shape, sets, cache = _setup(coli, L, H, I, E, k, 0, 16)
+    wr = synth.router_weights(95, 0, E, H)
+    b = synth.bias(95, 0, E)
+    x = synth.activations(95, 0, 0, T, H)
+    ws = coli.workspace(shape, T)
+    n = coli.lookahead(shape, _dev(x), cache, 0, router_w=_dev(wr), bias=_dev(b), ws=ws)
+    idx_ref, _ = oracle.route(oracle.router_logits(wr, x), b, k)
+    assert n == len(np.unique(idx_ref))
+    y = coli.layer_fwd(shape, _dev(x), shared_blob=sets[0].shared_blob, router_w=_dev(wr),
+                       bias=_dev(b), cache=cache, layer=0, ws=ws)
+    yr = coli.layer_fwd(shape, _dev(x), table=sets[0].table, shared_blob=sets[0].shared_blob,
+                        router_w=_dev(wr), bias=_dev(b))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), yr.cpu().numpy())
+    st = cache.stats()
+    assert st["misses"] == 0 and st["prefetch_hits"] == n
+    cache.close()
