@@ -59,6 +59,10 @@ def lib():
                                        ctypes.POINTER(Expert), ctypes.POINTER(Expert), vp, vp,
                                        vp, vp]
             L.oracle_num_threads.restype = ctypes.c_int
+            L.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
+            L.oracle_fp8_e4m3_value.restype = ctypes.c_double
+            L.oracle_fp8_block_dequant.argtypes = [vp, vp, i64, i64, vp]
+            L.oracle_convert_fp8_int4.argtypes = [vp, vp, i64, i64, i32, vp, vp]
             _lib = L
     return _lib
 
@@ -95,6 +99,34 @@ def dequantize_int4(q: np.ndarray, s: np.ndarray, cols: int, group: int = 0) -> 
     out = np.empty((q.shape[0], cols), dtype=np.float64)
     lib().oracle_dequantize_int4(_p(q), _p(s), q.shape[0], cols, group, _p(out))
     return out
+
+
+# ------------------------------------------------------------- FP8 converter
+
+def fp8_e4m3_value(b: int) -> float:
+    return float(lib().oracle_fp8_e4m3_value(b))
+
+
+def fp8_block_dequant(w8: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """w8 u8 [rows][cols] (e4m3 codes), scale f32 [ceil(rows/128)][ceil(cols/128)] -> f32."""
+    w8 = _c(w8, np.uint8)
+    scale = _c(scale, np.float32)
+    rows, cols = w8.shape
+    out = np.empty((rows, cols), dtype=np.float32)
+    if lib().oracle_fp8_block_dequant(_p(w8), _p(scale), rows, cols, _p(out)):
+        raise ValueError("oracle_fp8_block_dequant: bad arguments")
+    return out
+
+
+def convert_fp8_int4(w8: np.ndarray, scale: np.ndarray, group: int = 0):
+    w8 = _c(w8, np.uint8)
+    scale = _c(scale, np.float32)
+    rows, cols = w8.shape
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty((rows,) if group == 0 else (rows, cols // group), dtype=np.float32)
+    if lib().oracle_convert_fp8_int4(_p(w8), _p(scale), rows, cols, group, _p(q), _p(s)):
+        raise ValueError("oracle_convert_fp8_int4: bad arguments")
+    return q, s
 
 
 # -------------------------------------------------------------------- router

@@ -84,6 +84,48 @@ void oracle_dequantize_int4(const uint8_t* q, const float* s, int64_t rows, int6
             out[r * cols + c] = (double)nibble(q + r * (cols / 2), c) * scale_of(s, r, c, cols, group);
 }
 
+/* ------------------------------------------------------- FP8 converter
+ * [HF] conversion note: the container was made from the FP8 checkpoint by
+ * FP8 (e4m3, one scale factor per 128 x 128 block) -> f32 -> int4, rounding
+ * with np.rint. The e4m3 layout is the OCP 8-bit float E4M3: 1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes the
+ * subnormals m * 2^-9; there is no infinity, and S.1111.111 is NaN. Reading:
+ * the block of w[r][c] is (r / 128, c / 128) in a row-major scale array of
+ * ceil(rows/128) x ceil(cols/128) floats, and w = e4m3 value times the block's
+ * scale, one f32 rounding of the exact product. */
+double oracle_fp8_e4m3_value(uint8_t b) {
+    const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);                  /* subnormal: m/8 * 2^-6 */
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+int oracle_fp8_block_dequant(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
+                             float* w) {
+    if (rows < 0 || cols < 0) return -1;
+    const int64_t sc_cols = (cols + 127) / 128;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double v = oracle_fp8_e4m3_value(w8[r * cols + c]);
+            double f = (double)scale[(r / 128) * sc_cols + c / 128];
+            w[r * cols + c] = (float)(v * f);      /* exact in double, one rounding */
+        }
+    return 0;
+}
+
+int oracle_convert_fp8_int4(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
+                            int32_t group, uint8_t* q, float* s) {
+    if (rows < 0 || cols < 0) return -1;
+    float* w = (float*)malloc(sizeof(float) * ((size_t)(rows * cols) + 1));
+    if (!w) return -1;
+    int rc = oracle_fp8_block_dequant(w8, scale, rows, cols, w);
+    if (!rc) rc = oracle_quantize_int4(w, rows, cols, group, q, s);
+    free(w);
+    return rc;
+}
+
 /* ---------------------------------------------------------------- router
  * [P5] section 一/二 and [HF]: the router stays F32. Logits accumulate in
  * double and are rounded once. */

@@ -9,7 +9,8 @@
  * Pages cited (titles as published):
  *  [HF]  "jlnsrk/GLM-5.2-colibri-int4" (Hugging Face model card): container
  *        format (U8 packed int4 nibbles + F32 per-row scales) and the
- *        conversion note (np.rint matching the engine's lrintf).
+ *        conversion note (FP8 e4m3 with 128 x 128 block scales -> f32 ->
+ *        int4, np.rint matching the engine's lrintf).
  *  [P4]  "github一周涨11k⭐️！25GB 内存跑 744B GLM-5.2 模型！": section 三
  *        items 1 (sigmoid router, 8 of 256 experts per token) and 4
  *        (batch-union MoE); section 四 item 3 (DeepSeek-V3 aux-loss-free
@@ -69,6 +70,19 @@ int oracle_quantize_int4(const float* w, int64_t rows, int64_t cols, int32_t gro
 /* The float value a stored nibble stands for, in double: q * scale. */
 void oracle_dequantize_int4(const uint8_t* q, const float* s, int64_t rows, int64_t cols,
                             int32_t group, double* out);
+
+/* FP8 -> f32 -> int4 conversion ([HF] conversion note). The value of one
+ * OCP e4m3 byte (NaN for the two NaN codes). */
+double oracle_fp8_e4m3_value(uint8_t b);
+
+/* w [rows][cols] = e4m3(w8[r][c]) * scale[r/128][c/128] rounded once to f32;
+ * scale is row-major [ceil(rows/128)][ceil(cols/128)]. Returns 0 or -1. */
+int oracle_fp8_block_dequant(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
+                             float* w);
+
+/* The converter: oracle_fp8_block_dequant, then oracle_quantize_int4. */
+int oracle_convert_fp8_int4(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
+                            int32_t group, uint8_t* q, float* s);
 
 /* logits[t][e] = (float) sum_j (double) wr[e][j] * (double) x[t][j]. */
 void oracle_router_logits(const float* wr, const float* x, int32_t T, int32_t H, int32_t E,

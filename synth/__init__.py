@@ -113,6 +113,23 @@ def expert_weights(seed, layer, expert, hidden, inter, std=0.02):
     return g, u, d
 
 
+def fp8_block_matrix(seed, layer, expert, mat, rows, cols, std=0.02):
+    """A checkpoint-style FP8 matrix: the f32 expert matrix N(0, std), one
+    scale per 128 x 128 block (block max / 448, the largest e4m3 value), and
+    the e4m3 codes of w / scale (torch's float8_e4m3fn rounding). Returns
+    (codes u8 [rows][cols], scales f32 [ceil(rows/128)][ceil(cols/128)])."""
+    import torch
+    w = expert_matrix(seed, layer, expert, mat, rows, cols, std)
+    br, bc = (rows + 127) // 128, (cols + 127) // 128
+    pad = np.zeros((br * 128, bc * 128), np.float32)
+    pad[:rows, :cols] = np.abs(w)
+    amax = pad.reshape(br, 128, bc, 128).max(axis=(1, 3))
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    full = np.repeat(np.repeat(scale, 128, axis=0), 128, axis=1)[:rows, :cols]
+    codes = torch.from_numpy(w / full).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.ascontiguousarray(codes), scale
+
+
 def activations(seed, layer, t_first, T, hidden, std=1.0) -> np.ndarray:
     """x [T][H] f32 ~ N(0, std); token t uses stream (layer, t_first + t)."""
     x = np.empty((T, hidden), dtype=np.float32)
