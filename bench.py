@@ -60,10 +60,11 @@ def parse():
     ap.add_argument("--repin-every", type=int, default=64)
     ap.add_argument("--repin-decay", type=float, default=0.9)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "mtp", "stream", "copy"],
+                    choices=["decode", "prefill", "mtp", "stream", "copy", "convert"],
                     help="decode (headline, with the prefill line), prefill (that line alone), "
                          "mtp (gs64, 8-token verify batches), stream (16 layers from pinned host through an HBM cache), "
-                         "copy (plain 1 GiB device copy: bandwidth and counter calibration)")
+                         "copy (plain 1 GiB device copy: bandwidth and counter calibration), "
+                         "convert (FP8 -> int4 conversion of 32 experts)")
     return ap.parse_args()
 
 
@@ -427,6 +428,78 @@ def run_stream(args, coli, dev):
     }
 
 
+def run_convert(args, coli, dev):
+    """FP8 -> int4 conversion of GLM-5.2-shaped experts (hidden 6144, inter
+    2048): e4m3 codes with one scale per 128 x 128 block, as in the FP8
+    checkpoint, into per-row int4 blobs. 32 expert inputs resident in HBM (4
+    distinct generated ones, copied), converted K times."""
+    import torch
+    import synth
+    H, I, n_exp = 6144, 2048, 32
+    shape = coli.MoEShape(H, I, 256, 1, 8, 0)
+    blob_bytes = coli.blob_layout(shape)[1]
+    base = []
+    for e in range(4):
+        mats = [synth.fp8_block_matrix(args.seed, 0, e, m, r, c)
+                for m, (r, c) in ((synth.MAT_GATE, (I, H)), (synth.MAT_UP, (I, H)),
+                                  (synth.MAT_DOWN, (H, I)))]
+        base.append([torch.from_numpy(a).to(dev) for pair in mats for a in pair])
+    inputs = [[t.clone() for t in base[e % 4]] for e in range(n_exp)]
+    blobs = torch.empty((n_exp, blob_bytes), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def step():
+        for e in range(n_exp):
+            coli.convert_fp8_expert(shape, *inputs[e], blob=blobs[e], stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step()
+    torch.cuda.synchronize()
+    k = max(1, min(args.steps, 50))
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for _ in range(k):
+            step()
+        t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / k
+    in_bytes = sum(t.numel() * t.element_size() for t in inputs[0])
+    per_expert = in_bytes + blob_bytes
+    gbps = per_expert * n_exp / (ms / 1e3) / 1e9
+    # the f32 quantiser on the same experts' f32 weights (8 resident experts)
+    del inputs
+    f32 = [[torch.from_numpy(a).to(dev) for a in synth.expert_weights(args.seed, 0, e, H, I)]
+           for e in range(8)]
+    with torch.cuda.stream(stream):
+        for e in range(8):
+            coli.quantize_expert(shape, *f32[e], blob=blobs[e], stream=stream)
+        t0.record(stream)
+        for _ in range(k):
+            for e in range(8):
+                coli.quantize_expert(shape, *f32[e], blob=blobs[e], stream=stream)
+        t1.record(stream)
+    torch.cuda.synchronize()
+    ms_q = t0.elapsed_time(t1) / k / 8
+    q_bytes = sum(t.numel() * 4 for t in f32[0]) + blob_bytes
+    return {
+        "metric": "FP8 -> int4 expert conversion (GB/s of FP8 read + int4 written)",
+        "value": round(n_exp / (ms / 1e3), 1), "unit": "experts/s", "n_gpus": 1, "steps": k,
+        "warmup": max(1, args.warmup), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3 -> f32 -> int4 (per-row scales)",
+        "data": "synthetic checkpoint-style FP8 (N(0, 0.02) weights, block max / 448 scales)",
+        "config": {"workload": f"FP8 -> int4 conversion of {n_exp} GLM-5.2-shaped experts per step",
+                   "hidden": H, "inter": I, "experts_per_step": n_exp},
+        "roofline": {"bound": "hbm", "kernel": "fp8_wave_kernel (3 launches per expert)",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_expert": per_expert},
+        "quantize_f32": {"experts_per_s": round(1e3 / ms_q, 1), "us_per_expert": round(ms_q * 1e3, 2),
+                         "GBps": round(q_bytes / (ms_q / 1e3) / 1e9, 1), "bytes_per_expert": q_bytes},
+    }
+
+
 def run_copy(args, dev):
     """A plain device-to-device copy of 1 GiB, 20 times: the achievable
     read+write bandwidth, and the reference for scaling HBM byte counters."""
@@ -492,6 +565,8 @@ def main():
                     "unit": "TFLOP/s", "n_gpus": 1, **line}
         elif args.workload == "mtp":
             line = run_mtp(args, coli, dev)
+        elif args.workload == "convert":
+            line = run_convert(args, coli, dev)
         else:
             line = run_stream(args, coli, dev)
         print(json.dumps(line), flush=True)

@@ -105,6 +105,26 @@ COLI_API coli_status coli_quantize_expert(const coli_moe_shape* shape, const flo
                                  const float* d_up, const float* d_down, void* d_blob,
                                  void* stream);
 
+/* FP8 -> f32 -> int4 converter (model card "jlnsrk/GLM-5.2-colibri-int4",
+ * conversion note: the container was made from the FP8 checkpoint, e4m3 with
+ * one scale per 128 x 128 block, via f32, rounding as np.rint). d_w8
+ * [rows][cols] holds OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, subnormals at exponent 0, no infinity; the NaN codes 0x7F and
+ * 0xFF must not occur); d_scale is f32 [ceil(rows/128)][ceil(cols/128)]
+ * row-major. Each weight is w = e4m3 value * scale of its block, one f32
+ * rounding, then quantised exactly as coli_quantize_int4 does (bit-identical
+ * to the CPU reference). Same size rules and outputs as coli_quantize_int4. */
+COLI_API coli_status coli_convert_fp8_int4(const uint8_t* d_w8, const float* d_scale, int64_t rows,
+                                  int64_t cols, int32_t group, uint8_t* d_q, float* d_s,
+                                  void* stream);
+
+/* One expert from its three FP8 matrices (gate/up [I][H], down [H][I], each
+ * with its block scales) into the blob d_blob, like coli_quantize_expert. */
+COLI_API coli_status coli_convert_fp8_expert(const coli_moe_shape* shape, const uint8_t* d_gate8,
+                                    const float* d_gate_scale, const uint8_t* d_up8,
+                                    const float* d_up_scale, const uint8_t* d_down8,
+                                    const float* d_down_scale, void* d_blob, void* stream);
+
 /* Router logits d_logits [T][E] = d_x [T][H] . d_wr [E][H]^T: f32 inputs,
  * products and sum in double, one rounding to f32 (the router stays F32 in
  * the container, model card file table). */

@@ -21,7 +21,8 @@ PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 
 EXPORTED = [
     "coli_last_error", "coli_version", "coli_expert_blob_layout", "coli_quantize_int4",
-    "coli_quantize_expert", "coli_moe_router_logits", "coli_moe_route", "coli_moe_route_topp",
+    "coli_quantize_expert", "coli_convert_fp8_int4", "coli_convert_fp8_expert",
+    "coli_moe_router_logits", "coli_moe_route", "coli_moe_route_topp",
     "coli_moe_union_workspace_size", "coli_moe_union", "coli_moe_workspace_size",
     "coli_moe_expert_ffn", "coli_moe_layer_fwd", "coli_expert_cache_create",
     "coli_expert_cache_destroy", "coli_expert_cache_ensure", "coli_expert_cache_wait",
@@ -83,6 +84,8 @@ def lib():
             L.coli_expert_blob_layout.argtypes = [P(Shape), P(sz), P(sz)]
             L.coli_quantize_int4.argtypes = [vp, i64, i64, i32, vp, vp, vp]
             L.coli_quantize_expert.argtypes = [P(Shape), vp, vp, vp, vp, vp]
+            L.coli_convert_fp8_int4.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
+            L.coli_convert_fp8_expert.argtypes = [P(Shape), vp, vp, vp, vp, vp, vp, vp, vp]
             L.coli_moe_router_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
             L.coli_moe_route.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
             L.coli_moe_route_topp.argtypes = [vp, vp, i32, i32, i32, f32, vp, vp, vp]
@@ -196,6 +199,44 @@ def quantize_expert(shape: MoEShape, gate, up, down, blob=None, stream=None):
         blob = torch.empty(blob_layout(shape)[1], dtype=torch.uint8, device=gate.device)
     _check(lib().coli_quantize_expert(ctypes.byref(shape.c()), _ptr(gate), _ptr(up), _ptr(down),
                                       _ptr(blob), _stream(stream)))
+    return blob
+
+
+def convert_fp8_int4(w8, scale, group=0, q=None, s=None, stream=None):
+    """FP8 e4m3 codes (uint8 [rows][cols]) with block scales (f32
+    [ceil(rows/128)][ceil(cols/128)]) -> (q uint8 [rows][cols/2], s f32)."""
+    import torch
+    _need(w8, torch.uint8, "w8")
+    _need(scale, torch.float32, "scale")
+    rows, cols = w8.shape
+    if scale.numel() != ((rows + 127) // 128) * ((cols + 127) // 128):
+        raise ValueError("scale must hold one value per 128 x 128 block")
+    if q is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w8.device)
+    if s is None:
+        shp = (rows,) if group == 0 else (rows, cols // group)
+        s = torch.empty(shp, dtype=torch.float32, device=w8.device)
+    _check(lib().coli_convert_fp8_int4(_ptr(w8), _ptr(scale), rows, cols, group, _ptr(q), _ptr(s),
+                                       _stream(stream)))
+    return q, s
+
+
+def convert_fp8_expert(shape: MoEShape, gate8, gate_scale, up8, up_scale, down8, down_scale,
+                       blob=None, stream=None):
+    import torch
+    for t, n in ((gate8, "gate8"), (up8, "up8"), (down8, "down8")):
+        _need(t, torch.uint8, n)
+    for t, n in ((gate_scale, "gate_scale"), (up_scale, "up_scale"), (down_scale, "down_scale")):
+        _need(t, torch.float32, n)
+    H, I = shape.hidden, shape.inter
+    for t, sc, r, c in ((gate8, gate_scale, I, H), (up8, up_scale, I, H), (down8, down_scale, H, I)):
+        if tuple(t.shape) != (r, c) or sc.numel() != ((r + 127) // 128) * ((c + 127) // 128):
+            raise ValueError("FP8 matrix or scale shape does not match the layer shape")
+    if blob is None:
+        blob = torch.empty(blob_layout(shape)[1], dtype=torch.uint8, device=gate8.device)
+    _check(lib().coli_convert_fp8_expert(ctypes.byref(shape.c()), _ptr(gate8), _ptr(gate_scale),
+                                         _ptr(up8), _ptr(up_scale), _ptr(down8), _ptr(down_scale),
+                                         _ptr(blob), _stream(stream)))
     return blob
 
 

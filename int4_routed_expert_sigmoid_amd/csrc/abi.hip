@@ -144,6 +144,42 @@ coli_status coli_quantize_expert(const coli_moe_shape* shape, const float* d_gat
     COLI_GUARD_END
 }
 
+coli_status coli_convert_fp8_int4(const uint8_t* d_w8, const float* d_scale, int64_t rows,
+                                  int64_t cols, int32_t group, uint8_t* d_q, float* d_s,
+                                  void* stream) {
+    COLI_GUARD_BEGIN
+    if (rows < 0 || cols <= 0 || (cols & 1)) return fail(COLI_EINVAL, "convert_fp8: rows >= 0, cols even and > 0");
+    if (group != 0 && group != 64) return fail(COLI_EUNSUPPORTED, "convert_fp8: group must be 0 or 64");
+    if (group == 64 && cols % 64) return fail(COLI_EINVAL, "convert_fp8: group 64 needs cols % 64 == 0");
+    if (rows > 0 && (!d_w8 || !d_scale || !d_q || !d_s)) return fail(COLI_EINVAL, "convert_fp8: NULL pointer");
+    return launch_convert_fp8(d_w8, d_scale, rows, cols, group, d_q, d_s, (hipStream_t)stream);
+    COLI_GUARD_END
+}
+
+coli_status coli_convert_fp8_expert(const coli_moe_shape* shape, const uint8_t* d_gate8,
+                                    const float* d_gate_scale, const uint8_t* d_up8,
+                                    const float* d_up_scale, const uint8_t* d_down8,
+                                    const float* d_down_scale, void* d_blob, void* stream) {
+    COLI_GUARD_BEGIN
+    coli_status st = check_shape(shape);
+    if (st) return st;
+    if (!d_gate8 || !d_gate_scale || !d_up8 || !d_up_scale || !d_down8 || !d_down_scale || !d_blob)
+        return fail(COLI_EINVAL, "convert_fp8_expert: NULL pointer");
+    const int64_t H = shape->hidden, I = shape->inter;
+    const BlobLayout L = blob_layout(H, I, shape->group);
+    uint8_t* b = (uint8_t*)d_blob;
+    hipStream_t s = (hipStream_t)stream;
+    st = launch_convert_fp8(d_gate8, d_gate_scale, I, H, shape->group, b + L.gate_q,
+                            (float*)(b + L.gate_s), s);
+    if (st) return st;
+    st = launch_convert_fp8(d_up8, d_up_scale, I, H, shape->group, b + L.up_q,
+                            (float*)(b + L.up_s), s);
+    if (st) return st;
+    return launch_convert_fp8(d_down8, d_down_scale, H, I, shape->group, b + L.down_q,
+                              (float*)(b + L.down_s), s);
+    COLI_GUARD_END
+}
+
 coli_status coli_moe_router_logits(const float* d_wr, const float* d_x, int32_t T, int32_t H,
                                    int32_t E, float* d_logits, void* stream) {
     COLI_GUARD_BEGIN

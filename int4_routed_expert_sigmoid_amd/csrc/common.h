@@ -239,6 +239,10 @@ __device__ __forceinline__ constexpr int transpose_shift() {
 // (host functions implemented in the .hip files; all enqueue on `stream`)
 coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t group,
                             uint8_t* q, float* s, hipStream_t stream);
+// FP8 e4m3 codes w8 [rows][cols] with scales [ceil(rows/128)][ceil(cols/128)]
+// -> f32 -> int4, through the same quantiser kernels.
+coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
+                               int32_t group, uint8_t* q, float* s, hipStream_t stream);
 coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int32_t H,
                                  int32_t E, float* logits, hipStream_t stream);
 // Router for small batches (T <= kSmallT): logits (when router_w is given)
