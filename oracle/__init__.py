@@ -35,7 +35,7 @@ def build(force: bool = True) -> str:
 class Expert(ctypes.Structure):
     _fields_ = [("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p),
                 ("down_q", ctypes.c_void_p), ("gate_s", ctypes.c_void_p),
-                ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+                ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p), ("bits", ctypes.c_int32)]
 
 
 def lib():
@@ -48,6 +48,8 @@ def lib():
             vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
             L.oracle_quantize_int4.argtypes = [vp, i64, i64, i32, vp, vp]
             L.oracle_dequantize_int4.argtypes = [vp, vp, i64, i64, i32, vp]
+            L.oracle_quantize_int8.argtypes = [vp, i64, i64, i32, vp, vp]
+            L.oracle_dequantize_int8.argtypes = [vp, vp, i64, i64, i32, vp]
             L.oracle_router_logits.argtypes = [vp, vp, i32, i32, i32, vp]
             L.oracle_route.argtypes = [vp, vp, i32, i32, i32, vp, vp]
             L.oracle_route_topp.argtypes = [vp, vp, i32, i32, i32, f32, vp, vp]
@@ -91,6 +93,25 @@ def quantize_int4(w: np.ndarray, group: int = 0):
     if rc:
         raise ValueError("oracle_quantize_int4: bad arguments")
     return q, s
+
+
+def quantize_int8(w: np.ndarray, group: int = 0):
+    """w f32 [rows][cols] -> (q int8 [rows][cols], s f32 [rows] or [rows][cols/64])."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), dtype=np.int8)
+    s = np.empty((rows,) if group == 0 else (rows, cols // group), dtype=np.float32)
+    if lib().oracle_quantize_int8(_p(w), rows, cols, group, _p(q), _p(s)):
+        raise ValueError("oracle_quantize_int8: bad arguments")
+    return q, s
+
+
+def dequantize_int8(q: np.ndarray, s: np.ndarray, group: int = 0) -> np.ndarray:
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    out = np.empty(q.shape, dtype=np.float64)
+    lib().oracle_dequantize_int8(_p(q), _p(s), q.shape[0], q.shape[1], group, _p(out))
+    return out
 
 
 def dequantize_int4(q: np.ndarray, s: np.ndarray, cols: int, group: int = 0) -> np.ndarray:
@@ -174,19 +195,23 @@ def union(idx: np.ndarray, E: int):
 # ------------------------------------------------------------------- experts
 
 class QExpert:
-    """Host copy of one quantised expert: keeps the arrays alive for the C struct."""
+    """Host copy of one quantised expert: keeps the arrays alive for the C struct.
+    bits 4: packed nibbles; bits 8: signed bytes."""
 
-    def __init__(self, gate_q, up_q, down_q, gate_s, up_s, down_s):
-        self.parts = [_c(gate_q, np.uint8), _c(up_q, np.uint8), _c(down_q, np.uint8),
+    def __init__(self, gate_q, up_q, down_q, gate_s, up_s, down_s, bits=4):
+        qt = np.int8 if bits == 8 else np.uint8
+        self.bits = bits
+        self.parts = [_c(gate_q, qt), _c(up_q, qt), _c(down_q, qt),
                       _c(gate_s, np.float32), _c(up_s, np.float32), _c(down_s, np.float32)]
-        self.struct = Expert(*[a.ctypes.data for a in self.parts])
+        self.struct = Expert(*[a.ctypes.data for a in self.parts], bits)
 
     @classmethod
-    def quantize(cls, gate, up, down, group=0):
-        gq, gs = quantize_int4(gate, group)
-        uq, us = quantize_int4(up, group)
-        dq, ds = quantize_int4(down, group)
-        return cls(gq, uq, dq, gs, us, ds)
+    def quantize(cls, gate, up, down, group=0, bits=4):
+        qf = quantize_int8 if bits == 8 else quantize_int4
+        gq, gs = qf(gate, group)
+        uq, us = qf(up, group)
+        dq, ds = qf(down, group)
+        return cls(gq, uq, dq, gs, us, ds, bits)
 
 
 def expert_ffn(ex: QExpert, x: np.ndarray, H: int, I: int, group: int = 0) -> np.ndarray:

@@ -72,6 +72,49 @@ static int nibble(const uint8_t* row, int64_t c) {
     return v >= 8 ? v - 16 : v;
 }
 
+/* ------------------------------------------------------- int8 codec
+ * [P5] section 二 and the int8-MTP page: the MTP head must be int8 (an int4
+ * head's draft acceptance collapses); the converter's options include 8-bit
+ * tensors. The pages give no int8 formula; the reading mirrors the int4 rule
+ * with 127 in place of 7: scale = max|w| / 127 per row or 64-group (float
+ * division), q = rint(w / scale) half-to-even, clamped to [-128, 127], scale 0
+ * gives q = 0; q is stored one signed byte per weight, row-major. */
+static int8_t quant_one8(float w, float scale) {
+    if (scale == 0.0f) return 0;
+    float v = rintf(w / scale);
+    if (v > 127.0f) v = 127.0f;
+    if (v < -128.0f) v = -128.0f;
+    return (int8_t)v;
+}
+
+int oracle_quantize_int8(const float* w, int64_t rows, int64_t cols, int32_t group, int8_t* q,
+                         float* s) {
+    if (rows < 0 || cols <= 0) return -1;
+    if (group != 0 && group != 64) return -1;
+    if (group == 64 && cols % 64) return -1;
+    if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+    int64_t span = group ? group : cols;
+    int64_t per_row = cols / span;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < per_row; ++g) {
+            float m = 0.0f;
+            for (int64_t c = g * span; c < (g + 1) * span; ++c)
+                if (fabsf(w[r * cols + c]) > m) m = fabsf(w[r * cols + c]);
+            float scale = m / 127.0f;
+            s[r * per_row + g] = scale;
+            for (int64_t c = g * span; c < (g + 1) * span; ++c)
+                q[r * cols + c] = quant_one8(w[r * cols + c], scale);
+        }
+    return 0;
+}
+
+/* Stored integer of weight (r, c) of a matrix with `cols` columns: a nibble
+ * (bits 4) or a signed byte (bits 8). */
+static int qval(const uint8_t* q, int64_t r, int64_t c, int64_t cols, int bits) {
+    if (bits == 8) return (int)(int8_t)q[r * cols + c];
+    return nibble(q + r * (cols / 2), c);
+}
+
 static double scale_of(const float* s, int64_t r, int64_t c, int64_t cols, int32_t group) {
     if (group == 0) return (double)s[r];
     return (double)s[r * (cols / group) + c / group];
@@ -82,6 +125,13 @@ void oracle_dequantize_int4(const uint8_t* q, const float* s, int64_t rows, int6
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c)
             out[r * cols + c] = (double)nibble(q + r * (cols / 2), c) * scale_of(s, r, c, cols, group);
+}
+
+void oracle_dequantize_int8(const int8_t* q, const float* s, int64_t rows, int64_t cols,
+                            int32_t group, double* out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = (double)q[r * cols + c] * scale_of(s, r, c, cols, group);
 }
 
 /* ------------------------------------------------------- FP8 converter
@@ -253,23 +303,21 @@ int oracle_union(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* c
 void oracle_expert_ffn(const oracle_expert* ex, int32_t H, int32_t I, int32_t group,
                        const float* x, double* y) {
     double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    const int bits = ex->bits == 8 ? 8 : 4;
 #pragma omp parallel for schedule(static)
     for (int32_t r = 0; r < I; ++r) {
-        const uint8_t* gr = ex->gate_q + (int64_t)r * (H / 2);
-        const uint8_t* ur = ex->up_q + (int64_t)r * (H / 2);
         double g = 0.0, u = 0.0;
         for (int32_t c = 0; c < H; ++c) {
-            g += (double)nibble(gr, c) * scale_of(ex->gate_s, r, c, H, group) * (double)x[c];
-            u += (double)nibble(ur, c) * scale_of(ex->up_s, r, c, H, group) * (double)x[c];
+            g += (double)qval(ex->gate_q, r, c, H, bits) * scale_of(ex->gate_s, r, c, H, group) * (double)x[c];
+            u += (double)qval(ex->up_q, r, c, H, bits) * scale_of(ex->up_s, r, c, H, group) * (double)x[c];
         }
         h[r] = g / (1.0 + exp(-g)) * u;
     }
 #pragma omp parallel for schedule(static)
     for (int32_t c = 0; c < H; ++c) {
-        const uint8_t* dr = ex->down_q + (int64_t)c * (I / 2);
         double acc = 0.0;
         for (int32_t r = 0; r < I; ++r)
-            acc += (double)nibble(dr, r) * scale_of(ex->down_s, c, r, I, group) * h[r];
+            acc += (double)qval(ex->down_q, c, r, I, bits) * scale_of(ex->down_s, c, r, I, group) * h[r];
         y[c] = acc;
     }
     free(h);

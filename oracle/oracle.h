@@ -50,8 +50,9 @@ extern "C" {
 #endif
 
 /* Pointers to the six parts of one quantised expert (host memory). gate and up
- * are [inter][hidden/2] bytes, down is [hidden][inter/2]; the scales are one
- * float per row (group 0) or per 64 consecutive inputs of a row (group 64). */
+ * are [inter][hidden/2] bytes, down is [hidden][inter/2] (int4), or [inter][hidden]
+ * and [hidden][inter] signed bytes (int8); the scales are one float per row
+ * (group 0) or per 64 consecutive inputs of a row (group 64). */
 typedef struct oracle_expert {
     const uint8_t* gate_q;
     const uint8_t* up_q;
@@ -59,6 +60,7 @@ typedef struct oracle_expert {
     const float* gate_s;
     const float* up_s;
     const float* down_s;
+    int32_t bits;          /* 4: packed nibbles (0 means 4 as well); 8: one signed byte per weight */
 } oracle_expert;
 
 /* Quantise w [rows][cols] to packed nibbles q [rows][cols/2] and scales s.
@@ -66,6 +68,14 @@ typedef struct oracle_expert {
  * Returns 0, or -1 for bad arguments (cols odd, cols % 64 != 0 with group 64). */
 int oracle_quantize_int4(const float* w, int64_t rows, int64_t cols, int32_t group,
                          uint8_t* q, float* s);
+
+/* int8 codec (the MTP head must be int8): scale = max|w| / 127 per row or
+ * 64-group, q = rint(w / scale) half-even, clamped to [-128, 127]; q
+ * [rows][cols] signed bytes. Returns 0 or -1. */
+int oracle_quantize_int8(const float* w, int64_t rows, int64_t cols, int32_t group, int8_t* q,
+                         float* s);
+void oracle_dequantize_int8(const int8_t* q, const float* s, int64_t rows, int64_t cols,
+                            int32_t group, double* out);
 
 /* The float value a stored nibble stands for, in double: q * scale. */
 void oracle_dequantize_int4(const uint8_t* q, const float* s, int64_t rows, int64_t cols,

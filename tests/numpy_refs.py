@@ -41,6 +41,28 @@ def quantize_numpy(w: np.ndarray, group: int = 0):
     return packed, s, v
 
 
+def quantize8_numpy(w: np.ndarray, group: int = 0):
+    """int8: scale = max|w| / 127 in float32, numpy rint of the float32 quotient, clamp."""
+    w = np.asarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    span = cols if group == 0 else group
+    wg = w.reshape(rows, cols // span, span)
+    scale = (np.abs(wg).max(axis=2) / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.rint(wg / scale[:, :, None])
+    v = np.where(scale[:, :, None] == 0, 0, v)
+    q = np.clip(v, -128, 127).astype(np.int8).reshape(rows, cols)
+    return q, (scale.reshape(rows) if group == 0 else scale)
+
+
+def dequant8(q: np.ndarray, s: np.ndarray, group: int = 0) -> np.ndarray:
+    v = np.asarray(q, dtype=np.int8).astype(np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    if group == 0:
+        return v * s.reshape(-1, 1)
+    return v * np.repeat(s.reshape(v.shape[0], -1), group, axis=1)
+
+
 def dequant(q: np.ndarray, s: np.ndarray, cols: int, group: int = 0) -> np.ndarray:
     v = unpack_nibbles(q, cols).astype(np.float64)
     s = np.asarray(s, dtype=np.float64)
