@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle sample for about this long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wbits", type=int, default=4, choices=[4, 8],
+                    help="decode with int8 experts (8) instead of int4 (4, the headline)")
     ap.add_argument("--topp", type=float, default=0.0,
                     help="decode with the adaptive expert top-p (lossy; 0 = fixed top-8, the headline)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
@@ -108,13 +110,14 @@ def cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept, seconds):
     over about `seconds` of work."""
     import oracle
     H, I, E, k = shape.hidden, shape.inter, shape.n_routed, shape.top_k
+    bits = shape.wbits
     z = np.zeros((I, H), np.float32)
-    zero = oracle.QExpert.quantize(z, z, np.zeros((H, I), np.float32), 0)
+    zero = oracle.QExpert.quantize(z, z, np.zeros((H, I), np.float32), 0, bits=bits)
     experts = [zero] * E
     for e, (g, u, d) in kept.items():
         if e < E:
-            experts[e] = oracle.QExpert.quantize(g, u, d, 0)
-    shared = oracle.QExpert.quantize(*kept[E], 0)
+            experts[e] = oracle.QExpert.quantize(g, u, d, 0, bits=bits)
+    shared = oracle.QExpert.quantize(*kept[E], 0, bits=bits)
     x = np.ascontiguousarray(x_all[:sample])
     # the same tokens again until about `seconds` of CPU work (their ~50 experts,
     # about 1 GB of weights, do not stay in the CPU caches between passes)
@@ -572,7 +575,7 @@ def main():
         print(json.dumps(line), flush=True)
         return
     H, I, E, k = 6144, 2048, 256, 8
-    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0, args.topp)
+    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0, args.topp, args.wbits)
     seed = args.seed
     n_tok = args.warmup + args.steps
     log(f"decode workload: {n_tok} tokens, H={H} I={I} E={E}+1 k={k} topp={args.topp}")
@@ -643,8 +646,9 @@ def main():
     # with top-p: their mean over the timed tokens) and the shared one
     routed = (idx_d[args.warmup:] >= 0).sum(dim=1).double().mean().item()
     n_exp = routed + 1.0
-    gu_bytes = n_exp * (2 * I * (H // 2) + 2 * I * 4)
-    dn_bytes = n_exp * (H * (I // 2) + H * 4)
+    wb = args.wbits // 4                      # bytes per two weights
+    gu_bytes = n_exp * (2 * I * (H * wb // 2) + 2 * I * 4)
+    dn_bytes = n_exp * (H * (I * wb // 2) + H * 4)
     gu_avg_s = ms_gu / max(1, n_gu) / 1e3
     dn_avg_s = ms_dn / max(1, n_dn) / 1e3
     gu_gbps = gu_bytes / gu_avg_s / 1e9 if n_gu else None
@@ -653,7 +657,7 @@ def main():
     tok_s = args.steps / elapsed
 
     prefill = None
-    if not args.no_prefill:
+    if not args.no_prefill and args.wbits == 4:           # the MFMA path is int4 only
         log("prefill: 2048 tokens through the same layer (bf16 MFMA)")
         prefill = run_prefill(coli, shape, table, shared, seed, dev)
 
@@ -672,12 +676,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x f32 activations (exact int32 nibble products), f32 accumulate",
+        "dtype": f"int{args.wbits} weights x f32 activations (exact int32 nibble products), f32 accumulate",
         "data": "synthetic (seeded Philox N(0,0.02) weights, N(0,1) activations, f32 router)",
         "config": {"workload": "GLM-5.2-shaped MoE layer, batch-1 decode"
-                               + (f", adaptive expert top-p {args.topp}" if args.topp else ""),
+                               + (f", adaptive expert top-p {args.topp}" if args.topp else "")
+                               + (", int8 experts" if args.wbits == 8 else ""),
                    "hidden": H,
                    "inter": I, "n_routed": E, "n_shared": 1, "top_k": k, "group": 0,
+                   "wbits": args.wbits,
                    "tokens": args.steps, "graph": bool(args.graph), "topp": args.topp,
                    "routed_experts_per_token": round(routed, 4),
                    "eager_tokens_per_s": round(args.steps / elapsed_eager, 2)},
@@ -686,7 +692,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4) if gu_gbps else None,
                      "traffic": (measured_traffic("gemv_gateup_decode_traffic.json")
-                                 if args.topp == 0.0 else None),
+                                 if args.topp == 0.0 and args.wbits == 4 else None),
                      "bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_avg_s * 1e6, 3),
                      "launches_timed": n_gu},
         "expert_gemv": {"gateup_GBps": gu_gbps and round(gu_gbps, 1),

@@ -34,6 +34,15 @@
  * on a 256-byte boundary (coli_expert_blob_layout gives the offsets). A miss
  * of the expert cache is therefore one copy.
  *
+ * int8 experts (shape->wbits 8; the MTP head must be int8 per the int8-MTP
+ * page and the practical guide's section 二, and the pages give no int8
+ * formula): scale = max|w|/127 per row or 64-group, q = rint(w/scale)
+ * half-to-even clamped to [-128, 127]. The blob has the same parts with rows of
+ * H (or I) bytes: for every 32-element block, 16 bytes holding the high
+ * nibbles h = q >> 4, then 16 bytes holding l = (q & 15) - 8, both as signed
+ * nibbles in the int4 packing order, so that q = 16 h + l + 8. int8 layers run
+ * on the GEMV family only (COLI_PATH_MFMA returns COLI_EUNSUPPORTED).
+ *
  * Conventions for every call:
  *  - d_* pointers are device memory, h_* pointers host memory. The caller owns
  *    all of them; the library keeps none after a call returns (the expert
@@ -76,7 +85,8 @@ COLI_API const char* coli_version(void);
 
 /* Layer shape. Supported: hidden <= 16384 and inter <= 4096, positive multiples of 32 (and of
  * 64 when group == 64); 1 <= n_routed <= 1024; n_shared 0 or 1;
- * 1 <= top_k <= min(32, n_routed); group 0 or 64; routed_scale finite; topp in [0, 1]. */
+ * 1 <= top_k <= min(32, n_routed); group 0 or 64; routed_scale finite; topp in [0, 1];
+ * wbits 0, 4 or 8. */
 typedef struct coli_moe_shape {
     int32_t hidden;       /* H: model width, input and output of the layer */
     int32_t inter;        /* I: intermediate width of one expert */
@@ -87,6 +97,7 @@ typedef struct coli_moe_shape {
     float routed_scale;   /* multiplies the routed sum at the combine (1.0 = none) */
     float topp;           /* adaptive expert top-p, as coli_moe_route_topp: 0 (or 1) keeps
                              all top_k; in (0, 1) a token may use fewer experts (lossy) */
+    int32_t wbits;        /* expert weight codec: 4 (or 0) int4, 8 int8 (GEMV path only) */
 } coli_moe_shape;
 
 /* Offsets (bytes) of gate_q, up_q, down_q, gate_s, up_s, down_s inside one

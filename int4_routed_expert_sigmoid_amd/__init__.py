@@ -43,7 +43,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float), ("topp", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("topp", ctypes.c_float),
+                ("wbits", ctypes.c_int32)]
 
 
 class CacheCfg(ctypes.Structure):
@@ -160,10 +161,11 @@ class MoEShape:
     group: int = 0
     routed_scale: float = 1.0
     topp: float = 0.0
+    wbits: int = 4
 
     def c(self) -> Shape:
         return Shape(self.hidden, self.inter, self.n_routed, self.n_shared, self.top_k, self.group,
-                     self.routed_scale, self.topp)
+                     self.routed_scale, self.topp, self.wbits)
 
 
 def version() -> str:

@@ -41,6 +41,7 @@ coli_status check_shape(const coli_moe_shape* s) {
     if (!(s->routed_scale == s->routed_scale) || s->routed_scale > 3.4e38f || s->routed_scale < -3.4e38f)
         return fail(COLI_EINVAL, "routed_scale must be finite");
     if (!(s->topp >= 0.f && s->topp <= 1.f)) return fail(COLI_EINVAL, "topp must be in [0, 1]");
+    if (s->wbits != 0 && s->wbits != 4 && s->wbits != 8) return fail(COLI_EUNSUPPORTED, "wbits must be 4 or 8");
     return COLI_OK;
 }
 
@@ -107,7 +108,7 @@ coli_status coli_expert_blob_layout(const coli_moe_shape* shape, size_t off[6], 
     coli_status st = check_shape(shape);
     if (st) return st;
     if (!off || !blob_bytes) return fail(COLI_EINVAL, "off or blob_bytes is NULL");
-    const BlobLayout L = blob_layout(shape->hidden, shape->inter, shape->group);
+    const BlobLayout L = blob_layout(shape->hidden, shape->inter, shape->group, shape->wbits);
     off[0] = L.gate_q; off[1] = L.up_q; off[2] = L.down_q;
     off[3] = L.gate_s; off[4] = L.up_s; off[5] = L.down_s;
     *blob_bytes = L.bytes;
@@ -133,14 +134,15 @@ coli_status coli_quantize_expert(const coli_moe_shape* shape, const float* d_gat
     if (st) return st;
     if (!d_gate || !d_up || !d_down || !d_blob) return fail(COLI_EINVAL, "quantize_expert: NULL pointer");
     const int64_t H = shape->hidden, I = shape->inter;
-    const BlobLayout L = blob_layout(H, I, shape->group);
+    const int32_t wb = shape->wbits == 8 ? 8 : 4;
+    const BlobLayout L = blob_layout(H, I, shape->group, wb);
     uint8_t* b = (uint8_t*)d_blob;
     hipStream_t s = (hipStream_t)stream;
-    st = launch_quantize(d_gate, I, H, shape->group, b + L.gate_q, (float*)(b + L.gate_s), s);
+    st = launch_quantize(d_gate, I, H, shape->group, b + L.gate_q, (float*)(b + L.gate_s), s, wb);
     if (st) return st;
-    st = launch_quantize(d_up, I, H, shape->group, b + L.up_q, (float*)(b + L.up_s), s);
+    st = launch_quantize(d_up, I, H, shape->group, b + L.up_q, (float*)(b + L.up_s), s, wb);
     if (st) return st;
-    return launch_quantize(d_down, H, I, shape->group, b + L.down_q, (float*)(b + L.down_s), s);
+    return launch_quantize(d_down, H, I, shape->group, b + L.down_q, (float*)(b + L.down_s), s, wb);
     COLI_GUARD_END
 }
 
@@ -166,17 +168,18 @@ coli_status coli_convert_fp8_expert(const coli_moe_shape* shape, const uint8_t* 
     if (!d_gate8 || !d_gate_scale || !d_up8 || !d_up_scale || !d_down8 || !d_down_scale || !d_blob)
         return fail(COLI_EINVAL, "convert_fp8_expert: NULL pointer");
     const int64_t H = shape->hidden, I = shape->inter;
-    const BlobLayout L = blob_layout(H, I, shape->group);
+    const int32_t wb = shape->wbits == 8 ? 8 : 4;
+    const BlobLayout L = blob_layout(H, I, shape->group, wb);
     uint8_t* b = (uint8_t*)d_blob;
     hipStream_t s = (hipStream_t)stream;
     st = launch_convert_fp8(d_gate8, d_gate_scale, I, H, shape->group, b + L.gate_q,
-                            (float*)(b + L.gate_s), s);
+                            (float*)(b + L.gate_s), s, wb);
     if (st) return st;
     st = launch_convert_fp8(d_up8, d_up_scale, I, H, shape->group, b + L.up_q,
-                            (float*)(b + L.up_s), s);
+                            (float*)(b + L.up_s), s, wb);
     if (st) return st;
     return launch_convert_fp8(d_down8, d_down_scale, H, I, shape->group, b + L.down_q,
-                              (float*)(b + L.down_s), s);
+                              (float*)(b + L.down_s), s, wb);
     COLI_GUARD_END
 }
 

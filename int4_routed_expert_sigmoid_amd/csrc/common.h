@@ -31,15 +31,22 @@ coli_status hip_fail(hipError_t err, const char* what);
     } while (0)
 
 // ------------------------------------------------------------ blob layout
+// int4 rows hold two nibbles per byte. int8 rows hold, for every 32-element
+// block, 16 bytes of high nibbles h = q >> 4 (in [-8, 7]) and then 16 bytes of
+// low nibbles l = (q & 15) - 8 (in [-8, 7]), so q = 16 h + l + 8 and the int4
+// dot-product machinery serves both.
 struct BlobLayout {
     size_t gate_q, up_q, down_q, gate_s, up_s, down_s, bytes;
+    int32_t wbits;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-inline BlobLayout blob_layout(int64_t H, int64_t I, int32_t group) {
+inline BlobLayout blob_layout(int64_t H, int64_t I, int32_t group, int32_t wbits = 4) {
     BlobLayout L;
-    size_t gq = (size_t)I * (size_t)(H / 2), dq = (size_t)H * (size_t)(I / 2);
+    L.wbits = wbits == 8 ? 8 : 4;
+    const int64_t div = L.wbits == 8 ? 1 : 2;
+    size_t gq = (size_t)I * (size_t)(H / div), dq = (size_t)H * (size_t)(I / div);
     size_t gs = (size_t)I * (size_t)(group ? H / group : 1) * 4;
     size_t ds = (size_t)H * (size_t)(group ? I / group : 1) * 4;
     size_t o = 0;
@@ -112,6 +119,40 @@ __device__ __forceinline__ int block_dot(const uint4& w, const uint4* p) {
         a[i] = acc;
     }
     return a[0] + a[1] * 16 + a[2] * 256 + a[3] * 4096;
+}
+
+// One block of weights in registers: 16 bytes of nibbles (int4), or the high
+// and the low nibble planes of an int8 block (32 bytes).
+template <bool W8>
+struct WBlock {
+    uint4 v[W8 ? 2 : 1];
+};
+
+// Block `ch` of a weight row (row start `row`).
+template <bool W8>
+__device__ __forceinline__ WBlock<W8> load_wblock(const uint8_t* row, int ch) {
+    WBlock<W8> b;
+    if constexpr (W8) {
+        b.v[0] = ldg128(row + (size_t)ch * 32);
+        b.v[1] = ldg128(row + (size_t)ch * 32 + 16);
+    } else {
+        b.v[0] = ldg128(row + (size_t)ch * 16);
+    }
+    return b;
+}
+
+// sum over the block of q * X: int4 directly; int8 as 16 (h . X) + (l . X) +
+// 8 sum(X), with xsum = sum(X) of the block (digit_sum). Exact in int32:
+// |q X| <= 128 * 34952 per element.
+template <bool W8>
+__device__ __forceinline__ int wblock_dot(const WBlock<W8>& w, const uint4* p, int xsum) {
+    if constexpr (W8) return 16 * block_dot(w.v[0], p) + block_dot(w.v[1], p) + 8 * xsum;
+    else return block_dot(w.v[0], p);
+}
+
+// sum of the block's integers X (all-ones weights through the same dot).
+__device__ __forceinline__ int digit_sum(const uint4* p) {
+    return block_dot(make_uint4(0x11111111u, 0x11111111u, 0x11111111u, 0x11111111u), p);
 }
 
 // Encode 8 consecutive elements (this thread's quarter of a 32-element block;
@@ -238,11 +279,12 @@ __device__ __forceinline__ constexpr int transpose_shift() {
 // ------------------------------------------------- launch entry points
 // (host functions implemented in the .hip files; all enqueue on `stream`)
 coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t group,
-                            uint8_t* q, float* s, hipStream_t stream);
+                            uint8_t* q, float* s, hipStream_t stream, int32_t wbits = 4);
 // FP8 e4m3 codes w8 [rows][cols] with scales [ceil(rows/128)][ceil(cols/128)]
 // -> f32 -> int4, through the same quantiser kernels.
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
-                               int32_t group, uint8_t* q, float* s, hipStream_t stream);
+                               int32_t group, uint8_t* q, float* s, hipStream_t stream,
+                               int32_t wbits = 4);
 coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int32_t H,
                                  int32_t E, float* logits, hipStream_t stream);
 // Router for small batches (T <= kSmallT): logits (when router_w is given)
@@ -297,7 +339,7 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
                             float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
-                            int32_t I, int32_t group, hipStream_t stream);
+                            int32_t I, int32_t group, int32_t wbits, hipStream_t stream);
 // y [T][H] = shared row + rs * sum_j w[t][j] * y_rows[t*k + j] in slot order;
 // with idx (nullable) given, slots whose index is negative (dropped by top-p)
 // add nothing.

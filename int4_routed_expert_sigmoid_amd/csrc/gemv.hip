@@ -124,9 +124,9 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
                             float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
-                            int32_t I, int32_t group, hipStream_t stream) {
+                            int32_t I, int32_t group, int32_t wbits, hipStream_t stream) {
     if (max_items == 0) return COLI_OK;
-    const BlobLayout L = blob_layout(H, I, group);
+    const BlobLayout L = blob_layout(H, I, group, wbits);
     const int mt = max_count <= 1 ? 1 : max_count <= 2 ? 2 : max_count <= 4 ? 4 : 8;
     const dim3 g1((mt == 1 ? 2 : 1) * (I / kBlock), max_items);   // one token: gate and up apart
     bool ok;

@@ -21,7 +21,7 @@ namespace {
 // One work item's rows of this workgroup for all of its tokens, MT at a time.
 // ENC (one-token launches): h is formed and encoded in LDS (s_h: [CI][16]
 // digit words, [CI] scales); otherwise the blocks come from hplanes/hscale.
-template <int NCH, int MT, bool GS, bool ENC>
+template <int NCH, int MT, bool GS, bool ENC, bool W8>
 __device__ __forceinline__ void down_body(
     const WorkItem& it, const int32_t* __restrict__ rows_out, const float* __restrict__ gu,
     const uint32_t* __restrict__ hplanes, const float* __restrict__ hscale,
@@ -39,7 +39,7 @@ __device__ __forceinline__ void down_body(
     const bool live = rbase < H;                         // wave-uniform
     const uint8_t* dq = it.blob + L.down_q;
     const float* dsc = reinterpret_cast<const float*>(it.blob + L.down_s);
-    const size_t rowbytes = (size_t)I / 2;
+    const size_t rowbytes = (size_t)I / (W8 ? 1 : 2);
     const int gpr = GS ? I / 64 : 1;
 
     // the token loop is uniform over the workgroup (it holds barriers); waves
@@ -48,9 +48,9 @@ __device__ __forceinline__ void down_body(
     for (int m0 = 0; m0 < it.count; m0 += MT) {
         const int mc = min(MT, it.count - m0);
         if (!ENC && (m0 & 63) == 0) rowwin = rows_out[it.begin + min(m0 + lane, it.count - 1)];
-        uint4 wbuf[PD][LB][NCH];
+        WBlock<W8> wbuf[PD][LB][NCH];
         float fbuf[PD][LB][NCH];
-        auto load = [&](uint4 (&wv)[LB][NCH], float (&fv)[LB][NCH], int batch) {
+        auto load = [&](WBlock<W8> (&wv)[LB][NCH], float (&fv)[LB][NCH], int batch) {
 #pragma unroll
             for (int r = 0; r < LB; ++r) {
                 const int row = min(rbase + batch * LB + r, H - 1);   // rows past H: dropped
@@ -59,7 +59,7 @@ __device__ __forceinline__ void down_body(
                     // unconditional loads: lanes past the row end re-read its last
                     // block; their activation scales are zero
                     const int ch = min(lane + 64 * j, CI - 1);
-                    wv[r][j] = ldg128(dq + row * rowbytes + (size_t)ch * 16);
+                    wv[r][j] = load_wblock<W8>(dq + row * rowbytes, ch);
                     if (GS) fv[r][j] = ldg_f32(dsc + (size_t)row * gpr + (ch >> 1));
                 }
             }
@@ -108,7 +108,12 @@ __device__ __forceinline__ void down_body(
                     hs[m][j] = ENC ? s_scale[chc] : hscale[(size_t)outr * CI + chc];   // validity applied where used
                 }
             }
-            auto compute = [&](const uint4 (&wv)[LB][NCH], const float (&fv)[LB][NCH], int batch) {
+            int hsum[MT][NCH];                           // int8 weights: sum of each block's X
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int j = 0; j < NCH; ++j) hsum[m][j] = W8 ? digit_sum(hp[m][j]) : 0;
+            auto compute = [&](const WBlock<W8> (&wv)[LB][NCH], const float (&fv)[LB][NCH], int batch) {
                 float part[NV];
 #pragma unroll
                 for (int r = 0; r < LB; ++r)
@@ -120,7 +125,7 @@ __device__ __forceinline__ void down_body(
                             for (int j = 0; j < NCH; ++j) {
                                 const float x = lane + 64 * j < CI ? hs[m][j] : 0.f;
                                 const float f = GS ? x * fv[r][j] : x;
-                                acc += (float)block_dot(wv[r][j], hp[m][j]) * f;
+                                acc += (float)wblock_dot<W8>(wv[r][j], hp[m][j], hsum[m][j]) * f;
                             }
                         }
                         part[r * MT + m] = acc;
@@ -158,8 +163,8 @@ __device__ __forceinline__ void down_body(
 
 // MTK == 1: one token (h formed in LDS); MTK == 4: batches, each work item
 // taking the body that fits its token count (1, 2, or chunks of 4).
-template <int NCH, int MTK, bool GS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH == 1 && MTK == 1 && !GS ? 4 : NCH == 1 ? 3 : 2, 8)))
+template <int NCH, int MTK, bool GS, bool W8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W8 ? (NCH == 1 && MTK == 1 && !GS ? 3 : 2) : NCH == 1 && MTK == 1 && !GS ? 4 : NCH == 1 ? 3 : 2, 8)))
 void down_kernel(
     const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
     const int32_t* __restrict__ rows_out, const float* __restrict__ gu,
@@ -170,11 +175,11 @@ void down_kernel(
     if (item >= *n_items) return;
     const WorkItem it = items[item];
     if constexpr (MTK == 1) {
-        down_body<NCH, 1, GS, true>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
+        down_body<NCH, 1, GS, true, W8>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
     } else {
-        if (it.count == 1) down_body<NCH, 1, GS, false>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
-        else if (it.count == 2) down_body<NCH, 2, GS, false>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
-        else down_body<NCH, 4, GS, false>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
+        if (it.count == 1) down_body<NCH, 1, GS, false, W8>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
+        else if (it.count == 2) down_body<NCH, 2, GS, false, W8>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
+        else down_body<NCH, 4, GS, false, W8>(it, rows_out, gu, hplanes, hscale, y_rows, H, I, L, s_h);
     }
 }
 
@@ -183,8 +188,12 @@ void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_
               const int32_t* rows_out, const float* gu, const uint32_t* hp, const float* hs,
               float* y, int H, int I, const BlobLayout& L) {
     const size_t lds = MT == 1 ? (size_t)(I / kBlock) * (kWordsPerBlock + 1) * sizeof(uint32_t) : 0;
-    launch((down_kernel<NCH, MT, GS>), grid, dim3(256), lds, s, items, n_items, rows_out, gu, hp,
-           hs, y, H, I, L);
+    if (L.wbits == 8)
+        launch((down_kernel<NCH, MT, GS, true>), grid, dim3(256), lds, s, items, n_items, rows_out,
+               gu, hp, hs, y, H, I, L);
+    else
+        launch((down_kernel<NCH, MT, GS, false>), grid, dim3(256), lds, s, items, n_items, rows_out,
+               gu, hp, hs, y, H, I, L);
 }
 
 template <int NCH, bool GS>

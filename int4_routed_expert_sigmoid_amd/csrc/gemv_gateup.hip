@@ -24,7 +24,7 @@ namespace {
 // One work item's 32-row tile of NM matrices (from mat0) for all of its
 // tokens, MT at a time. ONE: a one-token launch, where every row's token is 0
 // (the activation planes then load without waiting for the token index).
-template <int W, int NCH, int MT, int NM, bool GS, bool ONE>
+template <int W, int NCH, int MT, int NM, bool GS, bool ONE, bool W8>
 __device__ __forceinline__ void gateup_body(
     const WorkItem& it, int tile, int mat0, const int32_t* __restrict__ rows_tok,
     const int32_t* __restrict__ rows_out, const uint32_t* __restrict__ xplanes,
@@ -45,7 +45,7 @@ __device__ __forceinline__ void gateup_body(
         wq[mt] = it.blob + (mat0 + mt ? L.up_q : L.gate_q);
         wsc[mt] = reinterpret_cast<const float*>(it.blob + (mat0 + mt ? L.up_s : L.gate_s));
     }
-    const size_t rowbytes = (size_t)H / 2;
+    const size_t rowbytes = (size_t)H / (W8 ? 1 : 2);
     const int gpr = GS ? H / 64 : 1;
 
     float (*red)[kBlock * NM * MT] = reinterpret_cast<float (*)[kBlock * NM * MT]>(red_raw);
@@ -56,9 +56,9 @@ __device__ __forceinline__ void gateup_body(
         if (!ONE && (m0 & 63) == 0) tokwin = rows_tok[it.begin + min(m0 + lane, it.count - 1)];
         // two register sets of weights; the first batch is requested before
         // the activation planes
-        uint4 wa[LB][NM][NCH], wb[LB][NM][NCH];
+        WBlock<W8> wa[LB][NM][NCH], wb[LB][NM][NCH];
         float fa[LB][NM][NCH], fb[LB][NM][NCH];
-        auto load = [&](uint4 (&wv)[LB][NM][NCH], float (&fv)[LB][NM][NCH], int batch) {
+        auto load = [&](WBlock<W8> (&wv)[LB][NM][NCH], float (&fv)[LB][NM][NCH], int batch) {
 #pragma unroll
             for (int r = 0; r < LB; ++r) {
                 const int row = r0 + batch * LB + r;
@@ -70,7 +70,7 @@ __device__ __forceinline__ void gateup_body(
                         // merge at): threads past the row end re-read its last
                         // block, and their activation scales are zero
                         const int ch = min(tid + 64 * W * j, C - 1);
-                        wv[r][mt][j] = ldg128(wq[mt] + row * rowbytes + (size_t)ch * 16);
+                        wv[r][mt][j] = load_wblock<W8>(wq[mt] + row * rowbytes, ch);
                         if (GS) fv[r][mt][j] = ldg_f32(wsc[mt] + (size_t)row * gpr + (ch >> 1));
                     }
             }
@@ -93,8 +93,13 @@ __device__ __forceinline__ void gateup_body(
                 xs[m][j] = xscale[(size_t)tok * C + chc];   // validity applied where it is used
             }
         }
+        int xsum[MT][NCH];                                // int8 weights: sum of each block's X
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) xsum[m][j] = W8 ? digit_sum(xp[m][j]) : 0;
 
-        auto compute = [&](const uint4 (&wv)[LB][NM][NCH], const float (&fv)[LB][NM][NCH], int batch) {
+        auto compute = [&](const WBlock<W8> (&wv)[LB][NM][NCH], const float (&fv)[LB][NM][NCH], int batch) {
             float part[NV];
 #pragma unroll
             for (int r = 0; r < LB; ++r)
@@ -108,7 +113,7 @@ __device__ __forceinline__ void gateup_body(
                             for (int j = 0; j < NCH; ++j) {
                                 const float x = tid + 64 * W * j < C ? xs[m][j] : 0.f;
                                 const float f = GS ? x * fv[r][mt][j] : x;
-                                acc += (float)block_dot(wv[r][mt][j], xp[m][j]) * f;
+                                acc += (float)wblock_dot<W8>(wv[r][mt][j], xp[m][j], xsum[m][j]) * f;
                             }
                         }
                         part[(r * NM + mt) * MT + m] = acc;
@@ -145,9 +150,9 @@ __device__ __forceinline__ void gateup_body(
 // Resident waves per SIMD the register budget must allow: the decode grid
 // (9 work items x 64 tiles x 2 matrices, 3 waves each) then fits on the chip
 // in one round.
-template <int NCH, int MTK, bool GS>
+template <int NCH, int MTK, bool GS, bool W8>
 constexpr int gateup_waves_per_eu() {
-    return NCH == 1 && MTK == 1 ? 4 : NCH == 1 && !GS ? 4 : NCH == 1 ? 3 : 2;
+    return W8 ? (NCH == 1 && MTK == 1 ? 3 : 2) : NCH == 1 && MTK == 1 ? 4 : NCH == 1 && !GS ? 4 : NCH == 1 ? 3 : 2;
 }
 
 // MTK == 1: one token; gate and up in separate workgroups (grid x interleaves
@@ -156,8 +161,8 @@ constexpr int gateup_waves_per_eu() {
 // read once for the pair, and each work item takes the body that fits its
 // token count (1, 2, or chunks of 4), which keeps the per-wave batches of
 // weight rows large for the many experts that see one or two tokens.
-template <int W, int NCH, int MTK, bool GS>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(gateup_waves_per_eu<NCH, MTK, GS>(), 8)))
+template <int W, int NCH, int MTK, bool GS, bool W8>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(gateup_waves_per_eu<NCH, MTK, GS, W8>(), 8)))
 void gateup_kernel(
     const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
     const int32_t* __restrict__ rows_tok, const int32_t* __restrict__ rows_out,
@@ -168,16 +173,16 @@ void gateup_kernel(
     if (item >= *n_items) return;
     const WorkItem it = items[item];
     if constexpr (MTK == 1) {
-        gateup_body<W, NCH, 1, 1, GS, true>(it, (int)blockIdx.x >> 1, (int)blockIdx.x & 1, rows_tok,
+        gateup_body<W, NCH, 1, 1, GS, true, W8>(it, (int)blockIdx.x >> 1, (int)blockIdx.x & 1, rows_tok,
                                       rows_out, xplanes, xscale, gu, H, I, L, red);
     } else {
         const int t = blockIdx.x;
         if (it.count == 1)
-            gateup_body<W, NCH, 1, 2, GS, false>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 1, 2, GS, false, W8>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
         else if (it.count == 2)
-            gateup_body<W, NCH, 2, 2, GS, false>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 2, 2, GS, false, W8>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
         else
-            gateup_body<W, NCH, 4, 2, GS, false>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 4, 2, GS, false, W8>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
     }
 }
 
@@ -185,7 +190,12 @@ template <int W, int NCH, int MTK, bool GS>
 void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
               const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp,
               const float* xs, float* gu, int H, int I, const BlobLayout& L) {
-    launch((gateup_kernel<W, NCH, MTK, GS>), grid, dim3(64 * W), 0, s, items, n_items,
+    if (L.wbits == 8) {
+        launch((gateup_kernel<W, NCH, MTK, GS, true>), grid, dim3(64 * W), 0, s, items, n_items,
+               rows_tok, rows_out, xp, xs, gu, H, I, L);
+        return;
+    }
+    launch((gateup_kernel<W, NCH, MTK, GS, false>), grid, dim3(64 * W), 0, s, items, n_items,
                        rows_tok, rows_out, xp, xs, gu, H, I, L);
 }
 

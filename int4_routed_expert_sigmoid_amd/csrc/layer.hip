@@ -19,8 +19,11 @@ static T* at(uint8_t* ws, size_t off) { return reinterpret_cast<T*>(ws + off); }
 // Decide the FFN path: the GEMV family for small batches, the bf16 MFMA
 // grouped GEMM for large ones (auto), or the caller's choice.
 static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, bool* mfma) {
-    const bool shape_ok = s->hidden % 64 == 0 && s->inter % 64 == 0;
+    // the MFMA path dequantises int4 weights only; int8 experts always take the GEMV family
+    const bool int8 = s->wbits == 8;
+    const bool shape_ok = s->hidden % 64 == 0 && s->inter % 64 == 0 && !int8;
     if (path == COLI_PATH_MFMA) {
+        if (int8) return fail(COLI_EUNSUPPORTED, "mfma path: int4 weights only");
         if (!shape_ok) return fail(COLI_EUNSUPPORTED, "mfma path: hidden and inter must be multiples of 64");
         *mfma = true;
     } else if (path == COLI_PATH_GEMV) {
@@ -63,7 +66,7 @@ static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, i
                            rows, at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
                            at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
                            at<float>(ws, W.gu), at<uint32_t>(ws, W.hplanes),
-                           at<float>(ws, W.hscale), y_rows, H, I, s->group, stream);
+                           at<float>(ws, W.hscale), y_rows, H, I, s->group, s->wbits, stream);
 }
 
 coli_status run_expert_ffn(const coli_moe_shape* s, const void* const* table, const float* x,

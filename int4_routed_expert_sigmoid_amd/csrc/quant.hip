@@ -13,25 +13,64 @@
 namespace coli {
 namespace {
 
-// q = rint(v / scale) with IEEE division, clamped to [-8, 7]. The quotient is
-// first formed as v * inv with inv = 1/scale correctly rounded: |q| <= 8 keeps
-// that within 2^-19 of the correctly rounded quotient, so the two can round
-// to different integers only when t lies within 2^-19 of a half-integer. Such
-// values (and non-finite t, e.g. from a subnormal scale) take the division.
+// q = rint(v / scale) with IEEE division, clamped to [QLO, QHI]. The quotient
+// is first formed as v * inv with inv = 1/scale correctly rounded: |q| <= 128
+// keeps that within 2^-15 of the correctly rounded quotient, so the two can
+// round to different integers only when t lies within 2^-15 of a
+// half-integer. Such values (and non-finite t, e.g. from a subnormal scale)
+// take the division.
+template <int QLO, int QHI>
 __device__ __forceinline__ int quant_q(float v, float scale, float inv) {
     const float t = v * inv;
     float r = rintf(t);
-    if (!(fabsf(fabsf(t - r) - 0.5f) > 0x1p-18f)) r = rintf(__fdiv_rn(v, scale));
-    return (int)fminf(fmaxf(r, -8.f), 7.f);
+    if (!(fabsf(fabsf(t - r) - 0.5f) > 0x1p-14f)) r = rintf(__fdiv_rn(v, scale));
+    return (int)fminf(fmaxf(r, (float)QLO), (float)QHI);
 }
 
+// int4: 8 nibbles of one output word.
 __device__ __forceinline__ uint32_t pack8(const float v[8], float scale) {
     uint32_t word = 0;
     if (scale == 0.f) return 0;
     const float inv = __fdiv_rn(1.0f, scale);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_q(v[i], scale, inv) & 15) << (4 * i);
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_q<-8, 7>(v[i], scale, inv) & 15) << (4 * i);
     return word;
+}
+
+// int8: the high-nibble word (q >> 4) and the low-nibble word ((q & 15) - 8)
+// of 8 columns.
+__device__ __forceinline__ void pack8_w8(const float v[8], float scale, uint32_t& hi, uint32_t& lo) {
+    hi = 0;
+    lo = 0x88888888u;                       // q = 0 everywhere: h = 0, l = -8
+    if (scale == 0.f) return;
+    lo = 0;
+    const float inv = __fdiv_rn(1.0f, scale);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int q = quant_q<-128, 127>(v[i], scale, inv);
+        hi |= (uint32_t)((q >> 4) & 15) << (4 * i);
+        lo |= (uint32_t)((q & 15) ^ 8) << (4 * i);
+    }
+}
+
+// Quantise and store 8 columns c0 .. c0+7 (c0 % 8 == 0) of a row starting at
+// qrow: int4 one word at byte c0/2; int8 two words, in the block's high and
+// low halves.
+template <bool W8>
+__device__ __forceinline__ void store8(uint8_t* qrow, int64_t c0, const float v[8], float scale,
+                                       int aligned_out) {
+    if constexpr (W8) {
+        uint32_t hi, lo;
+        pack8_w8(v, scale, hi, lo);
+        uint8_t* p = qrow + (c0 >> 5) * 32 + ((c0 & 31) >> 1);
+        *reinterpret_cast<uint32_t*>(p) = hi;            // int8 rows are 4-byte aligned
+        *reinterpret_cast<uint32_t*>(p + 16) = lo;
+    } else {
+        const uint32_t word = pack8(v, scale);
+        uint8_t* p = qrow + c0 / 2;
+        if (aligned_out) *reinterpret_cast<uint32_t*>(p) = word;
+        else for (int b = 0; b < 4; ++b) p[b] = (uint8_t)(word >> (8 * b));
+    }
 }
 
 // Value sources of the quantiser: f32 weights, or FP8 e4m3 codes with one f32
@@ -94,7 +133,7 @@ struct Fp8Src {
 };
 
 // One workgroup per row: block-wide max, then quantise and pack.
-template <typename Src>
+template <typename Src, bool W8>
 __global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t rows, int64_t cols,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ s, int aligned_out) {
@@ -115,17 +154,15 @@ __global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t rows, i
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float scale = __fdiv_rn(m, 7.0f);
+    const float scale = __fdiv_rn(m, W8 ? 127.0f : 7.0f);
     if (threadIdx.x == 0) s[r] = scale;
-    uint8_t* qr = q + r * (cols / 2);
+    uint8_t* qr = q + r * (W8 ? cols : cols / 2);
     for (int64_t i = threadIdx.x; i < words; i += blockDim.x) {
         float v[8];
         src.load8(r, 8 * i, v);
-        uint32_t word = pack8(v, scale);
-        if (aligned_out) *reinterpret_cast<uint32_t*>(qr + 4 * i) = word;
-        else for (int b = 0; b < 4; ++b) qr[4 * i + b] = (uint8_t)(word >> (8 * b));
+        store8<W8>(qr, 8 * i, v, scale, aligned_out);
     }
-    if (threadIdx.x == 0 && tail) {
+    if (!W8 && threadIdx.x == 0 && tail) {           // int8 rows are whole blocks
         float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int64_t c = 0; c < tail; ++c) v[c] = src.load1(r, words * 8 + c);
         uint32_t word = pack8(v, scale);
@@ -134,7 +171,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t rows, i
 }
 
 // gs64: eight threads (lanes 8g..8g+7) per 64-column group.
-template <typename Src>
+template <typename Src, bool W8>
 __global__ __launch_bounds__(256) void quant_g64_kernel(Src src, int64_t rows, int64_t cols,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ s, int aligned_out) {
@@ -151,13 +188,10 @@ __global__ __launch_bounds__(256) void quant_g64_kernel(Src src, int64_t rows, i
     m = fmaxf(m, __shfl_xor(m, 1));
     m = fmaxf(m, __shfl_xor(m, 2));
     m = fmaxf(m, __shfl_xor(m, 4));
-    const float scale = __fdiv_rn(m, 7.0f);
+    const float scale = __fdiv_rn(m, W8 ? 127.0f : 7.0f);
     if (i < total) {
         if ((wi & 7) == 0) s[r * (cols / 64) + wi / 8] = scale;
-        uint32_t word = pack8(v, scale);
-        uint8_t* qp = q + r * (cols / 2) + wi * 4;
-        if (aligned_out) *reinterpret_cast<uint32_t*>(qp) = word;
-        else for (int b = 0; b < 4; ++b) qp[b] = (uint8_t)(word >> (8 * b));
+        store8<W8>(q + r * (W8 ? cols : cols / 2), wi * 8, v, scale, aligned_out);
     }
 }
 
@@ -250,22 +284,37 @@ bool launch_fp8_wave(const uint8_t* w8, const float* scale, int64_t rows, int64_
     return true;
 }
 
-template <typename Src>
-coli_status launch_quant(const Src& src, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
-                         float* s, int aligned_out, hipStream_t stream) {
-    if (rows == 0) return COLI_OK;
+template <typename Src, bool W8>
+coli_status launch_quant_t(const Src& src, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
+                           float* s, int aligned_out, hipStream_t stream) {
     if (group == 0) {
         if (rows > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: too many rows");
-        launch(quant_row_kernel<Src>, dim3((unsigned)rows), dim3(256), 0, stream, src, rows, cols,
-               q, s, aligned_out);
+        launch(quant_row_kernel<Src, W8>, dim3((unsigned)rows), dim3(256), 0, stream, src, rows,
+               cols, q, s, aligned_out);
     } else {
         // the group of 8 lanes must not straddle rows: cols % 64 == 0 is required
         const int64_t total = rows * (cols / 8);
         const int64_t blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: tensor too large");
-        launch(quant_g64_kernel<Src>, dim3((unsigned)blocks), dim3(256), 0, stream, src, rows,
+        launch(quant_g64_kernel<Src, W8>, dim3((unsigned)blocks), dim3(256), 0, stream, src, rows,
                cols, q, s, aligned_out);
     }
+    return COLI_OK;
+}
+
+template <typename Src>
+coli_status launch_quant(const Src& src, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
+                         float* s, int aligned_out, hipStream_t stream, int32_t wbits) {
+    if (rows == 0) return COLI_OK;
+    coli_status st;
+    if (wbits == 8) {
+        if (cols % kBlock || (uintptr_t)q % 4)
+            return fail(COLI_EINVAL, "quantize: int8 rows need cols % 32 == 0 and 4-byte alignment");
+        st = launch_quant_t<Src, true>(src, rows, cols, group, q, s, 1, stream);
+    } else {
+        st = launch_quant_t<Src, false>(src, rows, cols, group, q, s, aligned_out, stream);
+    }
+    if (st) return st;
     COLI_CHECK_LAUNCH("quantize kernel launch");
     return COLI_OK;
 }
@@ -273,18 +322,19 @@ coli_status launch_quant(const Src& src, int64_t rows, int64_t cols, int32_t gro
 }  // namespace
 
 coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
-                            float* s, hipStream_t stream) {
+                            float* s, hipStream_t stream, int32_t wbits) {
     const int aligned = ((uintptr_t)w % 16 == 0) && ((uintptr_t)q % 4 == 0) &&
                         (cols % 8 == 0) ? 1 : 0;
     F32Src src{w, cols, aligned};
-    return launch_quant(src, rows, cols, group, q, s, aligned, stream);
+    return launch_quant(src, rows, cols, group, q, s, aligned, stream, wbits);
 }
 
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
-                               int32_t group, uint8_t* q, float* s, hipStream_t stream) {
+                               int32_t group, uint8_t* q, float* s, hipStream_t stream,
+                               int32_t wbits) {
     if (rows == 0) return COLI_OK;
-    if ((uintptr_t)w8 % 16 == 0 && (uintptr_t)q % 8 == 0 && cols % 16 == 0 && cols <= 8192 &&
-        rows <= 0x1fffffffLL) {
+    if (wbits != 8 && (uintptr_t)w8 % 16 == 0 && (uintptr_t)q % 8 == 0 && cols % 16 == 0 &&
+        cols <= 8192 && rows <= 0x1fffffffLL) {
         const bool ok = group == 0 ? launch_fp8_wave<false>(w8, scale, rows, cols, q, s, stream)
                                    : launch_fp8_wave<true>(w8, scale, rows, cols, q, s, stream);
         if (ok) {
@@ -295,7 +345,7 @@ coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t ro
     const int aligned_in = ((uintptr_t)w8 % 8 == 0) && (cols % 8 == 0) ? 1 : 0;
     const int aligned_out = ((uintptr_t)q % 4 == 0) && (cols % 8 == 0) ? 1 : 0;
     Fp8Src src{w8, scale, cols, (cols + 127) / 128, aligned_in};
-    return launch_quant(src, rows, cols, group, q, s, aligned_out, stream);
+    return launch_quant(src, rows, cols, group, q, s, aligned_out, stream, wbits);
 }
 
 }  // namespace coli

@@ -41,7 +41,7 @@ class ExpertSet:
         for e in ids:
             g, u, d = synth.expert_weights(seed, layer, e, H, I)
             host = keep_oracle is None or e in keep_oracle or e == E
-            qe = oracle.QExpert.quantize(g, u, d, G) if host else None
+            qe = oracle.QExpert.quantize(g, u, d, G, bits=shape.wbits) if host else None
             blob = coli.quantize_expert(shape, torch.from_numpy(g).to(dev),
                                         torch.from_numpy(u).to(dev), torch.from_numpy(d).to(dev))
             if e == E:
@@ -60,7 +60,8 @@ class ExpertSet:
             if qe is None:
                 if zero is None:
                     z = np.zeros((I, H), np.float32)
-                    zero = oracle.QExpert.quantize(z, z, np.zeros((H, I), np.float32), G)
+                    zero = oracle.QExpert.quantize(z, z, np.zeros((H, I), np.float32), G,
+                                                   bits=self.shape.wbits)
                 qe = zero
             out.append(qe)
         return out
