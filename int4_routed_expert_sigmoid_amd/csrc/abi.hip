@@ -73,6 +73,8 @@ WsLayout ws_layout(const coli_moe_shape* s, int32_t T, int32_t path) {
     W.hscale = take(R * (I / kBlock) * 4);
     W.y_rows = take(R * H * 4);
     W.phase = take(E);
+    W.codes = take(E * 8);
+    W.scores = take(E * 4);
     // bf16 MFMA path
     const size_t max_items = std::min<size_t>(E, n) + 1;
     W.max_tiles = gemm_tiles_max((int32_t)R, (int32_t)max_items);

@@ -71,6 +71,27 @@ struct WorkItem {
     int32_t row0;
 };
 
+// One-token routing folded into the gate/up GEMV: the router's first pass
+// has written one 64-bit selection code and one sigmoid score per expert;
+// every gate/up workgroup selects the top-k itself and derives its own work
+// item, and one workgroup publishes the routing and the work list for the
+// later passes. codes == nullptr: the work list comes from the router.
+struct FusedRoute {
+    const uint64_t* codes;      // [E] selection codes
+    const float* scores;        // [E] sigmoid scores
+    const void* const* table;   // [E] routed expert blobs
+    const void* shared;         // shared expert blob or nullptr
+    int32_t E, k;
+    float topp;
+    int32_t* idx;               // [k] routing out (slot order; -1 for dropped slots)
+    float* w;                   // [k]
+    int32_t* rows_tok;          // [k + 1]
+    int32_t* rows_out;          // [k + 1]
+    WorkItem* items;            // [1 + k] work list for the down pass
+    int32_t* n_items;
+};
+constexpr int kFusedMaxExperts = 256;   // four selection codes per lane
+
 // ------------------------------------------------------ activation digits
 // The GEMV family multiplies int4 weights by activations held as four planes
 // of signed base-16 digits per 32-element block: x_c ~= scale_b * X_c with
@@ -225,6 +246,107 @@ __device__ __forceinline__ int lane_xchg(int v) {
     }
 }
 
+// ------------------------------------------------------- expert selection
+// lbrq.cn article "github一周涨11k⭐️！25GB 内存跑 744B GLM-5.2 模型！", section 三
+// item 1 and section 四 item 3: sigmoid scores, a selection-only bias, top-k,
+// weights normalised over the selected (norm_topk_prob); adaptive expert
+// top-p from the practical guide (section 三 and the section 五 tuning table).
+
+// sigmoid in double, rounded once to f32
+__device__ __forceinline__ float sigmoid_score(float logit) {
+    return (float)(1.0 / (1.0 + exp(-(double)logit)));
+}
+
+// Selection order as one unsigned 64-bit number: the key's bits mapped so
+// that unsigned order is float order (high word), then the complement of the
+// expert id (low word), so a larger key wins and equal keys go to the lower
+// id. A -0.0 key is folded to +0.0 first (they compare equal as floats).
+// Every valid entry is nonzero; 0 marks an empty or taken entry.
+__device__ __forceinline__ uint64_t selection_code(float key, int e) {
+    const uint32_t b = __float_as_uint(key + 0.0f);
+    const uint32_t o = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+
+template <int S>
+__device__ __forceinline__ void max_step(uint64_t& v) {
+    const uint32_t hi = (uint32_t)lane_xchg<S>((int)(uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)lane_xchg<S>((int)(uint32_t)v);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+}
+
+// Result of select_topk in lane j < k: slot j's expert and its normalised
+// weight; kept (wave-uniform) is the number of slots kept by top-p (k without).
+struct TopK {
+    int my_idx;
+    float my_w;
+    int kept;
+};
+
+// Top-k of one token held by one wave, lane l holding the codes and scores of
+// experts l, l+64, ... (code 0: not an expert). Each of the k rounds takes the
+// lane maxima, a wave-wide maximum (butterfly over DPP / permlane partners, no
+// branches), and retires the winner; the picks come out in slot order. With
+// 0 < topp < 1 only the shortest slot-order prefix whose share of the k
+// selected scores reaches topp is kept: slot j is kept iff j == 0 or the share
+// of slots 0..j-1 is below topp (the shares only grow, so the kept slots are a
+// prefix). Weights are the scores normalised over the kept slots; shares and
+// sums are double, in slot order.
+template <int EPL>
+__device__ __forceinline__ TopK select_topk(uint64_t (&code)[EPL], const float (&score)[EPL],
+                                            int k, float topp) {
+    const int lane = threadIdx.x & 63;
+    double sum = 0.0;
+    double my_prev = 0.0;    // lane j (< k): sum of slots 0..j-1
+    float my_sel = 0.f;      // lane j (< k) keeps the score of slot j
+    int my_idx = 0;
+    for (int j = 0; j < k; ++j) {
+        uint64_t m = code[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) m = code[i] > m ? code[i] : m;
+        max_step<1>(m);
+        max_step<2>(m);
+        max_step<4>(m);
+        max_step<8>(m);
+        max_step<16>(m);
+        max_step<32>(m);
+        const uint32_t wlo = __builtin_amdgcn_readfirstlane((uint32_t)m);
+        const uint32_t whi = __builtin_amdgcn_readfirstlane((uint32_t)(m >> 32));
+        const uint64_t win = ((uint64_t)whi << 32) | wlo;
+        const int e = (int)~wlo;
+        float c = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const bool hit = code[i] == win;
+            c = hit ? score[i] : c;
+            code[i] = hit ? 0 : code[i];
+        }
+        const float s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), e & 63));
+        if (lane == j) { my_sel = s_sel; my_idx = e; my_prev = sum; }
+        sum += (double)s_sel;
+    }
+    int kept = k;
+    double ksum = sum;
+    if (topp > 0.f && topp < 1.f) {
+        const double share_before = sum == 0.0 ? (double)lane / (double)k : my_prev / sum;
+        const bool keep = lane < k && (lane == 0 || share_before < (double)topp);
+        kept = __popcll(__ballot(keep));
+        if (kept < k) {
+            // the kept prefix's sum is the running sum before slot `kept`
+            const uint64_t bits = (uint64_t)__double_as_longlong(my_prev);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, kept);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), kept);
+            ksum = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+        }
+    }
+    TopK r;
+    r.my_idx = my_idx;
+    r.my_w = (ksum == 0.0) ? (float)(1.0 / kept) : (float)((double)my_sel / ksum);
+    r.kept = kept;
+    return r;
+}
+
 template <int S, int N>
 __device__ __forceinline__ void transpose_stage(float* v, int lane) {
     constexpr int h = N / 2;
@@ -310,6 +432,8 @@ struct SmallRouterArgs {
     int32_t phase;
     int32_t T, E, k, H;
     float topp;                // adaptive expert top-p, active in (0, 1)
+    uint64_t* codes;           // [E] or NULL: one token, routing folded into the gate/up pass
+    float* scores;             // [E] with codes
 };
 coli_status launch_router_small(const SmallRouterArgs& a, hipStream_t stream);
 
@@ -339,7 +463,8 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
                             float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
-                            int32_t I, int32_t group, int32_t wbits, hipStream_t stream);
+                            int32_t I, int32_t group, int32_t wbits, const FusedRoute& fr,
+                            hipStream_t stream);
 // y [T][H] = shared row + rs * sum_j w[t][j] * y_rows[t*k + j] in slot order;
 // with idx (nullable) given, slots whose index is negative (dropped by top-p)
 // add nothing.

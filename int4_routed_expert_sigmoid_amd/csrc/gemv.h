@@ -11,7 +11,7 @@ namespace coli {
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
                      const uint32_t* xplanes, const float* xscale, float* gu, int H, int I,
-                     const BlobLayout& L);
+                     const BlobLayout& L, const FusedRoute& fr);
 
 constexpr int kDownRowsPerWave = 16;
 constexpr int kDownRowsPerBlock = 4 * kDownRowsPerWave;

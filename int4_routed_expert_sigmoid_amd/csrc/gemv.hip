@@ -124,7 +124,8 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
                             float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
-                            int32_t I, int32_t group, int32_t wbits, hipStream_t stream) {
+                            int32_t I, int32_t group, int32_t wbits, const FusedRoute& fr,
+                            hipStream_t stream) {
     if (max_items == 0) return COLI_OK;
     const BlobLayout L = blob_layout(H, I, group, wbits);
     const int mt = max_count <= 1 ? 1 : max_count <= 2 ? 2 : max_count <= 4 ? 4 : 8;
@@ -133,7 +134,7 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
     {
         ProfTag prof("gemv_gateup");
         ok = dispatch_gateup(mt, group, g1, stream, items, n_items, rows_tok, rows_out, xplanes,
-                             xscale, gu, H, I, L);
+                             xscale, gu, H, I, L, fr);
     }
     if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: hidden too large (max 16384)");
     COLI_CHECK_LAUNCH("gate/up GEMV launch");

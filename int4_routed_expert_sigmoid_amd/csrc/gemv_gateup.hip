@@ -138,7 +138,9 @@ __device__ __forceinline__ void gateup_body(
                 for (int w = 0; w < W; ++w) v += red[w][i];
                 if (!GS) v *= ldg_f32((mt ? wsc[NM - 1] : wsc[0]) + r0 + r);
                 if (mat0 + mt == 0) v = v / (1.f + expf(-v));          // gate: store silu(g)
-                const int out = rows_out[it.begin + m0 + m];
+                // one-token items carry their output row (rows_out may still be
+                // in flight when the routing is folded into this pass)
+                const int out = ONE ? it.row0 : rows_out[it.begin + m0 + m];
                 gu[((size_t)out * 2 + mat0 + mt) * I + r0 + r] = v;
             }
         }
@@ -146,6 +148,66 @@ __device__ __forceinline__ void gateup_body(
     }
 }
 
+
+// Work item `item` of a one-token call from the folded routing (FusedRoute):
+// every wave selects the top-k from the selection codes (select_topk), ranks
+// the kept picks by expert id (the work list order: shared expert first, then
+// the kept experts by id) and takes its own; workgroup (0, 0) publishes the
+// routing, the slot-list rows and the item count, and each (0, item)
+// workgroup its item, for the passes that follow. False: no such item (a slot
+// dropped by top-p).
+__device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkItem& it) {
+    constexpr int EPL = kFusedMaxExperts / 64;
+    const int lane = threadIdx.x & 63;
+    uint64_t code[EPL];
+    float score[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = min(lane + 64 * i, fr.E - 1);
+        code[i] = fr.codes[e];
+        score[i] = fr.scores[e];
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) code[i] = lane + 64 * i < fr.E ? code[i] : 0;
+    const TopK r = select_topk<EPL>(code, score, fr.k, fr.topp);
+    const int k = fr.k, kept = r.kept, base = fr.shared ? 1 : 0;
+    const bool mine = lane < kept;
+    int below = 0;                                   // rank of this lane's pick by expert id
+    for (int j = 0; j < kept; ++j) below += __builtin_amdgcn_readlane(r.my_idx, j) < r.my_idx;
+    if (blockIdx.x == 0 && item == 0 && threadIdx.x < 64) {
+        if (lane < k) {
+            fr.idx[lane] = mine ? r.my_idx : -1;
+            fr.w[lane] = mine ? r.my_w : 0.f;
+        }
+        if (mine) {
+            fr.rows_tok[below] = 0;
+            fr.rows_out[below] = lane;
+        }
+        if (lane == 0) {
+            fr.rows_tok[k] = 0;
+            fr.rows_out[k] = k;
+            *fr.n_items = base + kept;
+        }
+    }
+    if (item < base) {
+        it.blob = (const uint8_t*)fr.shared;
+        it.begin = k;
+        it.count = 1;
+        it.row0 = k;
+    } else {
+        const int rk = item - base;
+        if (rk >= kept) return false;
+        const uint64_t hit = __ballot(mine && below == rk);       // exactly one lane
+        const int src = (int)__builtin_ctzll(hit);
+        const int e = __builtin_amdgcn_readlane(r.my_idx, src);
+        it.blob = (const uint8_t*)fr.table[e];
+        it.begin = rk;
+        it.count = 1;
+        it.row0 = src;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) fr.items[item] = it;
+    return true;
+}
 
 // Resident waves per SIMD the register budget must allow: the decode grid
 // (9 work items x 64 tiles x 2 matrices, 3 waves each) then fits on the chip
@@ -167,11 +229,16 @@ void gateup_kernel(
     const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
     const int32_t* __restrict__ rows_tok, const int32_t* __restrict__ rows_out,
     const uint32_t* __restrict__ xplanes, const float* __restrict__ xscale,
-    float* __restrict__ gu, int H, int I, BlobLayout L) {
+    float* __restrict__ gu, int H, int I, BlobLayout L, FusedRoute fr) {
     __shared__ float red[W * kBlock * (MTK == 1 ? 1 : 2 * 4)];
     const int item = blockIdx.y;
-    if (item >= *n_items) return;
-    const WorkItem it = items[item];
+    WorkItem it;
+    if (MTK == 1 && fr.codes) {
+        if (!fused_item(fr, item, it)) return;
+    } else {
+        if (item >= *n_items) return;
+        it = items[item];
+    }
     if constexpr (MTK == 1) {
         gateup_body<W, NCH, 1, 1, GS, true, W8>(it, (int)blockIdx.x >> 1, (int)blockIdx.x & 1, rows_tok,
                                       rows_out, xplanes, xscale, gu, H, I, L, red);
@@ -189,34 +256,34 @@ void gateup_kernel(
 template <int W, int NCH, int MTK, bool GS>
 void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
               const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp,
-              const float* xs, float* gu, int H, int I, const BlobLayout& L) {
+              const float* xs, float* gu, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
     if (L.wbits == 8) {
         launch((gateup_kernel<W, NCH, MTK, GS, true>), grid, dim3(64 * W), 0, s, items, n_items,
-               rows_tok, rows_out, xp, xs, gu, H, I, L);
+               rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
         return;
     }
     launch((gateup_kernel<W, NCH, MTK, GS, false>), grid, dim3(64 * W), 0, s, items, n_items,
-                       rows_tok, rows_out, xp, xs, gu, H, I, L);
+                       rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
 }
 
 template <int W, int NCH, bool GS>
 void by_mt(int mt, dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
            const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp, const float* xs,
-           float* gu, int H, int I, const BlobLayout& L) {
-    if (mt == 1) launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
-    else launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
+           float* gu, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
+    if (mt == 1) launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+    else launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
 }
 
 template <bool GS>
 bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
               const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
               const uint32_t* xp, const float* xs, float* gu, int H, int I,
-              const BlobLayout& L) {
-    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
-    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
-    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
-    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
-    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L);
+              const BlobLayout& L, const FusedRoute& fr) {
+    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
     else return false;
     return true;
 }
@@ -226,12 +293,12 @@ bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
                      const uint32_t* xplanes, const float* xscale, float* gu, int H, int I,
-                     const BlobLayout& L) {
+                     const BlobLayout& L, const FusedRoute& fr) {
     const int C = H / kBlock;
     return group ? by_width<true>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                  xscale, gu, H, I, L)
+                                  xscale, gu, H, I, L, fr)
                  : by_width<false>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                   xscale, gu, H, I, L);
+                                   xscale, gu, H, I, L, fr);
 }
 
 }  // namespace coli

@@ -7,7 +7,8 @@ namespace coli {
 
 struct WsLayout {
     size_t logits, idx, w, counts, offsets, perm, unique, n_unique, n_items, union_ws, items,
-        rows_tok, rows_out, xplanes, xscale, gu, hplanes, hscale, y_rows, phase, tiles, n_tiles, xb, sx, hb, sh, bytes;
+        rows_tok, rows_out, xplanes, xscale, gu, hplanes, hscale, y_rows, phase, tiles, n_tiles, xb, sx, hb, sh,
+        codes, scores, bytes;
     size_t max_tiles;
 };
 

@@ -36,7 +36,7 @@ static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, b
 
 static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, int32_t T,
                            int32_t max_items, float* y_rows, uint8_t* ws, const WsLayout& W,
-                           bool x_encoded, hipStream_t stream) {
+                           bool x_encoded, hipStream_t stream, const FusedRoute* fused = nullptr) {
     const int32_t H = s->hidden, I = s->inter;
     if (mfma) {
         GemmArgs g;
@@ -62,11 +62,13 @@ static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, i
         if (st) return st;
     }
     const int32_t rows = (int32_t)((int64_t)T * s->top_k + T);
+    FusedRoute none{};
     return launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
                            rows, at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
                            at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
                            at<float>(ws, W.gu), at<uint32_t>(ws, W.hplanes),
-                           at<float>(ws, W.hscale), y_rows, H, I, s->group, s->wbits, stream);
+                           at<float>(ws, W.hscale), y_rows, H, I, s->group, s->wbits,
+                           fused ? *fused : none, stream);
 }
 
 coli_status run_expert_ffn(const coli_moe_shape* s, const void* const* table, const float* x,
@@ -103,6 +105,24 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
     int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, W.idx);
     float* w = w_out ? w_out : at<float>(ws, W.w);
     bool encoded = false;
+    // one token on the GEMV path: the gate/up pass routes (no separate plan pass)
+    const bool fold = T == 1 && !cache && !mfma && E <= kFusedMaxExperts;
+    FusedRoute fr{};
+    if (fold) {
+        fr.codes = at<uint64_t>(ws, W.codes);
+        fr.scores = at<float>(ws, W.scores);
+        fr.table = table;
+        fr.shared = shared_blob;
+        fr.E = E;
+        fr.k = k;
+        fr.topp = s->topp;
+        fr.idx = idx;
+        fr.w = w;
+        fr.rows_tok = at<int32_t>(ws, W.rows_tok);
+        fr.rows_out = at<int32_t>(ws, W.rows_out);
+        fr.items = at<WorkItem>(ws, W.items);
+        fr.n_items = at<int32_t>(ws, W.n_items);
+    }
     if (T <= kSmallT) {
         // router: logits + activation encoding, then route / union / work list
         SmallRouterArgs ra;
@@ -119,6 +139,8 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
         ra.phase_mask = nullptr; ra.phase = 0;
         ra.T = T; ra.E = E; ra.k = k; ra.H = H;
         ra.topp = s->topp;
+        ra.codes = fold ? at<uint64_t>(ws, W.codes) : nullptr;
+        ra.scores = fold ? at<float>(ws, W.scores) : nullptr;
         st = launch_router_small(ra, stream);
         if (st) return st;
         encoded = true;
@@ -146,7 +168,8 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
     }
     const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
     if (!cache) {
-        st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W, encoded, stream);
+        st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W, encoded, stream,
+                     fold ? &fr : nullptr);
         if (st) return st;
     } else {
         // place: read the routing back, make the experts resident (misses are

@@ -34,38 +34,9 @@ __global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ w
 
 constexpr int kMaxExpertsPerLane = 16;   // E <= 1024
 
-// Selection order as one unsigned 64-bit number: the key's bits mapped so
-// that unsigned order is float order (high word), then the complement of the
-// expert id (low word), so a larger key wins and equal keys go to the lower
-// id. A -0.0 key is folded to +0.0 first (they compare equal as floats).
-// Every valid entry is nonzero; 0 marks an empty or taken entry.
-__device__ __forceinline__ uint64_t selection_code(float key, int e) {
-    const uint32_t b = __float_as_uint(key + 0.0f);
-    const uint32_t o = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
-    return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
-}
-
-template <int S>
-__device__ __forceinline__ void max_step(uint64_t& v) {
-    const uint32_t hi = (uint32_t)lane_xchg<S>((int)(uint32_t)(v >> 32));
-    const uint32_t lo = (uint32_t)lane_xchg<S>((int)(uint32_t)v);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-}
-
-// Route one token with one wave. Lane l holds experts l, l+64, ... . Each of
-// the k rounds takes the lane maxima of the selection codes, a wave-wide
-// maximum (butterfly over DPP / permlane partners, no branches), and retires
-// the winner; the picks come out in slot order. The weights are normalised in
-// double in slot order.
-//
-// Adaptive expert top-p (practical guide "colibrì 實戰指南：以純 C 引擎在消費級
-// 硬體上串流運行 744B MoE 模型", section 三 and the section 五 tuning table; the
-// pages give no formula): with 0 < p < 1 only the shortest slot-order prefix
-// whose share of the k selected scores reaches p is kept. Slot j is kept iff
-// j == 0 or the share of slots 0..j-1 is below p; the shares only grow, so the
-// kept slots are a prefix. The prefix is renormalised over itself; dropped
-// slots get index -1 and weight 0. Shares and sums are double, in slot order.
+// Route one token with one wave (the selection helpers are in common.h).
+// Lane l holds experts l, l+64, ...; all loads first (clamped ids), then
+// branch-free arithmetic.
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ lrow,
                                             const float* __restrict__ bias, int E, int k,
@@ -74,7 +45,6 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow,
     const int lane = threadIdx.x & 63;
     uint64_t code[EPL];
     float score[EPL], lv[EPL], bv[EPL];
-    // all loads first (clamped ids), then branch-free arithmetic
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = min(lane + 64 * i, E - 1);
@@ -85,58 +55,16 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow,
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         const bool valid = e < E;
-        const float s = (float)(1.0 / (1.0 + exp(-(double)lv[i])));
+        const float s = sigmoid_score(lv[i]);
         score[i] = valid ? s : 0.f;
         code[i] = valid ? selection_code(s + bv[i], e) : 0;
     }
-    double sum = 0.0;
-    double my_prev = 0.0;    // lane j (< k): sum of slots 0..j-1
-    float my_sel = 0.f;      // lane j (< k) keeps the score of slot j
-    int my_idx = 0;
-    for (int j = 0; j < k; ++j) {
-        uint64_t m = code[0];
-#pragma unroll
-        for (int i = 1; i < EPL; ++i) m = code[i] > m ? code[i] : m;
-        max_step<1>(m);
-        max_step<2>(m);
-        max_step<4>(m);
-        max_step<8>(m);
-        max_step<16>(m);
-        max_step<32>(m);
-        const uint32_t wlo = __builtin_amdgcn_readfirstlane((uint32_t)m);
-        const uint32_t whi = __builtin_amdgcn_readfirstlane((uint32_t)(m >> 32));
-        const uint64_t win = ((uint64_t)whi << 32) | wlo;
-        const int e = (int)~wlo;
-        float c = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const bool hit = code[i] == win;
-            c = hit ? score[i] : c;
-            code[i] = hit ? 0 : code[i];
-        }
-        const float s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), e & 63));
-        if (lane == j) { my_sel = s_sel; my_idx = e; my_prev = sum; }
-        sum += (double)s_sel;
-    }
-    int kept = k;
-    double ksum = sum;
-    if (topp > 0.f && topp < 1.f) {
-        const double share_before = sum == 0.0 ? (double)lane / (double)k : my_prev / sum;
-        const bool keep = lane < k && (lane == 0 || share_before < (double)topp);
-        kept = __popcll(__ballot(keep));
-        if (kept < k) {
-            // the kept prefix's sum is the running sum before slot `kept`
-            const uint64_t bits = (uint64_t)__double_as_longlong(my_prev);
-            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, kept);
-            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), kept);
-            ksum = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-        }
-    }
+    const TopK r = select_topk<EPL>(code, score, k, topp);
     if (lane < k) {
-        const bool kp = lane < kept;
-        idx_row[lane] = kp ? my_idx : -1;
-        w_row[lane] = !kp ? 0.f : (ksum == 0.0) ? (float)(1.0 / kept) : (float)((double)my_sel / ksum);
-        if (lds_idx) lds_idx[lane] = kp ? my_idx : -1;
+        const bool kp = lane < r.kept;
+        idx_row[lane] = kp ? r.my_idx : -1;
+        w_row[lane] = kp ? r.my_w : 0.f;
+        if (lds_idx) lds_idx[lane] = kp ? r.my_idx : -1;
     }
 }
 
@@ -190,6 +118,15 @@ __global__ __launch_bounds__(kRouterThreads) void router_prep_kernel(SmallRouter
             acc = block_sum_f64(acc, shd);
             if (tid == 0) a.logits_out[(int64_t)t * E + e] = (float)acc;
         }
+    }
+    // one token with the routing folded into the gate/up pass: the score and
+    // the selection code of this workgroup's expert
+    if (a.codes && (int)blockIdx.x < E && tid == 0) {
+        const int e = blockIdx.x;
+        const float l = a.router_w ? a.logits_out[e] : a.logits_in[e];
+        const float s = sigmoid_score(l);
+        a.scores[e] = s;
+        a.codes[e] = selection_code(s + (a.bias ? a.bias[e] : 0.f), e);
     }
     // digit-plane encoding of x: one quarter block per thread
     const int C = H / kBlock;
@@ -416,9 +353,10 @@ coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int
 coli_status launch_router_small(const SmallRouterArgs& a, hipStream_t stream) {
     const int C = a.H / kBlock;
     const int enc_blocks = (int)(((int64_t)a.T * C * 4 + kRouterThreads - 1) / kRouterThreads);
-    const int grid = std::max(a.router_w ? a.E : 1, enc_blocks);
+    const int grid = std::max(a.router_w || a.codes ? a.E : 1, enc_blocks);
     launch(router_prep_kernel, dim3(grid), dim3(kRouterThreads), 0, stream, a);
     COLI_CHECK_LAUNCH("router prep kernel launch");
+    if (a.codes) return COLI_OK;        // the gate/up pass routes (FusedRoute)
     const int epl = (a.E + 63) / 64;
     const dim3 one(1), blk(kRouterThreads);
     if (epl <= 1) launch(router_plan_kernel<1>, one, blk, 0, stream, a);
