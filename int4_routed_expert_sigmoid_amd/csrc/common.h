@@ -268,14 +268,6 @@ __device__ __forceinline__ uint64_t selection_code(float key, int e) {
     return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
 }
 
-template <int S>
-__device__ __forceinline__ void max_step(uint64_t& v) {
-    const uint32_t hi = (uint32_t)lane_xchg<S>((int)(uint32_t)(v >> 32));
-    const uint32_t lo = (uint32_t)lane_xchg<S>((int)(uint32_t)v);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-}
-
 // Result of select_topk in lane j < k: slot j's expert and its normalised
 // weight; kept (wave-uniform) is the number of slots kept by top-p (k without).
 struct TopK {
@@ -284,45 +276,83 @@ struct TopK {
     int kept;
 };
 
+template <int S>
+__device__ __forceinline__ uint32_t umax_step(uint32_t v) {
+    const uint32_t o = (uint32_t)lane_xchg<S>((int)v);
+    return o > v ? o : v;
+}
+
+// Wave-wide maximum of an unsigned word (butterfly over the DPP / permlane
+// partners), returned uniform.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+    v = umax_step<1>(v);
+    v = umax_step<2>(v);
+    v = umax_step<4>(v);
+    v = umax_step<8>(v);
+    v = umax_step<16>(v);
+    v = umax_step<32>(v);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
 // Top-k of one token held by one wave, lane l holding the codes and scores of
-// experts l, l+64, ... (code 0: not an expert). Each of the k rounds takes the
-// lane maxima, a wave-wide maximum (butterfly over DPP / permlane partners, no
-// branches), and retires the winner; the picks come out in slot order. With
-// 0 < topp < 1 only the shortest slot-order prefix whose share of the k
-// selected scores reaches topp is kept: slot j is kept iff j == 0 or the share
-// of slots 0..j-1 is below topp (the shares only grow, so the kept slots are a
-// prefix). Weights are the scores normalised over the kept slots; shares and
-// sums are double, in slot order.
+// experts l, l+64, ... (code 0: not an expert). Each lane first sorts its codes
+// (descending); each of the k rounds then takes the wave-wide maximum of the
+// lanes' first codes, as the maximum of their high words (the keys) and, only
+// when several lanes share it, of their low words, and the winning lane drops
+// its first code. The picks come out in slot order. With 0 < topp < 1 only the
+// shortest slot-order prefix whose share of the k selected scores reaches topp
+// is kept: slot j is kept iff j == 0 or the share of slots 0..j-1 is below topp
+// (the shares only grow, so the kept slots are a prefix). Weights are the
+// scores normalised over the kept slots; shares and sums are double, in slot
+// order.
 template <int EPL>
 __device__ __forceinline__ TopK select_topk(uint64_t (&code)[EPL], const float (&score)[EPL],
                                             int k, float topp) {
     const int lane = threadIdx.x & 63;
+    uint64_t c[EPL];
+    float sc[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        c[i] = code[i];
+        sc[i] = score[i];
+    }
+    // odd-even transposition sort, descending by code
+#pragma unroll
+    for (int pass = 0; pass < EPL; ++pass)
+#pragma unroll
+        for (int i = pass & 1; i + 1 < EPL; i += 2) {
+            const bool sw = c[i + 1] > c[i];
+            const uint64_t a = c[i], b = c[i + 1];
+            const float fa = sc[i], fb = sc[i + 1];
+            c[i] = sw ? b : a;
+            c[i + 1] = sw ? a : b;
+            sc[i] = sw ? fb : fa;
+            sc[i + 1] = sw ? fa : fb;
+        }
     double sum = 0.0;
     double my_prev = 0.0;    // lane j (< k): sum of slots 0..j-1
     float my_sel = 0.f;      // lane j (< k) keeps the score of slot j
     int my_idx = 0;
     for (int j = 0; j < k; ++j) {
-        uint64_t m = code[0];
-#pragma unroll
-        for (int i = 1; i < EPL; ++i) m = code[i] > m ? code[i] : m;
-        max_step<1>(m);
-        max_step<2>(m);
-        max_step<4>(m);
-        max_step<8>(m);
-        max_step<16>(m);
-        max_step<32>(m);
-        const uint32_t wlo = __builtin_amdgcn_readfirstlane((uint32_t)m);
-        const uint32_t whi = __builtin_amdgcn_readfirstlane((uint32_t)(m >> 32));
-        const uint64_t win = ((uint64_t)whi << 32) | wlo;
-        const int e = (int)~wlo;
-        float c = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const bool hit = code[i] == win;
-            c = hit ? score[i] : c;
-            code[i] = hit ? 0 : code[i];
+        const uint32_t hi = (uint32_t)(c[0] >> 32), lo = (uint32_t)c[0];
+        const uint32_t mh = wave_umax(hi);
+        uint64_t top = __ballot(hi == mh);
+        if (__popcll(top) > 1) {                      // equal keys: the larger low word (lower id)
+            const uint32_t ml = wave_umax(hi == mh ? lo : 0u);
+            top = __ballot(hi == mh && lo == ml);
         }
-        const float s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), e & 63));
+        const int src = (int)__builtin_ctzll(top);
+        const int e = (int)~(uint32_t)__builtin_amdgcn_readlane((int)lo, src);
+        const float s_sel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[0]), src));
+        if (lane == src) {                            // the winner drops its first code
+#pragma unroll
+            for (int i = 0; i + 1 < EPL; ++i) {
+                c[i] = c[i + 1];
+                sc[i] = sc[i + 1];
+            }
+            c[EPL - 1] = 0;
+            sc[EPL - 1] = 0.f;
+        }
         if (lane == j) { my_sel = s_sel; my_idx = e; my_prev = sum; }
         sum += (double)s_sel;
     }

@@ -161,11 +161,13 @@ __device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkI
     const int lane = threadIdx.x & 63;
     uint64_t code[EPL];
     float score[EPL];
+    const void* ptr[EPL];                            // blob pointers, loaded with the codes
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = min(lane + 64 * i, fr.E - 1);
         code[i] = fr.codes[e];
         score[i] = fr.scores[e];
+        ptr[i] = fr.table[e];
     }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) code[i] = lane + 64 * i < fr.E ? code[i] : 0;
@@ -200,7 +202,14 @@ __device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkI
         const uint64_t hit = __ballot(mine && below == rk);       // exactly one lane
         const int src = (int)__builtin_ctzll(hit);
         const int e = __builtin_amdgcn_readlane(r.my_idx, src);
-        it.blob = (const uint8_t*)fr.table[e];
+        // expert e's pointer sits in lane e % 64, register e / 64 (both uniform)
+        const void* pe = ptr[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) pe = (e >> 6) == i ? ptr[i] : pe;
+        const uint64_t pb = (uint64_t)pe;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, e & 63);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), e & 63);
+        it.blob = (const uint8_t*)(((uint64_t)hi << 32) | lo);
         it.begin = rk;
         it.count = 1;
         it.row0 = src;

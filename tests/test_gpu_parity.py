@@ -209,3 +209,17 @@ def test_layer_mtp_verify_glm_shape(coli):
 
 def test_layer_routed_scale_no_shared(coli):
     _layer_case(coli, 512, 256, 16, 4, 0, 5, 3, "zipf", rs=2.5, n_shared=0)
+
+
+@pytest.mark.parametrize("E,k,n_shared,routing,seed", [
+    (16, 4, 0, "zipf", 11),        # one token, no shared expert: items start at the first routed one
+    (200, 8, 1, "router", 12),     # expert count not a multiple of 64
+    (256, 32, 1, "zipf", 13),      # the largest top_k
+    (1000, 8, 1, "zipf", 14),      # beyond the folded routing's 256 experts: separate plan pass
+    (8, 8, 1, "router", 15),       # k == E
+])
+def test_layer_one_token_shapes(coli, E, k, n_shared, routing, seed):
+    # one-token calls route inside the gate/up pass for E <= 256; the routing
+    # published for the later passes and the caller must match the oracle exactly
+    for t in range(2):
+        _layer_case(coli, 512, 256, E, k, 0, 1, seed * 10 + t, routing, rs=1.5, n_shared=n_shared)
