@@ -599,12 +599,16 @@ def main():
     idx_d = torch.empty((n_tok, k), dtype=torch.int32, device=dev)
     ws = coli.workspace(shape, 1, coli.PATH_GEMV, dev)
 
-    def token(t):
-        coli.layer_fwd(shape, x_d[t:t + 1], table=table, shared_blob=shared, router_w=wr_d,
-                       bias=b_d, y=y_d[t:t + 1], idx_out=idx_d[t:t + 1], path=coli.PATH_GEMV,
-                       ws=ws)
-
     stream = torch.cuda.Stream()
+    # one call per token with the fixed arguments prepared once (the eager
+    # pass below then keeps the GPU busy instead of waiting on the host)
+    call = coli.LayerCall(shape, 1, ws, table=table, shared_blob=shared, router_w=wr_d, bias=b_d,
+                          path=coli.PATH_GEMV, stream=stream)
+    xp, yp, ip = x_d.data_ptr(), y_d.data_ptr(), idx_d.data_ptr()
+
+    def token(t):
+        call(xp + t * H * 4, yp + t * H * 4, ip + t * k * 4)
+
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for t in range(args.warmup):

@@ -344,6 +344,30 @@ def layer_fwd(shape: MoEShape, x, table=None, shared_blob=None, logits=None, rou
     return y
 
 
+class LayerCall:
+    """coli_moe_layer_fwd with every argument but x, y and idx_out fixed, for
+    loops of same-shaped calls (one-token decode): the argument objects are
+    built once, so each call costs little host time. Pointers are device
+    addresses (ints); the caller keeps the tensors alive."""
+
+    def __init__(self, shape: MoEShape, T, ws, table=None, shared_blob=None, logits=None,
+                 router_w=None, bias=None, cache=None, layer=0, path=PATH_AUTO, stream=None):
+        self._shape = shape.c()
+        self._fn = lib().coli_moe_layer_fwd
+        self._keep = (ws, table, shared_blob, logits, router_w, bias, cache)
+        self._args = [ctypes.byref(self._shape), None, T, _ptr(logits), _ptr(router_w),
+                      _ptr(bias), _ptr(table), _ptr(shared_blob),
+                      None if cache is None else ctypes.c_void_p(cache.handle), layer, None, None,
+                      None, path, _ptr(ws), ws.numel(), _stream(stream)]
+
+    def __call__(self, x_ptr: int, y_ptr: int, idx_ptr: int = 0):
+        a = self._args
+        a[1], a[10], a[11] = x_ptr, y_ptr, idx_ptr or None
+        rc = self._fn(*a)
+        if rc != COLI_OK:
+            _check(rc)
+
+
 def lookahead(shape: MoEShape, x, cache, layer, logits=None, router_w=None, bias=None, ws=None,
               stream=None) -> int:
     """coli_moe_lookahead: route x with `layer`'s router and prefetch its picks;

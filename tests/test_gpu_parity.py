@@ -223,3 +223,26 @@ def test_layer_one_token_shapes(coli, E, k, n_shared, routing, seed):
     # published for the later passes and the caller must match the oracle exactly
     for t in range(2):
         _layer_case(coli, 512, 256, E, k, 0, 1, seed * 10 + t, routing, rs=1.5, n_shared=n_shared)
+
+
+def test_prepared_layer_call_matches_layer_fwd(coli):
+    # the prepared-argument call used by decode loops is the same entry point
+    import torch
+    H, I, E, k = 512, 256, 16, 4
+    shape = coli.MoEShape(H, I, E, 1, k, 0)
+    ex = ExpertSet(coli, shape, seed=16)
+    wr, b = _dev(synth.router_weights(16, 0, E, H)), _dev(synth.bias(16, 0, E))
+    x = _dev(synth.activations(16, 0, 0, 3, H))
+    ws = coli.workspace(shape, 1)
+    call = coli.LayerCall(shape, 1, ws, table=ex.table, shared_blob=ex.shared_blob, router_w=wr,
+                          bias=b)
+    y = torch.empty((3, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((3, k), dtype=torch.int32, device="cuda")
+    for t in range(3):
+        call(x.data_ptr() + t * H * 4, y.data_ptr() + t * H * 4, idx.data_ptr() + t * k * 4)
+    for t in range(3):
+        i1 = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        y1 = coli.layer_fwd(shape, x[t:t + 1], table=ex.table, shared_blob=ex.shared_blob,
+                            router_w=wr, bias=b, idx_out=i1)
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0], y[t]) and torch.equal(i1[0], idx[t])
