@@ -365,6 +365,9 @@ int oracle_layer(int32_t H, int32_t I, int32_t E, int32_t k, int32_t group, floa
     double* ys = (double*)malloc(sizeof(double) * (size_t)H);
     int32_t n_unique = 0;
     if (!lg || !idx || !w || !counts || !offsets || !perm || !unique || !ya || !ys) goto done;
+    /* rows of slots without an expert (dropped by top-p) hold NaN, so that
+     * using one would show in the result */
+    for (int64_t i = 0; i < n * H; ++i) ya[i] = NAN;
 
     if (logits) memcpy(lg, logits, sizeof(float) * (size_t)T * E);
     else oracle_router_logits(wr, x, T, H, E, lg);

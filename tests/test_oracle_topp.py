@@ -43,11 +43,12 @@ def test_worked_example():
         assert np.allclose(w[0, :n], wref, rtol=0, atol=2e-6), (p, b2, w[0])
 
 
-@pytest.mark.parametrize("p,kept", [(0.1, 1), (0.2, 2), (0.3, 3), (0.55, 5), (0.7, 6),
-                                    (0.85, 7), (0.9, 8), (0.999, 8)])
+@pytest.mark.parametrize("p,kept", [(0.1, 1), (0.2, 2), (0.3, 3), (0.5, 4), (0.55, 5), (0.7, 6),
+                                    (0.75, 6), (0.85, 7), (0.9, 8), (0.999, 8)])
 def test_equal_scores_closed_form(p, kept):
-    # equal scores: the share of j+1 slots is (j+1)/k, so ceil(p k) are kept,
-    # equal keys go to the lower index, and each kept weight is 1/kept
+    # equal scores: the share of j+1 slots is (j+1)/k, so ceil(p k) are kept
+    # (a share equal to p reaches it: 0.5 and 0.75 sit on a boundary), equal
+    # keys go to the lower index, and each kept weight is 1/kept
     k, E = 8, 32
     lg = np.full((3, E), 0.25, np.float32)
     assert kept == math.ceil(p * k)
