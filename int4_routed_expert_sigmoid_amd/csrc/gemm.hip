@@ -208,18 +208,20 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     f32x16 (&acc)[2][2] = GS ? part : out;
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = out[b][0] = out[b][1] = f32x16{};
-    uint4 P0[2], P1[2], Ar0 = {}, Ar1 = {};
+    // activation rows run two k steps ahead: set k & 1 holds k step k between
+    // its load and its store to LDS at the end of step k - 1
+    uint4 P0[2], P1[2], Ar[2][2] = {};
     float F0[2] = {}, F1[2] = {};                              // gs64: scales of the staged k step
-    auto ldA = [&](int kb) {
+    auto ldA = [&](int set, int kb) {
         if (aload) {
-            Ar0 = ldg16(arow + kb * 64);
-            Ar1 = ldg16(arow + kb * 64 + 8);
+            Ar[set][0] = ldg16(arow + kb * 64);
+            Ar[set][1] = ldg16(arow + kb * 64 + 8);
         }
     };
-    auto stA = [&](int buf) {
+    auto stA = [&](int buf, int set) {
         if (aload) {
-            *reinterpret_cast<uint4*>(&sA[buf][ar][aq * 16]) = Ar0;
-            *reinterpret_cast<uint4*>(&sA[buf][ar][aq * 16 + 8]) = Ar1;
+            *reinterpret_cast<uint4*>(&sA[buf][ar][aq * 16]) = Ar[set][0];
+            *reinterpret_cast<uint4*>(&sA[buf][ar][aq * 16 + 8]) = Ar[set][1];
         }
     };
     auto ldB = [&](uint4 (&P)[2], float (&F)[2], int kb) {
@@ -262,27 +264,33 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
             }
     };
     const int last = nk - 1;
-    ldA(0);
-    stA(0);
+    ldA(0, 0);
+    ldA(1, min(1, last));
+    stA(0, 0);
     ldB(P0, F0, 0);
     ldB(P1, F1, min(1, last));
     __syncthreads();
     // pairs of k steps (buffer 0 then 1) with no exit in between, so the
-    // accumulators stay in place across iterations; then the odd last step
+    // accumulators stay in place across iterations; then the odd last step.
+    // Each step first requests the activation block two steps ahead (the
+    // empty asm keeps the compiler from sinking those loads into the MFMAs,
+    // where the store at the step's end would wait for them).
     int kb = 0;
     for (; kb + 1 < nk; kb += 2) {
         if (GS && kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
-        ldA(kb + 1);
+        ldA(0, min(kb + 2, last));
+        asm volatile("" ::: "memory");
         mma(0, P0);
         if (GS) fold(kb, F0);
         ldB(P0, F0, min(kb + 2, last));
-        stA(1);
+        stA(1, 1);
         __syncthreads();
-        ldA(min(kb + 2, last));
+        ldA(1, min(kb + 3, last));
+        asm volatile("" ::: "memory");
         mma(1, P1);
         if (GS) fold(kb + 1, F1);
         ldB(P1, F1, min(kb + 3, last));
-        stA(0);
+        stA(0, 0);
         __syncthreads();
     }
     if (kb < nk) {
