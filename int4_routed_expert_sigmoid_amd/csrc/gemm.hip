@@ -187,7 +187,7 @@ __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& r
 // of down) and the tile's token halves (the second only when TWO). The 64 x 64
 // activation block of each k step is staged once per workgroup in LDS (double
 // buffered, one barrier per k step) and shared by the 4 waves; weight nibbles
-// go straight from HBM to registers, two k steps ahead. With GS, every k step
+// go straight from HBM to registers, two or four k steps ahead. With GS, every k step
 // is one 64-column scale group, folded into `out` with its scale and its
 // 136 * S correction; otherwise `out` holds the raw sums.
 constexpr int kLdsRow = 72;          // bf16 per LDS activation row (64 + 8 pad: conflict-free 16-B reads)
@@ -208,10 +208,15 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     f32x16 (&acc)[2][2] = GS ? part : out;
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = out[b][0] = out[b][1] = f32x16{};
-    // activation rows run two k steps ahead: set k & 1 holds k step k between
-    // its load and its store to LDS at the end of step k - 1
-    uint4 P0[2], P1[2], Ar[2][2] = {};
-    float F0[2] = {}, F1[2] = {};                              // gs64: scales of the staged k step
+    // activation rows run kA k steps ahead (2 with per-row scales, 1 with
+    // gs64): set k & 1 holds k step k between its load and its store to LDS
+    // at the end of step k - 1
+    constexpr int kA = GS ? 1 : 2;                             // (one set with kA == 1)
+    // weight nibbles run kD k steps ahead (4 with per-row scales; 2 with gs64,
+    // whose group sums and scale folds already fill the register file)
+    constexpr int kD = GS ? 2 : 4;
+    uint4 P[kD][2], Ar[2][2] = {};
+    float F[kD][2] = {};                                       // gs64: scales of the staged k steps
     auto ldA = [&](int set, int kb) {
         if (aload) {
             Ar[set][0] = ldg16(arow + kb * 64);
@@ -264,40 +269,49 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
             }
     };
     const int last = nk - 1;
+    // one k step (k & 1 == buf): request the activation block kA steps
+    // ahead, multiply the current one with its weight set, refill that set kD
+    // steps ahead, store the next activation block
+    auto step = [&](int k, int buf, uint4 (&Pk)[2], float (&Fk)[2]) {
+        if (GS && k % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, k);
+        ldA(kA == 2 ? buf : 0, min(k + kA, last));     // (k + 2) & 1 == buf
+        if (kA == 2) asm volatile("" ::: "memory");
+        mma(buf, Pk);
+        if (GS) fold(k, Fk);
+        ldB(Pk, Fk, min(k + kD, last));
+        stA(buf ^ 1, kA == 2 ? buf ^ 1 : 0);
+        __syncthreads();
+    };
     ldA(0, 0);
-    ldA(1, min(1, last));
+    if (kA == 2) ldA(1, min(1, last));
     stA(0, 0);
-    ldB(P0, F0, 0);
-    ldB(P1, F1, min(1, last));
+#pragma unroll
+    for (int d = 0; d < kD; ++d) ldB(P[d], F[d], min(d, last));
     __syncthreads();
-    // pairs of k steps (buffer 0 then 1) with no exit in between, so the
-    // accumulators stay in place across iterations; then the odd last step.
-    // Each step first requests the activation block two steps ahead (the
-    // empty asm keeps the compiler from sinking those loads into the MFMAs,
-    // where the store at the step's end would wait for them).
+    if constexpr (GS) {
+        // pairs of k steps, then the odd last step (no loads past it)
+        int kb = 0;
+        for (; kb + 1 < nk; kb += 2) {
+            step(kb, 0, P[0], F[0]);
+            step(kb + 1, 1, P[1], F[1]);
+        }
+        if (kb < nk) {
+            if (kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
+            mma(0, P[0]);
+            fold(kb, F[0]);
+        }
+        return;
+    }
+    // groups of kD k steps with no exit in between, so the accumulators stay
+    // in place across iterations; then the remaining steps
     int kb = 0;
-    for (; kb + 1 < nk; kb += 2) {
-        if (GS && kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
-        ldA(0, min(kb + 2, last));
-        asm volatile("" ::: "memory");
-        mma(0, P0);
-        if (GS) fold(kb, F0);
-        ldB(P0, F0, min(kb + 2, last));
-        stA(1, 1);
-        __syncthreads();
-        ldA(1, min(kb + 3, last));
-        asm volatile("" ::: "memory");
-        mma(1, P1);
-        if (GS) fold(kb + 1, F1);
-        ldB(P1, F1, min(kb + 3, last));
-        stA(0, 0);
-        __syncthreads();
+    for (; kb + kD - 1 < nk; kb += kD) {
+#pragma unroll
+        for (int d = 0; d < kD; ++d) step(kb + d, d & 1, P[d], F[d]);
     }
-    if (kb < nk) {
-        if (GS && kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
-        mma(0, P0);
-        if (GS) fold(kb, F0);
-    }
+#pragma unroll
+    for (int d = 0; d < kD - 1; ++d)
+        if (kb + d < nk) step(kb + d, d & 1, P[d], F[d]);
 }
 
 // ----------------------------------------------------------------- gate/up
