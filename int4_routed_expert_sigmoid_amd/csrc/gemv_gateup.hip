@@ -149,16 +149,26 @@ __device__ __forceinline__ void gateup_body(
 }
 
 
-// Work item `item` of a one-token call from the folded routing (FusedRoute):
-// every wave selects the top-k from the selection codes (select_topk), ranks
-// the kept picks by expert id (the work list order: shared expert first, then
-// the kept experts by id) and takes its own; workgroup (0, 0) publishes the
-// routing, the slot-list rows and the item count, and each (0, item)
-// workgroup its item, for the passes that follow. False: no such item (a slot
-// dropped by top-p).
+// Work item `item` of a one-token call from the folded routing (FusedRoute).
+// The shared expert's workgroups need no routing and start on their weights
+// at once. Every other wave selects the top-k from the selection codes
+// (select_topk), ranks the kept picks by expert id (the work list order:
+// shared expert first, then the kept experts by id) and takes its own;
+// workgroup (0, first routed item) publishes the routing, the slot-list rows
+// and the item count, and each (0, item) workgroup its item, for the passes
+// that follow. False: no such item (a slot dropped by top-p).
 __device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkItem& it) {
     constexpr int EPL = kFusedMaxExperts / 64;
     const int lane = threadIdx.x & 63;
+    const int k = fr.k, base = fr.shared ? 1 : 0;
+    if (item < base) {
+        it.blob = (const uint8_t*)fr.shared;
+        it.begin = k;
+        it.count = 1;
+        it.row0 = k;
+        if (blockIdx.x == 0 && threadIdx.x == 0) fr.items[item] = it;
+        return true;
+    }
     uint64_t code[EPL];
     float score[EPL];
     const void* ptr[EPL];                            // blob pointers, loaded with the codes
@@ -171,12 +181,12 @@ __device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkI
     }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) code[i] = lane + 64 * i < fr.E ? code[i] : 0;
-    const TopK r = select_topk<EPL>(code, score, fr.k, fr.topp);
-    const int k = fr.k, kept = r.kept, base = fr.shared ? 1 : 0;
+    const TopK r = select_topk<EPL>(code, score, k, fr.topp);
+    const int kept = r.kept;
     const bool mine = lane < kept;
     int below = 0;                                   // rank of this lane's pick by expert id
     for (int j = 0; j < kept; ++j) below += __builtin_amdgcn_readlane(r.my_idx, j) < r.my_idx;
-    if (blockIdx.x == 0 && item == 0 && threadIdx.x < 64) {
+    if (blockIdx.x == 0 && item == base && threadIdx.x < 64) {
         if (lane < k) {
             fr.idx[lane] = mine ? r.my_idx : -1;
             fr.w[lane] = mine ? r.my_w : 0.f;
@@ -191,12 +201,7 @@ __device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkI
             *fr.n_items = base + kept;
         }
     }
-    if (item < base) {
-        it.blob = (const uint8_t*)fr.shared;
-        it.begin = k;
-        it.count = 1;
-        it.row0 = k;
-    } else {
+    {
         const int rk = item - base;
         if (rk >= kept) return false;
         const uint64_t hit = __ballot(mine && below == rk);       // exactly one lane

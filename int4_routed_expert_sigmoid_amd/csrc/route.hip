@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 
 // ----------------------------------------------------- router, small T
 // Two launches for batches of up to kSmallT tokens. The first spreads over
-// many workgroups: each computes the logits of one expert (f32 router rows,
-// double sums) and encodes a share of the activations into digit planes.
+// many workgroups: one per expert computes its logits (f32 router rows,
+// double sums), the others encode the activations into digit planes.
 // The second is one workgroup: it routes the tokens, forms the batch union
 // (stable counting sort) and writes the FFN work list.
 constexpr int kRouterThreads = 256;
@@ -97,40 +97,64 @@ __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
     return sh[0] + sh[1] + sh[2] + sh[3];
 }
 
+// Workgroups [0, NR) (NR = E when there are router rows or selection codes to
+// write, else 0): one expert's logits for every token, then, for one token
+// with the routing folded into the gate/up pass, its score and selection
+// code. Workgroups from NR on: the digit-plane encoding of x, one quarter
+// block per thread.
 __global__ __launch_bounds__(kRouterThreads) void router_prep_kernel(SmallRouterArgs a) {
     __shared__ double shd[4];
     const int tid = threadIdx.x;
     const int T = a.T, E = a.E, H = a.H;
-    if (a.router_w && (int)blockIdx.x < E) {
+    const int NR = a.router_w || a.codes ? E : 0;
+    if ((int)blockIdx.x < NR) {
         const int e = blockIdx.x;
-        const float* wrow = a.router_w + (int64_t)e * H;
-        for (int t = 0; t < T; ++t) {
-            const float* xrow = a.x + (int64_t)t * H;
-            double acc = 0.0;
-            for (int j = tid * 4; j < H; j += kRouterThreads * 4) {
-                const float4 wv = *reinterpret_cast<const float4*>(wrow + j);
-                const float4 xv = *reinterpret_cast<const float4*>(xrow + j);
-                acc = fma((double)wv.x, (double)xv.x, acc);
-                acc = fma((double)wv.y, (double)xv.y, acc);
-                acc = fma((double)wv.z, (double)xv.z, acc);
-                acc = fma((double)wv.w, (double)xv.w, acc);
+        // the bias and given logit of this expert, requested before the row's loads
+        const float bias_e = a.codes && a.bias ? a.bias[e] : 0.f;
+        const float logit_in = a.codes && !a.router_w ? a.logits_in[e] : 0.f;
+        float logit0 = 0.f;                         // token 0's logit (thread 0)
+        if (a.router_w) {
+            const float* wrow = a.router_w + (int64_t)e * H;
+            constexpr int kStep = kRouterThreads * 4, kU = 8;   // floats per pass, passes per load group
+            for (int t = 0; t < T; ++t) {
+                const float* xrow = a.x + (int64_t)t * H;
+                double acc = 0.0;
+                // kU passes' loads in flight at once (clamped addresses, masked
+                // values), then the f64 FMAs in column order
+                for (int j0 = tid * 4; j0 < H; j0 += kU * kStep) {
+                    float4 wv[kU], xv[kU];
+#pragma unroll
+                    for (int u = 0; u < kU; ++u) {
+                        const int j = min(j0 + u * kStep, H - 4);
+                        wv[u] = *reinterpret_cast<const float4*>(wrow + j);
+                        xv[u] = *reinterpret_cast<const float4*>(xrow + j);
+                    }
+#pragma unroll
+                    for (int u = 0; u < kU; ++u) {
+                        if (j0 + u * kStep < H) {
+                            acc = fma((double)wv[u].x, (double)xv[u].x, acc);
+                            acc = fma((double)wv[u].y, (double)xv[u].y, acc);
+                            acc = fma((double)wv[u].z, (double)xv[u].z, acc);
+                            acc = fma((double)wv[u].w, (double)xv[u].w, acc);
+                        }
+                    }
+                }
+                acc = block_sum_f64(acc, shd);
+                if (tid == 0) {
+                    a.logits_out[(int64_t)t * E + e] = (float)acc;
+                    if (t == 0) logit0 = (float)acc;
+                }
             }
-            acc = block_sum_f64(acc, shd);
-            if (tid == 0) a.logits_out[(int64_t)t * E + e] = (float)acc;
         }
+        if (a.codes && tid == 0) {
+            const float s = sigmoid_score(a.router_w ? logit0 : logit_in);
+            a.scores[e] = s;
+            a.codes[e] = selection_code(s + bias_e, e);
+        }
+        return;
     }
-    // one token with the routing folded into the gate/up pass: the score and
-    // the selection code of this workgroup's expert
-    if (a.codes && (int)blockIdx.x < E && tid == 0) {
-        const int e = blockIdx.x;
-        const float l = a.router_w ? a.logits_out[e] : a.logits_in[e];
-        const float s = sigmoid_score(l);
-        a.scores[e] = s;
-        a.codes[e] = selection_code(s + (a.bias ? a.bias[e] : 0.f), e);
-    }
-    // digit-plane encoding of x: one quarter block per thread
     const int C = H / kBlock;
-    const int64_t g = (int64_t)blockIdx.x * kRouterThreads + tid;
+    const int64_t g = (int64_t)(blockIdx.x - NR) * kRouterThreads + tid;
     const int q = (int)(g & 3);
     const int64_t blk = g >> 2;
     const int64_t row = blk / C;
@@ -353,7 +377,7 @@ coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int
 coli_status launch_router_small(const SmallRouterArgs& a, hipStream_t stream) {
     const int C = a.H / kBlock;
     const int enc_blocks = (int)(((int64_t)a.T * C * 4 + kRouterThreads - 1) / kRouterThreads);
-    const int grid = std::max(a.router_w || a.codes ? a.E : 1, enc_blocks);
+    const int grid = (a.router_w || a.codes ? a.E : 0) + enc_blocks;
     launch(router_prep_kernel, dim3(grid), dim3(kRouterThreads), 0, stream, a);
     COLI_CHECK_LAUNCH("router prep kernel launch");
     if (a.codes) return COLI_OK;        // the gate/up pass routes (FusedRoute)
