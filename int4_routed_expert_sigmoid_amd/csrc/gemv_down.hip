@@ -45,8 +45,9 @@ __device__ __forceinline__ void down_body(
     // the token loop is uniform over the workgroup (it holds barriers); waves
     // past the last row only help to form h
     int rowwin = 0;                                      // output rows of a 64-token window, one per lane
-    for (int m0 = 0; m0 < it.count; m0 += MT) {
-        const int mc = min(MT, it.count - m0);
+    const int count = ENC ? 1 : it.count;             // one-token items: a constant trip count
+    for (int m0 = 0; m0 < count; m0 += MT) {
+        const int mc = ENC ? 1 : min(MT, count - m0);
         if (!ENC && (m0 & 63) == 0) rowwin = rows_out[it.begin + min(m0 + lane, it.count - 1)];
         WBlock<W8> wbuf[PD][LB][NCH];
         float fbuf[PD][LB][NCH];
@@ -57,35 +58,55 @@ __device__ __forceinline__ void down_body(
 #pragma unroll
                 for (int j = 0; j < NCH; ++j) {
                     // unconditional loads: lanes past the row end re-read its last
-                    // block; their activation scales are zero
+                    // block; their products are masked
                     const int ch = min(lane + 64 * j, CI - 1);
                     wv[r][j] = load_wblock<W8>(dq + row * rowbytes, ch);
                     if (GS) fv[r][j] = ldg_f32(dsc + (size_t)row * gpr + (ch >> 1));
                 }
             }
         };
-#pragma unroll
-        for (int b = 0; b < PD - 1; ++b) load(wbuf[b], fbuf[b], b);
-        asm volatile("" ::: "memory");    // keep these loads ahead of the barrier below
         // one token: h = silu(g) * u, one 8-element quarter of a block per
         // thread (the quarters of a block sit in 4 adjacent lanes, as the
         // encoder's shuffles require); every lane runs the encoder. Larger
         // batches read the blocks that the activation pass encoded once.
+        // Load order: the first pass's g and u, the per-row scales of the
+        // wave's rows (lane l: row rbase + l % 16), then the weights. Load
+        // counters retire in order, so forming h then waits for g and u alone,
+        // and no scale load sits behind the weights where it is used.
         const int nq = ENC ? CI * 4 : 0;
-        for (int i0 = 0; i0 < nq; i0 += 256) {
-            const int i = i0 + (int)threadIdx.x, ic = min(i, nq - 1);
-            const int m = ic / (CI * 4), rem = ic % (CI * 4), blk = rem >> 2, q = rem & 3;
-            const int outr = it.row0;                    // one token per item here
-            const float* gp = gu + (size_t)outr * 2 * I + blk * kBlock + q * 8;
+        float gq[8], uq[8];
+        auto load_gu = [&](int i0) {
+            const int ic = min(i0 + (int)threadIdx.x, nq - 1);
+            const float* gp = gu + (size_t)it.row0 * 2 * I + (ic >> 2) * kBlock + (ic & 3) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gq[e] = gp[e];
+                uq[e] = gp[I + e];
+            }
+        };
+        auto encode_pass = [&](int i0) {
+            const int i = i0 + (int)threadIdx.x, ic = min(i, nq - 1), blk = ic >> 2, q = ic & 3;
             float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = gp[e] * gp[I + e];          // silu(g) * u
+            for (int e = 0; e < 8; ++e) v[e] = gq[e] * uq[e];          // silu(g) * u
             uint32_t words[kPlanes];
             const float sc = encode_quarter(v, words);
             if (i < nq) {
 #pragma unroll
-                for (int p = 0; p < kPlanes; ++p) s_words[(m * CI + blk) * kWordsPerBlock + p * 4 + q] = words[p];
-                if (q == 0) s_scale[m * CI + blk] = m < mc ? sc : 0.f;
+                for (int p = 0; p < kPlanes; ++p) s_words[blk * kWordsPerBlock + p * 4 + q] = words[p];
+                if (q == 0) s_scale[blk] = sc;
+            }
+        };
+        if constexpr (ENC) load_gu(0);
+        const float rsc = GS ? 1.f : ldg_f32(dsc + min(rbase + (lane % kDownRowsPerWave), H - 1));
+#pragma unroll
+        for (int b = 0; b < PD - 1; ++b) load(wbuf[b], fbuf[b], b);
+        asm volatile("" ::: "memory");    // keep these loads ahead of the waits below
+        if constexpr (ENC) {
+            encode_pass(0);
+            for (int i0 = 256; i0 < nq; i0 += 256) {
+                load_gu(i0);
+                encode_pass(i0);
             }
         }
         __syncthreads();
@@ -123,9 +144,11 @@ __device__ __forceinline__ void down_body(
                         if (m < mc) {
 #pragma unroll
                             for (int j = 0; j < NCH; ++j) {
-                                const float x = lane + 64 * j < CI ? hs[m][j] : 0.f;
-                                const float f = GS ? x * fv[r][j] : x;
-                                acc += (float)wblock_dot<W8>(wv[r][j], hp[m][j], hsum[m][j]) * f;
+                                // blocks past the row end add nothing (mask on the product,
+                                // so that it is not hoisted with a wait for hs)
+                                const float f = GS ? hs[m][j] * fv[r][j] : hs[m][j];
+                                const float t = (float)wblock_dot<W8>(wv[r][j], hp[m][j], hsum[m][j]) * f;
+                                acc += lane + 64 * j < CI ? t : 0.f;
                             }
                         }
                         part[r * MT + m] = acc;
@@ -134,26 +157,40 @@ __device__ __forceinline__ void down_body(
                 const int vi = lane >> SH;
                 const int r = vi / MT, m = vi % MT;
                 const int row = rbase + batch * LB + r;
-                if ((lane & ((1 << SH) - 1)) == 0 && m < mc && row < H) {
-                    const int outr = rows_out[it.begin + m0 + m];
-                    y_rows[(size_t)outr * H + row] = v * (GS ? 1.f : ldg_f32(dsc + row));
-                }
+                // scale and output row from registers (a global load here would
+                // wait for the prefetched weights); a one-token item's output
+                // row is its gu row
+                const float sc = GS ? 1.f : __shfl(rsc, batch * LB + r);
+                const int outr = ENC ? it.row0 : __shfl(rowwin, (m0 & 63) + m);
+                if ((lane & ((1 << SH) - 1)) == 0 && m < mc && row < H)
+                    y_rows[(size_t)outr * H + row] = v * sc;
             };
+            // each batch's loads are issued before the wait for an earlier one;
+            // the empty asm statements keep the scheduler from moving a wait
+            // above them, and no load is left under a runtime condition (the
+            // wait-count pass would merge it by draining the batch in flight)
             if constexpr (PD == 3) {
 #pragma unroll
                 for (int b = 0; b < NBT; ++b) {
                     if (b + 2 < NBT) load(wbuf[(b + 2) % 3], fbuf[(b + 2) % 3], b + 2);
+                    asm volatile("" ::: "memory");
                     compute(wbuf[b % 3], fbuf[b % 3], b);
                 }
             } else {
                 static_assert(NBT % 2 == 0, "batch count must be even");
 #pragma unroll 1
-                for (int b = 0; b < NBT; b += 2) {
+                for (int b = 0; b < NBT - 2; b += 2) {
                     load(wbuf[1], fbuf[1], b + 1);
+                    asm volatile("" ::: "memory");
                     compute(wbuf[0], fbuf[0], b);
-                    if (b + 2 < NBT) load(wbuf[0], fbuf[0], b + 2);
+                    load(wbuf[0], fbuf[0], b + 2);
+                    asm volatile("" ::: "memory");
                     compute(wbuf[1], fbuf[1], b + 1);
                 }
+                load(wbuf[1], fbuf[1], NBT - 1);
+                asm volatile("" ::: "memory");
+                compute(wbuf[0], fbuf[0], NBT - 2);
+                compute(wbuf[1], fbuf[1], NBT - 1);
             }
         }
         __syncthreads();

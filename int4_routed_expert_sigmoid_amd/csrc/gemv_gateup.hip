@@ -50,10 +50,28 @@ __device__ __forceinline__ void gateup_body(
 
     float (*red)[kBlock * NM * MT] = reinterpret_cast<float (*)[kBlock * NM * MT]>(red_raw);
 
-    int tokwin = 0;                                   // tokens of a 64-token window, one per lane
-    for (int m0 = 0; m0 < it.count; m0 += MT) {
-        const int mc = min(MT, it.count - m0);
-        if (!ONE && (m0 & 63) == 0) tokwin = rows_tok[it.begin + min(m0 + lane, it.count - 1)];
+    // the per-row scales this thread applies in the epilogue, requested before
+    // the weights: loaded where they are used, they would wait for every load
+    // issued before them
+    constexpr int NOUT = kBlock * NM * MT, NIT = (NOUT + 64 * W - 1) / (64 * W);
+    float rsc[NIT];
+#pragma unroll
+    for (int q = 0; q < NIT; ++q) {
+        const int i = min(tid + q * 64 * W, NOUT - 1);
+        const int mt = (i / MT) % NM, r = i / (MT * NM);
+        rsc[q] = GS ? 1.f : ldg_f32(wsc[mt] + r0 + r);
+    }
+
+    int tokwin = 0, outwin = 0;                       // tokens and output rows of a 64-token window, one per lane
+    // a one-token item runs the loop once (a constant trip count, so that the
+    // first weight loads lead the activation loads)
+    const int count = ONE ? 1 : it.count;
+    for (int m0 = 0; m0 < count; m0 += MT) {
+        const int mc = ONE ? 1 : min(MT, count - m0);
+        if (!ONE && (m0 & 63) == 0) {
+            tokwin = rows_tok[it.begin + min(m0 + lane, it.count - 1)];
+            outwin = rows_out[it.begin + min(m0 + lane, it.count - 1)];
+        }
         // two register sets of weights; the first batch is requested before
         // the activation planes
         WBlock<W8> wa[LB][NM][NCH], wb[LB][NM][NCH];
@@ -68,7 +86,7 @@ __device__ __forceinline__ void gateup_body(
                     for (int j = 0; j < NCH; ++j) {
                         // unconditional loads (no branch for the wait-count pass to
                         // merge at): threads past the row end re-read its last
-                        // block, and their activation scales are zero
+                        // block, and their products are masked
                         const int ch = min(tid + 64 * W * j, C - 1);
                         wv[r][mt][j] = load_wblock<W8>(wq[mt] + row * rowbytes, ch);
                         if (GS) fv[r][mt][j] = ldg_f32(wsc[mt] + (size_t)row * gpr + (ch >> 1));
@@ -93,6 +111,11 @@ __device__ __forceinline__ void gateup_body(
                 xs[m][j] = xscale[(size_t)tok * C + chc];   // validity applied where it is used
             }
         }
+        // the second batch is requested before anything waits for the first
+        // (load counters retire in order); the empty asm statements keep the
+        // scheduler from moving a wait above the next batch's loads
+        load(wb, fb, 1);
+        asm volatile("" ::: "memory");
         int xsum[MT][NCH];                                // int8 weights: sum of each block's X
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -111,9 +134,12 @@ __device__ __forceinline__ void gateup_body(
                         if (m < mc) {
 #pragma unroll
                             for (int j = 0; j < NCH; ++j) {
-                                const float x = tid + 64 * W * j < C ? xs[m][j] : 0.f;
-                                const float f = GS ? x * fv[r][mt][j] : x;
-                                acc += (float)wblock_dot<W8>(wv[r][mt][j], xp[m][j], xsum[m][j]) * f;
+                                // blocks past the row end add nothing; the mask sits on the
+                                // product, so it is not hoisted (with a wait for xs) above
+                                // the first weight loads
+                                const float f = GS ? xs[m][j] * fv[r][mt][j] : xs[m][j];
+                                const float t = (float)wblock_dot<W8>(wv[r][mt][j], xp[m][j], xsum[m][j]) * f;
+                                acc += tid + 64 * W * j < C ? t : 0.f;
                             }
                         }
                         part[(r * NM + mt) * MT + m] = acc;
@@ -122,25 +148,39 @@ __device__ __forceinline__ void gateup_body(
             if ((lane & ((1 << SH) - 1)) == 0)
                 red[wave][batch * NV + (lane >> SH)] = v;
         };
+        // the last pair peeled: no load under a condition, which the wait-count
+        // pass would merge by draining the batch in flight
 #pragma unroll 1
-        for (int b = 0; b < NBT; b += 2) {
-            load(wb, fb, b + 1);
+        for (int b = 0; b < NBT - 2; b += 2) {
             compute(wa, fa, b);
-            if (b + 2 < NBT) load(wa, fa, b + 2);
+            load(wa, fa, b + 2);
+            asm volatile("" ::: "memory");
             compute(wb, fb, b + 1);
+            load(wb, fb, b + 3);
+            asm volatile("" ::: "memory");
         }
+        compute(wa, fa, NBT - 2);
+        compute(wb, fb, NBT - 1);
         __syncthreads();
-        for (int i = tid; i < kBlock * NM * MT; i += 64 * W) {
+        // output rows of this chunk's tokens (one-token items carry theirs:
+        // rows_out may still be in flight when the routing is folded in)
+        int outs[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            outs[m] = ONE ? it.row0 : __builtin_amdgcn_readlane(outwin, (m0 & 63) + m);
+#pragma unroll
+        for (int q = 0; q < NIT; ++q) {
+            const int i = tid + q * 64 * W;
             const int m = i % MT, mt = (i / MT) % NM, r = i / (MT * NM);
-            if (m < mc) {
+            if (i < NOUT && m < mc) {
                 float v = 0.f;
 #pragma unroll
                 for (int w = 0; w < W; ++w) v += red[w][i];
-                if (!GS) v *= ldg_f32((mt ? wsc[NM - 1] : wsc[0]) + r0 + r);
+                v *= rsc[q];
                 if (mat0 + mt == 0) v = v / (1.f + expf(-v));          // gate: store silu(g)
-                // one-token items carry their output row (rows_out may still be
-                // in flight when the routing is folded into this pass)
-                const int out = ONE ? it.row0 : rows_out[it.begin + m0 + m];
+                int out = outs[0];
+#pragma unroll
+                for (int mm = 1; mm < MT; ++mm) out = m == mm ? outs[mm] : out;
                 gu[((size_t)out * 2 + mat0 + mt) * I + r0 + r] = v;
             }
         }
