@@ -209,13 +209,19 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = out[b][0] = out[b][1] = f32x16{};
     // activation rows run kA k steps ahead (2 with per-row scales, 1 with
-    // gs64): set k & 1 holds k step k between its load and its store to LDS
-    // at the end of step k - 1
-    constexpr int kA = GS ? 1 : 2;                             // (one set with kA == 1)
+    // gs64): register set k % kA holds k step k between its load and its
+    // store to LDS at the end of step k - 1
+    constexpr int kA = GS ? 1 : 2;
     // weight nibbles run kD k steps ahead (4 with per-row scales; 2 with gs64,
-    // whose group sums and scale folds already fill the register file)
+    // whose group sums and scale folds already fill the register file). With
+    // per-row scales they are requested kGrp k steps at a time: one k step
+    // reads 32 bytes of each weight row, so kGrp steps issued back to back
+    // read 32 * kGrp consecutive bytes of it while its cache line is in
+    // flight, instead of fetching the line again for every step.
     constexpr int kD = GS ? 2 : 4;
-    uint4 P[kD][2], Ar[2][2] = {};
+    constexpr int kGrp = GS ? 1 : 2;
+    static_assert(kD % kGrp == 0, "load groups must tile the weight sets");
+    uint4 P[kD][2], Ar[kA][2] = {};
     float F[kD][2] = {};                                       // gs64: scales of the staged k steps
     auto ldA = [&](int set, int kb) {
         if (aload) {
@@ -272,18 +278,19 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     // one k step (k & 1 == buf): request the activation block kA steps
     // ahead, multiply the current one with its weight set, refill that set kD
     // steps ahead, store the next activation block
-    auto step = [&](int k, int buf, uint4 (&Pk)[2], float (&Fk)[2]) {
+    auto step = [&](int k, int buf, uint4 (&Pk)[2], float (&Fk)[2], auto&& loadB) {
         if (GS && k % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, k);
-        ldA(kA == 2 ? buf : 0, min(k + kA, last));     // (k + 2) & 1 == buf
-        if (kA == 2) asm volatile("" ::: "memory");
+        ldA(k % kA, min(k + kA, last));
+        if (kA >= 2) asm volatile("" ::: "memory");
         mma(buf, Pk);
         if (GS) fold(k, Fk);
-        ldB(Pk, Fk, min(k + kD, last));
-        stA(buf ^ 1, kA == 2 ? buf ^ 1 : 0);
+        loadB();
+        stA(buf ^ 1, (k + 1) % kA);
         __syncthreads();
     };
     ldA(0, 0);
-    if (kA == 2) ldA(1, min(1, last));
+#pragma unroll
+    for (int j = 1; j < kA; ++j) ldA(j, min(j, last));
     stA(0, 0);
 #pragma unroll
     for (int d = 0; d < kD; ++d) ldB(P[d], F[d], min(d, last));
@@ -292,8 +299,8 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
         // pairs of k steps, then the odd last step (no loads past it)
         int kb = 0;
         for (; kb + 1 < nk; kb += 2) {
-            step(kb, 0, P[0], F[0]);
-            step(kb + 1, 1, P[1], F[1]);
+            step(kb, 0, P[0], F[0], [&] { ldB(P[0], F[0], min(kb + kD, last)); });
+            step(kb + 1, 1, P[1], F[1], [&] { ldB(P[1], F[1], min(kb + 1 + kD, last)); });
         }
         if (kb < nk) {
             if (kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
@@ -302,16 +309,29 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
         }
         return;
     }
-    // groups of kD k steps with no exit in between, so the accumulators stay
-    // in place across iterations; then the remaining steps
-    int kb = 0;
-    for (; kb + kD - 1 < nk; kb += kD) {
+    // groups of U k steps (U = max(kD, kA), so that every register set index
+    // is a constant) with no exit in between, so the accumulators stay in
+    // place across iterations; then the remaining steps. The last step of each
+    // load group refills the group's weight sets with the k steps kD ahead of
+    // them (clamped to the last step near the end).
+    constexpr int U = kD > kA ? kD : kA;
+    auto refill = [&](int k, int d, bool tail) {
+        const int dd = d % kD, base = k - dd;
+        if ((dd + 1) % kGrp == 0) {
 #pragma unroll
-        for (int d = 0; d < kD; ++d) step(kb + d, d & 1, P[d], F[d]);
+            for (int j = dd + 1 - kGrp; j <= dd; ++j)
+                if (!tail || base + j + kD <= last) ldB(P[j], F[j], min(base + j + kD, last));
+        }
+    };
+    int kb = 0;
+    for (; kb + U - 1 < nk; kb += U) {
+#pragma unroll
+        for (int d = 0; d < U; ++d)
+            step(kb + d, d & 1, P[d % kD], F[d % kD], [&] { refill(kb + d, d, false); });
     }
 #pragma unroll
-    for (int d = 0; d < kD - 1; ++d)
-        if (kb + d < nk) step(kb + d, d & 1, P[d], F[d]);
+    for (int d = 0; d < U - 1; ++d)
+        if (kb + d < nk) step(kb + d, d & 1, P[d % kD], F[d % kD], [&] { refill(kb + d, d, true); });
 }
 
 // ----------------------------------------------------------------- gate/up
