@@ -30,6 +30,9 @@ def _dev(a):
 @pytest.mark.parametrize("H,I,group,T,k,E", [
     (256, 128, 0, 4, 2, 8), (256, 128, 64, 4, 2, 8), (512, 256, 0, 1, 8, 16),
     (192, 320, 64, 9, 3, 6), (1024, 512, 0, 100, 4, 8), (512, 384, 64, 130, 6, 12),
+    # experts with 128-token tiles and remainders of every size; a half-live
+    # last row block (I = 320) and fewer k steps than one unrolled group (H = 192)
+    (512, 256, 0, 300, 4, 8), (192, 320, 0, 700, 3, 6),
 ])
 def test_expert_ffn_mfma(coli, H, I, group, T, k, E):
     import torch
