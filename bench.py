@@ -199,6 +199,8 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
     flops_gu = 2.0 * 2 * H * I * (T * k + T)
     flops_dn = 2.0 * H * I * (T * k + T)
     gu_s, dn_s = ms_gu / max(1, n_gu) / 1e3, ms_dn / max(1, n_dn) / 1e3
+    used = int((counts > 0).sum()) + shape.n_shared           # experts whose weights the call reads
+    weight_bytes = used * coli.blob_layout(shape)[1]
     return {
         "workload": "prefill, 2048 tokens, Zipf(1.1) + 10% uniform routing, same layer",
         "tokens_per_s": round(T / dt, 1),
@@ -210,6 +212,12 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
         "gemm_frac_of_bf16_peak": round((flops_gu + flops_dn) / (gu_s + dn_s) / 1e12 / BF16_PEAK_TFLOPS, 4) if n_gu else None,
         "algorithmic_tflop": round((flops_gu + flops_dn) / 1e12, 4),
         "experts_used": int((counts > 0).sum()),
+        # routed experts by tokens routed to them (M), bins [lo, hi)
+        "tokens_per_expert_histogram": {f"{lo}-{hi - 1}": int(((counts >= lo) & (counts < hi)).sum())
+                                        for lo, hi in ((1, 9), (9, 17), (17, 33), (33, 65), (65, 129),
+                                                       (129, 257), (257, 513), (513, T + 1))},
+        # every resident weight byte read once per call, over the two GEMMs' time
+        "weights_GBps_over_gemm_time": round(weight_bytes / (gu_s + dn_s) / 1e9, 1) if n_gu else None,
         "tokens_per_expert_max": int(counts.max()),
         "tokens_per_expert_median": float(np.median(counts[counts > 0])),
         "tokens_per_expert_min": int(counts[counts > 0].min()),
