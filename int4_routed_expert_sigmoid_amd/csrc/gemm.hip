@@ -191,6 +191,15 @@ __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& r
 // is one 64-column scale group, folded into `out` with its scale and its
 // 136 * S correction; otherwise `out` holds the raw sums.
 constexpr int kLdsRow = 72;          // bf16 per LDS activation row (64 + 8 pad: conflict-free 16-B reads)
+constexpr int kSB = 4 * 2 * 32 * 128;  // bytes of the per-wave weight-line regions of a workgroup
+
+// Lane `src`'s pointer (a 64-bit value through two 32-bit shuffles).
+__device__ __forceinline__ const uint8_t* shfl_ptr(const uint8_t* p, int src) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
 
 template <bool GS, bool TWO>
 __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int nk,
@@ -199,7 +208,7 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
                                          const float* __restrict__ sums, const int32_t* __restrict__ rows,
                                          const WorkItem& it, int m0,
                                          uint16_t (*sA)[kTileM][kLdsRow], float* s_cs,
-                                         f32x16 (&out)[2][2]) {
+                                         uint8_t* sB, f32x16 (&out)[2][2]) {
     const int lane = threadIdx.x & 63, ln = lane & 31, lh = lane >> 5;
     const int ar = threadIdx.x >> 2, aq = threadIdx.x & 3;     // staging: row, 16-column quarter
     const bool aload = TWO || ar < 32;                         // wave-uniform
@@ -292,10 +301,10 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
 #pragma unroll
     for (int j = 1; j < kA; ++j) ldA(j, min(j, last));
     stA(0, 0);
-#pragma unroll
-    for (int d = 0; d < kD; ++d) ldB(P[d], F[d], min(d, last));
-    __syncthreads();
     if constexpr (GS) {
+#pragma unroll
+        for (int d = 0; d < kD; ++d) ldB(P[d], F[d], min(d, last));
+        __syncthreads();
         // pairs of k steps, then the odd last step (no loads past it)
         int kb = 0;
         for (; kb + 1 < nk; kb += 2) {
@@ -309,29 +318,77 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
         }
         return;
     }
-    // groups of U k steps (U = max(kD, kA), so that every register set index
-    // is a constant) with no exit in between, so the accumulators stay in
-    // place across iterations; then the remaining steps. The last step of each
-    // load group refills the group's weight sets with the k steps kD ahead of
-    // them (clamped to the last step near the end).
-    constexpr int U = kD > kA ? kD : kA;
-    auto refill = [&](int k, int d, bool tail) {
-        const int dd = d % kD, base = k - dd;
-        if ((dd + 1) % kGrp == 0) {
+    // Per-row scales: weight rows go through the wave's own LDS region in whole
+    // cache lines. Every 4 k steps the wave requests the next 4 steps of its
+    // 64 rows (gate and up, or two column blocks of down) as 8 loads of 8 rows
+    // x 128 bytes each: a load touches 8 lines and uses all of each, where
+    // the MFMA operand layout would touch 32 lines and use 32 bytes of each.
+    // At the end of a group the wave stores the next group into its region
+    // (16-byte chunks XOR-swizzled by row, so that the operand reads below
+    // are conflict-free) and each k step reads its operands from there. Only
+    // the wave itself reads its region, and one wave's LDS operations execute
+    // in order, so no barrier is needed.
+    uint8_t* sBw = sB + (threadIdx.x >> 6) * (2 * 32 * 128);
+    const int rowbytes = nk * 32;                              // bytes of one weight row
+    // rows q * 8 + lane / 8 as byte offsets from the wave's first row
+    // (each taken from a lane of that row with lh == 0)
+    const uint8_t* base[2] = {shfl_ptr(b0, 0), shfl_ptr(b1, 0)};
+    uint32_t ro[2][4];
 #pragma unroll
-            for (int j = dd + 1 - kGrp; j <= dd; ++j)
-                if (!tail || base + j + kD <= last) ldB(P[j], F[j], min(base + j + kD, last));
-        }
+    for (int q = 0; q < 4; ++q) {
+        const int src = q * 8 + (lane >> 3);
+        ro[0][q] = (uint32_t)(shfl_ptr(b0, src) - base[0]);
+        ro[1][q] = (uint32_t)(shfl_ptr(b1, src) - base[1]);
+    }
+    uint4 Q[2][4];
+    auto ldG = [&](int g) {
+        const uint32_t off = (uint32_t)min(g * 128 + (lane & 7) * 16, rowbytes - 16);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Q[m][q] = ldg16(base[m] + (ro[m][q] + off));
     };
-    int kb = 0;
-    for (; kb + U - 1 < nk; kb += U) {
+    auto stG = [&]() {
 #pragma unroll
-        for (int d = 0; d < U; ++d)
-            step(kb + d, d & 1, P[d % kD], F[d % kD], [&] { refill(kb + d, d, false); });
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = q * 8 + (lane >> 3);
+                *reinterpret_cast<uint4*>(sBw + (m * 32 + r) * 128 + (((lane & 7) ^ (r & 7)) * 16)) = Q[m][q];
+            }
+    };
+    auto ldP = [&](int d, uint4 (&Pk)[2]) {                    // k step d of the group: its 32 bytes
+        const int c = d * 2 + lh;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            Pk[m] = *reinterpret_cast<const uint4*>(sBw + (m * 32 + ln) * 128 + ((c ^ (ln & 7)) * 16));
+    };
+    const int ng = (nk + 3) / 4, last_g = ng - 1;
+    auto kstep = [&](int k, int d, bool group_end, int g) {
+        ldA(k % kA, min(k + kA, last));
+        if (kA >= 2) asm volatile("" ::: "memory");
+        uint4 Pk[2];
+        ldP(d, Pk);
+        mma(d & 1, Pk);
+        stA((d & 1) ^ 1, (k + 1) % kA);
+        if (group_end) {
+            stG();
+            ldG(min(g + 2, last_g));
+        }
+        __syncthreads();
+    };
+    ldG(0);
+    stG();
+    ldG(min(1, last_g));
+    __syncthreads();
+    int g = 0;
+    for (; g < last_g; ++g) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) kstep(g * 4 + d, d, d == 3, g);
     }
 #pragma unroll
-    for (int d = 0; d < U - 1; ++d)
-        if (kb + d < nk) step(kb + d, d & 1, P[d % kD], F[d % kD], [&] { refill(kb + d, d, true); });
+    for (int d = 0; d < 4; ++d)
+        if (g * 4 + d < nk) kstep(g * 4 + d, d, false, g);
 }
 
 // ----------------------------------------------------------------- gate/up
@@ -341,7 +398,7 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
 // values that the down GEMM's correction needs.
 template <bool GS, bool TWO>
 __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& it, int m0, int rb,
-                                            uint16_t (*sA)[kTileM][kLdsRow], float* s_cs,
+                                            uint16_t (*sA)[kTileM][kLdsRow], float* s_cs, uint8_t* sB,
                                             const float* s_tot, const int* s_out,
                                             float (*s_part)[kTileM]) {
     const int H = a.H, I = a.I, G = H / 64;
@@ -363,7 +420,7 @@ __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& i
     f32x16 out[2][2];
     mainloop<GS, TWO>(arow, G, it.blob + L.gate_q + boff, it.blob + L.up_q + boff,
                       gsc + (size_t)irow * G, usc + (size_t)irow * G, a.sx, a.rows_tok, it, m0,
-                      sA, s_cs, out);
+                      sA, s_cs, sB, out);
 
 #pragma unroll
     for (int mb = 0; mb < (TWO ? 2 : 1); ++mb) {
@@ -403,9 +460,13 @@ __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& i
     }
 }
 
+// Three resident waves per SIMD with per-row scales (three workgroups per
+// CU also fit the LDS), two with gs64 (its group sums in registers).
 template <bool GS>
-__global__ __launch_bounds__(256) void gemm_gateup_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GS ? 2 : 3)))
+void gemm_gateup_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
+    __shared__ __align__(16) uint8_t sB[GS ? 16 : kSB];   // per-row scales: weight-line regions
     __shared__ float s_part[4][kTileM];          // per-wave token sums of bf16(h)
     __shared__ float s_tot[kTileM];              // per-token sum of the bf16 x row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
@@ -427,8 +488,8 @@ __global__ __launch_bounds__(256) void gemm_gateup_kernel(GemmArgs a) {
         s_tot[threadIdx.x] = s;
     }
     // (the main loop's first barrier publishes s_tot)
-    if (it.count - m0 > 32) gateup_tile<GS, true>(a, it, m0, rb, sA, s_cs, s_tot, s_out, s_part);
-    else gateup_tile<GS, false>(a, it, m0, rb, sA, s_cs, s_tot, s_out, s_part);
+    if (it.count - m0 > 32) gateup_tile<GS, true>(a, it, m0, rb, sA, s_cs, sB, s_tot, s_out, s_part);
+    else gateup_tile<GS, false>(a, it, m0, rb, sA, s_cs, sB, s_tot, s_out, s_part);
 }
 
 // -------------------------------------------------------------------- down
@@ -436,7 +497,7 @@ __global__ __launch_bounds__(256) void gemm_gateup_kernel(GemmArgs a) {
 // 64w..64w+63 as two 32-column blocks.
 template <bool GS, bool TWO>
 __device__ __forceinline__ void down_tile(const GemmArgs& a, const WorkItem& it, int m0, int rb,
-                                          uint16_t (*sA)[kTileM][kLdsRow], float* s_cs,
+                                          uint16_t (*sA)[kTileM][kLdsRow], float* s_cs, uint8_t* sB,
                                           const float* s_tot, const int* s_out) {
     const int H = a.H, I = a.I, GI = I / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -453,7 +514,7 @@ __device__ __forceinline__ void down_tile(const GemmArgs& a, const WorkItem& it,
     f32x16 out[2][2];
     mainloop<GS, TWO>(arow, GI, dq + (size_t)cc0 * (I / 2) + lh * 16, dq + (size_t)cc1 * (I / 2) + lh * 16,
                       dsc + (size_t)cc0 * GI, dsc + (size_t)cc1 * GI, a.sh, a.rows_out, it, m0,
-                      sA, s_cs, out);
+                      sA, s_cs, sB, out);
 
     const int cols[2] = {c0, c1};
 #pragma unroll
@@ -473,8 +534,10 @@ __device__ __forceinline__ void down_tile(const GemmArgs& a, const WorkItem& it,
 }
 
 template <bool GS>
-__global__ __launch_bounds__(256) void gemm_down_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GS ? 2 : 3)))
+void gemm_down_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
+    __shared__ __align__(16) uint8_t sB[GS ? 16 : kSB];   // per-row scales: weight-line regions
     __shared__ float s_tot[kTileM];              // per-row sum of the bf16 h row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
     __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: 136 * group sums, [row][group]
@@ -494,8 +557,8 @@ __global__ __launch_bounds__(256) void gemm_down_kernel(GemmArgs a) {
         for (int q = 0; q < GI; ++q) s += a.sh[(size_t)o * GI + q];
         s_tot[threadIdx.x] = s;
     }
-    if (it.count - m0 > 32) down_tile<GS, true>(a, it, m0, rb, sA, s_cs, s_tot, s_out);
-    else down_tile<GS, false>(a, it, m0, rb, sA, s_cs, s_tot, s_out);
+    if (it.count - m0 > 32) down_tile<GS, true>(a, it, m0, rb, sA, s_cs, sB, s_tot, s_out);
+    else down_tile<GS, false>(a, it, m0, rb, sA, s_cs, sB, s_tot, s_out);
 }
 
 }  // namespace
