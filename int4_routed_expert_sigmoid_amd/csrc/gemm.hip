@@ -163,7 +163,7 @@ __device__ __forceinline__ void stage_group_sums(float* s, const float* sums, co
 // activation rows and weight rows. Workgroup L runs on XCD L % 8, and each XCD
 // takes one contiguous eighth of the units, so a group's reuse stays inside
 // one XCD's L2. Returns false for units past the device-side tile count.
-constexpr int kGroupTiles = 4;
+constexpr int kGroupTiles = 2;
 
 __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& rb) {
     const int n = n_tiles * n_rb;
