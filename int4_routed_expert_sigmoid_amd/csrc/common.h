@@ -120,6 +120,11 @@ __device__ __forceinline__ uint4 ldg128(const uint8_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Scheduling boundary: the backend's machine scheduler moves nothing across
+// it. Loads through const __restrict__ pointers count as invariant, so an
+// empty asm statement with a memory clobber does not hold them in place.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Plain global load of one float through a global-address-space pointer.
 __device__ __forceinline__ float ldg_f32(const float* p) { return *(global_f32*)(p); }
 

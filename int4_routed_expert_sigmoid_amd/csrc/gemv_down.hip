@@ -101,7 +101,7 @@ __device__ __forceinline__ void down_body(
         const float rsc = GS ? 1.f : ldg_f32(dsc + min(rbase + (lane % kDownRowsPerWave), H - 1));
 #pragma unroll
         for (int b = 0; b < PD - 1; ++b) load(wbuf[b], fbuf[b], b);
-        asm volatile("" ::: "memory");    // keep these loads ahead of the waits below
+        sched_fence();    // keep these loads ahead of the waits below
         if constexpr (ENC) {
             encode_pass(0);
             for (int i0 = 256; i0 < nq; i0 += 256) {
@@ -166,14 +166,14 @@ __device__ __forceinline__ void down_body(
                     y_rows[(size_t)outr * H + row] = v * sc;
             };
             // each batch's loads are issued before the wait for an earlier one;
-            // the empty asm statements keep the scheduler from moving a wait
+            // the scheduling fences keep the scheduler from moving a wait
             // above them, and no load is left under a runtime condition (the
             // wait-count pass would merge it by draining the batch in flight)
             if constexpr (PD == 3) {
 #pragma unroll
                 for (int b = 0; b < NBT; ++b) {
                     if (b + 2 < NBT) load(wbuf[(b + 2) % 3], fbuf[(b + 2) % 3], b + 2);
-                    asm volatile("" ::: "memory");
+                    sched_fence();
                     compute(wbuf[b % 3], fbuf[b % 3], b);
                 }
             } else {
@@ -181,14 +181,14 @@ __device__ __forceinline__ void down_body(
 #pragma unroll 1
                 for (int b = 0; b < NBT - 2; b += 2) {
                     load(wbuf[1], fbuf[1], b + 1);
-                    asm volatile("" ::: "memory");
+                    sched_fence();
                     compute(wbuf[0], fbuf[0], b);
                     load(wbuf[0], fbuf[0], b + 2);
-                    asm volatile("" ::: "memory");
+                    sched_fence();
                     compute(wbuf[1], fbuf[1], b + 1);
                 }
                 load(wbuf[1], fbuf[1], NBT - 1);
-                asm volatile("" ::: "memory");
+                sched_fence();
                 compute(wbuf[0], fbuf[0], NBT - 2);
                 compute(wbuf[1], fbuf[1], NBT - 1);
             }

@@ -112,10 +112,10 @@ __device__ __forceinline__ void gateup_body(
             }
         }
         // the second batch is requested before anything waits for the first
-        // (load counters retire in order); the empty asm statements keep the
+        // (load counters retire in order); the scheduling fences keep the
         // scheduler from moving a wait above the next batch's loads
         load(wb, fb, 1);
-        asm volatile("" ::: "memory");
+        sched_fence();
         int xsum[MT][NCH];                                // int8 weights: sum of each block's X
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -154,10 +154,10 @@ __device__ __forceinline__ void gateup_body(
         for (int b = 0; b < NBT - 2; b += 2) {
             compute(wa, fa, b);
             load(wa, fa, b + 2);
-            asm volatile("" ::: "memory");
+            sched_fence();
             compute(wb, fb, b + 1);
             load(wb, fb, b + 3);
-            asm volatile("" ::: "memory");
+            sched_fence();
         }
         compute(wa, fa, NBT - 2);
         compute(wb, fb, NBT - 1);
