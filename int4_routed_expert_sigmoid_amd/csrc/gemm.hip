@@ -186,10 +186,11 @@ __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& r
 // for its two 32-row weight blocks b (gate and up rows, or two column blocks
 // of down) and the tile's token halves (the second only when TWO). The 64 x 64
 // activation block of each k step is staged once per workgroup in LDS (double
-// buffered, one barrier per k step) and shared by the 4 waves; weight nibbles
-// go straight from HBM to registers, two or four k steps ahead. With GS, every k step
-// is one 64-column scale group, folded into `out` with its scale and its
-// 136 * S correction; otherwise `out` holds the raw sums.
+// buffered, one barrier per k step) and shared by the 4 waves. Weight nibbles
+// pass through the wave's own LDS region in whole cache lines (per-row
+// scales) or go straight from HBM to registers two k steps ahead (gs64). With
+// GS, every k step is one 64-column scale group, folded into `out` with its
+// scale and its 136 * S correction; otherwise `out` holds the raw sums.
 constexpr int kLdsRow = 72;          // bf16 per LDS activation row (64 + 8 pad: conflict-free 16-B reads)
 constexpr int kSB = 4 * 2 * 32 * 128;  // bytes of the per-wave weight-line regions of a workgroup
 
@@ -221,15 +222,9 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     // gs64): register set k % kA holds k step k between its load and its
     // store to LDS at the end of step k - 1
     constexpr int kA = GS ? 1 : 2;
-    // weight nibbles run kD k steps ahead (4 with per-row scales; 2 with gs64,
-    // whose group sums and scale folds already fill the register file). With
-    // per-row scales they are requested kGrp k steps at a time: one k step
-    // reads 32 bytes of each weight row, so kGrp steps issued back to back
-    // read 32 * kGrp consecutive bytes of it while its cache line is in
-    // flight, instead of fetching the line again for every step.
-    constexpr int kD = GS ? 2 : 4;
-    constexpr int kGrp = GS ? 1 : 2;
-    static_assert(kD % kGrp == 0, "load groups must tile the weight sets");
+    // gs64: weight nibbles and their group scales run kD k steps ahead in
+    // registers (the group sums and scale folds leave no room for more)
+    constexpr int kD = 2;
     uint4 P[kD][2], Ar[kA][2] = {};
     float F[kD][2] = {};                                       // gs64: scales of the staged k steps
     auto ldA = [&](int set, int kb) {
@@ -284,7 +279,7 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
             }
     };
     const int last = nk - 1;
-    // one k step (k & 1 == buf): request the activation block kA steps
+    // one gs64 k step (k & 1 == buf): request the activation block kA steps
     // ahead, multiply the current one with its weight set, refill that set kD
     // steps ahead, store the next activation block
     auto step = [&](int k, int buf, uint4 (&Pk)[2], float (&Fk)[2], auto&& loadB) {
