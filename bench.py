@@ -570,7 +570,7 @@ def main():
     if args.steps is None:
         args.steps = 512 if args.workload == "stream" else 1000
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "one-GPU benchmark: the layer runs on a single GPU here (how it would shard is described, not run); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
