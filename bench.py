@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--topp", type=float, default=0.0,
                     help="decode with the adaptive expert top-p (lossy; 0 = fixed top-8, the headline)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
+    ap.add_argument("--group", type=int, default=0, choices=[0, 64],
+                    help="prefill workload: scale group of the experts (0 per-row, 64 gs64)")
     ap.add_argument("--pinned-layers", type=int, default=13,
                     help="stream workload: distinct pinned layer pools (the rest reuse them)")
     ap.add_argument("--policies", default="lru",
@@ -202,7 +204,8 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
     used = int((counts > 0).sum()) + shape.n_shared           # experts whose weights the call reads
     weight_bytes = used * coli.blob_layout(shape)[1]
     return {
-        "workload": "prefill, 2048 tokens, Zipf(1.1) + 10% uniform routing, same layer",
+        "workload": "prefill, 2048 tokens, Zipf(1.1) + 10% uniform routing, same layer"
+                    + (", gs64 experts" if shape.group else ""),
         "tokens_per_s": round(T / dt, 1),
         "ms_per_call": round(dt * 1e3, 4),
         "tflops_layer": round((flops_gu + flops_dn) / dt / 1e12, 2),
@@ -584,7 +587,7 @@ def main():
         if args.workload == "copy":
             line = run_copy(args, dev)
         elif args.workload == "prefill":
-            shape = coli.MoEShape(6144, 2048, 256, 1, 8, 0, 1.0)
+            shape = coli.MoEShape(6144, 2048, 256, 1, 8, args.group, 1.0)
             arena, table, shared, _ = build_experts(coli, shape, args.seed, dev)
             line = run_prefill(coli, shape, table, shared, args.seed, dev,
                                calls=max(1, min(args.steps, 50)), warmup=max(1, args.warmup))

@@ -187,10 +187,9 @@ __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& r
 // of down) and the tile's token halves (the second only when TWO). The 64 x 64
 // activation block of each k step is staged once per workgroup in LDS (double
 // buffered, one barrier per k step) and shared by the 4 waves. Weight nibbles
-// pass through the wave's own LDS region in whole cache lines (per-row
-// scales) or go straight from HBM to registers two k steps ahead (gs64). With
-// GS, every k step is one 64-column scale group, folded into `out` with its
-// scale and its 136 * S correction; otherwise `out` holds the raw sums.
+// pass through the wave's own LDS region in whole cache lines. With GS, every
+// k step is one 64-column scale group, folded into `out` with its scale and
+// its 136 * S correction; otherwise `out` holds the raw sums.
 constexpr int kLdsRow = 72;          // bf16 per LDS activation row (64 + 8 pad: conflict-free 16-B reads)
 constexpr int kSB = 4 * 2 * 32 * 128;  // bytes of the per-wave weight-line regions of a workgroup
 
@@ -222,11 +221,10 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     // gs64): register set k % kA holds k step k between its load and its
     // store to LDS at the end of step k - 1
     constexpr int kA = GS ? 1 : 2;
-    // gs64: weight nibbles and their group scales run kD k steps ahead in
-    // registers (the group sums and scale folds leave no room for more)
-    constexpr int kD = 2;
-    uint4 P[kD][2], Ar[kA][2] = {};
-    float F[kD][2] = {};                                       // gs64: scales of the staged k steps
+    // gs64: the group scales of the weight rows run kF k steps ahead
+    constexpr int kF = 2;
+    uint4 Ar[kA][2] = {};
+    float F[kF][2] = {};                                       // gs64: scales of the staged k steps
     auto ldA = [&](int set, int kb) {
         if (aload) {
             Ar[set][0] = ldg16(arow + kb * 64);
@@ -239,13 +237,9 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
             *reinterpret_cast<uint4*>(&sA[buf][ar][aq * 16 + 8]) = Ar[set][1];
         }
     };
-    auto ldB = [&](uint4 (&P)[2], float (&F)[2], int kb) {
-        P[0] = ldg16(b0 + kb * 32);
-        P[1] = ldg16(b1 + kb * 32);
-        if (GS) {
-            F[0] = gs0[kb];
-            F[1] = gs1[kb];
-        }
+    auto ldF = [&](float (&F)[2], int kb) {
+        F[0] = gs0[kb];
+        F[1] = gs1[kb];
     };
     auto mma = [&](int buf, const uint4 (&P)[2]) {
         const uint4* r0 = reinterpret_cast<const uint4*>(&sA[buf][ln][lh * 32]);
@@ -279,92 +273,81 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
             }
     };
     const int last = nk - 1;
-    // one gs64 k step (k & 1 == buf): request the activation block kA steps
-    // ahead, multiply the current one with its weight set, refill that set kD
-    // steps ahead, store the next activation block
-    auto step = [&](int k, int buf, uint4 (&Pk)[2], float (&Fk)[2], auto&& loadB) {
-        if (GS && k % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, k);
-        ldA(k % kA, min(k + kA, last));
-        if (kA >= 2) asm volatile("" ::: "memory");
-        mma(buf, Pk);
-        if (GS) fold(k, Fk);
-        loadB();
-        stA(buf ^ 1, (k + 1) % kA);
-        __syncthreads();
-    };
     ldA(0, 0);
 #pragma unroll
     for (int j = 1; j < kA; ++j) ldA(j, min(j, last));
     stA(0, 0);
     if constexpr (GS) {
 #pragma unroll
-        for (int d = 0; d < kD; ++d) ldB(P[d], F[d], min(d, last));
-        __syncthreads();
-        // pairs of k steps, then the odd last step (no loads past it)
-        int kb = 0;
-        for (; kb + 1 < nk; kb += 2) {
-            step(kb, 0, P[0], F[0], [&] { ldB(P[0], F[0], min(kb + kD, last)); });
-            step(kb + 1, 1, P[1], F[1], [&] { ldB(P[1], F[1], min(kb + 1 + kD, last)); });
-        }
-        if (kb < nk) {
-            if (kb % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, kb);
-            mma(0, P[0]);
-            fold(kb, F[0]);
-        }
-        return;
+        for (int j = 0; j < kF; ++j) ldF(F[j], min(j, last));
     }
-    // Per-row scales: weight rows go through the wave's own LDS region in whole
-    // cache lines. Every 4 k steps the wave requests the next 4 steps of its
-    // 64 rows (gate and up, or two column blocks of down) as 8 loads of 8 rows
-    // x 128 bytes each: a load touches 8 lines and uses all of each, where
+    // Weight rows go through the wave's own LDS region in whole (per-row
+    // scales) or half (gs64, whose group sums and folds leave fewer registers)
+    // cache lines. Every GL k steps the wave requests the next GL steps of its
+    // 64 rows (gate and up, or two column blocks of down): a load of RPI rows
+    // x GL * 32 bytes touches RPI lines and uses GL * 32 bytes of each, where
     // the MFMA operand layout would touch 32 lines and use 32 bytes of each.
     // At the end of a group the wave stores the next group into its region
-    // (16-byte chunks XOR-swizzled by row, so that the operand reads below
-    // are conflict-free) and each k step reads its operands from there. Only
-    // the wave itself reads its region, and one wave's LDS operations execute
-    // in order, so no barrier is needed.
-    uint8_t* sBw = sB + (threadIdx.x >> 6) * (2 * 32 * 128);
+    // (16-byte chunks XOR-swizzled by row, so that eight consecutive rows fall
+    // on distinct banks for the operand reads below) and each k step reads its
+    // operands from there. Only the wave itself reads its region, and one
+    // wave's LDS operations execute in order, so no barrier is needed.
+    constexpr int GL = GS ? 2 : 4;                             // k steps per load group
+    constexpr int NG = 2 * GL;                                 // 16-byte chunks per row and group
+    constexpr int RPI = 64 / NG;                               // rows per load
+    constexpr int NI = 32 / RPI;                               // loads per matrix and group
+    auto swz = [](int r) { return (r / (16 / NG)) & (NG - 1); };
+    uint8_t* sBw = sB + (threadIdx.x >> 6) * (2 * 32 * 16 * NG);
     const int rowbytes = nk * 32;                              // bytes of one weight row
-    // rows q * 8 + lane / 8 as byte offsets from the wave's first row
+    // rows q * RPI + lane / NG as byte offsets from the wave's first row
     // (each taken from a lane of that row with lh == 0)
     const uint8_t* base[2] = {shfl_ptr(b0, 0), shfl_ptr(b1, 0)};
-    uint32_t ro[2][4];
+    uint32_t ro[2][NI];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int src = q * 8 + (lane >> 3);
+    for (int q = 0; q < NI; ++q) {
+        const int src = q * RPI + lane / NG;
         ro[0][q] = (uint32_t)(shfl_ptr(b0, src) - base[0]);
         ro[1][q] = (uint32_t)(shfl_ptr(b1, src) - base[1]);
     }
-    uint4 Q[2][4];
+    uint4 Q[2][NI];
     auto ldG = [&](int g) {
-        const uint32_t off = (uint32_t)min(g * 128 + (lane & 7) * 16, rowbytes - 16);
+        const uint32_t off = (uint32_t)min(g * GL * 32 + (lane % NG) * 16, rowbytes - 16);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) Q[m][q] = ldg16(base[m] + (ro[m][q] + off));
+            for (int q = 0; q < NI; ++q) Q[m][q] = ldg16(base[m] + (ro[m][q] + off));
     };
     auto stG = [&]() {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = q * 8 + (lane >> 3);
-                *reinterpret_cast<uint4*>(sBw + (m * 32 + r) * 128 + (((lane & 7) ^ (r & 7)) * 16)) = Q[m][q];
+            for (int q = 0; q < NI; ++q) {
+                const int r = q * RPI + lane / NG;
+                *reinterpret_cast<uint4*>(sBw + (m * 32 + r) * (16 * NG) + (((lane % NG) ^ swz(r)) * 16)) = Q[m][q];
             }
     };
     auto ldP = [&](int d, uint4 (&Pk)[2]) {                    // k step d of the group: its 32 bytes
         const int c = d * 2 + lh;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            Pk[m] = *reinterpret_cast<const uint4*>(sBw + (m * 32 + ln) * 128 + ((c ^ (ln & 7)) * 16));
+            Pk[m] = *reinterpret_cast<const uint4*>(sBw + (m * 32 + ln) * (16 * NG) + ((c ^ swz(ln)) * 16));
     };
-    const int ng = (nk + 3) / 4, last_g = ng - 1;
+    const int ng = (nk + GL - 1) / GL, last_g = ng - 1;
+    // one k step (k & 1 == d & 1 == the LDS activation buffer): request the
+    // activation block kA steps ahead, multiply the current one with the
+    // step's weights; gs64: fold the group sums with their scales and request
+    // the scales kF steps ahead; store the next activation block
     auto kstep = [&](int k, int d, bool group_end, int g) {
+        if (GS && k % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, k);
         ldA(k % kA, min(k + kA, last));
         if (kA >= 2) asm volatile("" ::: "memory");
         uint4 Pk[2];
         ldP(d, Pk);
         mma(d & 1, Pk);
+        if constexpr (GS) {
+            fold(k, F[d % kF]);
+            ldF(F[d % kF], min(k + kF, last));
+        }
         stA((d & 1) ^ 1, (k + 1) % kA);
         if (group_end) {
             stG();
@@ -379,11 +362,11 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     int g = 0;
     for (; g < last_g; ++g) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) kstep(g * 4 + d, d, d == 3, g);
+        for (int d = 0; d < GL; ++d) kstep(g * GL + d, d, d == GL - 1, g);
     }
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-        if (g * 4 + d < nk) kstep(g * 4 + d, d, false, g);
+    for (int d = 0; d < GL; ++d)
+        if (g * GL + d < nk) kstep(g * GL + d, d, false, g);
 }
 
 // ----------------------------------------------------------------- gate/up
@@ -461,7 +444,7 @@ template <bool GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GS ? 2 : 3)))
 void gemm_gateup_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
-    __shared__ __align__(16) uint8_t sB[GS ? 16 : kSB];   // per-row scales: weight-line regions
+    __shared__ __align__(16) uint8_t sB[kSB];    // the waves' weight-line regions
     __shared__ float s_part[4][kTileM];          // per-wave token sums of bf16(h)
     __shared__ float s_tot[kTileM];              // per-token sum of the bf16 x row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
@@ -532,7 +515,7 @@ template <bool GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GS ? 2 : 3)))
 void gemm_down_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
-    __shared__ __align__(16) uint8_t sB[GS ? 16 : kSB];   // per-row scales: weight-line regions
+    __shared__ __align__(16) uint8_t sB[kSB];    // the waves' weight-line regions
     __shared__ float s_tot[kTileM];              // per-row sum of the bf16 h row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
     __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: 136 * group sums, [row][group]
