@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const WorkItem* __restrict__
 
 constexpr int kCsChunk = 64;        // 64-column groups staged in LDS at a time (gs64)
 
-// Stage 136 * sums[row(m0 + t)][q] for the 64 tile rows t and the groups
+// Stage -136 * sums[row(m0 + t)][q] for the 64 tile rows t and the groups
 // q = q0 .. q0 + 63 (clamped to n_groups) as s[t * 64 + q - q0]. Called by the
 // whole workgroup at the same k block; the barriers fence the previous chunk's
 // readers and publish the new one.
@@ -150,7 +150,7 @@ __device__ __forceinline__ void stage_group_sums(float* s, const float* sums, co
         const int t = i / kCsChunk, q = i % kCsChunk;
         if (q < nq) {
             const int r = rows[it.begin + min(m0 + t, it.count - 1)];
-            s[i] = kOffset * sums[(size_t)r * n_groups + q0 + q];
+            s[i] = -kOffset * sums[(size_t)r * n_groups + q0 + q];
         }
     }
     __syncthreads();
@@ -188,8 +188,9 @@ __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& r
 // activation block of each k step is staged once per workgroup in LDS (double
 // buffered, one barrier per k step) and shared by the 4 waves. Weight nibbles
 // pass through the wave's own LDS region in whole cache lines. With GS, every
-// k step is one 64-column scale group, folded into `out` with its scale and
-// its 136 * S correction; otherwise `out` holds the raw sums.
+// k step is one 64-column scale group: its sums start from the -136 * S
+// correction (the C operand of the step's first MFMA, read from LDS) and are
+// folded into `out` with the group's scale; otherwise `out` holds the raw sums.
 constexpr int kLdsRow = 72;          // bf16 per LDS activation row (64 + 8 pad: conflict-free 16-B reads)
 constexpr int kSB = 4 * 2 * 32 * 128;  // bytes of the per-wave weight-line regions of a workgroup
 
@@ -241,7 +242,7 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
         F[0] = gs0[kb];
         F[1] = gs1[kb];
     };
-    auto mma = [&](int buf, const uint4 (&P)[2]) {
+    auto mma = [&](int buf, const uint4 (&P)[2], const f32x16 (&C)[2]) {
         const uint4* r0 = reinterpret_cast<const uint4*>(&sA[buf][ln][lh * 32]);
         const uint4* r1 = reinterpret_cast<const uint4*>(&sA[buf][32 + ln][lh * 32]);
 #pragma unroll
@@ -253,24 +254,26 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
             for (int b = 0; b < 2; ++b) {
                 const uint32_t w = s == 0 ? P[b].x : s == 1 ? P[b].y : s == 2 ? P[b].z : P[b].w;
                 const bf16x8 bb = nib8_to_bf16(w);
-                acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bb, acc[b][0], 0, 0, 0);
-                if (TWO) acc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bb, acc[b][1], 0, 0, 0);
+                const bool first = GS && s == 0;             // gs64: the group starts from C
+                acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bb, first ? C[0] : acc[b][0], 0, 0, 0);
+                if (TWO) acc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bb, first ? C[1] : acc[b][1], 0, 0, 0);
             }
         }
     };
-    auto fold = [&](int kb, const float (&f)[2]) {
+    auto ldC = [&](int kb, f32x16 (&C)[2]) {                  // gs64: -136 * S of the k step's group
         const float* cs_k = s_cs + kb % kCsChunk;
 #pragma unroll
         for (int mb = 0; mb < (TWO ? 2 : 1); ++mb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float cs = cs_k[(mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)) * kCsChunk];
+            for (int j = 0; j < 16; ++j) C[mb][j] = cs_k[(mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)) * kCsChunk];
+    };
+    auto fold = [&](const float (&f)[2]) {
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    out[b][mb][j] = fmaf(f[b], acc[b][mb][j] - cs, out[b][mb][j]);
-                    acc[b][mb][j] = 0.f;
-                }
-            }
+        for (int mb = 0; mb < (TWO ? 2 : 1); ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) out[b][mb][j] = fmaf(f[b], acc[b][mb][j], out[b][mb][j]);
     };
     const int last = nk - 1;
     ldA(0, 0);
@@ -341,11 +344,13 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
         if (GS && k % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, k);
         ldA(k % kA, min(k + kA, last));
         if (kA >= 2) asm volatile("" ::: "memory");
+        f32x16 C[2];
+        if constexpr (GS) ldC(k, C);
         uint4 Pk[2];
         ldP(d, Pk);
-        mma(d & 1, Pk);
+        mma(d & 1, Pk, C);
         if constexpr (GS) {
-            fold(k, F[d % kF]);
+            fold(F[d % kF]);
             ldF(F[d % kF], min(k + kF, last));
         }
         stA((d & 1) ^ 1, (k + 1) % kA);
@@ -448,7 +453,7 @@ void gemm_gateup_kernel(GemmArgs a) {
     __shared__ float s_part[4][kTileM];          // per-wave token sums of bf16(h)
     __shared__ float s_tot[kTileM];              // per-token sum of the bf16 x row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
-    __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: 136 * group sums, [token][group]
+    __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: -136 * group sums, [token][group]
     int tile, rb;
     if (!unit_of(*a.n_tiles, (a.I + 127) / 128, tile, rb)) return;
     const int2 td = a.tiles[tile];
@@ -518,7 +523,7 @@ void gemm_down_kernel(GemmArgs a) {
     __shared__ __align__(16) uint8_t sB[kSB];    // the waves' weight-line regions
     __shared__ float s_tot[kTileM];              // per-row sum of the bf16 h row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
-    __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: 136 * group sums, [row][group]
+    __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: -136 * group sums, [row][group]
     int tile, rb;
     if (!unit_of(*a.n_tiles, (a.H + 255) / 256, tile, rb)) return;
     const int2 td = a.tiles[tile];
