@@ -13,10 +13,13 @@ bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem
                      const uint32_t* xplanes, const float* xscale, float* gu, int H, int I,
                      const BlobLayout& L, const FusedRoute& fr);
 
-constexpr int kDownRowsPerWave = 16;
-constexpr int kDownRowsPerBlock = 4 * kDownRowsPerWave;
+// Down-matrix rows per wave (4 waves per workgroup). One-token launches take
+// 8: twice the workgroups for the same 9 x 6 MB read keep more of it in flight
+// (a read-only kernel of that shape: 9.9 us at 8 rows per wave, 10.5 us at 16);
+// batches take 16, which shares each wave's activation blocks over more rows.
+constexpr int down_rows_per_wave(int mt) { return mt == 1 ? 8 : 16; }
 
-// Launch the down kernel on grid (ceil(H/64), max_items) into y_rows. mt == 1
+// Launch the down kernel on grid (ceil(H / (4 * down_rows_per_wave(mt))), max_items) into y_rows. mt == 1
 // forms h = silu(g) * u from gu itself; larger mt reads the digit blocks of h
 // (hplanes, hscale) written by the activation pass. False if I is outside the
 // instantiated range.

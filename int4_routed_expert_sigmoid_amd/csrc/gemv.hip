@@ -144,7 +144,8 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
                rows, I, hplanes, hscale);
         COLI_CHECK_LAUNCH("activation kernel launch");
     }
-    const dim3 g2((H + kDownRowsPerBlock - 1) / kDownRowsPerBlock, max_items);
+    const int down_rows = 4 * down_rows_per_wave(mt);
+    const dim3 g2((H + down_rows - 1) / down_rows, max_items);
     {
         ProfTag prof("gemv_down");
         ok = dispatch_down(mt, group, g2, stream, items, n_items, rows_out, gu, hplanes, hscale,

@@ -2,11 +2,11 @@
 // every (expert, token) pair of a work list (practical guide section 二:
 // gate, up, down adjacent; SwiGLU).
 //
-// Workgroup: 4 waves x 16 rows of one work item's down matrix. For one token
-// it first forms h = silu(g) * u from the f32 silu(g) and u of the gate/up pass and encodes each
-// 32-element block into digit planes (common.h) in LDS, once for the
-// workgroup; for batches the activation pass has encoded the blocks once per
-// row. Lane l owns the 32-column blocks l + 64*j of h and
+// Workgroup: 4 waves x RPW rows of one work item's down matrix (8 for one-token
+// launches, 16 for batches). For one token it first forms h = silu(g) * u from
+// the f32 silu(g) and u of the gate/up pass and encodes each 32-element block
+// into digit planes (common.h) in LDS, once for the workgroup; for batches the
+// activation pass has encoded the blocks once per row. Lane l owns the 32-column blocks l + 64*j of h and
 // reads each row's 16 bytes in those blocks with one 128-bit load. Rows go in
 // batches of LB = 4/MT rows whose LB*MT partials per lane are summed over the
 // wave by one transpose-reduction; loads run two batches ahead (one token,
@@ -29,13 +29,14 @@ __device__ __forceinline__ void down_body(
     constexpr int LB = (4 / MT) > 0 ? (4 / MT) : 1;      // rows per batch
     constexpr int NV = LB * MT;                          // partials per batch (4, or 8 for MT 8)
     constexpr int SH = transpose_shift<NV>();
-    constexpr int NBT = kDownRowsPerWave / LB;           // batches per wave
+    constexpr int RPW = down_rows_per_wave(ENC ? 1 : 4); // rows per wave (ENC: one-token launch)
+    constexpr int NBT = RPW / LB;                        // batches per wave
     constexpr int PD = (NCH == 1 && ENC) ? 3 : 2;        // weight register sets (prefetch depth + 1)
     const int CI = I / kBlock;
     uint32_t* s_words = s_h;
     float* s_scale = reinterpret_cast<float*>(s_h + (size_t)MT * CI * kWordsPerBlock);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rbase = blockIdx.x * kDownRowsPerBlock + wave * kDownRowsPerWave;
+    const int rbase = (blockIdx.x * 4 + wave) * RPW;
     const bool live = rbase < H;                         // wave-uniform
     const uint8_t* dq = it.blob + L.down_q;
     const float* dsc = reinterpret_cast<const float*>(it.blob + L.down_s);
@@ -70,7 +71,7 @@ __device__ __forceinline__ void down_body(
         // encoder's shuffles require); every lane runs the encoder. Larger
         // batches read the blocks that the activation pass encoded once.
         // Load order: the first pass's g and u, the per-row scales of the
-        // wave's rows (lane l: row rbase + l % 16), then the weights. Load
+        // wave's rows (lane l: row rbase + l % RPW), then the weights. Load
         // counters retire in order, so forming h then waits for g and u alone,
         // and no scale load sits behind the weights where it is used.
         const int nq = ENC ? CI * 4 : 0;
@@ -98,7 +99,7 @@ __device__ __forceinline__ void down_body(
             }
         };
         if constexpr (ENC) load_gu(0);
-        const float rsc = GS ? 1.f : ldg_f32(dsc + min(rbase + (lane % kDownRowsPerWave), H - 1));
+        const float rsc = GS ? 1.f : ldg_f32(dsc + min(rbase + (lane % RPW), H - 1));
 #pragma unroll
         for (int b = 0; b < PD - 1; ++b) load(wbuf[b], fbuf[b], b);
         sched_fence();    // keep these loads ahead of the waits below
