@@ -134,7 +134,7 @@ struct Fp8Src {
 
 // One workgroup per row: block-wide max, then quantise and pack.
 template <typename Src, bool W8>
-__global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t rows, int64_t cols,
+__global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t cols,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ s, int aligned_out) {
     __shared__ float red[4];
@@ -289,7 +289,7 @@ coli_status launch_quant_t(const Src& src, int64_t rows, int64_t cols, int32_t g
                            float* s, int aligned_out, hipStream_t stream) {
     if (group == 0) {
         if (rows > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: too many rows");
-        launch(quant_row_kernel<Src, W8>, dim3((unsigned)rows), dim3(256), 0, stream, src, rows,
+        launch(quant_row_kernel<Src, W8>, dim3((unsigned)rows), dim3(256), 0, stream, src,
                cols, q, s, aligned_out);
     } else {
         // the group of 8 lanes must not straddle rows: cols % 64 == 0 is required

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void plan_kernel(
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ unique,
     const int32_t* __restrict__ n_unique, const void* const* __restrict__ table,
-    const void* shared_blob, int T, int k, int E, const uint8_t* __restrict__ phase_mask,
+    const void* shared_blob, int T, int k, const uint8_t* __restrict__ phase_mask,
     int phase, WorkItem* __restrict__ items, int32_t* __restrict__ n_items,
     int32_t* __restrict__ rows_tok, int32_t* __restrict__ rows_out) {
     __shared__ int sh[256];
@@ -232,7 +232,7 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
                         hipStream_t stream) {
     const int rows = T * k + T;
     launch(plan_kernel, dim3(std::max(1, (rows + 255) / 256)), dim3(256), 0, stream, offsets, perm, unique,
-                       n_unique, blob_table, shared_blob, T, k, E, phase_mask, phase, items,
+                       n_unique, blob_table, shared_blob, T, k, phase_mask, phase, items,
                        n_items, rows_tok, rows_out);
     COLI_CHECK_LAUNCH("plan kernel launch");
     return COLI_OK;
