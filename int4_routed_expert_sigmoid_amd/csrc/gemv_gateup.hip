@@ -14,7 +14,8 @@
 // and scaled once into an f32 partial. Rows go in batches of LB = 4/MT rows:
 // a batch yields LB*NM*MT partials per lane (NM matrices), summed over the wave by one
 // transpose-reduction and over the W waves through LDS; the next batch's
-// loads are issued before the current batch is computed. The workgroup ends
+// loads are issued before the current batch is computed (the next two for
+// one-token int4 tiles). The workgroup ends
 // by writing silu(g) (or u), with the per-row scale applied first, as f32.
 #include "gemv.h"
 
@@ -116,6 +117,16 @@ __device__ __forceinline__ void gateup_body(
         // scheduler from moving a wait above the next batch's loads
         load(wb, fb, 1);
         sched_fence();
+        // one token, int4: a third register set keeps three batches in flight
+        // (the batch count is a constant, so the sets rotate with static
+        // indices; with int8 weights the third set measured slower)
+        constexpr bool R3 = ONE && !W8;
+        WBlock<W8> wc[LB][NM][NCH];
+        float fc[LB][NM][NCH];
+        if constexpr (R3) {
+            load(wc, fc, 2);
+            sched_fence();
+        }
         int xsum[MT][NCH];                                // int8 weights: sum of each block's X
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -148,19 +159,31 @@ __device__ __forceinline__ void gateup_body(
             if ((lane & ((1 << SH) - 1)) == 0)
                 red[wave][batch * NV + (lane >> SH)] = v;
         };
-        // the last pair peeled: no load under a condition, which the wait-count
-        // pass would merge by draining the batch in flight
+        if constexpr (R3) {
+            static_assert(NBT == 8, "one-token tiles are 8 batches of 4 rows");
+            compute(wa, fa, 0); load(wa, fa, 3); sched_fence();
+            compute(wb, fb, 1); load(wb, fb, 4); sched_fence();
+            compute(wc, fc, 2); load(wc, fc, 5); sched_fence();
+            compute(wa, fa, 3); load(wa, fa, 6); sched_fence();
+            compute(wb, fb, 4); load(wb, fb, 7); sched_fence();
+            compute(wc, fc, 5);
+            compute(wa, fa, 6);
+            compute(wb, fb, 7);
+        } else {
+            // the last pair peeled: no load under a condition, which the
+            // wait-count pass would merge by draining the batch in flight
 #pragma unroll 1
-        for (int b = 0; b < NBT - 2; b += 2) {
-            compute(wa, fa, b);
-            load(wa, fa, b + 2);
-            sched_fence();
-            compute(wb, fb, b + 1);
-            load(wb, fb, b + 3);
-            sched_fence();
+            for (int b = 0; b < NBT - 2; b += 2) {
+                compute(wa, fa, b);
+                load(wa, fa, b + 2);
+                sched_fence();
+                compute(wb, fb, b + 1);
+                load(wb, fb, b + 3);
+                sched_fence();
+            }
+            compute(wa, fa, NBT - 2);
+            compute(wb, fb, NBT - 1);
         }
-        compute(wa, fa, NBT - 2);
-        compute(wb, fb, NBT - 1);
         __syncthreads();
         // output rows of this chunk's tokens (one-token items carry theirs:
         // rows_out may still be in flight when the routing is folded in)
