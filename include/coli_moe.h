@@ -187,10 +187,10 @@ COLI_API coli_status coli_moe_union(const int32_t* d_idx, int32_t T, int32_t k, 
 #define COLI_PATH_MFMA 2   /* bf16 MFMA grouped GEMM on dequantised tiles */
 
 /* Workspace bytes for coli_moe_expert_ffn / coli_moe_layer_fwd with T tokens.
- * The workspace (device memory, owned by the caller) must be zero-filled once
- * before its first use: it holds arrival counters that every call leaves at
- * zero again. A workspace serves one call at a time: calls that share one
- * must be ordered on a stream. */
+ * The workspace is device memory owned by the caller. It needs no
+ * initialisation: every call writes each region it reads before reading it.
+ * A workspace serves one call at a time: calls that share one must be ordered
+ * on a stream. */
 COLI_API coli_status coli_moe_workspace_size(const coli_moe_shape* shape, int32_t T, int32_t path,
                                     size_t* bytes);
 
@@ -270,7 +270,11 @@ COLI_API coli_status coli_expert_cache_destroy(struct coli_expert_cache* cache);
  * enqueues one host-to-device copy on the copy stream. h_miss_mask[i]
  * (nullable) is set to 1 for a miss. Duplicate ids count once. COLI_EBUSY if
  * n exceeds the layer's slots. Host-side bookkeeping only; never blocks on
- * the GPU. */
+ * the GPU. It takes no compute stream: everything it enqueues goes on the
+ * cache's copy stream, and the compute stream is joined by
+ * coli_expert_cache_wait. If a copy cannot be enqueued the call returns
+ * COLI_EHIP with that copy's slot left empty (its expert not resident and not
+ * counted as a miss); copies enqueued before it in the same call stand. */
 COLI_API coli_status coli_expert_cache_ensure(struct coli_expert_cache* cache, int32_t layer,
                                      const int32_t* h_ids, int32_t n, int32_t* h_miss_mask);
 
@@ -362,6 +366,11 @@ COLI_API coli_status coli_moe_lookahead(const coli_moe_shape* shape, const float
                                int32_t layer, int32_t* h_started, void* d_ws, size_t ws_bytes,
                                void* stream);
 
+/* Testing: make the next n host-to-device copies of any expert cache fail with
+ * COLI_EHIP before anything is enqueued (n = 0 turns it off). Process-wide.
+ * Lets the error path of a failed copy be exercised without a faulty device. */
+COLI_API coli_status coli_debug_fail_copies(int32_t n);
+
 /* ---------------------------------------------------------- kernel timing
  * Optional HIP-event timing of the library's main kernels, recorded on the
  * stream each kernel runs on. coli_profile_enable(n) pre-creates n event
@@ -373,6 +382,19 @@ COLI_API coli_status coli_moe_lookahead(const coli_moe_shape* shape, const float
 COLI_API coli_status coli_profile_enable(int32_t max_records);
 COLI_API coli_status coli_profile_clear(void);
 COLI_API coli_status coli_profile_summary(const char* name, int64_t* count, double* total_ms);
+
+/* Measurement: enqueue on `stream` one more launch of an expert-FFN pass of
+ * the last coli_moe_layer_fwd call made with d_ws, which must have been an
+ * uncached GEMV-path call (T <= 16, path COLI_PATH_GEMV or AUTO) with the same
+ * shape, T, d_blob_table and d_shared_blob. which = 0: the gate/up GEMV (one
+ * token: with the routing folded in, which it publishes again into d_ws);
+ * 1: the down GEMV (with, for batches, the activation pass before it). The
+ * pass reads and writes d_ws only and recomputes what the call computed, so
+ * back-to-back launches of one kernel can be captured in a graph and timed.
+ * The caller's y and routing outputs are not touched. */
+COLI_API coli_status coli_profile_rerun(const coli_moe_shape* shape, int32_t T,
+                                        const void* const* d_blob_table, const void* d_shared_blob,
+                                        int32_t which, void* d_ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,8 @@ EXPORTED = [
     "coli_expert_cache_release", "coli_expert_cache_table", "coli_expert_cache_stats",
     "coli_expert_cache_reset", "coli_expert_cache_pin", "coli_expert_cache_usage",
     "coli_expert_cache_pin_hot", "coli_expert_cache_repin", "coli_expert_cache_prefetch",
-    "coli_moe_lookahead", "coli_profile_enable", "coli_profile_clear", "coli_profile_summary",
+    "coli_moe_lookahead", "coli_debug_fail_copies", "coli_profile_enable", "coli_profile_clear",
+    "coli_profile_summary", "coli_profile_rerun",
 ]
 
 
@@ -112,9 +113,11 @@ def lib():
             L.coli_expert_cache_prefetch.argtypes = [vp, i32, vp, i32, P(i32)]
             L.coli_moe_lookahead.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, i32, P(i32), vp,
                                              sz, vp]
+            L.coli_debug_fail_copies.argtypes = [i32]
             L.coli_profile_enable.argtypes = [i32]
             L.coli_profile_clear.argtypes = []
             L.coli_profile_summary.argtypes = [ctypes.c_char_p, P(i64), P(ctypes.c_double)]
+            L.coli_profile_rerun.argtypes = [P(Shape), i32, vp, vp, i32, vp, sz, vp]
             _lib = L
     return _lib
 
@@ -298,9 +301,10 @@ def workspace_size(shape: MoEShape, T: int, path: int = PATH_AUTO) -> int:
 
 
 def workspace(shape: MoEShape, T: int, path: int = PATH_AUTO, device="cuda"):
-    """Zero-filled workspace (its arrival counters must start at zero)."""
+    """A workspace of the size coli_moe_workspace_size gives (no initialisation
+    needed: every call writes what it reads)."""
     import torch
-    return torch.zeros(max(1, workspace_size(shape, T, path)), dtype=torch.uint8, device=device)
+    return torch.empty(max(1, workspace_size(shape, T, path)), dtype=torch.uint8, device=device)
 
 
 def blob_table(blobs, device="cuda"):
@@ -360,9 +364,9 @@ class LayerCall:
                       None if cache is None else ctypes.c_void_p(cache.handle), layer, None, None,
                       None, path, _ptr(ws), ws.numel(), _stream(stream)]
 
-    def __call__(self, x_ptr: int, y_ptr: int, idx_ptr: int = 0):
+    def __call__(self, x_ptr: int, y_ptr: int, idx_ptr: int = 0, w_ptr: int = 0):
         a = self._args
-        a[1], a[10], a[11] = x_ptr, y_ptr, idx_ptr or None
+        a[1], a[10], a[11], a[12] = x_ptr, y_ptr, idx_ptr or None, w_ptr or None
         rc = self._fn(*a)
         if rc != COLI_OK:
             _check(rc)
@@ -384,6 +388,12 @@ def lookahead(shape: MoEShape, x, cache, layer, logits=None, router_w=None, bias
     return n.value
 
 
+def debug_fail_copies(n: int):
+    """coli_debug_fail_copies: the next n expert-cache copies fail (COLI_EHIP)
+    before anything is enqueued."""
+    _check(lib().coli_debug_fail_copies(n))
+
+
 def profile_enable(max_records: int):
     _check(lib().coli_profile_enable(max_records))
 
@@ -398,6 +408,13 @@ def profile_summary(name: str):
     ms = ctypes.c_double()
     _check(lib().coli_profile_summary(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def profile_rerun(shape: MoEShape, T: int, table, shared_blob, which: int, ws, stream=None):
+    """coli_profile_rerun: one more launch of the gate/up (which=0) or down (1)
+    GEMV pass of the last layer call made with `ws`."""
+    _check(lib().coli_profile_rerun(ctypes.byref(shape.c()), T, _ptr(table), _ptr(shared_blob),
+                                    which, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 class ExpertCache:

@@ -295,6 +295,23 @@ coli_status coli_moe_layer_fwd(const coli_moe_shape* shape, const float* d_x, in
     COLI_GUARD_END
 }
 
+coli_status coli_profile_rerun(const coli_moe_shape* shape, int32_t T,
+                              const void* const* d_blob_table, const void* d_shared_blob,
+                              int32_t which, void* d_ws, size_t ws_bytes, void* stream) {
+    COLI_GUARD_BEGIN
+    coli_status st = check_shape(shape);
+    if (st) return st;
+    if (T <= 0 || T > kSmallT) return fail(COLI_EINVAL, "profile_rerun: T must be in [1, 16]");
+    if (which != 0 && which != 1) return fail(COLI_EINVAL, "profile_rerun: which must be 0 or 1");
+    if (!d_blob_table) return fail(COLI_EINVAL, "profile_rerun: blob table missing");
+    if (shape->n_shared == 1 && !d_shared_blob) return fail(COLI_EINVAL, "profile_rerun: shared blob missing");
+    const WsLayout W = ws_layout(shape, T, COLI_PATH_GEMV);
+    if (!d_ws || ws_bytes < W.bytes) return fail(COLI_ENOMEM, "profile_rerun: workspace too small");
+    return run_rerun(shape, T, d_blob_table, shape->n_shared ? d_shared_blob : nullptr, which,
+                     (uint8_t*)d_ws, W, (hipStream_t)stream);
+    COLI_GUARD_END
+}
+
 coli_status coli_moe_lookahead(const coli_moe_shape* shape, const float* d_x, int32_t T,
                                const float* d_logits, const float* d_router_w, const float* d_bias,
                                struct coli_expert_cache* cache, int32_t layer, int32_t* h_started,

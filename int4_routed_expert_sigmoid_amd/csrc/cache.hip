@@ -62,13 +62,21 @@ struct coli_expert_cache {
     std::vector<std::pair<hipEvent_t, hipEvent_t>> timers;
     std::vector<bool> timer_live;
     size_t timer_next = 0;
-    // pinned staging of the cached layer call: routing read back, phase per expert
-    int32_t* h_idx = nullptr;
-    size_t h_idx_cap = 0;
+    // pinned staging of the cached layer call, allocated by create: the
+    // routing is read back through h_idx in chunks of kStagingIds entries;
+    // h_phase holds the phase of every expert of every layer
+    int32_t* h_idx = nullptr;          // [kStagingIds]
     uint8_t* h_phase = nullptr;        // [layer][expert]
 };
 
 namespace coli {
+
+// Routing entries read back per chunk through the pinned staging buffer.
+constexpr size_t kStagingIds = 16384;
+
+// Host-forced copy failures (coli_debug_fail_copies): the next n copies fail
+// before anything is enqueued.
+static int32_t g_fail_copies = 0;
 
 static coli_status harvest_timer(coli_expert_cache* c, size_t i, bool wait) {
     if (!c->timer_live[i]) return COLI_OK;
@@ -107,13 +115,62 @@ static std::vector<char> open_slots(coli_expert_cache* c, int32_t layer) {
     return ex;
 }
 
-// Copy expert e of `layer` into slot `victim` (evicting its occupant).
+// Copy expert e of `layer` into slot `victim` (evicting its occupant). If a
+// HIP call fails the error is returned with the slot left empty (its old
+// occupant forgotten, e not resident) and the counters unchanged.
 static coli_status load_slot(coli_expert_cache* c, int32_t layer, int32_t e, int victim,
                              uint64_t now) {
     const int S = c->cfg.slots_per_layer, E = c->cfg.n_experts;
     auto& sl = c->slots[layer][victim];
-    if (sl.expert >= 0) {
-        c->where[layer][sl.expert] = -1;
+    const int32_t old = sl.expert;
+    auto evict = [&]() {
+        if (old >= 0) c->where[layer][old] = -1;
+        sl.expert = -1;
+        sl.prefetched = false;
+        sl.pinned = false;
+    };
+    if (!c->dry) {
+        auto failed = [&](hipError_t err, const char* what) {
+            evict();
+            sl.pending = false;
+            return hip_fail(err, what);
+        };
+        if (g_fail_copies > 0) {
+            --g_fail_copies;
+            return failed(hipErrorOutOfMemory, "cache copy (host-forced failure)");
+        }
+        hipStream_t cs = (hipStream_t)c->cfg.copy_stream;
+        const size_t bb = c->cfg.blob_bytes;
+        uint8_t* dst = (uint8_t*)c->cfg.d_arena + ((size_t)layer * S + victim) * bb;
+        const uint8_t* src = c->pools[layer] + (size_t)e * bb;
+        hipError_t err;
+        if (sl.release_recorded && (err = hipStreamWaitEvent(cs, sl.release, 0)) != hipSuccess)
+            return failed(err, "cache copy: wait for the slot's release");
+        const size_t ti = c->timer_next;
+        coli_status hs = harvest_timer(c, ti, true);
+        if (hs) {
+            evict();
+            return hs;
+        }
+        if ((err = hipEventRecord(c->timers[ti].first, cs)) != hipSuccess)
+            return failed(err, "cache copy: timer start");
+        if ((err = hipMemcpyAsync(dst, src, bb, hipMemcpyHostToDevice, cs)) != hipSuccess)
+            return failed(err, "cache copy: hipMemcpyAsync");
+        if ((err = hipEventRecord(c->timers[ti].second, cs)) != hipSuccess)
+            return failed(err, "cache copy: timer stop");
+        c->timer_next = (ti + 1) % c->timers.size();
+        c->timer_live[ti] = true;
+        // pointer of the expert in the device table: a constant pinned source
+        if ((err = hipMemcpyAsync(c->d_tables + (size_t)layer * E + e,
+                                  c->h_slot_ptrs + ((size_t)layer * S + victim) * sizeof(void*),
+                                  sizeof(void*), hipMemcpyHostToDevice, cs)) != hipSuccess)
+            return failed(err, "cache copy: pointer table update");
+        if ((err = hipEventRecord(sl.ready, cs)) != hipSuccess)
+            return failed(err, "cache copy: ready event");
+        sl.pending = true;
+    }
+    if (old >= 0) {
+        c->where[layer][old] = -1;
         c->st.evictions++;
     }
     sl.expert = e;
@@ -121,26 +178,6 @@ static coli_status load_slot(coli_expert_cache* c, int32_t layer, int32_t e, int
     sl.prefetched = false;
     c->where[layer][e] = victim;
     c->st.bytes_h2d += c->cfg.blob_bytes;
-    if (c->dry) return COLI_OK;
-    sl.pending = true;
-    hipStream_t cs = (hipStream_t)c->cfg.copy_stream;
-    const size_t bb = c->cfg.blob_bytes;
-    uint8_t* dst = (uint8_t*)c->cfg.d_arena + ((size_t)layer * S + victim) * bb;
-    const uint8_t* src = c->pools[layer] + (size_t)e * bb;
-    if (sl.release_recorded) COLI_CHECK_HIP(hipStreamWaitEvent(cs, sl.release, 0));
-    const size_t ti = c->timer_next;
-    c->timer_next = (ti + 1) % c->timers.size();
-    coli_status hs = harvest_timer(c, ti, true);
-    if (hs) return hs;
-    COLI_CHECK_HIP(hipEventRecord(c->timers[ti].first, cs));
-    COLI_CHECK_HIP(hipMemcpyAsync(dst, src, bb, hipMemcpyHostToDevice, cs));
-    COLI_CHECK_HIP(hipEventRecord(c->timers[ti].second, cs));
-    c->timer_live[ti] = true;
-    // pointer of the expert in the device table: a constant pinned source
-    COLI_CHECK_HIP(hipMemcpyAsync(c->d_tables + (size_t)layer * E + e,
-                                  c->h_slot_ptrs + ((size_t)layer * S + victim) * sizeof(void*),
-                                  sizeof(void*), hipMemcpyHostToDevice, cs));
-    COLI_CHECK_HIP(hipEventRecord(sl.ready, cs));
     return COLI_OK;
 }
 
@@ -199,23 +236,29 @@ coli_status cache_layer_table(coli_expert_cache* c, int32_t layer, int32_t n_exp
 // Placement step of a cached layer call: read the routing back (blocking),
 // make the selected experts of `layer` resident, and upload the phase of each
 // selected expert (0: resident before the call, 1: copied by it) to d_phase.
+// The experts named by d_idx [n] (entries < 0: slots dropped by top-p),
+// read back to the host through the pinned staging in chunks (blocking).
+static coli_status read_routing(coli_expert_cache* c, const int32_t* d_idx, int32_t n,
+                                hipStream_t stream, std::vector<int32_t>* ids) {
+    ids->clear();
+    ids->reserve((size_t)n);
+    for (size_t i0 = 0; i0 < (size_t)n; i0 += kStagingIds) {
+        const size_t m = std::min(kStagingIds, (size_t)n - i0);
+        COLI_CHECK_HIP(hipMemcpyAsync(c->h_idx, d_idx + i0, sizeof(int32_t) * m,
+                                      hipMemcpyDeviceToHost, stream));
+        COLI_CHECK_HIP(hipStreamSynchronize(stream));
+        for (size_t i = 0; i < m; ++i)
+            if (c->h_idx[i] >= 0) ids->push_back(c->h_idx[i]);
+    }
+    return COLI_OK;
+}
+
 coli_status cache_place(coli_expert_cache* c, int32_t layer, const int32_t* d_idx, int32_t n,
                         uint8_t* d_phase, int32_t* n_miss, hipStream_t stream) {
     if (c->dry) return fail(COLI_EINVAL, "cache: a bookkeeping-only cache cannot serve layer calls");
-    if ((size_t)n > c->h_idx_cap) {
-        if (c->h_idx) COLI_CHECK_HIP(hipHostFree(c->h_idx));
-        c->h_idx = nullptr;
-        c->h_idx_cap = 0;
-        COLI_CHECK_HIP(hipHostMalloc((void**)&c->h_idx, sizeof(int32_t) * (size_t)n * 2, hipHostMallocDefault));
-        c->h_idx_cap = (size_t)n * 2;
-    }
-    COLI_CHECK_HIP(hipMemcpyAsync(c->h_idx, d_idx, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
-    COLI_CHECK_HIP(hipStreamSynchronize(stream));
-    // slots dropped by the adaptive top-p (index -1) need no expert
     std::vector<int32_t> ids;
-    ids.reserve((size_t)n);
-    for (int32_t i = 0; i < n; ++i)
-        if (c->h_idx[i] >= 0) ids.push_back(c->h_idx[i]);
+    coli_status rs = read_routing(c, d_idx, n, stream, &ids);
+    if (rs) return rs;
     std::vector<int32_t> miss(ids.size());
     coli_status st = coli_expert_cache_ensure(c, layer, ids.data(), (int32_t)ids.size(), miss.data());
     if (st) return st;
@@ -237,19 +280,9 @@ coli_status cache_place(coli_expert_cache* c, int32_t layer, const int32_t* d_id
 coli_status cache_prefetch_routed(coli_expert_cache* c, int32_t layer, const int32_t* d_idx,
                                   int32_t n, int32_t* started, hipStream_t stream) {
     if (c->dry) return fail(COLI_EINVAL, "cache: a bookkeeping-only cache cannot prefetch routed experts");
-    if ((size_t)n > c->h_idx_cap) {
-        if (c->h_idx) COLI_CHECK_HIP(hipHostFree(c->h_idx));
-        c->h_idx = nullptr;
-        c->h_idx_cap = 0;
-        COLI_CHECK_HIP(hipHostMalloc((void**)&c->h_idx, sizeof(int32_t) * (size_t)n * 2, hipHostMallocDefault));
-        c->h_idx_cap = (size_t)n * 2;
-    }
-    COLI_CHECK_HIP(hipMemcpyAsync(c->h_idx, d_idx, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
-    COLI_CHECK_HIP(hipStreamSynchronize(stream));
     std::vector<int32_t> ids;
-    ids.reserve((size_t)n);
-    for (int32_t i = 0; i < n; ++i)
-        if (c->h_idx[i] >= 0) ids.push_back(c->h_idx[i]);
+    coli_status rs = read_routing(c, d_idx, n, stream, &ids);
+    if (rs) return rs;
     return coli_expert_cache_prefetch(c, layer, ids.data(), (int32_t)ids.size(), started);
 }
 
@@ -306,6 +339,8 @@ COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct 
                 }
             if (hipHostMalloc((void**)&c->h_phase, (size_t)L * E, hipHostMallocDefault) != hipSuccess)
                 return cleanup(COLI_EHIP, "cache_create: pinned phase table allocation failed");
+            if (hipHostMalloc((void**)&c->h_idx, sizeof(int32_t) * kStagingIds, hipHostMallocDefault) != hipSuccess)
+                return cleanup(COLI_EHIP, "cache_create: pinned routing staging allocation failed");
             std::memset(c->h_phase, 0, (size_t)L * E);
             c->timers.resize(64);
             c->timer_live.assign(64, false);
@@ -318,6 +353,12 @@ COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct 
     } catch (const std::bad_alloc&) {
         return fail(COLI_ENOMEM, "cache_create: host allocation failed");
     }
+}
+
+COLI_API coli_status coli_debug_fail_copies(int32_t n) {
+    if (n < 0) return fail(COLI_EINVAL, "debug_fail_copies: n must be >= 0");
+    g_fail_copies = n;
+    return COLI_OK;
 }
 
 COLI_API coli_status coli_expert_cache_destroy(struct coli_expert_cache* c) {

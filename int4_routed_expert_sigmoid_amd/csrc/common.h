@@ -494,12 +494,14 @@ coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* pla
 // gu [rows][2][I] f32 holds silu(g) and u between the two passes; for
 // batches (max_count > 1) an activation pass encodes h = silu(g) * u of all
 // `rows` rows into hplanes [rows][I/32][16] / hscale [rows][I/32].
+// passes: kPassGateUp and/or kPassDown (the activation pass goes with down).
+constexpr int kPassGateUp = 1, kPassDown = 2, kPassBoth = 3;
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
                             float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
                             int32_t I, int32_t group, int32_t wbits, const FusedRoute& fr,
-                            hipStream_t stream);
+                            hipStream_t stream, int passes = kPassBoth);
 // y [T][H] = shared row + rs * sum_j w[t][j] * y_rows[t*k + j] in slot order;
 // with idx (nullable) given, slots whose index is negative (dropped by top-p)
 // add nothing.

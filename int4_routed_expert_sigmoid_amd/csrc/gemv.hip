@@ -125,19 +125,22 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
                             float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
                             int32_t I, int32_t group, int32_t wbits, const FusedRoute& fr,
-                            hipStream_t stream) {
+                            hipStream_t stream, int passes) {
     if (max_items == 0) return COLI_OK;
     const BlobLayout L = blob_layout(H, I, group, wbits);
     const int mt = max_count <= 1 ? 1 : max_count <= 2 ? 2 : max_count <= 4 ? 4 : 8;
     const dim3 g1((mt == 1 ? 2 : 1) * (I / kBlock), max_items);   // one token: gate and up apart
-    bool ok;
-    {
-        ProfTag prof("gemv_gateup");
-        ok = dispatch_gateup(mt, group, g1, stream, items, n_items, rows_tok, rows_out, xplanes,
-                             xscale, gu, H, I, L, fr);
+    bool ok = true;
+    if (passes & kPassGateUp) {
+        {
+            ProfTag prof("gemv_gateup");
+            ok = dispatch_gateup(mt, group, g1, stream, items, n_items, rows_tok, rows_out, xplanes,
+                                 xscale, gu, H, I, L, fr);
+        }
+        if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: hidden too large (max 16384)");
+        COLI_CHECK_LAUNCH("gate/up GEMV launch");
     }
-    if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: hidden too large (max 16384)");
-    COLI_CHECK_LAUNCH("gate/up GEMV launch");
+    if (!(passes & kPassDown)) return COLI_OK;
     if (mt > 1) {
         const int64_t threads = (int64_t)rows * (I / kBlock) * 4;
         launch(act_encode_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, gu,

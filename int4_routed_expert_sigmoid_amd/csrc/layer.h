@@ -26,6 +26,12 @@ coli_status run_layer(const coli_moe_shape* shape, const float* x, int32_t T, co
                       float* y, int32_t* idx_out, float* w_out, int32_t path, uint8_t* ws,
                       const WsLayout& W, hipStream_t stream);
 
+// One GEMV pass (which: 0 gate/up, 1 down) of the last uncached GEMV-path
+// layer call on ws, enqueued again (measurement).
+coli_status run_rerun(const coli_moe_shape* shape, int32_t T, const void* const* table,
+                      const void* shared_blob, int32_t which, uint8_t* ws, const WsLayout& W,
+                      hipStream_t stream);
+
 // Expert-cache hooks used by run_layer (cache.hip).
 coli_status cache_layer_table(struct coli_expert_cache* cache, int32_t layer, int32_t n_experts,
                               const void* const** table);

@@ -36,7 +36,8 @@ static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, b
 
 static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, int32_t T,
                            int32_t max_items, float* y_rows, uint8_t* ws, const WsLayout& W,
-                           bool x_encoded, hipStream_t stream, const FusedRoute* fused = nullptr) {
+                           bool x_encoded, hipStream_t stream, const FusedRoute* fused = nullptr,
+                           int passes = kPassBoth) {
     const int32_t H = s->hidden, I = s->inter;
     if (mfma) {
         GemmArgs g;
@@ -68,7 +69,33 @@ static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, i
                            at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
                            at<float>(ws, W.gu), at<uint32_t>(ws, W.hplanes),
                            at<float>(ws, W.hscale), y_rows, H, I, s->group, s->wbits,
-                           fused ? *fused : none, stream);
+                           fused ? *fused : none, stream, passes);
+}
+
+// One token on the GEMV path without a cache: the routing is folded into the
+// gate/up pass.
+static bool folds_routing(const coli_moe_shape* s, int32_t T, bool cached, bool mfma) {
+    return T == 1 && !cached && !mfma && s->n_routed <= kFusedMaxExperts;
+}
+
+static FusedRoute fused_route(const coli_moe_shape* s, const void* const* table,
+                              const void* shared_blob, int32_t* idx, float* w, uint8_t* ws,
+                              const WsLayout& W) {
+    FusedRoute fr{};
+    fr.codes = at<uint64_t>(ws, W.codes);
+    fr.scores = at<float>(ws, W.scores);
+    fr.table = table;
+    fr.shared = shared_blob;
+    fr.E = s->n_routed;
+    fr.k = s->top_k;
+    fr.topp = s->topp;
+    fr.idx = idx;
+    fr.w = w;
+    fr.rows_tok = at<int32_t>(ws, W.rows_tok);
+    fr.rows_out = at<int32_t>(ws, W.rows_out);
+    fr.items = at<WorkItem>(ws, W.items);
+    fr.n_items = at<int32_t>(ws, W.n_items);
+    return fr;
 }
 
 coli_status run_expert_ffn(const coli_moe_shape* s, const void* const* table, const float* x,
@@ -106,23 +133,8 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
     float* w = w_out ? w_out : at<float>(ws, W.w);
     bool encoded = false;
     // one token on the GEMV path: the gate/up pass routes (no separate plan pass)
-    const bool fold = T == 1 && !cache && !mfma && E <= kFusedMaxExperts;
-    FusedRoute fr{};
-    if (fold) {
-        fr.codes = at<uint64_t>(ws, W.codes);
-        fr.scores = at<float>(ws, W.scores);
-        fr.table = table;
-        fr.shared = shared_blob;
-        fr.E = E;
-        fr.k = k;
-        fr.topp = s->topp;
-        fr.idx = idx;
-        fr.w = w;
-        fr.rows_tok = at<int32_t>(ws, W.rows_tok);
-        fr.rows_out = at<int32_t>(ws, W.rows_out);
-        fr.items = at<WorkItem>(ws, W.items);
-        fr.n_items = at<int32_t>(ws, W.n_items);
-    }
+    const bool fold = folds_routing(s, T, cache != nullptr, mfma);
+    const FusedRoute fr = fold ? fused_route(s, table, shared_blob, idx, w, ws, W) : FusedRoute{};
     if (T <= kSmallT) {
         // router: logits + activation encoding, then route / union / work list
         SmallRouterArgs ra;
@@ -202,6 +214,23 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
     const bool adaptive = s->topp > 0.f && s->topp < 1.f;
     return launch_combine(at<float>(ws, W.y_rows), w, adaptive ? idx : nullptr, T, k, H,
                           shared_blob ? 1 : 0, s->routed_scale, y, stream);
+}
+
+coli_status run_rerun(const coli_moe_shape* s, int32_t T, const void* const* table,
+                      const void* shared_blob, int32_t which, uint8_t* ws, const WsLayout& W,
+                      hipStream_t stream) {
+    bool mfma = false;
+    coli_status st = pick_mfma(s, T, COLI_PATH_GEMV, &mfma);
+    if (st) return st;
+    const int32_t E = s->n_routed, k = s->top_k;
+    const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
+    // the routing the gate/up pass republishes goes to the workspace's own copy
+    const bool fold = folds_routing(s, T, false, false);
+    const FusedRoute fr = fold ? fused_route(s, table, shared_blob, at<int32_t>(ws, W.idx),
+                                             at<float>(ws, W.w), ws, W)
+                               : FusedRoute{};
+    return run_ffn(s, false, nullptr, T, max_items, at<float>(ws, W.y_rows), ws, W, true, stream,
+                   fold ? &fr : nullptr, which == 0 ? kPassGateUp : kPassDown);
 }
 
 coli_status run_lookahead(const coli_moe_shape* s, const float* x, int32_t T, const float* logits,

@@ -14,11 +14,13 @@ namespace coli {
 namespace {
 
 // q = rint(v / scale) with IEEE division, clamped to [QLO, QHI]. The quotient
-// is first formed as v * inv with inv = 1/scale correctly rounded: |q| <= 128
-// keeps that within 2^-15 of the correctly rounded quotient, so the two can
-// round to different integers only when t lies within 2^-15 of a
-// half-integer. Such values (and non-finite t, e.g. from a subnormal scale)
-// take the division.
+// is first formed as t = v * inv with inv = 1/scale correctly rounded. With
+// |v / scale| <= 128 (int8; <= 8 for int4), t lies within 128 * 2^-23 = 2^-16
+// of the exact quotient (2^-20 for int4), and the correctly rounded quotient
+// within half an ulp (2^-17) of it, so rint(t) can differ from rint of the
+// correctly rounded quotient only when t lies within 2^-15 (int4: 2^-19) of a
+// half-integer. The window used is 2^-14, twice the wider bound: such values
+// (and non-finite t, e.g. from a subnormal scale) take the division.
 template <int QLO, int QHI>
 __device__ __forceinline__ int quant_q(float v, float scale, float inv) {
     const float t = v * inv;

@@ -61,6 +61,8 @@ def lib():
                                        ctypes.POINTER(Expert), ctypes.POINTER(Expert), vp, vp,
                                        vp, vp]
             L.oracle_num_threads.restype = ctypes.c_int
+            L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            L.oracle_set_num_threads.restype = None
             L.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
             L.oracle_fp8_e4m3_value.restype = ctypes.c_double
             L.oracle_fp8_block_dequant.argtypes = [vp, vp, i64, i64, vp]
@@ -79,6 +81,11 @@ def _c(a, dt):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the oracle's loops (results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------- quantiser

@@ -23,6 +23,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the OpenMP loops that follow (n >= 1); changes no result, since
+ * every output element is summed by one thread in its stated order. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------- quantiser
  * [HF] container: each quantised weight is a U8 tensor of packed int4 nibbles
  * plus an F32 scale per row; the conversion rounds with np.rint, matching the

@@ -141,6 +141,7 @@ int oracle_layer(int32_t H, int32_t I, int32_t E, int32_t k, int32_t group, floa
 
 /* Threads the oracle's parallel loops use (1 without OpenMP). */
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

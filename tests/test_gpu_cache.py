@@ -155,3 +155,53 @@ def test_lookahead_with_router(coli):
     st = cache.stats()
     assert st["misses"] == 0 and st["prefetch_hits"] == n
     cache.close()
+
+
+def test_copy_failure_leaves_slot_empty(coli):
+    """A copy that cannot be enqueued (forced from the host before any copy is
+    issued) returns COLI_EHIP, leaves its slot empty and counts nothing; the
+    next lookup of that expert copies it, and the layer output is unchanged."""
+    import torch
+    L, H, I, E, k, slots = 1, 256, 128, 8, 2, 4
+    shape, sets, cache = _setup(coli, L, H, I, E, k, 0, slots)
+    try:
+        cache.ensure(0, [0, 1, 2, 3])                 # fills the four slots
+        cache.wait(0)                                 # (a copied slot counts as late until waited on)
+        cache.release(0)
+        torch.cuda.synchronize()
+        before = cache.stats()
+        coli.debug_fail_copies(1)
+        with pytest.raises(coli.ColiError) as ei:
+            cache.ensure(0, [4])                      # would evict expert 0 (the oldest)
+        assert ei.value.code == coli.COLI_EHIP
+        after = cache.stats()
+        for key in ("misses", "evictions", "bytes_h2d"):
+            assert after[key] == before[key], key
+        coli.debug_fail_copies(0)
+        # expert 4 is not resident and the failed slot's old occupant is gone:
+        # both are copied (4 into the empty slot, 0 over the oldest other slot,
+        # expert 1's); experts 2 and 3 are still hits
+        miss = cache.ensure(0, [4, 0])
+        assert miss.tolist() == [1, 1]
+        assert cache.stats()["misses"] == before["misses"] + 2
+        cache.wait(0)
+        cache.release(0)
+        miss = cache.ensure(0, [2, 3])
+        assert miss.tolist() == [0, 0]
+        assert cache.stats()["misses"] == before["misses"] + 2
+        cache.wait(0)
+        cache.release(0)
+        torch.cuda.synchronize()
+        # a cached layer call after the failure equals the resident one bit for bit
+        x = synth.activations(60, 0, 0, 3, H)
+        lg = synth.zipf_logits(60, 0, 0, 3, E, s=1.1)
+        coli.debug_fail_copies(0)
+        yc = coli.layer_fwd(shape, _dev(x), shared_blob=sets[0].shared_blob, logits=_dev(lg),
+                            cache=cache, layer=0)
+        yr = coli.layer_fwd(shape, _dev(x), table=sets[0].table, shared_blob=sets[0].shared_blob,
+                            logits=_dev(lg))
+        torch.cuda.synchronize()
+        assert torch.equal(yc, yr)
+    finally:
+        coli.debug_fail_copies(0)
+        cache.close()

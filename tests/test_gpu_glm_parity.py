@@ -1,0 +1,214 @@
+"""Parity at the full GLM-5.2 layer shape (hidden 6144, inter 2048, 256 + 1
+experts, top-8), in the launch configurations the benchmark times:
+
+- decode (batch 1, per-row scales, f32 router with bias): routing of all 1,000
+  tokens of the benchmark's workload against the oracle, bit for bit; the
+  outputs of 64 tokens spread over the run at 1e-3;
+- MTP verify (gs64, 125 steps of 8 tokens, Zipf(1.1) logits): routing, weights
+  and the batch union of every step bit for bit; the outputs of 64 tokens
+  (8 whole steps spread over the run) at 1e-3;
+- prefill (2048 tokens, Zipf(1.1) + 10% uniform, bf16 MFMA), per-row and gs64
+  experts: routing of every token bit for bit, the outputs of 64 tokens spread
+  over the batch at 2e-2.
+
+Every routed expert is resident on the device; the oracle holds copies of the
+experts the sampled tokens use."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import ExpertSet, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+H, I, E, K = 6144, 2048, 256, 8
+N_DECODE = 1000            # tokens of the decode workload
+T_MTP, STEPS_MTP = 8, 125  # MTP verify: 8-token steps, 1,000 tokens
+T_PREFILL = 2048
+N_SAMPLE = 64
+
+
+@pytest.fixture(scope="module")
+def coli():
+    import int4_routed_expert_sigmoid_amd as c
+    c.lib()
+    return c
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _spread(n, count):
+    return np.unique(np.linspace(0, n - 1, count).round().astype(int))
+
+
+# ------------------------------------------------------------- workloads
+def _decode_inputs():
+    wr = synth.router_weights(0, 0, E, H)
+    b = synth.bias(0, 0, E)
+    x = synth.activations(0, 0, 0, N_DECODE, H)
+    return wr, b, x
+
+
+def _mtp_inputs():
+    lg = synth.zipf_logits(0, 0, 0, T_MTP * STEPS_MTP, E, s=1.1)
+    x = synth.activations(0, 0, 0, T_MTP * STEPS_MTP, H)
+    return lg, x
+
+
+def _prefill_inputs():
+    lg = synth.zipf_logits(0, 1, 0, T_PREFILL, E, s=1.1, mix=0.1)
+    x = synth.activations(0, 1, 0, T_PREFILL, H)
+    return lg, x
+
+
+def _mtp_sample_steps():
+    return _spread(STEPS_MTP, N_SAMPLE // T_MTP)
+
+
+@pytest.fixture(scope="module")
+def rowwise(coli):
+    """All 257 per-row experts on the device; oracle copies of those used by the
+    sampled decode and prefill tokens."""
+    wr, b, x = _decode_inputs()
+    sd = _spread(N_DECODE, N_SAMPLE)
+    need = set(np.unique(oracle.route(oracle.router_logits(wr, x[sd]), b, K)[0]).tolist())
+    lg, _ = _prefill_inputs()
+    sp = _spread(T_PREFILL, N_SAMPLE)
+    need |= set(np.unique(oracle.route(lg[sp], None, K)[0]).tolist())
+    shape = coli.MoEShape(H, I, E, 1, K, 0)
+    return shape, ExpertSet(coli, shape, seed=0, which=range(E), keep_oracle=need)
+
+
+@pytest.fixture(scope="module")
+def gs64(coli):
+    """All 257 gs64 experts on the device; oracle copies of those used by the
+    sampled MTP steps and prefill tokens."""
+    lg, _ = _mtp_inputs()
+    rows = np.concatenate([np.arange(s * T_MTP, (s + 1) * T_MTP) for s in _mtp_sample_steps()])
+    need = set(np.unique(oracle.route(lg[rows], None, K)[0]).tolist())
+    lgp, _ = _prefill_inputs()
+    need |= set(np.unique(oracle.route(lgp[_spread(T_PREFILL, N_SAMPLE)], None, K)[0]).tolist())
+    shape = coli.MoEShape(H, I, E, 1, K, 64)
+    return shape, ExpertSet(coli, shape, seed=0, which=range(E), keep_oracle=need)
+
+
+# ----------------------------------------------------------------- decode
+def test_decode_glm_routing_all_tokens_and_64_outputs(coli, rowwise):
+    import torch
+    shape, ex = rowwise
+    wr, b, x = _decode_inputs()
+    wr_d, b_d, x_d = _dev(wr), _dev(b), _dev(x)
+    y = torch.empty((N_DECODE, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((N_DECODE, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((N_DECODE, K), dtype=torch.float32, device="cuda")
+    ws = coli.workspace(shape, 1, coli.PATH_GEMV)
+    # one token per call: the decode launch sequence (routing folded into gate/up)
+    for t in range(N_DECODE):
+        coli.layer_fwd(shape, x_d[t:t + 1], table=ex.table, shared_blob=ex.shared_blob,
+                       router_w=wr_d, bias=b_d, y=y[t:t + 1], idx_out=idx[t:t + 1],
+                       w_out=w[t:t + 1], path=coli.PATH_GEMV, ws=ws)
+    torch.cuda.synchronize()
+    idx_ref, w_ref = oracle.route(oracle.router_logits(wr, x), b, K)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), "routing differs on some of the 1,000 tokens"
+    assert np.array_equal(w.cpu().numpy(), w_ref)
+    sd = _spread(N_DECODE, N_SAMPLE)
+    _, y64, idx_s, _ = oracle.layer(x[sd], ex.oracle_list(), ex.shared_oracle, K, 0, 1.0,
+                                    wr=wr, bias=b)
+    assert np.array_equal(idx_s, idx_ref[sd])
+    err = rel_l2_rows(y.cpu().numpy()[sd], y64)
+    assert err.max() <= 1e-3, f"max rel L2 {err.max():.3e}"
+
+
+# -------------------------------------------------------------- MTP verify
+def test_mtp_verify_glm_full_run(coli, gs64):
+    import torch
+    shape, ex = gs64
+    lg, x = _mtp_inputs()
+    n = T_MTP * STEPS_MTP
+    lg_d, x_d = _dev(lg), _dev(x)
+    y = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((n, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, K), dtype=torch.float32, device="cuda")
+    ws = coli.workspace(shape, T_MTP, coli.PATH_GEMV)
+    for s in range(STEPS_MTP):
+        sl = slice(s * T_MTP, (s + 1) * T_MTP)
+        coli.layer_fwd(shape, x_d[sl], table=ex.table, shared_blob=ex.shared_blob, logits=lg_d[sl],
+                       y=y[sl], idx_out=idx[sl], w_out=w[sl], path=coli.PATH_GEMV, ws=ws)
+    torch.cuda.synchronize()
+    idx_ref, w_ref = oracle.route(lg, None, K)
+    idx_g = idx.cpu().numpy()
+    assert np.array_equal(idx_g, idx_ref)
+    assert np.array_equal(w.cpu().numpy(), w_ref)
+    # the batch union of every step, and that it names each expert once
+    n_unique = []
+    for s in range(STEPS_MTP):
+        sl = slice(s * T_MTP, (s + 1) * T_MTP)
+        counts, offsets, perm, unique, nu = coli.union(idx[sl], E)
+        c, o, p, u = oracle.union(idx_ref[sl], E)
+        torch.cuda.synchronize()
+        nu = int(nu.cpu()[0])
+        assert np.array_equal(counts.cpu().numpy(), c)
+        assert np.array_equal(offsets.cpu().numpy(), o)
+        assert np.array_equal(perm.cpu().numpy(), p)
+        assert nu == len(u) and np.array_equal(unique.cpu().numpy()[:nu], u)
+        assert len(set(u.tolist())) == len(u)
+        n_unique.append(nu)
+    assert 20 <= np.mean(n_unique) <= 60           # Zipf(1.1): tokens share experts
+    rows = np.concatenate([np.arange(s * T_MTP, (s + 1) * T_MTP) for s in _mtp_sample_steps()])
+    _, y64, _, _ = oracle.layer(x[rows], ex.oracle_list(), ex.shared_oracle, K, 64, 1.0,
+                                logits=lg[rows])
+    err = rel_l2_rows(y.cpu().numpy()[rows], y64)
+    assert err.max() <= 1e-3, f"max rel L2 {err.max():.3e}"
+
+
+# ------------------------------------------------------------------ prefill
+def _prefill_case(coli, shape, ex, group):
+    import torch
+    lg, x = _prefill_inputs()
+    idx = torch.empty((T_PREFILL, K), dtype=torch.int32, device="cuda")
+    y = coli.layer_fwd(shape, _dev(x), table=ex.table, shared_blob=ex.shared_blob, logits=_dev(lg),
+                       idx_out=idx, path=coli.PATH_MFMA)
+    torch.cuda.synchronize()
+    idx_ref, _ = oracle.route(lg, None, K)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    sp = _spread(T_PREFILL, N_SAMPLE)
+    _, y64, _, _ = oracle.layer(x[sp], ex.oracle_list(), ex.shared_oracle, K, group, 1.0,
+                                logits=lg[sp])
+    err = rel_l2_rows(y.cpu().numpy()[sp], y64)
+    assert err.max() <= 2e-2, f"max rel L2 {err.max():.3e}"
+    return err
+
+
+def test_prefill_glm_rowwise_64_tokens(coli, rowwise):
+    shape, ex = rowwise
+    _prefill_case(coli, shape, ex, 0)
+
+
+def test_prefill_glm_gs64_64_tokens(coli, gs64):
+    # gs64 experts at hidden 6144: 96 scale groups per gate/up row, so the
+    # group sums are staged in two chunks of 64 and 32
+    shape, ex = gs64
+    _prefill_case(coli, shape, ex, 64)
+
+
+def test_prefill_gs64_largest_hidden(coli):
+    """gs64 MFMA path at hidden 16384 (256 scale groups per gate/up row: four
+    chunks of staged group sums) and inter 4096."""
+    import torch
+    Hh, Ih, Eh, kh, T = 16384, 4096, 4, 1, 40
+    shape = coli.MoEShape(Hh, Ih, Eh, 1, kh, 64)
+    ex = ExpertSet(coli, shape, seed=44)
+    lg = synth.zipf_logits(44, 0, 0, T, Eh, s=1.1)
+    x = synth.activations(44, 0, 0, T, Hh)
+    idx = torch.empty((T, kh), dtype=torch.int32, device="cuda")
+    y = coli.layer_fwd(shape, _dev(x), table=ex.table, shared_blob=ex.shared_blob, logits=_dev(lg),
+                       idx_out=idx, path=coli.PATH_MFMA)
+    torch.cuda.synchronize()
+    _, y64, idx_ref, _ = oracle.layer(x, ex.oracle_list(), ex.shared_oracle, kh, 64, 1.0, logits=lg)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    err = rel_l2_rows(y.cpu().numpy(), y64)
+    assert err.max() <= 2e-2, f"max rel L2 {err.max():.3e}"

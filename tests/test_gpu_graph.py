@@ -85,3 +85,41 @@ def test_graph_replay_matches_eager(coli, T, group, path):
     assert np.array_equal(i_e[:T].cpu().numpy(), idx_ref)
     err = rel_l2_rows(y_e[:T].cpu().numpy(), y64)
     assert err.max() <= tol, f"max rel L2 {err.max():.3e}"
+
+
+@pytest.mark.parametrize("T,group,topp", [(1, 0, 0.0), (8, 64, 0.0), (1, 0, 0.6), (5, 0, 0.6)])
+def test_profile_rerun_recomputes_the_call(coli, T, group, topp):
+    """coli_profile_rerun (the benchmark's graph of back-to-back GEMV launches)
+    enqueues a pass of the last layer call again: the workspace it rewrites
+    must come out byte for byte as the call left it, and a graph of reruns
+    over several workspaces must leave each one unchanged too."""
+    import torch
+    H, I, E, k, seed = 512, 256, 16, 4, 43
+    shape = coli.MoEShape(H, I, E, 1, k, group, 1.0, topp)
+    ex = ExpertSet(coli, shape, seed=seed)
+    wr_d, b_d = _dev(synth.router_weights(seed, 0, E, H)), _dev(synth.bias(seed, 0, E))
+    n = 3
+    x = _dev(synth.activations(seed, 0, 0, n * T, H))
+    nb = coli.workspace_size(shape, T, coli.PATH_GEMV)
+    ws = torch.empty((n, nb), dtype=torch.uint8, device="cuda")
+    for i in range(n):
+        coli.layer_fwd(shape, x[i * T:(i + 1) * T], table=ex.table, shared_blob=ex.shared_blob,
+                       router_w=wr_d, bias=b_d, path=coli.PATH_GEMV, ws=ws[i])
+    torch.cuda.synchronize()
+    before = ws.clone()
+    for which in (0, 1):
+        coli.profile_rerun(shape, T, ex.table, ex.shared_blob, which, ws[0])
+    torch.cuda.synchronize()
+    assert torch.equal(ws, before)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n):
+            for which in (0, 1):
+                coli.profile_rerun(shape, T, ex.table, ex.shared_blob, which, ws[i], stream=stream)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ws, before)
+    with pytest.raises(coli.ColiError):
+        coli.profile_rerun(shape, 17, ex.table, ex.shared_blob, 0, ws[0])

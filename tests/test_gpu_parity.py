@@ -49,6 +49,47 @@ def test_quantize_bit_exact(coli, rows, cols, group):
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
+def _near_half_rows(n_rows, seed):
+    """Rows of 64 values whose quotients w / scale land on, or within a few ulps
+    of, half-integers: element 0 is the row maximum m (so scale = m / 7), the
+    others are h * scale for half-integers |h| <= 6.5, nudged by -3..3 ulps.
+    Rows with m = 7 (scale 1) and m = 3.5 (scale 0.5) give exact halves; the
+    others give quotients just either side of them, where the kernels' fast
+    quotient must defer to the exact division."""
+    rng = np.random.default_rng(seed)
+    halves = np.arange(-6.5, 7.0, 1.0)
+    rows = []
+    for r in range(n_rows):
+        m = np.float32([7.0, 3.5, 1.0, 0.3, 2.0 ** -3, 13.7][r % 6] * (1 + (r // 6) * 0.173))
+        scale = np.float32(m / np.float32(7.0))
+        h = rng.choice(halves, 63)
+        v = (h * np.float64(scale)).astype(np.float32)
+        nudge = rng.integers(-3, 4, 63) if r % 6 >= 2 else np.zeros(63, np.int64)
+        for step in range(3):                      # |nudge| one-ulp steps toward its sign
+            toward = np.where(nudge > 0, np.float32(np.inf), np.float32(-np.inf))
+            v = np.where(np.abs(nudge) > step, np.nextafter(v, toward), v).astype(np.float32)
+        row = np.concatenate([[m], v]).astype(np.float32)
+        rng.shuffle(row)
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("group", [0, 64])
+def test_quantize_near_half_quotients(coli, group):
+    import torch
+    w = _near_half_rows(96, 5)
+    if group == 64:
+        w = w.reshape(24, 256)                      # four groups per row, each with its own max
+    q, s = coli.quantize_int4(_dev(w), group)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_int4(w, group)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    # the exact halves are really there (scale 1 rows: w itself is the quotient)
+    exact = w.reshape(-1, 64)[0]
+    assert np.any(np.abs(exact - np.round(exact)) == 0.5)
+
+
 def test_quantize_expert_layout(coli):
     import torch
     shape = coli.MoEShape(256, 128, 8, 1, 2, 64)
