@@ -3,13 +3,16 @@
 Default workload (the headline): batch-1 decode, hidden 6144, inter 2048, 256
 routed + 1 shared experts, top-8 sigmoid routing from an f32 router, per-row
 int4 scales, all 257 expert blobs (4.86 GB) resident in HBM, 1,000 seeded
-tokens. A step is one token through the whole layer (router logits, route,
-union, gate/up GEMV, down GEMV, combine); steps run back to back on one stream
-(replayed from a HIP graph captured over all timed tokens).
+tokens. Every token is one pass of the whole layer (router logits, route,
+union, gate/up GEMV, down GEMV, combine), run back to back on one stream. A
+step is one pass over the 1,000-token workload, replayed from a HIP graph
+captured over all of its tokens; --steps K times K replays.
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (gate/up
-GEMV, HIP-event timed on its own stream inside the timed region) and the CPU
-oracle timed on a bounded sample of the same workload.
+GEMV: graph-replayed back-to-back launches timed with HIP events on their
+stream, with the shared expert and router read from memory that the MALL no
+longer holds, and the same warm), a parity check of the timed outputs against
+the CPU oracle, and the oracle itself timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+N_ROTATE = 14          # copies of the shared expert and router for the cold-MALL runs
 
 
 def log(msg):
@@ -37,10 +41,19 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed tokens (default 1000; 512 for the stream workload)")
-    ap.add_argument("--warmup", type=int, default=10)
+                    help="timed steps: decode, replays of the 1,000-token workload (default 10); "
+                         "mtp, 8-token verify batches (125); stream, tokens (512); prefill and "
+                         "convert, calls (10)")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tokens", type=int, default=1000, help="decode: tokens of the workload")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--graph", type=int, default=1, help="replay the timed tokens from a HIP graph")
+    ap.add_argument("--mall", default="cold", choices=["cold", "warm"],
+                    help="decode headline: cold, the shared expert and router rotate over "
+                         f"{N_ROTATE} copies so the MALL holds none of them when a token reads "
+                         "them (as in a model of many layers); warm, one copy, re-read every token")
+    ap.add_argument("--parity-tokens", type=int, default=64,
+                    help="timed outputs compared with the oracle (routing: every token)")
+    ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8, help="tokens of the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle sample for about this long")
@@ -72,11 +85,25 @@ def parse():
     return ap.parse_args()
 
 
-def build_experts(coli, shape, seed, dev, keep_host=(), layer=0):
+def spread(n, count):
+    """`count` indices spread evenly over range(n)."""
+    return np.unique(np.linspace(0, n - 1, min(n, count)).round().astype(int))
+
+
+def rel_l2_rows(y, ref):
+    a = np.asarray(y, np.float64)
+    b = np.asarray(ref, np.float64)
+    den = np.linalg.norm(b, axis=1)
+    return np.linalg.norm(a - b, axis=1) / np.where(den > 0, den, 1.0)
+
+
+def build_experts(coli, shape, seed, dev, oracle_ids=(), layer=0):
     """All routed + shared experts of `layer` quantised on the GPU from seeded
-    f32 weights. Returns (arena, table, shared_blob, host f32 copies of
-    `keep_host`)."""
+    f32 weights. The experts in `oracle_ids` are also quantised by the oracle
+    from the same f32 weights. Returns (arena, table, shared_blob, {id: oracle
+    expert})."""
     import torch
+    import oracle
     import synth
     H, I, E = shape.hidden, shape.inter, shape.n_routed
     nbytes = coli.blob_layout(shape)[1]
@@ -87,53 +114,352 @@ def build_experts(coli, shape, seed, dev, keep_host=(), layer=0):
     g_h = torch.empty((I, H), dtype=torch.float32).pin_memory()
     u_h = torch.empty((I, H), dtype=torch.float32).pin_memory()
     d_h = torch.empty((H, I), dtype=torch.float32).pin_memory()
-    kept = {}
+    qx = {}
     for e in range(E + 1):
         synth.expert_matrix(seed, layer, e, synth.MAT_GATE, I, H, out=g_h.numpy())
         synth.expert_matrix(seed, layer, e, synth.MAT_UP, I, H, out=u_h.numpy())
         synth.expert_matrix(seed, layer, e, synth.MAT_DOWN, H, I, out=d_h.numpy())
-        if e in keep_host:
-            kept[e] = (g_h.numpy().copy(), u_h.numpy().copy(), d_h.numpy().copy())
         g_d.copy_(g_h, non_blocking=True)
         u_d.copy_(u_h, non_blocking=True)
         d_d.copy_(d_h, non_blocking=True)
         coli.quantize_expert(shape, g_d, u_d, d_d, blob=arena[e * nbytes:(e + 1) * nbytes])
+        if e in oracle_ids:             # the CPU quantises while the GPU works
+            qx[e] = oracle.QExpert.quantize(g_h.numpy(), u_h.numpy(), d_h.numpy(), shape.group,
+                                            bits=shape.wbits)
         torch.cuda.synchronize()
         if e % 64 == 0:
             log(f"experts quantised: {e + 1}/{E + 1}")
     blobs = [arena.data_ptr() + e * nbytes for e in range(E)]
     table = coli.blob_table(blobs, dev)
     shared = arena[E * nbytes:(E + 1) * nbytes]
-    return arena, table, shared, kept
+    return arena, table, shared, qx
 
 
-def cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept, seconds):
-    """The oracle's whole layer on `sample` tokens of the same workload, timed
-    over about `seconds` of work."""
+def oracle_list(qx, shape):
+    """Oracle experts [E] (ids without a copy get one all-zero expert) and the shared one."""
     import oracle
-    H, I, E, k = shape.hidden, shape.inter, shape.n_routed, shape.top_k
-    bits = shape.wbits
+    H, I, E = shape.hidden, shape.inter, shape.n_routed
     z = np.zeros((I, H), np.float32)
-    zero = oracle.QExpert.quantize(z, z, np.zeros((H, I), np.float32), 0, bits=bits)
-    experts = [zero] * E
-    for e, (g, u, d) in kept.items():
-        if e < E:
-            experts[e] = oracle.QExpert.quantize(g, u, d, 0, bits=bits)
-    shared = oracle.QExpert.quantize(*kept[E], 0, bits=bits)
-    x = np.ascontiguousarray(x_all[:sample])
-    # the same tokens again until about `seconds` of CPU work (their ~50 experts,
-    # about 1 GB of weights, do not stay in the CPU caches between passes)
+    zero = oracle.QExpert.quantize(z, z, np.zeros((H, I), np.float32), shape.group,
+                                   bits=shape.wbits)
+    return [qx.get(e, zero) for e in range(E)], qx[E]
+
+
+def check_outputs(y_gpu, y_ref64, tol):
+    err = rel_l2_rows(y_gpu, y_ref64)
+    return {"y_tokens_checked": int(len(err)), "y_max_rel_l2": float(f"{err.max():.3e}"),
+            "y_tol": tol, "y_pass": bool(err.max() <= tol)}
+
+
+def sleep_cycles_for(stream, ms):
+    """Argument of torch.cuda._sleep (a bounded spin kernel) that holds the
+    stream for about `ms` milliseconds, from one timed probe of 2^20 cycles."""
+    import torch
+    probe = 1 << 20
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(probe)                 # first launch outside the timing
+        a.record()
+        torch.cuda._sleep(probe)
+        b.record()
+    b.synchronize()
+    per_cycle = max(a.elapsed_time(b), 1e-3) / probe
+    return max(1, int(ms / per_cycle))
+
+
+def time_replays(graph, stream, n):
+    """Milliseconds of each of n replays, HIP events on the graph's stream."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for i in range(n):
+            graph.replay()
+            evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+
+
+def cpu_baseline(coli_shape, x, oracle_args, seconds, label):
+    """The oracle's whole layer on the sample x, repeated for about `seconds`
+    on every core, then one pass over two tokens on one core (extrapolated)."""
+    import oracle
+    threads = oracle.num_threads()
     reps, dt = 0, 0.0
     t0 = time.perf_counter()
     while dt < seconds and reps < 1000:
-        oracle.layer(x, experts, shared, k, 0, 1.0, wr=wr, bias=b, topp=shape.topp)
+        oracle.layer(x, **oracle_args)
         reps += 1
         dt = time.perf_counter() - t0
-    return {"value": reps * sample / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"first {sample} tokens of the decode workload, {reps} passes ({reps * sample} "
-                      f"token-layers), whole layer (router logits, route, union, 9 expert FFNs, "
-                      f"combine), scalar C, f64 accumulation, OpenMP over output rows; {dt:.1f} s"}
+    oracle.set_num_threads(1)
+    try:
+        n1 = min(2, len(x))
+        t1 = time.perf_counter()
+        oracle.layer(np.ascontiguousarray(x[:n1]), **oracle_args)
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": reps * len(x) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(x)} tokens of the {label} workload spread over the run, {reps} passes "
+                      f"({reps * len(x)} token-layers), whole layer (router logits, route, union, "
+                      f"9 expert FFNs, combine), scalar C, f64 accumulation, OpenMP over output "
+                      f"rows; {dt:.1f} s",
+            "one_core": {"value": round(n1 / dt1, 4), "unit": "tokens/s", "cores": 1,
+                         "kind": "oracle, extrapolated",
+                         "sample": f"{n1} tokens once on one thread ({dt1:.2f} s)"}}
+
+
+def gemv_graph_rates(coli, shape, table, shared_of, wr_of, bias, x_d, tokens, stream, replays):
+    """Back-to-back graph-replayed launches of each GEMV pass. Every token is
+    first run once through the layer with a workspace of its own (shared expert
+    and router copy shared_of(t), wr_of(t)); then a graph of `tokens`
+    gate/up launches (coli_profile_rerun), one per token's workspace, and one
+    of the down launches are each replayed `replays` times, timed with HIP
+    events on their stream. Returns (gate/up us, down us) per launch (median
+    replay / tokens)."""
+    import torch
+    H = shape.hidden
+    nb = coli.workspace_size(shape, 1, coli.PATH_GEMV)
+    ws = torch.empty((tokens, nb), dtype=torch.uint8, device=x_d.device)
+    y = torch.empty((1, H), dtype=torch.float32, device=x_d.device)
+    with torch.cuda.stream(stream):
+        for t in range(tokens):
+            coli.layer_fwd(shape, x_d[t:t + 1], table=table, shared_blob=shared_of(t),
+                           router_w=wr_of(t), bias=bias, y=y, path=coli.PATH_GEMV, ws=ws[t],
+                           stream=stream)
+    torch.cuda.synchronize()
+    out = []
+    for which in (0, 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(tokens):
+                coli.profile_rerun(shape, 1, table, shared_of(t), which, ws[t], stream=stream)
+        torch.cuda.synchronize()
+        g.replay()                                     # uploads the graph
+        torch.cuda.synchronize()
+        ms = time_replays(g, stream, replays)
+        out.append(float(np.median(ms)) * 1e3 / tokens)
+        del g
+    del ws
+    return out[0], out[1]
+
+
+def run_decode(args, coli, dev):
+    import torch
+    import oracle
+    import synth
+    H, I, E, k = 6144, 2048, 256, 8
+    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0, args.topp, args.wbits)
+    seed, N = args.seed, args.tokens
+    K, W = args.steps, args.warmup
+    log(f"decode workload: {N} tokens per step, {W} + {K} steps, H={H} I={I} E={E}+1 k={k} "
+        f"topp={args.topp} wbits={args.wbits}")
+    wr = synth.router_weights(seed, 0, E, H)
+    b = synth.bias(seed, 0, E)
+    x_all = synth.activations(seed, 0, 0, N, H)
+
+    # oracle routing of every token (checked against the timed outputs), and
+    # the experts of the sampled tokens, which the oracle also needs
+    parity = not args.no_parity
+    sample = spread(N, args.parity_tokens)
+    need = set()
+    if parity or not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        idx_ref, w_ref = oracle.route(oracle.router_logits(wr, x_all), b, k, topp=args.topp)
+        need |= set(np.unique(idx_ref[sample]).tolist()) - {-1}
+        log(f"oracle routing of {N} tokens: {time.perf_counter() - t0:.1f} s")
+    with_prefill = not args.no_prefill and args.wbits == 4        # the MFMA path is int4 only
+    if with_prefill and parity:
+        lgp = synth.zipf_logits(seed, 1, 0, 2048, E, s=1.1, mix=0.1)
+        need |= set(np.unique(oracle.route(lgp[spread(2048, args.parity_tokens)], None, k)[0]).tolist())
+    t0 = time.perf_counter()
+    arena, table, shared, qx = build_experts(coli, shape, seed, dev, oracle_ids=need | {E})
+    log(f"experts ready in {time.perf_counter() - t0:.1f} s ({len(qx)} also on the oracle side)")
+
+    wr_d = torch.from_numpy(wr).to(dev)
+    b_d = torch.from_numpy(b).to(dev)
+    x_d = torch.from_numpy(x_all).to(dev)
+    # cold-MALL copies of the shared expert and the router: token t reads copy
+    # t % N_ROTATE, so between two reads of one copy about 13 tokens' weights
+    # (2.3 GB) stream through the 256 MB MALL
+    shared_c = [shared] + [shared.clone() for _ in range(N_ROTATE - 1)]
+    wr_c = [wr_d] + [wr_d.clone() for _ in range(N_ROTATE - 1)]
+    ws = coli.workspace(shape, 1, coli.PATH_GEMV, dev)
+    stream = torch.cuda.Stream()
+    # one prepared call per copy (the loops below then cost the host little)
+    calls = [coli.LayerCall(shape, 1, ws, table=table, shared_blob=shared_c[i], router_w=wr_c[i],
+                            bias=b_d, path=coli.PATH_GEMV, stream=stream) for i in range(N_ROTATE)]
+    outs = {m: (torch.empty((N, H), dtype=torch.float32, device=dev),
+                torch.empty((N, k), dtype=torch.int32, device=dev),
+                torch.empty((N, k), dtype=torch.float32, device=dev)) for m in ("cold", "warm")}
+
+    def token(t, mall):
+        y_d, idx_d, w_d = outs[mall]
+        c = calls[t % N_ROTATE] if mall == "cold" else calls[0]
+        c(x_d.data_ptr() + t * H * 4, y_d.data_ptr() + t * H * 4, idx_d.data_ptr() + t * k * 4,
+          w_d.data_ptr() + t * k * 4)
+
+    graphs = {}
+    for mall in ("cold", "warm"):
+        with torch.cuda.stream(stream):
+            for t in range(min(N, 16)):
+                token(t, mall)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(N):
+                token(t, mall)
+        torch.cuda.synchronize()
+        graphs[mall] = g
+    head, other = args.mall, "warm" if args.mall == "cold" else "cold"
+
+    # timed region: W untimed, then K timed replays of the N-token graph
+    for _ in range(max(1, W)):
+        graphs[head].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    per_step = time_replays(graphs[head], stream, K)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tok_s = K * N / elapsed
+    graphs[other].replay()
+    torch.cuda.synchronize()
+    per_step_other = time_replays(graphs[other], stream, max(2, K // 4))
+    log(f"decode ({head}): {tok_s:.0f} tokens/s; {other}: "
+        f"{N / (np.median(per_step_other) / 1e3):.0f} tokens/s")
+
+    # the GEMV kernels: graph-replayed back-to-back launches, cold and warm
+    reps = max(3, min(K, 10))
+    rot = lambda t: shared_c[t % N_ROTATE]
+    rot_wr = lambda t: wr_c[t % N_ROTATE]
+    gu_cold, dn_cold = gemv_graph_rates(coli, shape, table, rot, rot_wr, b_d, x_d, N, stream, reps)
+    gu_warm, dn_warm = gemv_graph_rates(coli, shape, table, lambda t: shared, lambda t: wr_d, b_d,
+                                        x_d, N, stream, reps)
+    # and eagerly, with HIP events attached to each dispatch (hipExtLaunchKernel);
+    # each chunk of tokens queued behind a short GPU sleep so the launches run
+    # back to back as in the graph instead of each starting on an idle GPU
+    chunk = 100
+    sleep_cycles = sleep_cycles_for(stream, chunk * 0.08)      # 80 us of host time per token
+    coli.profile_enable(2 * N + 16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for c0 in range(0, N, chunk):
+            torch.cuda._sleep(sleep_cycles)
+            for t in range(c0, min(c0 + chunk, N)):
+                token(t, head)
+    torch.cuda.synchronize()
+    n_gu, ms_gu = coli.profile_summary("gemv_gateup")
+    n_dn, ms_dn = coli.profile_summary("gemv_down")
+    coli.profile_enable(0)
+
+    y_d, idx_d, w_d = outs[head]
+    # algorithmic bytes per token: the routed experts the token uses (8, fewer
+    # with top-p: their mean over the tokens) and the shared one
+    routed = (idx_d >= 0).sum(dim=1).double().mean().item()
+    n_exp = routed + 1.0
+    wb = args.wbits // 4                      # bytes per two weights
+    gu_bytes = n_exp * (2 * I * (H * wb // 2) + 2 * I * 4)
+    dn_bytes = n_exp * (H * (I * wb // 2) + H * 4)
+    gbps = lambda nbytes, us: nbytes / (us * 1e-6) / 1e9
+    gu_us = gu_cold if head == "cold" else gu_warm
+    dn_us = dn_cold if head == "cold" else dn_warm
+    eager_gu_us = ms_gu / max(1, n_gu) * 1e3
+    eager_dn_us = ms_dn / max(1, n_dn) * 1e3
+
+    result_parity = None
+    if parity:
+        y_o, idx_o, _ = outs[other]
+        torch.cuda.synchronize()
+        idx_g = idx_d.cpu().numpy()
+        t0 = time.perf_counter()
+        experts, sh = oracle_list(qx, shape)
+        _, y64, _, _ = oracle.layer(x_all[sample], experts, sh, k, 0, 1.0, wr=wr, bias=b,
+                                    topp=args.topp)
+        result_parity = {
+            "idx_tokens_checked": N,
+            "idx_mismatch_tokens": int((idx_g != idx_ref).any(axis=1).sum()),
+            "w_mismatch_tokens": int((w_d.cpu().numpy() != w_ref).any(axis=1).sum()),
+            **check_outputs(y_d.cpu().numpy()[sample], y64, 1e-3),
+            "cold_equals_warm": bool(torch.equal(y_d, y_o) and torch.equal(idx_d, idx_o)),
+        }
+        result_parity["pass"] = bool(result_parity["idx_mismatch_tokens"] == 0 and
+                                     result_parity["w_mismatch_tokens"] == 0 and
+                                     result_parity["y_pass"] and result_parity["cold_equals_warm"])
+        log(f"parity: {result_parity} ({time.perf_counter() - t0:.1f} s)")
+
+    prefill = None
+    if with_prefill:
+        log("prefill: 2048 tokens through the same layer (bf16 MFMA)")
+        prefill = run_prefill(coli, shape, table, shared, seed, dev,
+                              qx=qx if parity else None, parity_tokens=args.parity_tokens)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        experts, sh = oracle_list(qx, shape)
+        xs = np.ascontiguousarray(x_all[sample[:args.cpu_sample]])
+        cpu = cpu_baseline(shape, xs, dict(experts=experts, shared=sh, k=k, group=0,
+                                           routed_scale=1.0, wr=wr, bias=b, topp=args.topp),
+                           args.cpu_seconds, "decode")
+
+    med = float(np.median(per_step))
+    med_other = float(np.median(per_step_other))
+    return {
+        "metric": "MoE-layer tokens/s at decode (int4 weight GB/s vs HBM peak) + prefill TFLOP/s",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(1e3 * elapsed / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"int{args.wbits} weights x 16-bit block-scaled activations (x and h as four "
+                 f"signed base-16 digit planes per 32-element block, one f32 scale per block), "
+                 f"exact int32 block sums, f32 accumulate",
+        "data": "synthetic (seeded Philox N(0,0.02) weights, N(0,1) activations, f32 router)",
+        "config": {"workload": "GLM-5.2-shaped MoE layer, batch-1 decode"
+                               + (f", adaptive expert top-p {args.topp}" if args.topp else "")
+                               + (", int8 experts" if args.wbits == 8 else ""),
+                   "hidden": H, "inter": I, "n_routed": E, "n_shared": 1, "top_k": k, "group": 0,
+                   "wbits": args.wbits, "tokens": N, "tokens_per_step": N, "graph": True,
+                   "mall": head, "topp": args.topp, "routed_experts_per_token": round(routed, 4)},
+        "step_ms": {"median": round(med, 4), "min": round(min(per_step), 4),
+                    "max": round(max(per_step), 4), "us_per_token_median": round(med * 1e3 / N, 3)},
+        f"{other}_mall": {"tokens_per_s_median": round(N / (med_other / 1e3), 2),
+                          "us_per_token_median": round(med_other * 1e3 / N, 3)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_gateup",
+                     "achieved": round(gbps(gu_bytes, gu_us), 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps(gu_bytes, gu_us) / HBM_PEAK_GBPS, 4),
+                     "traffic": (measured_traffic("gemv_gateup_decode_traffic.json")
+                                 if args.topp == 0.0 and args.wbits == 4 else None),
+                     "traffic_source": "profiles/gemv_gateup_decode_traffic.json (rocprofv3 "
+                                       "FETCH_SIZE + WRITE_SIZE, calibrated; null once the "
+                                       "kernel's sources change)",
+                     "bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_us, 3),
+                     "timing": f"graph of {N} back-to-back launches (one per token), median of "
+                               f"{reps} replays, HIP events on the launch stream, {head} MALL",
+                     "graph_frac": round(gbps(gu_bytes, gu_us) / HBM_PEAK_GBPS, 4),
+                     "cold_frac": round(gbps(gu_bytes, gu_cold) / HBM_PEAK_GBPS, 4),
+                     "warm_frac": round(gbps(gu_bytes, gu_warm) / HBM_PEAK_GBPS, 4),
+                     "eager_frac": round(gbps(gu_bytes, eager_gu_us) / HBM_PEAK_GBPS, 4),
+                     "eager_avg_launch_us": round(eager_gu_us, 3),
+                     "launches_timed": N * reps},
+        "expert_gemv": {
+            "gateup_us": {"cold": round(gu_cold, 3), "warm": round(gu_warm, 3),
+                          "eager": round(eager_gu_us, 3)},
+            "down_us": {"cold": round(dn_cold, 3), "warm": round(dn_warm, 3),
+                        "eager": round(eager_dn_us, 3)},
+            "gateup_GBps": round(gbps(gu_bytes, gu_us), 1),
+            "down_GBps": round(gbps(dn_bytes, dn_us), 1),
+            "down_frac": round(gbps(dn_bytes, dn_us) / HBM_PEAK_GBPS, 4),
+            "both_GBps": round(gbps(gu_bytes + dn_bytes, gu_us + dn_us), 1),
+            "both_frac": round(gbps(gu_bytes + dn_bytes, gu_us + dn_us) / HBM_PEAK_GBPS, 4),
+            "bytes_per_token": round(gu_bytes + dn_bytes)},
+        "parity": result_parity,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
 
 
 def measured_traffic(kernel_json):
@@ -153,30 +479,20 @@ def measured_traffic(kernel_json):
         return None
 
 
-def sleep_cycles_for(stream, ms):
-    """Argument of torch.cuda._sleep (a bounded spin kernel) that holds the
-    stream for about `ms` milliseconds, from one timed probe of 2^20 cycles."""
-    import torch
-    probe = 1 << 20
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(probe)                 # first launch outside the timing
-        a.record()
-        torch.cuda._sleep(probe)
-        b.record()
-    b.synchronize()
-    per_cycle = max(a.elapsed_time(b), 1e-3) / probe
-    return max(1, int(ms / per_cycle))
-
-
-def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
+def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3, qx=None,
+                parity_tokens=64):
     """2048-token prefill through the same layer: Zipf(1.1) + 10% uniform
-    routing (router logits with that popularity), bf16 MFMA grouped GEMM."""
+    routing (router logits with that popularity), bf16 MFMA grouped GEMM.
+    With oracle experts (qx), the outputs of `parity_tokens` tokens and the
+    routing of all are checked against the oracle."""
     import torch
+    import oracle
     import synth
     H, I, E, k, T = shape.hidden, shape.inter, shape.n_routed, shape.top_k, 2048
-    lg = torch.from_numpy(synth.zipf_logits(seed, 1, 0, T, E, s=1.1, mix=0.1)).to(dev)
-    x = torch.from_numpy(synth.activations(seed, 1, 0, T, H)).to(dev)
+    lg_np = synth.zipf_logits(seed, 1, 0, T, E, s=1.1, mix=0.1)
+    x_np = synth.activations(seed, 1, 0, T, H)
+    lg = torch.from_numpy(lg_np).to(dev)
+    x = torch.from_numpy(x_np).to(dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     ws = coli.workspace(shape, T, coli.PATH_MFMA, dev)
@@ -196,13 +512,28 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
     dt = (time.perf_counter() - t0) / calls
     n_gu, ms_gu = coli.profile_summary("gemm_gateup")
     n_dn, ms_dn = coli.profile_summary("gemm_down")
+    n_gv, ms_gv = coli.profile_summary("gemv_gateup")
+    n_gd, ms_gd = coli.profile_summary("gemv_down")
     coli.profile_enable(0)
     counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=E)
     flops_gu = 2.0 * 2 * H * I * (T * k + T)
     flops_dn = 2.0 * H * I * (T * k + T)
     gu_s, dn_s = ms_gu / max(1, n_gu) / 1e3, ms_dn / max(1, n_dn) / 1e3
+    gv_s = (ms_gv + ms_gd) / max(1, calls) / 1e3
     used = int((counts > 0).sum()) + shape.n_shared           # experts whose weights the call reads
     weight_bytes = used * coli.blob_layout(shape)[1]
+    par = None
+    if qx is not None:
+        sp = spread(T, parity_tokens)
+        idx_ref, _ = oracle.route(lg_np, None, k)
+        experts, sh = oracle_list(qx, shape)
+        _, y64, _, _ = oracle.layer(x_np[sp], experts, sh, k, shape.group, 1.0, logits=lg_np[sp])
+        par = {"idx_tokens_checked": T,
+               "idx_mismatch_tokens": int((idx.cpu().numpy() != idx_ref).any(axis=1).sum()),
+               **check_outputs(y.cpu().numpy()[sp], y64, 2e-2)}
+        par["pass"] = bool(par["idx_mismatch_tokens"] == 0 and par["y_pass"])
+        log(f"prefill parity: {par}")
+    gemm_s = gu_s + dn_s
     return {
         "workload": "prefill, 2048 tokens, Zipf(1.1) + 10% uniform routing, same layer"
                     + (", gs64 experts" if shape.group else ""),
@@ -211,46 +542,59 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3):
         "tflops_layer": round((flops_gu + flops_dn) / dt / 1e12, 2),
         "gemm_gateup_us": round(gu_s * 1e6, 2),
         "gemm_down_us": round(dn_s * 1e6, 2),
-        "gemm_tflops": round((flops_gu + flops_dn) / (gu_s + dn_s) / 1e12, 2) if n_gu else None,
-        "gemm_frac_of_bf16_peak": round((flops_gu + flops_dn) / (gu_s + dn_s) / 1e12 / BF16_PEAK_TFLOPS, 4) if n_gu else None,
+        "gemv_small_experts_us": round(gv_s * 1e6, 2) if n_gv else 0.0,
+        "gemm_tflops": round((flops_gu + flops_dn) / gemm_s / 1e12, 2) if n_gu else None,
+        "gemm_frac_of_bf16_peak": round((flops_gu + flops_dn) / gemm_s / 1e12 / BF16_PEAK_TFLOPS, 4) if n_gu else None,
         "algorithmic_tflop": round((flops_gu + flops_dn) / 1e12, 4),
         "experts_used": int((counts > 0).sum()),
         # routed experts by tokens routed to them (M), bins [lo, hi)
         "tokens_per_expert_histogram": {f"{lo}-{hi - 1}": int(((counts >= lo) & (counts < hi)).sum())
                                         for lo, hi in ((1, 9), (9, 17), (17, 33), (33, 65), (65, 129),
                                                        (129, 257), (257, 513), (513, T + 1))},
-        # every resident weight byte read once per call, over the two GEMMs' time
-        "weights_GBps_over_gemm_time": round(weight_bytes / (gu_s + dn_s) / 1e9, 1) if n_gu else None,
+        # every resident weight byte read once per call, over the call's time
+        "weights_GBps_over_call": round(weight_bytes / dt / 1e9, 1),
         "tokens_per_expert_max": int(counts.max()),
         "tokens_per_expert_median": float(np.median(counts[counts > 0])),
         "tokens_per_expert_min": int(counts[counts > 0].min()),
+        "parity": par,
     }
 
 
 def run_mtp(args, coli, dev):
     """MTP-verify batches: gs64 scales, 8 tokens per call, router logits with
-    Zipf(1.1) popularity (Gumbel top-k), bias 0, 125 calls = 1,000 tokens."""
+    Zipf(1.1) popularity (Gumbel top-k), bias 0; K timed calls (125 = 1,000
+    tokens) replayed from one graph. Routing of every timed token and the
+    outputs of 8 whole calls spread over the run are checked against the
+    oracle."""
     import torch
+    import oracle
     import synth
     H, I, E, k, T = 6144, 2048, 256, 8, 8
     shape = coli.MoEShape(H, I, E, 1, k, 64, 1.0)
-    steps = max(1, args.steps // T)
-    warm = max(1, args.warmup // T + 1)
+    steps = max(1, args.steps)
+    warm = max(1, args.warmup)
     n = steps + warm
+    lg_np = synth.zipf_logits(args.seed, 0, 0, n * T, E, s=1.1)
+    x_np = synth.activations(args.seed, 0, 0, n * T, H)
+    parity = not args.no_parity
+    psteps = warm + spread(steps, max(1, args.parity_tokens // T))
+    prow = np.concatenate([np.arange(s * T, (s + 1) * T) for s in psteps])
+    need = set(np.unique(oracle.route(lg_np[prow], None, k)[0]).tolist()) if parity else set()
     t0 = time.perf_counter()
-    arena, table, shared, _ = build_experts(coli, shape, args.seed, dev)
+    arena, table, shared, qx = build_experts(coli, shape, args.seed, dev, oracle_ids=need | {E})
     log(f"gs64 experts ready in {time.perf_counter() - t0:.1f} s")
-    lg = torch.from_numpy(synth.zipf_logits(args.seed, 0, 0, n * T, E, s=1.1)).to(dev)
-    x = torch.from_numpy(synth.activations(args.seed, 0, 0, n * T, H)).to(dev)
+    lg = torch.from_numpy(lg_np).to(dev)
+    x = torch.from_numpy(x_np).to(dev)
     y = torch.empty((n * T, H), dtype=torch.float32, device=dev)
     idx = torch.empty((n * T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((n * T, k), dtype=torch.float32, device=dev)
     ws = coli.workspace(shape, T, coli.PATH_GEMV, dev)
     stream = torch.cuda.Stream()
 
     def call(i):
         sl = slice(i * T, (i + 1) * T)
         coli.layer_fwd(shape, x[sl], table=table, shared_blob=shared, logits=lg[sl], y=y[sl],
-                       idx_out=idx[sl], path=coli.PATH_GEMV, ws=ws)
+                       idx_out=idx[sl], w_out=wts[sl], path=coli.PATH_GEMV, ws=ws, stream=stream)
 
     with torch.cuda.stream(stream):
         for i in range(warm):
@@ -264,8 +608,7 @@ def run_mtp(args, coli, dev):
     graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    graph.replay()
-    torch.cuda.synchronize()
+    ms = time_replays(graph, stream, 1)
     elapsed = time.perf_counter() - t0
     coli.profile_enable(2 * steps + 8)
     with torch.cuda.stream(stream):
@@ -285,12 +628,37 @@ def run_mtp(args, coli, dev):
     dn_s = ms_dn / max(1, n_dn) / 1e3
     gbps = float((gu_bytes + dn_bytes).mean()) / (gu_s + dn_s) / 1e9
     tok_s = steps * T / elapsed
+    par = None
+    if parity:
+        idx_ref, w_ref = oracle.route(lg_np, None, k)
+        experts, sh = oracle_list(qx, shape)
+        _, y64, _, _ = oracle.layer(x_np[prow], experts, sh, k, 64, 1.0, logits=lg_np[prow])
+        idx_g = idx.cpu().numpy()
+        # the union of every timed step against the oracle's
+        union_bad = 0
+        for s_ in range(warm, n):
+            rows = slice(s_ * T, (s_ + 1) * T)
+            c, o, p, u, nu = coli.union(idx[rows], E)
+            c_r, o_r, p_r, u_r = oracle.union(idx_ref[rows], E)
+            ok = (np.array_equal(c.cpu().numpy(), c_r) and np.array_equal(o.cpu().numpy(), o_r)
+                  and np.array_equal(p.cpu().numpy(), p_r) and int(nu.cpu()[0]) == len(u_r)
+                  and np.array_equal(u.cpu().numpy()[:len(u_r)], u_r))
+            union_bad += 0 if ok else 1
+        par = {"idx_tokens_checked": n * T,
+               "idx_mismatch_tokens": int((idx_g != idx_ref).any(axis=1).sum()),
+               "w_mismatch_tokens": int((wts.cpu().numpy() != w_ref).any(axis=1).sum()),
+               "union_steps_checked": steps, "union_mismatch_steps": union_bad,
+               **check_outputs(y.cpu().numpy()[prow], y64, 1e-3)}
+        par["pass"] = bool(par["idx_mismatch_tokens"] == 0 and par["w_mismatch_tokens"] == 0
+                           and union_bad == 0 and par["y_pass"])
+        log(f"mtp parity: {par}")
     return {
         "metric": "MTP-verify tokens/s (gs64, 8-token batches; weight GB/s vs HBM peak)",
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(1e3 * elapsed / steps, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights (gs64) x f32 activations (exact int32 nibble products), f32 accumulate",
+        "dtype": "int4 weights (gs64) x 16-bit block-scaled activations (four signed base-16 "
+                 "digit planes per 32-element block), exact int32 block sums, f32 accumulate",
         "data": "synthetic (seeded Philox N(0,0.02) weights, N(0,1) activations, Zipf(1.1) logits)",
         "config": {"workload": "MTP-verify batches of 8 tokens, GLM-5.2-shaped layer, gs64",
                    "hidden": H, "inter": I, "n_routed": E, "top_k": k, "group": 64,
@@ -298,10 +666,12 @@ def run_mtp(args, coli, dev):
         "unique_experts_per_token": round(float(uniq.mean()) / T, 3),
         "unique_experts_per_step_mean": round(float(uniq.mean()), 2),
         "unique_experts_per_step_range": [int(uniq.min()), int(uniq.max())],
+        "weight_bytes_per_step_mean": round(float((gu_bytes + dn_bytes).mean())),
         "roofline": {"bound": "hbm", "kernel": "gemv_gateup + gemv_down",
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "avg_gateup_us": round(gu_s * 1e6, 2), "avg_down_us": round(dn_s * 1e6, 2)},
+        "parity": par,
     }
 
 
@@ -447,7 +817,8 @@ def run_stream(args, coli, dev):
         "n_gpus": 1, "steps": n_tok - cold, "warmup": cold,
         "ms_per_step": main["ms_per_token_warm"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights x f32 activations (exact int32 nibble products), f32 accumulate",
+        "dtype": "int4 weights x 16-bit block-scaled activations (four signed base-16 digit planes "
+                 "per 32-element block), exact int32 block sums, f32 accumulate",
         "data": "synthetic (seeded Philox weights; layer l holds the layer-0 experts in a seeded order; locality routing)",
         "config": {"workload": "streaming decode, 16 GLM-5.2-shaped layers, 64-slot HBM cache per layer",
                    "hidden": H, "inter": I, "n_routed": E, "top_k": k, "layers": L, "slots": S,
@@ -456,6 +827,8 @@ def run_stream(args, coli, dev):
         **{key: v for key, v in main.items() if key != "policy"},
         "policies": results[1:],
     }
+
+
 
 
 def run_convert(args, coli, dev):
@@ -571,181 +944,46 @@ def pinned_bytes(nbytes):
 def main():
     args = parse()
     if args.steps is None:
-        args.steps = 512 if args.workload == "stream" else 1000
+        args.steps = {"stream": 512, "mtp": 125, "decode": 10}.get(args.workload, 10)
     if args.gpus != 1:
-        print(json.dumps({"error": "one-GPU benchmark: the layer runs on a single GPU here (how it would shard is described, not run); --gpus must be 1",
+        print(json.dumps({"error": "one-GPU benchmark: the layer runs on a single GPU here (how it "
+                                   "would shard is described, not run); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
-
-    import synth
     import int4_routed_expert_sigmoid_amd as coli
-    import oracle
 
+    coli.lib()                              # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")
-    if args.workload != "decode":
-        if args.workload == "copy":
-            line = run_copy(args, dev)
-        elif args.workload == "prefill":
-            shape = coli.MoEShape(6144, 2048, 256, 1, 8, args.group, 1.0)
-            arena, table, shared, _ = build_experts(coli, shape, args.seed, dev)
-            line = run_prefill(coli, shape, table, shared, args.seed, dev,
-                               calls=max(1, min(args.steps, 50)), warmup=max(1, args.warmup))
-            line = {"metric": "prefill TFLOP/s (2048 tokens, bf16 MFMA)", "value": line["tflops_layer"],
-                    "unit": "TFLOP/s", "n_gpus": 1, **line}
-        elif args.workload == "mtp":
-            line = run_mtp(args, coli, dev)
-        elif args.workload == "convert":
-            line = run_convert(args, coli, dev)
-        else:
-            line = run_stream(args, coli, dev)
-        print(json.dumps(line), flush=True)
-        return
-    H, I, E, k = 6144, 2048, 256, 8
-    shape = coli.MoEShape(H, I, E, 1, k, 0, 1.0, args.topp, args.wbits)
-    seed = args.seed
-    n_tok = args.warmup + args.steps
-    log(f"decode workload: {n_tok} tokens, H={H} I={I} E={E}+1 k={k} topp={args.topp}")
-
-    wr = synth.router_weights(seed, 0, E, H)
-    b = synth.bias(seed, 0, E)
-    x_all = synth.activations(seed, 0, 0, n_tok, H)
-    sample = 0 if args.no_cpu_baseline else min(args.cpu_sample, n_tok)
-    keep = set()
-    if sample:
-        idx_s, _ = oracle.route(oracle.router_logits(wr, x_all[:sample]), b, k)
-        keep = set(np.unique(idx_s).tolist()) | {E}
-    t0 = time.perf_counter()
-    arena, table, shared, kept = build_experts(coli, shape, seed, dev, keep)
-    log(f"experts ready in {time.perf_counter() - t0:.1f} s")
-
-    wr_d = torch.from_numpy(wr).to(dev)
-    b_d = torch.from_numpy(b).to(dev)
-    x_d = torch.from_numpy(x_all).to(dev)
-    y_d = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
-    idx_d = torch.empty((n_tok, k), dtype=torch.int32, device=dev)
-    ws = coli.workspace(shape, 1, coli.PATH_GEMV, dev)
-
-    stream = torch.cuda.Stream()
-    # one call per token with the fixed arguments prepared once (the eager
-    # pass below then keeps the GPU busy instead of waiting on the host)
-    call = coli.LayerCall(shape, 1, ws, table=table, shared_blob=shared, router_w=wr_d, bias=b_d,
-                          path=coli.PATH_GEMV, stream=stream)
-    xp, yp, ip = x_d.data_ptr(), y_d.data_ptr(), idx_d.data_ptr()
-
-    def token(t):
-        call(xp + t * H * 4, yp + t * H * 4, ip + t * k * 4)
-
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for t in range(args.warmup):
-            token(t)
-    torch.cuda.synchronize()
-
-    # timed region 1: the K tokens replayed from one HIP graph (how a decode
-    # loop is deployed); gives `value`
-    graph = None
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for t in range(args.warmup, n_tok):
-                token(t)
-        torch.cuda.synchronize()
-        graph.replay()                      # first replay uploads the graph
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        elapsed_graph = time.perf_counter() - t0
-    # timed region 2: the same K tokens launched eagerly, with HIP events
-    # attached to each GEMV kernel's dispatch on the stream it runs on (HIP
-    # cannot time events recorded inside a captured graph). The host issues a
-    # token more slowly than the GPU runs it, so each chunk of tokens is queued
-    # behind a short GPU sleep (a bounded spin kernel, longer than the host
-    # needs to queue the chunk): the timed kernels then run back to back, as
-    # in the graph, instead of each starting on an idle GPU.
-    chunk = 100
-    sleep_cycles = sleep_cycles_for(stream, chunk * 0.08)      # 80 us of host time per token
-    coli.profile_enable(2 * args.steps + 16)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for c0 in range(args.warmup, n_tok, chunk):
-            torch.cuda._sleep(sleep_cycles)
-            for t in range(c0, min(c0 + chunk, n_tok)):
-                token(t)
-    torch.cuda.synchronize()
-    n_gu, ms_gu = coli.profile_summary("gemv_gateup")
-    n_dn, ms_dn = coli.profile_summary("gemv_down")
-    coli.profile_enable(0)
-    if graph is None:                       # --graph 0: plain eager timing for `value`
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            for t in range(args.warmup, n_tok):
-                token(t)
-        torch.cuda.synchronize()
-        elapsed_graph = time.perf_counter() - t0
-    elapsed = elapsed_graph
-
-    # algorithmic bytes per token: the routed experts the token uses (8, fewer
-    # with top-p: their mean over the timed tokens) and the shared one
-    routed = (idx_d[args.warmup:] >= 0).sum(dim=1).double().mean().item()
-    n_exp = routed + 1.0
-    wb = args.wbits // 4                      # bytes per two weights
-    gu_bytes = n_exp * (2 * I * (H * wb // 2) + 2 * I * 4)
-    dn_bytes = n_exp * (H * (I * wb // 2) + H * 4)
-    gu_avg_s = ms_gu / max(1, n_gu) / 1e3
-    dn_avg_s = ms_dn / max(1, n_dn) / 1e3
-    gu_gbps = gu_bytes / gu_avg_s / 1e9 if n_gu else None
-    dn_gbps = dn_bytes / dn_avg_s / 1e9 if n_dn else None
-    gemv_gbps = (gu_bytes + dn_bytes) / (gu_avg_s + dn_avg_s) / 1e9 if n_gu and n_dn else None
-    tok_s = args.steps / elapsed
-
-    prefill = None
-    if not args.no_prefill and args.wbits == 4:           # the MFMA path is int4 only
-        log("prefill: 2048 tokens through the same layer (bf16 MFMA)")
-        prefill = run_prefill(coli, shape, table, shared, seed, dev)
-
-    cpu = None
-    if sample:
-        cpu = cpu_baseline_decode(shape, seed, wr, b, x_all, sample, kept, args.cpu_seconds)
-
-    line = {
-        "metric": "MoE-layer tokens/s at decode (int4 weight GB/s vs HBM peak) + prefill TFLOP/s",
-        "value": round(tok_s, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": f"int{args.wbits} weights x f32 activations (exact int32 nibble products), f32 accumulate",
-        "data": "synthetic (seeded Philox N(0,0.02) weights, N(0,1) activations, f32 router)",
-        "config": {"workload": "GLM-5.2-shaped MoE layer, batch-1 decode"
-                               + (f", adaptive expert top-p {args.topp}" if args.topp else "")
-                               + (", int8 experts" if args.wbits == 8 else ""),
-                   "hidden": H,
-                   "inter": I, "n_routed": E, "n_shared": 1, "top_k": k, "group": 0,
-                   "wbits": args.wbits,
-                   "tokens": args.steps, "graph": bool(args.graph), "topp": args.topp,
-                   "routed_experts_per_token": round(routed, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_gateup",
-                     "achieved": round(gu_gbps, 1) if gu_gbps else None,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4) if gu_gbps else None,
-                     "traffic": (measured_traffic("gemv_gateup_decode_traffic.json")
-                                 if args.topp == 0.0 and args.wbits == 4 else None),
-                     "bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_avg_s * 1e6, 3),
-                     "launches_timed": n_gu},
-        "expert_gemv": {"gateup_GBps": gu_gbps and round(gu_gbps, 1),
-                        "down_GBps": dn_gbps and round(dn_gbps, 1),
-                        "both_GBps": gemv_gbps and round(gemv_gbps, 1),
-                        "down_avg_us": round(dn_avg_s * 1e6, 3)},
-        "prefill": prefill,
-        "cpu_baseline": cpu,
-    }
+    if args.workload == "decode":
+        line = run_decode(args, coli, dev)
+    elif args.workload == "copy":
+        line = run_copy(args, dev)
+    elif args.workload == "prefill":
+        shape = coli.MoEShape(6144, 2048, 256, 1, 8, args.group, 1.0)
+        parity = not args.no_parity
+        need = set()
+        if parity:
+            import oracle
+            import synth
+            lgp = synth.zipf_logits(args.seed, 1, 0, 2048, 256, s=1.1, mix=0.1)
+            need = set(np.unique(oracle.route(lgp[spread(2048, args.parity_tokens)], None, 8)[0]).tolist())
+        arena, table, shared, qx = build_experts(coli, shape, args.seed, dev,
+                                                 oracle_ids=need | {256} if parity else ())
+        line = run_prefill(coli, shape, table, shared, args.seed, dev,
+                           calls=max(1, min(args.steps, 50)), warmup=max(1, args.warmup),
+                           qx=qx if parity else None, parity_tokens=args.parity_tokens)
+        line = {"metric": "prefill TFLOP/s (2048 tokens, bf16 MFMA)", "value": line["tflops_layer"],
+                "unit": "TFLOP/s", "n_gpus": 1,
+                "dtype": "int4 weights (exact bf16 q + 136) x bf16 activations, f32 accumulate",
+                "steps": max(1, min(args.steps, 50)),
+                "warmup": max(1, args.warmup), **line}
+    elif args.workload == "mtp":
+        line = run_mtp(args, coli, dev)
+    elif args.workload == "convert":
+        line = run_convert(args, coli, dev)
+    else:
+        line = run_stream(args, coli, dev)
     print(json.dumps(line), flush=True)
 
 
