@@ -225,6 +225,26 @@ COLI_API coli_status coli_moe_layer_fwd(const coli_moe_shape* shape, const float
                                int32_t layer, float* d_y, int32_t* d_idx_out, float* d_w_out,
                                int32_t path, void* d_ws, size_t ws_bytes, void* stream);
 
+/* coli_moe_layer_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same launch sequence and results, with resident experts
+ * only (no cache), running on a static scratch array of 64 MiB per device
+ * instead of a caller's workspace. The call allocates nothing. A call whose
+ * workspace would exceed 64 MiB (coli_moe_workspace_size; about 130 tokens at
+ * hidden 6144, inter 2048, 256 experts, top-8) returns COLI_ENOMEM before
+ * anything is enqueued. The scratch belongs to the calling thread's current
+ * device; the first call on a device looks up its address (make that first
+ * call outside graph capture). Every call on one device shares that device's
+ * scratch and leaves its contents behind: calls that may overlap on one device
+ * (two streams, or two threads) race and must be ordered by the caller. */
+COLI_API coli_status coli_moe_layer_fwd_noalloc(const coli_moe_shape* shape, const float* d_x,
+                                               int32_t T, const float* d_logits,
+                                               const float* d_router_w, const float* d_bias,
+                                               const void* const* d_blob_table,
+                                               const void* d_shared_blob, float* d_y,
+                                               int32_t* d_idx_out, float* d_w_out, int32_t path,
+                                               void* stream);
+
 /* ------------------------------------------------------------ expert cache
  * Per-layer LRU of expert blobs in an HBM arena, filled from pinned host
  * memory (practical guide section 二: per-layer LRU; a miss is one read of the

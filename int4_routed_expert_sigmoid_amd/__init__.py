@@ -24,7 +24,8 @@ EXPORTED = [
     "coli_quantize_expert", "coli_convert_fp8_int4", "coli_convert_fp8_expert",
     "coli_moe_router_logits", "coli_moe_route", "coli_moe_route_topp",
     "coli_moe_union_workspace_size", "coli_moe_union", "coli_moe_workspace_size",
-    "coli_moe_expert_ffn", "coli_moe_layer_fwd", "coli_expert_cache_create",
+    "coli_moe_expert_ffn", "coli_moe_layer_fwd", "coli_moe_layer_fwd_noalloc",
+    "coli_expert_cache_create",
     "coli_expert_cache_destroy", "coli_expert_cache_ensure", "coli_expert_cache_wait",
     "coli_expert_cache_release", "coli_expert_cache_table", "coli_expert_cache_stats",
     "coli_expert_cache_reset", "coli_expert_cache_pin", "coli_expert_cache_usage",
@@ -98,6 +99,8 @@ def lib():
                                               sz, vp]
             L.coli_moe_layer_fwd.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, vp, i32, vp,
                                              vp, vp, i32, vp, sz, vp]
+            L.coli_moe_layer_fwd_noalloc.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                     vp, i32, vp]
             L.coli_expert_cache_create.argtypes = [P(CacheCfg), P(vp)]
             L.coli_expert_cache_destroy.argtypes = [vp]
             L.coli_expert_cache_ensure.argtypes = [vp, i32, vp, i32, vp]
@@ -345,6 +348,22 @@ def layer_fwd(shape: MoEShape, x, table=None, shared_blob=None, logits=None, rou
                                     None if cache is None else ctypes.c_void_p(cache.handle), layer,
                                     _ptr(y), _ptr(idx_out), _ptr(w_out), path, _ptr(ws), ws.numel(),
                                     _stream(stream)))
+    return y
+
+
+def layer_fwd_noalloc(shape: MoEShape, x, table, shared_blob=None, logits=None, router_w=None,
+                      bias=None, y=None, idx_out=None, w_out=None, path=PATH_AUTO, stream=None):
+    """coli_moe_layer_fwd_noalloc: the layer on the library's static scratch
+    (no workspace, no cache). `y` must be given to allocate nothing here too."""
+    import torch
+    _need(x, torch.float32, "x")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, shape.hidden), dtype=torch.float32, device=x.device)
+    _check(lib().coli_moe_layer_fwd_noalloc(ctypes.byref(shape.c()), _ptr(x), T, _ptr(logits),
+                                            _ptr(router_w), _ptr(bias), _ptr(table),
+                                            _ptr(shared_blob), _ptr(y), _ptr(idx_out), _ptr(w_out),
+                                            path, _stream(stream)))
     return y
 
 

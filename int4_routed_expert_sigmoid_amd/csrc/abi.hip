@@ -2,6 +2,7 @@
 // sequence of each call (include/coli_moe.h documents every entry point).
 #include <algorithm>
 #include <exception>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -86,6 +87,37 @@ WsLayout ws_layout(const coli_moe_shape* s, int32_t T, int32_t path) {
     W.sh = take(R * (I / 64) * 4);
     W.bytes = o;
     return W;
+}
+
+// ------------------------------------------------ allocation-free layer call
+// coli_moe_layer_fwd_noalloc runs on this file-scope device array instead of a
+// caller's workspace. Every GPU the library runs on holds its own copy until
+// the process ends. In host code `scratch` names a host-side stand-in, never
+// the device memory: the device address is looked up once per device with
+// hipGetSymbolAddress and only that pointer is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the calling thread's current device,
+// looked up on the first call there.
+static coli_status scratch_on_current_device(uint8_t** out) {
+    int dev = -1;
+    COLI_CHECK_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(COLI_EUNSUPPORTED, "noalloc: device ordinal above 63");
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "noalloc: hipGetSymbolAddress(scratch)");
+        if (!p) return fail(COLI_EHIP, "noalloc: no device address for the scratch array");
+        g_scratch_ptr[dev] = (uint8_t*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return COLI_OK;
 }
 
 }  // namespace coli
@@ -292,6 +324,37 @@ coli_status coli_moe_layer_fwd(const coli_moe_shape* shape, const float* d_x, in
     return run_layer(shape, d_x, T, d_logits, d_router_w, d_bias, d_blob_table,
                      shape->n_shared ? d_shared_blob : nullptr, cache, layer, d_y, d_idx_out,
                      d_w_out, path, (uint8_t*)d_ws, W, (hipStream_t)stream);
+    COLI_GUARD_END
+}
+
+coli_status coli_moe_layer_fwd_noalloc(const coli_moe_shape* shape, const float* d_x, int32_t T,
+                                       const float* d_logits, const float* d_router_w,
+                                       const float* d_bias, const void* const* d_blob_table,
+                                       const void* d_shared_blob, float* d_y, int32_t* d_idx_out,
+                                       float* d_w_out, int32_t path, void* stream) {
+    COLI_GUARD_BEGIN
+    coli_status st = check_shape(shape);
+    if (st) return st;
+    if (T < 0) return fail(COLI_EINVAL, "layer_fwd_noalloc: T < 0");
+    if (path < 0 || path > 2) return fail(COLI_EINVAL, "layer_fwd_noalloc: path must be 0, 1 or 2");
+    if ((d_logits == nullptr) == (d_router_w == nullptr))
+        return fail(COLI_EINVAL, "layer_fwd_noalloc: give exactly one of logits and router_w");
+    if (shape->n_shared == 1 && !d_shared_blob) return fail(COLI_EINVAL, "layer_fwd_noalloc: shared blob missing");
+    if (!d_blob_table) return fail(COLI_EINVAL, "layer_fwd_noalloc: blob table missing");
+    if (T == 0) return COLI_OK;
+    if (!d_x || !d_y) return fail(COLI_EINVAL, "layer_fwd_noalloc: NULL pointer");
+    const WsLayout W = ws_layout(shape, T, path);
+    if (W.bytes > kScratchBytes)
+        return fail(COLI_ENOMEM, "layer_fwd_noalloc: this call needs " + std::to_string(W.bytes) +
+                                 " bytes of scratch; the static scratch holds " +
+                                 std::to_string(kScratchBytes) +
+                                 " (use coli_moe_layer_fwd with a workspace, or fewer tokens)");
+    uint8_t* ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st) return st;
+    return run_layer(shape, d_x, T, d_logits, d_router_w, d_bias, d_blob_table,
+                     shape->n_shared ? d_shared_blob : nullptr, nullptr, 0, d_y, d_idx_out,
+                     d_w_out, path, ws, W, (hipStream_t)stream);
     COLI_GUARD_END
 }
 
