@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--topp", type=float, default=0.0,
                     help="decode with the adaptive expert top-p (lossy; 0 = fixed top-8, the headline)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
+    ap.add_argument("--prefill-mix", type=float, default=0.1,
+                    help="prefill routing: share of uniform popularity mixed with Zipf(1.1) (0.1 is "
+                         "the workload; 1.0 spreads the 2048 tokens evenly, about 64 per expert)")
     ap.add_argument("--group", type=int, default=0, choices=[0, 64],
                     help="prefill workload: scale group of the experts (0 per-row, 64 gs64)")
     ap.add_argument("--pinned-layers", type=int, default=13,
@@ -270,7 +273,7 @@ def run_decode(args, coli, dev):
         log(f"oracle routing of {N} tokens: {time.perf_counter() - t0:.1f} s")
     with_prefill = not args.no_prefill and args.wbits == 4        # the MFMA path is int4 only
     if with_prefill and parity:
-        lgp = synth.zipf_logits(seed, 1, 0, 2048, E, s=1.1, mix=0.1)
+        lgp = synth.zipf_logits(seed, 1, 0, 2048, E, s=1.1, mix=args.prefill_mix)
         need |= set(np.unique(oracle.route(lgp[spread(2048, args.parity_tokens)], None, k)[0]).tolist())
     t0 = time.perf_counter()
     arena, table, shared, qx = build_experts(coli, shape, seed, dev, oracle_ids=need | {E})
@@ -391,7 +394,8 @@ def run_decode(args, coli, dev):
     if with_prefill:
         log("prefill: 2048 tokens through the same layer (bf16 MFMA)")
         prefill = run_prefill(coli, shape, table, shared, seed, dev,
-                              qx=qx if parity else None, parity_tokens=args.parity_tokens)
+                              qx=qx if parity else None, parity_tokens=args.parity_tokens,
+                              mix=args.prefill_mix)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -480,7 +484,7 @@ def measured_traffic(kernel_json):
 
 
 def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3, qx=None,
-                parity_tokens=64):
+                parity_tokens=64, mix=0.1):
     """2048-token prefill through the same layer: Zipf(1.1) + 10% uniform
     routing (router logits with that popularity), bf16 MFMA grouped GEMM.
     With oracle experts (qx), the outputs of `parity_tokens` tokens and the
@@ -489,17 +493,18 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3, qx=No
     import oracle
     import synth
     H, I, E, k, T = shape.hidden, shape.inter, shape.n_routed, shape.top_k, 2048
-    lg_np = synth.zipf_logits(seed, 1, 0, T, E, s=1.1, mix=0.1)
+    lg_np = synth.zipf_logits(seed, 1, 0, T, E, s=1.1, mix=mix)
     x_np = synth.activations(seed, 1, 0, T, H)
     lg = torch.from_numpy(lg_np).to(dev)
     x = torch.from_numpy(x_np).to(dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    ws = coli.workspace(shape, T, coli.PATH_MFMA, dev)
+    ws = coli.workspace(shape, T, coli.PATH_AUTO, dev)
 
     def call():
+        # automatic path: bf16 MFMA tiles, experts with at most 4 tokens on the GEMV family
         coli.layer_fwd(shape, x, table=table, shared_blob=shared, logits=lg, y=y, idx_out=idx,
-                       path=coli.PATH_MFMA, ws=ws)
+                       path=coli.PATH_AUTO, ws=ws)
 
     for _ in range(warmup):
         call()
@@ -535,7 +540,7 @@ def run_prefill(coli, shape, table, shared, seed, dev, calls=10, warmup=3, qx=No
         log(f"prefill parity: {par}")
     gemm_s = gu_s + dn_s
     return {
-        "workload": "prefill, 2048 tokens, Zipf(1.1) + 10% uniform routing, same layer"
+        "workload": f"prefill, 2048 tokens, Zipf(1.1) + {100 * mix:g}% uniform routing, same layer"
                     + (", gs64 experts" if shape.group else ""),
         "tokens_per_s": round(T / dt, 1),
         "ms_per_call": round(dt * 1e3, 4),
@@ -966,13 +971,14 @@ def main():
         if parity:
             import oracle
             import synth
-            lgp = synth.zipf_logits(args.seed, 1, 0, 2048, 256, s=1.1, mix=0.1)
+            lgp = synth.zipf_logits(args.seed, 1, 0, 2048, 256, s=1.1, mix=args.prefill_mix)
             need = set(np.unique(oracle.route(lgp[spread(2048, args.parity_tokens)], None, 8)[0]).tolist())
         arena, table, shared, qx = build_experts(coli, shape, args.seed, dev,
                                                  oracle_ids=need | {256} if parity else ())
         line = run_prefill(coli, shape, table, shared, args.seed, dev,
                            calls=max(1, min(args.steps, 50)), warmup=max(1, args.warmup),
-                           qx=qx if parity else None, parity_tokens=args.parity_tokens)
+                           qx=qx if parity else None, parity_tokens=args.parity_tokens,
+                           mix=args.prefill_mix)
         line = {"metric": "prefill TFLOP/s (2048 tokens, bf16 MFMA)", "value": line["tflops_layer"],
                 "unit": "TFLOP/s", "n_gpus": 1,
                 "dtype": "int4 weights (exact bf16 q + 136) x bf16 activations, f32 accumulate",

@@ -81,6 +81,8 @@ WsLayout ws_layout(const coli_moe_shape* s, int32_t T, int32_t path) {
     W.max_tiles = gemm_tiles_max((int32_t)R, (int32_t)max_items);
     W.tiles = take(W.max_tiles * 8);
     W.n_tiles = take(4);
+    W.gv_items = take(max_items * sizeof(WorkItem));
+    W.n_gv = take(4);
     W.xb = take((size_t)T * H * 2);
     W.sx = take((size_t)T * (H / 64) * 4);
     W.hb = take(R * I * 2);

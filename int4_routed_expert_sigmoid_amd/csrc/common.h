@@ -490,12 +490,25 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
                         hipStream_t stream);
 coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* planes, float* scales,
                           hipStream_t stream);
+// Digit planes of the rows a work list reads, for up to max_count tokens per
+// item: h_mode 0 encodes x [rows_idx[r]] (K = hidden) into planes [rows_idx[r]];
+// h_mode 1 encodes h = silu(g) * u from src = gu [R][2][K] (K = inter) of row
+// rows_idx[r] into planes [rows_idx[r]].
+coli_status launch_encode_items(const WorkItem* items, const int32_t* n_items, int32_t max_items,
+                                int32_t max_count, const int32_t* rows_idx, const float* src,
+                                int32_t K, int h_mode, uint32_t* planes, float* scales,
+                                hipStream_t stream);
+
+// Prefill split: with the MFMA path chosen automatically, an expert with at
+// most this many tokens runs on the GEMV family instead of MFMA tiles.
+constexpr int kGemvMaxTokens = 4;
 // gate/up then down GEMV over a work list.
 // gu [rows][2][I] f32 holds silu(g) and u between the two passes; for
 // batches (max_count > 1) an activation pass encodes h = silu(g) * u of all
 // `rows` rows into hplanes [rows][I/32][16] / hscale [rows][I/32].
-// passes: kPassGateUp and/or kPassDown (the activation pass goes with down).
-constexpr int kPassGateUp = 1, kPassDown = 2, kPassBoth = 3;
+// passes: kPassGateUp and/or kPassDown (the activation pass of batches goes
+// with down unless kPassNoAct is set: the caller has encoded h itself).
+constexpr int kPassGateUp = 1, kPassDown = 2, kPassBoth = 3, kPassNoAct = 4;
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,

@@ -19,13 +19,16 @@ struct GemmArgs {
     float* y_rows;             // [R][H] unweighted expert outputs, by output row
     BlobLayout L;
     int32_t H, I, group;
+    int32_t gv_max;            // items with at most this many tokens go to the GEMV list (0: none)
+    WorkItem* gv_items;        // [max_items] GEMV work list (items in order)
+    int32_t* n_gv;
 };
 
 // Upper bound of the number of 64-token tiles for `rows` slot-list rows
 // spread over at most `max_items` work items.
 size_t gemm_tiles_max(int32_t rows, int32_t max_items);
 
-// prep (x -> bf16 + group sums), tile list, gate/up GEMM, down GEMM.
+// prep (x -> bf16 + group sums), tile list (and GEMV list), gate/up GEMM, down GEMM.
 coli_status launch_mfma_ffn(const GemmArgs& a, const float* x, int32_t T, int32_t max_tiles,
                             hipStream_t stream);
 

@@ -108,32 +108,48 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ x, 
 }
 
 // ------------------------------------------------------------ tile list
-// (item, first token) of every 64-token tile, items in order.
+// (item, first token) of every 64-token tile, items in order. Items with at
+// most gv_max tokens get no tiles: they are compacted, in order, into the
+// GEMV work list gv_items / *n_gv (gv_max 0: every item takes tiles).
 __global__ __launch_bounds__(256) void tiles_kernel(const WorkItem* __restrict__ items,
                                                     const int32_t* __restrict__ n_items,
                                                     int2* __restrict__ tiles,
-                                                    int32_t* __restrict__ n_tiles) {
+                                                    int32_t* __restrict__ n_tiles, int gv_max,
+                                                    WorkItem* __restrict__ gv_items,
+                                                    int32_t* __restrict__ n_gv) {
     __shared__ int sh[256];
+    __shared__ int sg[256];
     const int t = threadIdx.x;
     const int ni = *n_items;
-    int base = 0;
+    int base = 0, gbase = 0;
     for (int i0 = 0; i0 < ni; i0 += 256) {
         const int i = i0 + t;
-        const int c = i < ni ? (items[i].count + kTileM - 1) / kTileM : 0;
+        WorkItem it{};
+        if (i < ni) it = items[i];
+        const bool small = i < ni && it.count <= gv_max;
+        const int c = (i < ni && !small) ? (it.count + kTileM - 1) / kTileM : 0;
         sh[t] = c;
+        sg[t] = small ? 1 : 0;
         __syncthreads();
         for (int o = 1; o < 256; o <<= 1) {
             const int add = t >= o ? sh[t - o] : 0;
+            const int addg = t >= o ? sg[t - o] : 0;
             __syncthreads();
             sh[t] += add;
+            sg[t] += addg;
             __syncthreads();
         }
         const int start = base + sh[t] - c;
         for (int j = 0; j < c; ++j) tiles[start + j] = make_int2(i, j * kTileM);
+        if (small) gv_items[gbase + sg[t] - 1] = it;
         base += sh[255];
+        gbase += sg[255];
         __syncthreads();
     }
-    if (t == 0) *n_tiles = base;
+    if (t == 0) {
+        *n_tiles = base;
+        *n_gv = gbase;
+    }
 }
 
 constexpr int kCsChunk = 64;        // 64-column groups staged in LDS at a time (gs64)
@@ -166,15 +182,14 @@ __device__ __forceinline__ void stage_group_sums(float* s, const float* sums, co
 constexpr int kGroupTiles = 2;
 
 __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& rb) {
-    const int n = n_tiles * n_rb;
-    const int per = (n + 7) / 8;
-    const int local = blockIdx.x >> 3;
-    if (local >= per) return false;
-    const int w = (int)(blockIdx.x & 7) * per + local;
-    if (w >= n) return false;
-    const int gsz = kGroupTiles * n_rb;
-    const int grp = w / gsz, r = w % gsz;
+    const int gsz = kGroupTiles * n_rb;                      // units per group
+    const int n_groups = (n_tiles + kGroupTiles - 1) / kGroupTiles;
+    const int xcd = (int)(blockIdx.x & 7), local = (int)(blockIdx.x >> 3);
+    const int grp = (local / gsz) * 8 + xcd;                 // XCD x takes groups x, x + 8, ...
+    if (grp >= n_groups) return false;
+    const int r = local % gsz;
     const int gt = min(kGroupTiles, n_tiles - grp * kGroupTiles);
+    if (r >= gt * n_rb) return false;
     rb = r / gt;
     tile = grp * kGroupTiles + r % gt;
     return true;
@@ -418,7 +433,7 @@ __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& i
             const int mi = mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);     // token in the tile
             const float g = GS ? out[0][mb][j] : fg * (out[0][mb][j] - kOffset * s_tot[mi]);
             const float u = GS ? out[1][mb][j] : fu * (out[1][mb][j] - kOffset * s_tot[mi]);
-            const float h = g / (1.f + expf(-g)) * u;
+            const float h = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
             rsum[j] = bf16_round(h);
             const int o = s_out[mi];
             if (o >= 0 && wlive) a.hb[(size_t)o * I + slot_pos(irow)] = bf16_bits(h);
@@ -551,6 +566,12 @@ void gemm_down_kernel(GemmArgs a) {
 
 }  // namespace
 
+// Workgroups per XCD for unit_of: whole groups, the groups dealt round-robin.
+static size_t unit_slots(int32_t max_tiles, int n_rb) {
+    const size_t n_groups = ((size_t)max_tiles + kGroupTiles - 1) / kGroupTiles;
+    return (n_groups + 7) / 8 * (size_t)kGroupTiles * (size_t)n_rb;
+}
+
 size_t gemm_tiles_max(int32_t rows, int32_t max_items) {
     return (size_t)rows / kTileM + (size_t)max_items + 1;
 }
@@ -563,18 +584,19 @@ coli_status launch_mfma_ffn(const GemmArgs& a, const float* x, int32_t T, int32_
     launch(prep_kernel, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream, x, T,
            a.H, a.xb, a.sx);
     COLI_CHECK_LAUNCH("prep kernel launch");
-    launch(tiles_kernel, dim3(1), dim3(256), 0, stream, a.items, a.n_items, a.tiles, a.n_tiles);
+    launch(tiles_kernel, dim3(1), dim3(256), 0, stream, a.items, a.n_items, a.tiles, a.n_tiles,
+           a.gv_max, a.gv_items, a.n_gv);
     COLI_CHECK_LAUNCH("tile list kernel launch");
     {
         ProfTag prof("gemm_gateup");
-        const dim3 grid((unsigned)(8 * (((size_t)max_tiles * ((a.I + 127) / 128) + 7) / 8)));
+        const dim3 grid((unsigned)(8 * unit_slots(max_tiles, (a.I + 127) / 128)));
         if (a.group) launch(gemm_gateup_kernel<true>, grid, dim3(256), 0, stream, a);
         else launch(gemm_gateup_kernel<false>, grid, dim3(256), 0, stream, a);
     }
     COLI_CHECK_LAUNCH("gate/up GEMM launch");
     {
         ProfTag prof("gemm_down");
-        const dim3 grid((unsigned)(8 * (((size_t)max_tiles * ((a.H + 255) / 256) + 7) / 8)));
+        const dim3 grid((unsigned)(8 * unit_slots(max_tiles, (a.H + 255) / 256)));
         if (a.group) launch(gemm_down_kernel<true>, grid, dim3(256), 0, stream, a);
         else launch(gemm_down_kernel<false>, grid, dim3(256), 0, stream, a);
     }

@@ -67,6 +67,42 @@ __global__ __launch_bounds__(256) void act_encode_kernel(const float* __restrict
     }
 }
 
+// Digit planes of the rows a work list reads (launch_encode_items). Thread
+// (m, block, quarter) of item blockIdx.y; the four quarters of a block are
+// adjacent lanes and leave together when m is past the item's tokens.
+template <bool HM>
+__global__ __launch_bounds__(256) void encode_items_kernel(const WorkItem* __restrict__ items,
+                                                           const int32_t* __restrict__ n_items,
+                                                           const int32_t* __restrict__ rows_idx,
+                                                           const float* __restrict__ src, int K,
+                                                           uint32_t* __restrict__ planes,
+                                                           float* __restrict__ scales) {
+    if ((int)blockIdx.y >= *n_items) return;
+    const WorkItem it = items[blockIdx.y];
+    const int C = K / kBlock;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int m = (int)(g / (C * 4)), rem = (int)(g % (C * 4));
+    if (m >= it.count) return;
+    const int row = rows_idx[it.begin + m];
+    const int blk = rem >> 2, q = rem & 3;
+    float v[8];
+    if constexpr (HM) {
+        const float* gp = src + (size_t)row * 2 * K + blk * kBlock + q * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = gp[e] * gp[K + e];               // silu(g) * u
+    } else {
+        const float* p = src + (size_t)row * K + blk * kBlock + q * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = p[e];
+    }
+    uint32_t words[kPlanes];
+    const float sc = encode_quarter(v, words);
+    uint32_t* dst = planes + ((size_t)row * C + blk) * kWordsPerBlock;
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p) dst[p * 4 + q] = words[p];
+    if (q == 0) scales[(size_t)row * C + blk] = sc;
+}
+
 // ----------------------------------------------------------------- combine
 // y[t][c] = shared[t][c] + rs * sum_j w[t][j] * y_rows[t*k + j][c], slot order.
 // Grid: (column blocks of 256, tokens); the slot loads are issued in groups of
@@ -120,6 +156,19 @@ coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* pla
     return COLI_OK;
 }
 
+coli_status launch_encode_items(const WorkItem* items, const int32_t* n_items, int32_t max_items,
+                                int32_t max_count, const int32_t* rows_idx, const float* src,
+                                int32_t K, int h_mode, uint32_t* planes, float* scales,
+                                hipStream_t stream) {
+    if (max_items == 0 || max_count == 0) return COLI_OK;
+    const int64_t threads = (int64_t)max_count * (K / kBlock) * 4;
+    const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)max_items);
+    if (h_mode) launch(encode_items_kernel<true>, grid, dim3(256), 0, stream, items, n_items, rows_idx, src, K, planes, scales);
+    else launch(encode_items_kernel<false>, grid, dim3(256), 0, stream, items, n_items, rows_idx, src, K, planes, scales);
+    COLI_CHECK_LAUNCH("item encoding kernel launch");
+    return COLI_OK;
+}
+
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
                             int32_t max_count, int32_t rows, const int32_t* rows_tok,
                             const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
@@ -141,7 +190,7 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
         COLI_CHECK_LAUNCH("gate/up GEMV launch");
     }
     if (!(passes & kPassDown)) return COLI_OK;
-    if (mt > 1) {
+    if (mt > 1 && !(passes & kPassNoAct)) {
         const int64_t threads = (int64_t)rows * (I / kBlock) * 4;
         launch(act_encode_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, gu,
                rows, I, hplanes, hscale);

@@ -17,11 +17,16 @@ template <typename T>
 static T* at(uint8_t* ws, size_t off) { return reinterpret_cast<T*>(ws + off); }
 
 // Decide the FFN path: the GEMV family for small batches, the bf16 MFMA
-// grouped GEMM for large ones (auto), or the caller's choice.
-static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, bool* mfma) {
+// grouped GEMM for large ones (auto), or the caller's choice. *split: with
+// the MFMA path chosen automatically, experts with at most kGemvMaxTokens
+// tokens run on the GEMV family (the batch union reads each of them once
+// either way; for so few tokens a dense tile would be mostly padding).
+static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, bool* mfma,
+                             bool* split = nullptr) {
     // the MFMA path dequantises int4 weights only; int8 experts always take the GEMV family
     const bool int8 = s->wbits == 8;
     const bool shape_ok = s->hidden % 64 == 0 && s->inter % 64 == 0 && !int8;
+    if (split) *split = false;
     if (path == COLI_PATH_MFMA) {
         if (int8) return fail(COLI_EUNSUPPORTED, "mfma path: int4 weights only");
         if (!shape_ok) return fail(COLI_EUNSUPPORTED, "mfma path: hidden and inter must be multiples of 64");
@@ -30,6 +35,7 @@ static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, b
         *mfma = false;
     } else {
         *mfma = shape_ok && T > kSmallT;
+        if (split) *split = *mfma;
     }
     return COLI_OK;
 }
@@ -37,7 +43,7 @@ static coli_status pick_mfma(const coli_moe_shape* s, int32_t T, int32_t path, b
 static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, int32_t T,
                            int32_t max_items, float* y_rows, uint8_t* ws, const WsLayout& W,
                            bool x_encoded, hipStream_t stream, const FusedRoute* fused = nullptr,
-                           int passes = kPassBoth) {
+                           int passes = kPassBoth, bool split = false) {
     const int32_t H = s->hidden, I = s->inter;
     if (mfma) {
         GemmArgs g;
@@ -54,9 +60,34 @@ static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, i
         g.y_rows = y_rows;
         g.L = blob_layout(H, I, s->group);
         g.H = H; g.I = I; g.group = s->group;
-        const int32_t max_tiles = (int32_t)gemm_tiles_max(
-            (int32_t)((int64_t)T * s->top_k + T), max_items);
-        return launch_mfma_ffn(g, x, T, max_tiles, stream);
+        g.gv_max = split ? kGemvMaxTokens : 0;
+        g.gv_items = at<WorkItem>(ws, W.gv_items);
+        g.n_gv = at<int32_t>(ws, W.n_gv);
+        const int32_t rows = (int32_t)((int64_t)T * s->top_k + T);
+        const int32_t max_tiles = (int32_t)gemm_tiles_max(rows, max_items);
+        coli_status st = launch_mfma_ffn(g, x, T, max_tiles, stream);
+        if (st || !split) return st;
+        // the experts with few tokens: GEMV family over the compacted list,
+        // with the digit planes of just the rows it reads
+        const int32_t* rows_tok = at<int32_t>(ws, W.rows_tok);
+        const int32_t* rows_out = at<int32_t>(ws, W.rows_out);
+        st = launch_encode_items(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows_tok, x, H, 0,
+                                 at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
+        if (st) return st;
+        FusedRoute none{};
+        st = launch_gemv_ffn(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows, rows_tok, rows_out,
+                             at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), at<float>(ws, W.gu),
+                             at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_rows, H, I,
+                             s->group, s->wbits, none, stream, kPassGateUp);
+        if (st) return st;
+        st = launch_encode_items(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows_out,
+                                 at<float>(ws, W.gu), I, 1, at<uint32_t>(ws, W.hplanes),
+                                 at<float>(ws, W.hscale), stream);
+        if (st) return st;
+        return launch_gemv_ffn(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows, rows_tok, rows_out,
+                               at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), at<float>(ws, W.gu),
+                               at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_rows, H, I,
+                               s->group, s->wbits, none, stream, kPassDown | kPassNoAct);
     }
     if (!x_encoded) {
         coli_status st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
@@ -103,15 +134,16 @@ coli_status run_expert_ffn(const coli_moe_shape* s, const void* const* table, co
                            const int32_t* unique, const int32_t* n_unique, float* y_assign,
                            int32_t path, uint8_t* ws, const WsLayout& W, hipStream_t stream) {
     const int32_t E = s->n_routed, k = s->top_k;
-    bool mfma = false;
-    coli_status st = pick_mfma(s, T, path, &mfma);
+    bool mfma = false, split = false;
+    coli_status st = pick_mfma(s, T, path, &mfma, &split);
     if (st) return st;
     st = launch_plan(offsets, perm, unique, n_unique, table, nullptr, T, k, E, nullptr, 0,
                      at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items),
                      at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
     if (st) return st;
     const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k);
-    return run_ffn(s, mfma, x, T, max_items, y_assign, ws, W, false, stream);
+    return run_ffn(s, mfma, x, T, max_items, y_assign, ws, W, false, stream, nullptr, kPassBoth,
+                   split);
 }
 
 coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const float* logits,
@@ -126,8 +158,8 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
     }
     // with a cache the work items are formed after placement (table unused here)
     const void* const* route_table = cache ? nullptr : table;
-    bool mfma = false;
-    coli_status st = pick_mfma(s, T, path, &mfma);
+    bool mfma = false, split = false;
+    coli_status st = pick_mfma(s, T, path, &mfma, &split);
     if (st) return st;
     int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, W.idx);
     float* w = w_out ? w_out : at<float>(ws, W.w);
@@ -181,7 +213,7 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
     const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
     if (!cache) {
         st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W, encoded, stream,
-                     fold ? &fr : nullptr);
+                     fold ? &fr : nullptr, kPassBoth, split);
         if (st) return st;
     } else {
         // place: read the routing back, make the experts resident (misses are
@@ -204,7 +236,7 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
                              at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out), stream);
             if (st) return st;
             st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W,
-                         encoded || phase == 1, stream);
+                         encoded || phase == 1, stream, nullptr, kPassBoth, split);
             if (st) return st;
         }
         st = coli_expert_cache_release(cache, layer, (void*)stream);

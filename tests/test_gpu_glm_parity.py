@@ -166,12 +166,12 @@ def test_mtp_verify_glm_full_run(coli, gs64):
 
 
 # ------------------------------------------------------------------ prefill
-def _prefill_case(coli, shape, ex, group):
+def _prefill_case(coli, shape, ex, group, path):
     import torch
     lg, x = _prefill_inputs()
     idx = torch.empty((T_PREFILL, K), dtype=torch.int32, device="cuda")
     y = coli.layer_fwd(shape, _dev(x), table=ex.table, shared_blob=ex.shared_blob, logits=_dev(lg),
-                       idx_out=idx, path=coli.PATH_MFMA)
+                       idx_out=idx, path=path)
     torch.cuda.synchronize()
     idx_ref, _ = oracle.route(lg, None, K)
     assert np.array_equal(idx.cpu().numpy(), idx_ref)
@@ -184,15 +184,16 @@ def _prefill_case(coli, shape, ex, group):
 
 
 def test_prefill_glm_rowwise_64_tokens(coli, rowwise):
+    # the automatic path, as the benchmark runs it
     shape, ex = rowwise
-    _prefill_case(coli, shape, ex, 0)
+    _prefill_case(coli, shape, ex, 0, coli.PATH_AUTO)
 
 
 def test_prefill_glm_gs64_64_tokens(coli, gs64):
     # gs64 experts at hidden 6144: 96 scale groups per gate/up row, so the
     # group sums are staged in two chunks of 64 and 32
     shape, ex = gs64
-    _prefill_case(coli, shape, ex, 64)
+    _prefill_case(coli, shape, ex, 64, coli.PATH_MFMA)
 
 
 def test_prefill_gs64_largest_hidden(coli):

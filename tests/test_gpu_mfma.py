@@ -95,3 +95,39 @@ def test_layer_prefill_glm_shape_sampled(coli):
                                 logits=lg[sample])
     err = rel_l2_rows(y.cpu().numpy()[sample], y64)
     assert err.max() <= TOL, f"max rel L2 {err.max():.3e}"
+
+
+def test_auto_path_sends_few_token_experts_to_gemv(coli):
+    """With the path chosen automatically for a batch above 16 tokens, experts
+    with at most 4 tokens run on the GEMV family (f32-accurate, 1e-3) and the
+    rest on the bf16 MFMA tiles (2e-2): routing is built so that experts 0-2
+    get 2, 4 and 5 tokens and experts 3-7 the rest."""
+    import torch
+    H, I, E, k, T = 512, 256, 8, 2, 40
+    shape = coli.MoEShape(H, I, E, 0, k, 0)
+    first = [0] * 2 + [1] * 4 + [2] * 5 + [3 + t % 5 for t in range(T - 11)]
+    lg = np.full((T, E), -4.0, np.float32)
+    for t in range(T):
+        lg[t, first[t]] = 4.0
+        lg[t, 3 + (t + 2) % 5 if first[t] < 3 else 3 + (first[t] - 3 + 1) % 5] = 3.0
+    idx_np, _ = oracle.route(lg, None, k)
+    c, o, p, u = oracle.union(idx_np, E)
+    assert c[:3].tolist() == [2, 4, 5] and c[3:].min() > 4
+    ex = ExpertSet(coli, shape, seed=35, which=u, shared=False)
+    x = synth.activations(35, 0, 0, T, H)
+    uu = np.zeros(E, np.int32)
+    uu[:len(u)] = u
+    args = (shape, ex.table, _dev(x), _dev(o), _dev(p), _dev(uu), _dev(np.array([len(u)], np.int32)))
+    y_auto = coli.expert_ffn(*args, path=coli.PATH_AUTO)
+    y_mfma = coli.expert_ffn(*args, path=coli.PATH_MFMA)
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn_union(ex.oracle_list(), x, k, o, p, u, H, I, 0)
+    e_auto = rel_l2_rows(y_auto.cpu().numpy(), ref)
+    e_mfma = rel_l2_rows(y_mfma.cpu().numpy(), ref)
+    expert_of_row = idx_np.reshape(-1)
+    small = c[expert_of_row] <= 4
+    assert small.sum() == 6
+    assert e_auto[small].max() <= 1e-3            # GEMV family
+    assert e_auto[~small].max() <= TOL            # MFMA tiles
+    assert e_mfma[small].max() > 1e-3             # the same rows on bf16 tiles
+    assert np.array_equal(y_auto.cpu().numpy()[~small], y_mfma.cpu().numpy()[~small])
