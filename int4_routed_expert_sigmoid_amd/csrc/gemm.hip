@@ -176,9 +176,10 @@ __device__ __forceinline__ void stage_group_sums(float* s, const float* sums, co
 // Work unit = (64-token tile, block of weight rows). Units are taken in a
 // grouped order: kGroupTiles consecutive tiles (usually of one expert, or of a
 // few small ones) times every row block, so that the units of a group share
-// activation rows and weight rows. Workgroup L runs on XCD L % 8, and each XCD
-// takes one contiguous eighth of the units, so a group's reuse stays inside
-// one XCD's L2. Returns false for units past the device-side tile count.
+// activation rows and weight rows. Workgroup L runs on XCD L % 8; the groups
+// are dealt round-robin over the XCDs (XCD x takes groups x, x + 8, ...), so a
+// group's reuse stays inside one XCD's L2 and every XCD starts on the first,
+// largest experts. Returns false for units past the device-side tile count.
 constexpr int kGroupTiles = 2;
 
 __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& rb) {
