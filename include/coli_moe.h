@@ -230,7 +230,7 @@ COLI_API coli_status coli_moe_layer_fwd(const coli_moe_shape* shape, const float
  * allocation): the same launch sequence and results, with resident experts
  * only (no cache), running on a static scratch array of 64 MiB per device
  * instead of a caller's workspace. The call allocates nothing. A call whose
- * workspace would exceed 64 MiB (coli_moe_workspace_size; about 130 tokens at
+ * workspace would exceed 64 MiB (coli_moe_workspace_size; about 200 tokens at
  * hidden 6144, inter 2048, 256 experts, top-8) returns COLI_ENOMEM before
  * anything is enqueued. The scratch belongs to the calling thread's current
  * device; the first call on a device looks up its address (make that first

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -181,31 +182,83 @@ __device__ __forceinline__ int digit_sum(const uint4* p) {
     return block_dot(make_uint4(0x11111111u, 0x11111111u, 0x11111111u, 0x11111111u), p);
 }
 
-// Encode 8 consecutive elements (this thread's quarter of a 32-element block;
-// the four quarters are lanes 4i..4i+3 of the wave) into one word per plane.
-// Returns the block scale (identical in the four lanes).
-__device__ __forceinline__ float encode_quarter(const float v[8], uint32_t words[kPlanes]) {
+// The intermediate h = silu(g) * u enters the down pass in blocks of 16
+// elements (kHBlock), two per 32-column weight block: the same digit-plane
+// words (elements 0-15 of a 32-column block in words x and y of each plane,
+// 16-31 in z and w), with one scale per half. The gate/up pass encodes h
+// itself, and a workgroup of it holds 16 consecutive rows of both matrices.
+constexpr int kHBlock = 16;
+
+// sums over the two 16-column halves of a block of q * X. Exact.
+__device__ __forceinline__ int2 block_dot_halves(const uint4& w, const uint4* p) {
+    int lo[kPlanes], hi[kPlanes];
+#pragma unroll
+    for (int i = 0; i < kPlanes; ++i) {
+        lo[i] = dot8(w.y, p[i].y, dot8(w.x, p[i].x, 0));
+        hi[i] = dot8(w.w, p[i].w, dot8(w.z, p[i].z, 0));
+    }
+    return make_int2(lo[0] + lo[1] * 16 + lo[2] * 256 + lo[3] * 4096,
+                     hi[0] + hi[1] * 16 + hi[2] * 256 + hi[3] * 4096);
+}
+
+// the halves' sums of the block's integers X
+__device__ __forceinline__ int2 digit_sum_halves(const uint4* p) {
+    return block_dot_halves(make_uint4(0x11111111u, 0x11111111u, 0x11111111u, 0x11111111u), p);
+}
+
+// wblock_dot per 16-column half (xsum: digit_sum_halves of the block)
+template <bool W8>
+__device__ __forceinline__ int2 wblock_dot_halves(const WBlock<W8>& w, const uint4* p, int2 xsum) {
+    if constexpr (W8) {
+        const int2 h = block_dot_halves(w.v[0], p), l = block_dot_halves(w.v[1], p);
+        return make_int2(16 * h.x + l.x + 8 * xsum.x, 16 * h.y + l.y + 8 * xsum.y);
+    } else {
+        return block_dot_halves(w.v[0], p);
+    }
+}
+
+// X = rint(v * inv) clamped to [-kDigitMax, kDigitMax], as its four signed
+// base-16 digits (lowest first), each as a 4-bit two's-complement nibble.
+__device__ __forceinline__ void digit_nibbles(float v, float inv, uint32_t nib[kPlanes]) {
+    int X = (int)rintf(v * inv);
+    X = min(max(X, -kDigitMax), kDigitMax);
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p) {
+        const int d = ((X + 8) & 15) - 8;
+        X = (X - d) >> 4;
+        nib[p] = (uint32_t)(d & 15);
+    }
+}
+
+// Encode 8 consecutive elements (this thread's part of a block of 8 * NL
+// elements; the NL parts of a block are lanes NL*i .. NL*i + NL - 1 of the
+// wave) into one word per plane. Returns the block scale (identical in the NL
+// lanes). NL = 4: 32-element blocks of x; NL = 2: 16-element blocks of h.
+template <int NL>
+__device__ __forceinline__ float encode_octet(const float v[8], uint32_t words[kPlanes]) {
+    static_assert(NL == 2 || NL == 4, "blocks of 16 or 32 elements");
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
     m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
+    if constexpr (NL == 4) m = fmaxf(m, __shfl_xor(m, 2));
 #pragma unroll
     for (int p = 0; p < kPlanes; ++p) words[p] = 0u;
     if (m == 0.f) return 0.f;
     const float inv = (float)kDigitMax / m;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        int X = (int)rintf(v[i] * inv);
-        X = min(max(X, -kDigitMax), kDigitMax);
+        uint32_t nib[kPlanes];
+        digit_nibbles(v[i], inv, nib);
 #pragma unroll
-        for (int p = 0; p < kPlanes; ++p) {
-            int d = ((X + 8) & 15) - 8;
-            X = (X - d) >> 4;
-            words[p] |= (uint32_t)(d & 15) << (4 * i);
-        }
+        for (int p = 0; p < kPlanes; ++p) words[p] |= nib[p] << (4 * i);
     }
     return m / (float)kDigitMax;
+}
+
+// 32-element blocks (x): the four quarters of a block in lanes 4i..4i+3
+__device__ __forceinline__ float encode_quarter(const float v[8], uint32_t words[kPlanes]) {
+    return encode_octet<4>(v, words);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -249,6 +302,59 @@ __device__ __forceinline__ int lane_xchg(int v) {
     } else {
         return __float_as_int(dpp_f(__int_as_float(v), S));
     }
+}
+
+// The same encoding of a 16-element block of h spread over the lanes: a
+// group of G lanes (G a power of two, aligned) holds the block in lane order,
+// NE elements per lane (e0 .. e0 + NE - 1), DUP lanes in a row holding the
+// same elements (they compute the same and contribute once), so that the
+// first G/2 lanes hold elements 0-7 and the others 8-15. Returns the block
+// scale; afterwards lane G*i holds the plane words of elements 0-7 and lane
+// G*i + G/2 those of elements 8-15. The maximum and the OR of the nibbles go
+// over the DPP / permlane partners (lane_xchg), which generate the group.
+template <int G, int DUP, int NE>
+__device__ __forceinline__ float encode_h16_lanes(const float (&v)[NE], int e0,
+                                                  uint32_t words[kPlanes]) {
+    static_assert((G / DUP) * NE == kHBlock, "the group holds one 16-element block");
+    static_assert(G >= 4 && G <= 32, "groups of 4 to 32 lanes");
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) m = fmaxf(m, fabsf(v[i]));
+    auto xmax = [&](auto s) {
+        constexpr int S = decltype(s)::value;
+        if constexpr (S < G) m = fmaxf(m, __int_as_float(lane_xchg<S>(__float_as_int(m))));
+    };
+    xmax(std::integral_constant<int, 1>{});
+    xmax(std::integral_constant<int, 2>{});
+    xmax(std::integral_constant<int, 4>{});
+    xmax(std::integral_constant<int, 8>{});
+    xmax(std::integral_constant<int, 16>{});
+    const bool once = ((threadIdx.x & 63) % DUP) == 0;
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p) words[p] = 0u;
+    if (m != 0.f) {
+        const float inv = (float)kDigitMax / m;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            uint32_t nib[kPlanes];
+            digit_nibbles(v[i], inv, nib);
+            const int sh = 4 * ((e0 + i) & 7);
+#pragma unroll
+            for (int p = 0; p < kPlanes; ++p) words[p] |= once ? nib[p] << sh : 0u;
+        }
+    }
+    auto xor_or = [&](auto s) {
+        constexpr int S = decltype(s)::value;
+        if constexpr (S < G / 2) {
+#pragma unroll
+            for (int p = 0; p < kPlanes; ++p) words[p] |= (uint32_t)lane_xchg<S>((int)words[p]);
+        }
+    };
+    xor_or(std::integral_constant<int, 1>{});
+    xor_or(std::integral_constant<int, 2>{});
+    xor_or(std::integral_constant<int, 4>{});
+    xor_or(std::integral_constant<int, 8>{});
+    return m == 0.f ? 0.f : m / (float)kDigitMax;
 }
 
 // ------------------------------------------------------- expert selection
@@ -490,31 +596,27 @@ coli_status launch_plan(const int32_t* offsets, const int32_t* perm,
                         hipStream_t stream);
 coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* planes, float* scales,
                           hipStream_t stream);
-// Digit planes of the rows a work list reads, for up to max_count tokens per
-// item: h_mode 0 encodes x [rows_idx[r]] (K = hidden) into planes [rows_idx[r]];
-// h_mode 1 encodes h = silu(g) * u from src = gu [R][2][K] (K = inter) of row
-// rows_idx[r] into planes [rows_idx[r]].
+// Digit planes of x [rows_idx[r]] (K = hidden) into planes [rows_idx[r]] for
+// the rows a work list reads, up to max_count tokens per item.
 coli_status launch_encode_items(const WorkItem* items, const int32_t* n_items, int32_t max_items,
-                                int32_t max_count, const int32_t* rows_idx, const float* src,
-                                int32_t K, int h_mode, uint32_t* planes, float* scales,
-                                hipStream_t stream);
+                                int32_t max_count, const int32_t* rows_idx, const float* x,
+                                int32_t K, uint32_t* planes, float* scales, hipStream_t stream);
 
 // Prefill split: with the MFMA path chosen automatically, an expert with at
 // most this many tokens runs on the GEMV family instead of MFMA tiles.
 constexpr int kGemvMaxTokens = 4;
-// gate/up then down GEMV over a work list.
-// gu [rows][2][I] f32 holds silu(g) and u between the two passes; for
-// batches (max_count > 1) an activation pass encodes h = silu(g) * u of all
-// `rows` rows into hplanes [rows][I/32][16] / hscale [rows][I/32].
-// passes: kPassGateUp and/or kPassDown (the activation pass of batches goes
-// with down unless kPassNoAct is set: the caller has encoded h itself).
-constexpr int kPassGateUp = 1, kPassDown = 2, kPassBoth = 3, kPassNoAct = 4;
+// gate/up then down GEMV over a work list. The gate/up pass writes h =
+// silu(g) * u of every (item, token) row it computes as digit planes of
+// 16-element blocks: hplanes [rows][I/32][16] u32 (the words of a 32-column
+// block, kHBlock), hscale [rows][I/32][2]; the down pass reads them.
+// passes: kPassGateUp and/or kPassDown.
+constexpr int kPassGateUp = 1, kPassDown = 2, kPassBoth = 3;
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
-                            int32_t max_count, int32_t rows, const int32_t* rows_tok,
-                            const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
-                            float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
-                            int32_t I, int32_t group, int32_t wbits, const FusedRoute& fr,
-                            hipStream_t stream, int passes = kPassBoth);
+                            int32_t max_count, const int32_t* rows_tok, const int32_t* rows_out,
+                            const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
+                            float* hscale, float* y_rows, int32_t H, int32_t I, int32_t group,
+                            int32_t wbits, const FusedRoute& fr, hipStream_t stream,
+                            int passes = kPassBoth);
 // y [T][H] = shared row + rs * sum_j w[t][j] * y_rows[t*k + j] in slot order;
 // with idx (nullable) given, slots whose index is negative (dropped by top-p)
 // add nothing.

@@ -1,6 +1,6 @@
 // int4 dequant GEMV family for decode and small per-expert token counts:
-// activation encoding, the launch of the gate/up and down passes
-// (gemv_gateup.hip, gemv_down.hip) and the slot-order combine.
+// encoding of x, the launch of the gate/up and down passes (gemv_gateup.hip,
+// gemv_down.hip) and the slot-order combine.
 //
 // Expert FFN (practical guide section 二: gate, up and down stored adjacently;
 // SwiGLU): h = silu(gate x) * (up x), y = down h, for every (expert, token)
@@ -40,41 +40,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
     }
 }
 
-// ------------------------------------------------------------- activation
-// h = silu(g) * u for rows [0, R) of gu [R][2][I] (silu(g), u), each 32-element block
-// encoded into digit planes: planes [R][I/32][4][4] u32, scales [R][I/32].
-// One 8-element quarter per thread; the quarters of a block sit in 4 adjacent
-// lanes and every lane runs the encoder (its shuffles need them all).
-__global__ __launch_bounds__(256) void act_encode_kernel(const float* __restrict__ gu, int R, int I,
-                                                         uint32_t* __restrict__ hplanes,
-                                                         float* __restrict__ hscale) {
-    const int CI = I / kBlock;
-    const int64_t nq = (int64_t)R * CI * 4;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t ic = i < nq ? i : nq - 1;
-    const int row = (int)(ic / (CI * 4)), rem = (int)(ic % (CI * 4)), blk = rem >> 2, q = rem & 3;
-    const float* gp = gu + (size_t)row * 2 * I + blk * kBlock + q * 8;
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = gp[e] * gp[I + e];                 // silu(g) * u
-    uint32_t words[kPlanes];
-    const float sc = encode_quarter(v, words);
-    if (i < nq) {
-        uint32_t* dst = hplanes + ((size_t)row * CI + blk) * kWordsPerBlock;
-#pragma unroll
-        for (int p = 0; p < kPlanes; ++p) dst[p * 4 + q] = words[p];
-        if (q == 0) hscale[(size_t)row * CI + blk] = sc;
-    }
-}
-
-// Digit planes of the rows a work list reads (launch_encode_items). Thread
+// Digit planes of the x rows a work list reads (launch_encode_items). Thread
 // (m, block, quarter) of item blockIdx.y; the four quarters of a block are
 // adjacent lanes and leave together when m is past the item's tokens.
-template <bool HM>
 __global__ __launch_bounds__(256) void encode_items_kernel(const WorkItem* __restrict__ items,
                                                            const int32_t* __restrict__ n_items,
                                                            const int32_t* __restrict__ rows_idx,
-                                                           const float* __restrict__ src, int K,
+                                                           const float* __restrict__ x, int K,
                                                            uint32_t* __restrict__ planes,
                                                            float* __restrict__ scales) {
     if ((int)blockIdx.y >= *n_items) return;
@@ -86,15 +58,9 @@ __global__ __launch_bounds__(256) void encode_items_kernel(const WorkItem* __res
     const int row = rows_idx[it.begin + m];
     const int blk = rem >> 2, q = rem & 3;
     float v[8];
-    if constexpr (HM) {
-        const float* gp = src + (size_t)row * 2 * K + blk * kBlock + q * 8;
+    const float* p = x + (size_t)row * K + blk * kBlock + q * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = gp[e] * gp[K + e];               // silu(g) * u
-    } else {
-        const float* p = src + (size_t)row * K + blk * kBlock + q * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = p[e];
-    }
+    for (int e = 0; e < 8; ++e) v[e] = p[e];
     uint32_t words[kPlanes];
     const float sc = encode_quarter(v, words);
     uint32_t* dst = planes + ((size_t)row * C + blk) * kWordsPerBlock;
@@ -157,51 +123,44 @@ coli_status launch_encode(const float* x, int32_t rows, int32_t K, uint32_t* pla
 }
 
 coli_status launch_encode_items(const WorkItem* items, const int32_t* n_items, int32_t max_items,
-                                int32_t max_count, const int32_t* rows_idx, const float* src,
-                                int32_t K, int h_mode, uint32_t* planes, float* scales,
-                                hipStream_t stream) {
+                                int32_t max_count, const int32_t* rows_idx, const float* x,
+                                int32_t K, uint32_t* planes, float* scales, hipStream_t stream) {
     if (max_items == 0 || max_count == 0) return COLI_OK;
     const int64_t threads = (int64_t)max_count * (K / kBlock) * 4;
     const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)max_items);
-    if (h_mode) launch(encode_items_kernel<true>, grid, dim3(256), 0, stream, items, n_items, rows_idx, src, K, planes, scales);
-    else launch(encode_items_kernel<false>, grid, dim3(256), 0, stream, items, n_items, rows_idx, src, K, planes, scales);
+    launch(encode_items_kernel, grid, dim3(256), 0, stream, items, n_items, rows_idx, x, K, planes,
+           scales);
     COLI_CHECK_LAUNCH("item encoding kernel launch");
     return COLI_OK;
 }
 
 coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32_t max_items,
-                            int32_t max_count, int32_t rows, const int32_t* rows_tok,
-                            const int32_t* rows_out, const uint32_t* xplanes, const float* xscale,
-                            float* gu, uint32_t* hplanes, float* hscale, float* y_rows, int32_t H,
-                            int32_t I, int32_t group, int32_t wbits, const FusedRoute& fr,
-                            hipStream_t stream, int passes) {
+                            int32_t max_count, const int32_t* rows_tok, const int32_t* rows_out,
+                            const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
+                            float* hscale, float* y_rows, int32_t H, int32_t I, int32_t group,
+                            int32_t wbits, const FusedRoute& fr, hipStream_t stream, int passes) {
     if (max_items == 0) return COLI_OK;
     const BlobLayout L = blob_layout(H, I, group, wbits);
     const int mt = max_count <= 1 ? 1 : max_count <= 2 ? 2 : max_count <= 4 ? 4 : 8;
-    const dim3 g1((mt == 1 ? 2 : 1) * (I / kBlock), max_items);   // one token: gate and up apart
+    // one token: 16-row tiles of both matrices; batches: 32-row tiles
+    const dim3 g1((mt == 1 ? 2 : 1) * (I / kBlock), max_items);
     bool ok = true;
     if (passes & kPassGateUp) {
         {
             ProfTag prof("gemv_gateup");
             ok = dispatch_gateup(mt, group, g1, stream, items, n_items, rows_tok, rows_out, xplanes,
-                                 xscale, gu, H, I, L, fr);
+                                 xscale, hplanes, hscale, H, I, L, fr);
         }
         if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: hidden too large (max 16384)");
         COLI_CHECK_LAUNCH("gate/up GEMV launch");
     }
     if (!(passes & kPassDown)) return COLI_OK;
-    if (mt > 1 && !(passes & kPassNoAct)) {
-        const int64_t threads = (int64_t)rows * (I / kBlock) * 4;
-        launch(act_encode_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, gu,
-               rows, I, hplanes, hscale);
-        COLI_CHECK_LAUNCH("activation kernel launch");
-    }
     const int down_rows = 4 * down_rows_per_wave(mt);
     const dim3 g2((H + down_rows - 1) / down_rows, max_items);
     {
         ProfTag prof("gemv_down");
-        ok = dispatch_down(mt, group, g2, stream, items, n_items, rows_out, gu, hplanes, hscale,
-                           y_rows, H, I, L);
+        ok = dispatch_down(mt, group, g2, stream, items, n_items, rows_out, hplanes, hscale, y_rows,
+                           H, I, L);
     }
     if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: inter too large (max 4096)");
     COLI_CHECK_LAUNCH("down GEMV launch");

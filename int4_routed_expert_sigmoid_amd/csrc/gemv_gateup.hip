@@ -2,65 +2,70 @@
 //
 // Expert FFN (practical guide section 二: gate, up and down stored adjacently;
 // SwiGLU): g = gate x and u = up x for every (expert, token) pair of a work
-// list, each expert's rows streamed once per pass of up to MT tokens; the
-// down pass forms h = silu(g) * u.
+// list, each expert's rows streamed once per pass of up to MT tokens, and
+// h = silu(g) * u encoded for the down pass.
 //
-// Workgroup: 32 rows of one work item's gate or up matrix (one token; grid x
-// interleaves tile and matrix, so a decode token's 9 work items give 1152
-// workgroups) or of both (batches). W waves split the reduction axis: thread tid owns the
-// 32-column blocks tid + 64*W*j and reads the 16 bytes of each row that fall
-// in them with one 128-bit load. Each block's nibbles are multiplied by the
-// token's digit planes with v_dot8_i32_i4 (exact int32 per block, common.h)
-// and scaled once into an f32 partial. Rows go in batches of LB = 4/MT rows:
-// a batch yields LB*NM*MT partials per lane (NM matrices), summed over the wave by one
+// Workgroup: a tile of consecutive rows of both of a work item's matrices, 16
+// rows (one token: a decode token's 9 work items give 9 x 128 workgroups) or
+// 32 (batches). W waves split the reduction axis: thread tid owns the 32-column
+// blocks tid + 64*W*j and reads the 16 bytes of each row that fall in them
+// with one 128-bit load. Each block's nibbles are multiplied by the token's
+// digit planes with v_dot8_i32_i4 (exact int32 per block, common.h) and scaled
+// once into an f32 partial. Rows go in batches of LB rows of both matrices: a
+// batch yields LB*2*MT partials per lane, summed over the wave by one
 // transpose-reduction and over the W waves through LDS; the next batch's
 // loads are issued before the current batch is computed (the next two for
-// one-token int4 tiles). The workgroup ends
-// by writing silu(g) (or u), with the per-row scale applied first, as f32.
+// one-token int4 tiles). The workgroup ends by applying the per-row scales,
+// forming h = silu(g) * u for its rows and writing h as digit planes of
+// 16-element blocks (kHBlock) with one scale each.
 #include "gemv.h"
 
 namespace coli {
 namespace {
 
-// One work item's 32-row tile of NM matrices (from mat0) for all of its
-// tokens, MT at a time. ONE: a one-token launch, where every row's token is 0
-// (the activation planes then load without waiting for the token index).
-template <int W, int NCH, int MT, int NM, bool GS, bool ONE, bool W8>
+// One work item's tile of both matrices for all of its tokens, MT at a time.
+// ONE: a one-token launch, where every row's token is 0 (the activation
+// planes then load without waiting for the token index) and a tile has 16
+// rows; batches take 32.
+template <int W, int NCH, int MT, bool GS, bool ONE, bool W8>
 __device__ __forceinline__ void gateup_body(
-    const WorkItem& it, int tile, int mat0, const int32_t* __restrict__ rows_tok,
+    const WorkItem& it, int tile, const int32_t* __restrict__ rows_tok,
     const int32_t* __restrict__ rows_out, const uint32_t* __restrict__ xplanes,
-    const float* __restrict__ xscale, float* __restrict__ gu, int H, int I, const BlobLayout& L,
-    float* red_raw) {
-    constexpr int LB = (4 / MT) > 0 ? (4 / MT) : 1;   // rows per batch
+    const float* __restrict__ xscale, uint32_t* __restrict__ hplanes, float* __restrict__ hscale,
+    int H, int I, const BlobLayout& L, float* red_raw) {
+    constexpr int NM = 2;                             // gate and up
+    constexpr int ROWS = ONE ? 16 : 32;               // rows of each matrix per tile
+    constexpr int LB = ONE ? 2 : ((4 / MT) > 0 ? (4 / MT) : 1);   // rows per batch
     constexpr int NV = LB * NM * MT;                  // partials per batch (4 or 8)
     constexpr int SH = transpose_shift<NV>();
-    constexpr int NBT = kBlock / LB;                  // batches per tile (even)
+    constexpr int NBT = ROWS / LB;                    // batches per tile (even)
     static_assert(NBT % 2 == 0, "batch count must be even");
-    const int r0 = tile * kBlock;
+    const int r0 = tile * ROWS;
     const int C = H / kBlock;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint8_t* wq[NM];
     const float* wsc[NM];
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) {
-        wq[mt] = it.blob + (mat0 + mt ? L.up_q : L.gate_q);
-        wsc[mt] = reinterpret_cast<const float*>(it.blob + (mat0 + mt ? L.up_s : L.gate_s));
+        wq[mt] = it.blob + (mt ? L.up_q : L.gate_q);
+        wsc[mt] = reinterpret_cast<const float*>(it.blob + (mt ? L.up_s : L.gate_s));
     }
     const size_t rowbytes = (size_t)H / (W8 ? 1 : 2);
     const int gpr = GS ? H / 64 : 1;
 
-    float (*red)[kBlock * NM * MT] = reinterpret_cast<float (*)[kBlock * NM * MT]>(red_raw);
+    float (*red)[ROWS * NM * MT] = reinterpret_cast<float (*)[ROWS * NM * MT]>(red_raw);
 
-    // the per-row scales this thread applies in the epilogue, requested before
-    // the weights: loaded where they are used, they would wait for every load
+    // the per-row scales this thread applies in the epilogue (thread t:
+    // token t / ROWS, row t % ROWS of both matrices), requested before the
+    // weights: loaded where they are used, they would wait for every load
     // issued before them
-    constexpr int NOUT = kBlock * NM * MT, NIT = (NOUT + 64 * W - 1) / (64 * W);
-    float rsc[NIT];
+    constexpr int NTH = MT * ROWS, NIT = (NTH + 64 * W - 1) / (64 * W);
+    float rsg[NIT], rsu[NIT];
 #pragma unroll
     for (int q = 0; q < NIT; ++q) {
-        const int i = min(tid + q * 64 * W, NOUT - 1);
-        const int mt = (i / MT) % NM, r = i / (MT * NM);
-        rsc[q] = GS ? 1.f : ldg_f32(wsc[mt] + r0 + r);
+        const int r = min(tid + q * 64 * W, NTH - 1) % ROWS;
+        rsg[q] = GS ? 1.f : ldg_f32(wsc[0] + r0 + r);
+        rsu[q] = GS ? 1.f : ldg_f32(wsc[1] + r0 + r);
     }
 
     int tokwin = 0, outwin = 0;                       // tokens and output rows of a 64-token window, one per lane
@@ -160,7 +165,7 @@ __device__ __forceinline__ void gateup_body(
                 red[wave][batch * NV + (lane >> SH)] = v;
         };
         if constexpr (R3) {
-            static_assert(NBT == 8, "one-token tiles are 8 batches of 4 rows");
+            static_assert(NBT == 8, "one-token tiles are 8 batches of 2 rows of both matrices");
             compute(wa, fa, 0); load(wa, fa, 3); sched_fence();
             compute(wb, fb, 1); load(wb, fb, 4); sched_fence();
             compute(wc, fc, 2); load(wc, fc, 5); sched_fence();
@@ -191,23 +196,39 @@ __device__ __forceinline__ void gateup_body(
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             outs[m] = ONE ? it.row0 : __builtin_amdgcn_readlane(outwin, (m0 & 63) + m);
+        // thread t: row r = t % ROWS of token t / ROWS; the waves' partials of
+        // its gate and up rows summed, the row scales applied, h = silu(g) * u
+        // formed and each 16-row block encoded across its 16 lanes
+        const int CI = I / kBlock;
 #pragma unroll
         for (int q = 0; q < NIT; ++q) {
-            const int i = tid + q * 64 * W;
-            const int m = i % MT, mt = (i / MT) % NM, r = i / (MT * NM);
-            if (i < NOUT && m < mc) {
-                float v = 0.f;
+            const int t = tid + q * 64 * W, tc = min(t, NTH - 1);
+            const int m = tc / ROWS, r = tc % ROWS;
+            float g = 0.f, u = 0.f;
 #pragma unroll
-                for (int w = 0; w < W; ++w) v += red[w][i];
-                v *= rsc[q];
-                if (mat0 + mt == 0) v = v / (1.f + expf(-v));          // gate: store silu(g)
+            for (int w = 0; w < W; ++w) {
+                g += red[w][(r * NM + 0) * MT + m];
+                u += red[w][(r * NM + 1) * MT + m];
+            }
+            g *= rsg[q];
+            u *= rsu[q];
+            g = g / (1.f + expf(-g));                                   // silu(g)
+            const float hv[1] = {g * u};
+            uint32_t words[kPlanes];
+            const float sc = encode_h16_lanes<kHBlock, 1, 1>(hv, r % kHBlock, words);
+            if (t < NTH && (r % 8) == 0 && m < mc) {
                 int out = outs[0];
 #pragma unroll
                 for (int mm = 1; mm < MT; ++mm) out = m == mm ? outs[mm] : out;
-                gu[((size_t)out * 2 + mat0 + mt) * I + r0 + r] = v;
+                const int rg = r0 + r / kHBlock * kHBlock, h16 = (rg / kHBlock) & 1;
+                const size_t blk = (size_t)out * CI + rg / kBlock;
+                uint32_t* dst = hplanes + blk * kWordsPerBlock;
+#pragma unroll
+                for (int p = 0; p < kPlanes; ++p) dst[p * 4 + h16 * 2 + ((r % kHBlock) >> 3)] = words[p];
+                if (r % kHBlock == 0) hscale[blk * 2 + h16] = sc;
             }
         }
-        __syncthreads();
+        if constexpr (!ONE) __syncthreads();   // red is reused by the next chunk
     }
 }
 
@@ -294,19 +315,20 @@ constexpr int gateup_waves_per_eu() {
     return W8 ? (NCH == 1 && MTK == 1 ? 3 : 2) : NCH == 1 && MTK == 1 ? 4 : NCH == 1 && !GS ? 4 : NCH == 1 ? 3 : 2;
 }
 
-// MTK == 1: one token; gate and up in separate workgroups (grid x interleaves
-// tile and matrix: twice the workgroups, half the registers). MTK == 4:
-// batches; both matrices in one workgroup, so that the activation planes are
-// read once for the pair, and each work item takes the body that fits its
-// token count (1, 2, or chunks of 4), which keeps the per-wave batches of
-// weight rows large for the many experts that see one or two tokens.
+// MTK == 1: one token, 16-row tiles (twice the workgroups of 32-row tiles,
+// half the registers each). MTK == 4: batches, 32-row tiles; each work item
+// takes the body that fits its token count (1, 2, or chunks of 4), which
+// keeps the per-wave batches of weight rows large for the many experts that
+// see one or two tokens. Both read the activation planes once for the pair
+// of matrices.
 template <int W, int NCH, int MTK, bool GS, bool W8>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(gateup_waves_per_eu<NCH, MTK, GS, W8>(), 8)))
 void gateup_kernel(
     const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
     const int32_t* __restrict__ rows_tok, const int32_t* __restrict__ rows_out,
     const uint32_t* __restrict__ xplanes, const float* __restrict__ xscale,
-    float* __restrict__ gu, int H, int I, BlobLayout L, FusedRoute fr) {
+    uint32_t* __restrict__ hplanes, float* __restrict__ hscale, int H, int I, BlobLayout L,
+    FusedRoute fr) {
     __shared__ float red[W * kBlock * (MTK == 1 ? 1 : 2 * 4)];
     const int item = blockIdx.y;
     WorkItem it;
@@ -316,51 +338,51 @@ void gateup_kernel(
         if (item >= *n_items) return;
         it = items[item];
     }
+    const int t = blockIdx.x;
     if constexpr (MTK == 1) {
-        gateup_body<W, NCH, 1, 1, GS, true, W8>(it, (int)blockIdx.x >> 1, (int)blockIdx.x & 1, rows_tok,
-                                      rows_out, xplanes, xscale, gu, H, I, L, red);
+        gateup_body<W, NCH, 1, GS, true, W8>(it, t, rows_tok, rows_out, xplanes, xscale, hplanes, hscale, H, I, L, red);
     } else {
-        const int t = blockIdx.x;
         if (it.count == 1)
-            gateup_body<W, NCH, 1, 2, GS, false, W8>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 1, GS, false, W8>(it, t, rows_tok, rows_out, xplanes, xscale, hplanes, hscale, H, I, L, red);
         else if (it.count == 2)
-            gateup_body<W, NCH, 2, 2, GS, false, W8>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 2, GS, false, W8>(it, t, rows_tok, rows_out, xplanes, xscale, hplanes, hscale, H, I, L, red);
         else
-            gateup_body<W, NCH, 4, 2, GS, false, W8>(it, t, 0, rows_tok, rows_out, xplanes, xscale, gu, H, I, L, red);
+            gateup_body<W, NCH, 4, GS, false, W8>(it, t, rows_tok, rows_out, xplanes, xscale, hplanes, hscale, H, I, L, red);
     }
 }
 
 template <int W, int NCH, int MTK, bool GS>
 void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
               const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp,
-              const float* xs, float* gu, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
+              const float* xs, uint32_t* hp, float* hs, int H, int I, const BlobLayout& L,
+              const FusedRoute& fr) {
     if (L.wbits == 8) {
         launch((gateup_kernel<W, NCH, MTK, GS, true>), grid, dim3(64 * W), 0, s, items, n_items,
-               rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+               rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
         return;
     }
     launch((gateup_kernel<W, NCH, MTK, GS, false>), grid, dim3(64 * W), 0, s, items, n_items,
-                       rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+                       rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
 }
 
 template <int W, int NCH, bool GS>
 void by_mt(int mt, dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
            const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp, const float* xs,
-           float* gu, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
-    if (mt == 1) launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
-    else launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+           uint32_t* hp, float* hs, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
+    if (mt == 1) launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+    else launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
 }
 
 template <bool GS>
 bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
               const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
-              const uint32_t* xp, const float* xs, float* gu, int H, int I,
+              const uint32_t* xp, const float* xs, uint32_t* hp, float* hs, int H, int I,
               const BlobLayout& L, const FusedRoute& fr) {
-    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
-    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
-    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
-    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
-    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, gu, H, I, L, fr);
+    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
     else return false;
     return true;
 }
@@ -369,13 +391,13 @@ bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
 
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
-                     const uint32_t* xplanes, const float* xscale, float* gu, int H, int I,
-                     const BlobLayout& L, const FusedRoute& fr) {
+                     const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
+                     float* hscale, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
     const int C = H / kBlock;
     return group ? by_width<true>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                  xscale, gu, H, I, L, fr)
+                                  xscale, hplanes, hscale, H, I, L, fr)
                  : by_width<false>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                   xscale, gu, H, I, L, fr);
+                                   xscale, hplanes, hscale, H, I, L, fr);
 }
 
 }  // namespace coli

@@ -68,39 +68,28 @@ static coli_status run_ffn(const coli_moe_shape* s, bool mfma, const float* x, i
         coli_status st = launch_mfma_ffn(g, x, T, max_tiles, stream);
         if (st || !split) return st;
         // the experts with few tokens: GEMV family over the compacted list,
-        // with the digit planes of just the rows it reads
+        // with the digit planes of just the x rows it reads
         const int32_t* rows_tok = at<int32_t>(ws, W.rows_tok);
         const int32_t* rows_out = at<int32_t>(ws, W.rows_out);
-        st = launch_encode_items(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows_tok, x, H, 0,
+        st = launch_encode_items(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows_tok, x, H,
                                  at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
         if (st) return st;
         FusedRoute none{};
-        st = launch_gemv_ffn(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows, rows_tok, rows_out,
-                             at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), at<float>(ws, W.gu),
-                             at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_rows, H, I,
-                             s->group, s->wbits, none, stream, kPassGateUp);
-        if (st) return st;
-        st = launch_encode_items(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows_out,
-                                 at<float>(ws, W.gu), I, 1, at<uint32_t>(ws, W.hplanes),
-                                 at<float>(ws, W.hscale), stream);
-        if (st) return st;
-        return launch_gemv_ffn(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows, rows_tok, rows_out,
-                               at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), at<float>(ws, W.gu),
+        return launch_gemv_ffn(g.gv_items, g.n_gv, max_items, kGemvMaxTokens, rows_tok, rows_out,
+                               at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
                                at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_rows, H, I,
-                               s->group, s->wbits, none, stream, kPassDown | kPassNoAct);
+                               s->group, s->wbits, none, stream, kPassBoth);
     }
     if (!x_encoded) {
         coli_status st = launch_encode(x, T, H, at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale), stream);
         if (st) return st;
     }
-    const int32_t rows = (int32_t)((int64_t)T * s->top_k + T);
     FusedRoute none{};
     return launch_gemv_ffn(at<WorkItem>(ws, W.items), at<int32_t>(ws, W.n_items), max_items, T,
-                           rows, at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
+                           at<int32_t>(ws, W.rows_tok), at<int32_t>(ws, W.rows_out),
                            at<uint32_t>(ws, W.xplanes), at<float>(ws, W.xscale),
-                           at<float>(ws, W.gu), at<uint32_t>(ws, W.hplanes),
-                           at<float>(ws, W.hscale), y_rows, H, I, s->group, s->wbits,
-                           fused ? *fused : none, stream, passes);
+                           at<uint32_t>(ws, W.hplanes), at<float>(ws, W.hscale), y_rows, H, I,
+                           s->group, s->wbits, fused ? *fused : none, stream, passes);
 }
 
 // One token on the GEMV path without a cache: the routing is folded into the

@@ -102,7 +102,7 @@ def test_noalloc_refuses_calls_beyond_the_scratch(coli):
     import torch
     H, I, E, k = 6144, 2048, 256, 8
     shape = coli.MoEShape(H, I, E, 1, k, 0)
-    T = 400                                        # workspace about 190 MB, above the 64 MiB scratch
+    T = 400                                        # workspace about 131 MB, above the 64 MiB scratch
     assert coli.workspace_size(shape, T) > 64 << 20
     x = torch.zeros((T, H), dtype=torch.float32, device="cuda")
     lg = torch.zeros((T, E), dtype=torch.float32, device="cuda")
