@@ -217,56 +217,6 @@ __device__ __forceinline__ int2 wblock_dot_halves(const WBlock<W8>& w, const uin
     }
 }
 
-// X = rint(v * inv) clamped to [-kDigitMax, kDigitMax], as its four signed
-// base-16 digits (lowest first), each as a 4-bit two's-complement nibble.
-__device__ __forceinline__ void digit_nibbles(float v, float inv, uint32_t nib[kPlanes]) {
-    int X = (int)rintf(v * inv);
-    X = min(max(X, -kDigitMax), kDigitMax);
-#pragma unroll
-    for (int p = 0; p < kPlanes; ++p) {
-        const int d = ((X + 8) & 15) - 8;
-        X = (X - d) >> 4;
-        nib[p] = (uint32_t)(d & 15);
-    }
-}
-
-// Encode 8 consecutive elements (this thread's part of a block of 8 * NL
-// elements; the NL parts of a block are lanes NL*i .. NL*i + NL - 1 of the
-// wave) into one word per plane. Returns the block scale (identical in the NL
-// lanes). NL = 4: 32-element blocks of x; NL = 2: 16-element blocks of h.
-template <int NL>
-__device__ __forceinline__ float encode_octet(const float v[8], uint32_t words[kPlanes]) {
-    static_assert(NL == 2 || NL == 4, "blocks of 16 or 32 elements");
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    if constexpr (NL == 4) m = fmaxf(m, __shfl_xor(m, 2));
-#pragma unroll
-    for (int p = 0; p < kPlanes; ++p) words[p] = 0u;
-    if (m == 0.f) return 0.f;
-    const float inv = (float)kDigitMax / m;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t nib[kPlanes];
-        digit_nibbles(v[i], inv, nib);
-#pragma unroll
-        for (int p = 0; p < kPlanes; ++p) words[p] |= nib[p] << (4 * i);
-    }
-    return m / (float)kDigitMax;
-}
-
-// 32-element blocks (x): the four quarters of a block in lanes 4i..4i+3
-__device__ __forceinline__ float encode_quarter(const float v[8], uint32_t words[kPlanes]) {
-    return encode_octet<4>(v, words);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 // ------------------------------------------------- wave transpose-reduce
 // Sums N partials (N a power of two <= 64) over the 64 lanes of a wave in
 // one pass: every stage pairs each lane with a partner in the other half of
@@ -302,6 +252,71 @@ __device__ __forceinline__ int lane_xchg(int v) {
     } else {
         return __float_as_int(dpp_f(__int_as_float(v), S));
     }
+}
+
+// X = rint(v * inv) clamped to [-kDigitMax, kDigitMax], as its four signed
+// base-16 digits (lowest first), each as a 4-bit two's-complement nibble.
+__device__ __forceinline__ void digit_nibbles(float v, float inv, uint32_t nib[kPlanes]) {
+    int X = (int)rintf(v * inv);
+    X = min(max(X, -kDigitMax), kDigitMax);
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p) {
+        const int d = ((X + 8) & 15) - 8;
+        X = (X - d) >> 4;
+        nib[p] = (uint32_t)(d & 15);
+    }
+}
+
+// Encode 8 consecutive elements (this thread's part of a block of 8 * NL
+// elements; the NL parts of a block are lanes NL*i .. NL*i + NL - 1 of the
+// wave) into one word per plane. Returns the block scale (identical in the NL
+// lanes). NL = 4: 32-element blocks of x; NL = 2: 16-element blocks of h.
+template <int NL>
+__device__ __forceinline__ float encode_octet(const float v[8], uint32_t words[kPlanes]) {
+    static_assert(NL == 2 || NL == 4, "blocks of 16 or 32 elements");
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __int_as_float(lane_xchg<1>(__float_as_int(m))));
+    if constexpr (NL == 4) m = fmaxf(m, __int_as_float(lane_xchg<2>(__float_as_int(m))));
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p) words[p] = 0u;
+    if (m == 0.f) return 0.f;
+    const float inv = (float)kDigitMax / m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t nib[kPlanes];
+        digit_nibbles(v[i], inv, nib);
+#pragma unroll
+        for (int p = 0; p < kPlanes; ++p) words[p] |= nib[p] << (4 * i);
+    }
+    return m / (float)kDigitMax;
+}
+
+// 32-element blocks (x): the four quarters of a block in lanes 4i..4i+3
+__device__ __forceinline__ float encode_quarter(const float v[8], uint32_t words[kPlanes]) {
+    return encode_octet<4>(v, words);
+}
+
+// Wave-wide sum of a double, every lane receiving the total: a butterfly over
+// the DPP / permlane partners (lane_xchg), both halves of the value moved by
+// each exchange. A fixed order, so the result is the same on every call.
+template <int S>
+__device__ __forceinline__ double xchg_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)lane_xchg<S>((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)lane_xchg<S>((int)(uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += xchg_f64<32>(v);
+    v += xchg_f64<16>(v);
+    v += xchg_f64<8>(v);
+    v += xchg_f64<4>(v);
+    v += xchg_f64<2>(v);
+    v += xchg_f64<1>(v);
+    return v;
 }
 
 // The same encoding of a 16-element block of h spread over the lanes: a

@@ -27,8 +27,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ w
     const float* xrow = x + (int64_t)t * H;
     double acc = 0.0;
     for (int j = lane; j < H; j += 64) acc = fma((double)wrow[j], (double)xrow[j], acc);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    acc = wave_sum_f64(acc);
     if (lane == 0) logits[pair] = (float)acc;
 }
 
@@ -88,8 +87,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 constexpr int kRouterThreads = 256;
 
 __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    v = wave_sum_f64(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     __syncthreads();
     if (lane == 0) sh[wave] = v;
