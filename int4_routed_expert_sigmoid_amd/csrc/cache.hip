@@ -15,13 +15,16 @@
 //    id), makes the copy stream wait for the compute that last read that slot
 //    (its release event), enqueues one host-to-device copy of the whole blob
 //    and the slot's ready event, and marks the slot pending until a compute
-//    stream has waited for it;
+//    stream has waited for it; the copy stream carries nothing else, so the
+//    copies of one call run back to back on the DMA engine;
 //  - ensure(): hits refresh their age; each miss is copied into a slot that
 //    this call does not name; a named expert whose copy is still pending (a
 //    prefetch or a pin) is reported like a miss, so its compute runs after
 //    wait();
 //  - wait(): the compute stream waits for the ready events of every slot the
-//    last ensure() named (completed events cost nothing);
+//    last ensure() named (completed events cost nothing), then, if copies
+//    have changed the layer's device pointer table since the last wait,
+//    uploads the table from its host mirror on that stream;
 //  - release(): records, on the compute stream, the release event of those
 //    slots; a later eviction of any of them waits for it. Until then pin and
 //    prefetch leave those slots alone.
@@ -56,6 +59,13 @@ struct coli_expert_cache {
     std::vector<std::vector<double>> heat;         // [layer][expert] decaying session heat
     void** d_tables = nullptr;                     // device [layer][expert]
     uint8_t* h_slot_ptrs = nullptr;                // pinned: device address of every slot
+    // host mirror of d_tables (updated by every copy), the pinned row each
+    // upload reads, and the event after that upload (the row is rewritten
+    // only once it has been read)
+    std::vector<void*> h_tables;                   // [layer][expert]
+    void** h_table_stage = nullptr;                // pinned [layer][expert]
+    std::vector<hipEvent_t> table_done;            // [layer]
+    std::vector<char> table_dirty, table_recorded; // [layer]
     uint64_t clock = 0;
     coli_cache_stats st{};
     // copy timing: ring of (start, stop) pairs, summed as they complete
@@ -160,11 +170,12 @@ static coli_status load_slot(coli_expert_cache* c, int32_t layer, int32_t e, int
             return failed(err, "cache copy: timer stop");
         c->timer_next = (ti + 1) % c->timers.size();
         c->timer_live[ti] = true;
-        // pointer of the expert in the device table: a constant pinned source
-        if ((err = hipMemcpyAsync(c->d_tables + (size_t)layer * E + e,
-                                  c->h_slot_ptrs + ((size_t)layer * S + victim) * sizeof(void*),
-                                  sizeof(void*), hipMemcpyHostToDevice, cs)) != hipSuccess)
-            return failed(err, "cache copy: pointer table update");
+        // the expert's pointer goes to the host mirror of the layer's table;
+        // wait() uploads it on the compute stream (a small copy here would
+        // put a blit between the DMA copies of the copy stream)
+        std::memcpy(&c->h_tables[(size_t)layer * E + e],
+                    c->h_slot_ptrs + ((size_t)layer * S + victim) * sizeof(void*), sizeof(void*));
+        c->table_dirty[layer] = 1;
         if ((err = hipEventRecord(sl.ready, cs)) != hipSuccess)
             return failed(err, "cache copy: ready event");
         sl.pending = true;
@@ -339,6 +350,15 @@ COLI_API coli_status coli_expert_cache_create(const coli_cache_cfg* cfg, struct 
                 }
             if (hipHostMalloc((void**)&c->h_phase, (size_t)L * E, hipHostMallocDefault) != hipSuccess)
                 return cleanup(COLI_EHIP, "cache_create: pinned phase table allocation failed");
+            c->h_tables.assign((size_t)L * E, nullptr);
+            c->table_dirty.assign(L, 0);
+            c->table_recorded.assign(L, 0);
+            c->table_done.assign(L, nullptr);
+            if (hipHostMalloc((void**)&c->h_table_stage, sizeof(void*) * (size_t)L * E, hipHostMallocDefault) != hipSuccess)
+                return cleanup(COLI_EHIP, "cache_create: pinned table staging allocation failed");
+            for (int l = 0; l < L; ++l)
+                if (hipEventCreateWithFlags(&c->table_done[l], hipEventDisableTiming) != hipSuccess)
+                    return cleanup(COLI_EHIP, "cache_create: event creation failed");
             if (hipHostMalloc((void**)&c->h_idx, sizeof(int32_t) * kStagingIds, hipHostMallocDefault) != hipSuccess)
                 return cleanup(COLI_EHIP, "cache_create: pinned routing staging allocation failed");
             std::memset(c->h_phase, 0, (size_t)L * E);
@@ -373,8 +393,11 @@ COLI_API coli_status coli_expert_cache_destroy(struct coli_expert_cache* c) {
         if (t.first) (void)hipEventDestroy(t.first);
         if (t.second) (void)hipEventDestroy(t.second);
     }
+    for (hipEvent_t ev : c->table_done)
+        if (ev) (void)hipEventDestroy(ev);
     if (c->d_tables) (void)hipFree(c->d_tables);
     if (c->h_slot_ptrs) (void)hipHostFree(c->h_slot_ptrs);
+    if (c->h_table_stage) (void)hipHostFree(c->h_table_stage);
     if (c->h_idx) (void)hipHostFree(c->h_idx);
     if (c->h_phase) (void)hipHostFree(c->h_phase);
     delete c;
@@ -447,6 +470,17 @@ COLI_API coli_status coli_expert_cache_wait(struct coli_expert_cache* c, int32_t
     for (int32_t s : c->used[layer]) {
         COLI_CHECK_HIP(hipStreamWaitEvent((hipStream_t)stream, c->slots[layer][s].ready, 0));
         c->slots[layer][s].pending = false;
+    }
+    if (c->table_dirty[layer]) {
+        const size_t E = (size_t)c->cfg.n_experts;
+        void** row = c->h_table_stage + (size_t)layer * E;
+        if (c->table_recorded[layer]) COLI_CHECK_HIP(hipEventSynchronize(c->table_done[layer]));
+        std::memcpy(row, &c->h_tables[(size_t)layer * E], E * sizeof(void*));
+        COLI_CHECK_HIP(hipMemcpyAsync(c->d_tables + (size_t)layer * E, row, E * sizeof(void*),
+                                      hipMemcpyHostToDevice, (hipStream_t)stream));
+        COLI_CHECK_HIP(hipEventRecord(c->table_done[layer], (hipStream_t)stream));
+        c->table_recorded[layer] = 1;
+        c->table_dirty[layer] = 0;
     }
     return COLI_OK;
 }
