@@ -80,10 +80,12 @@ def parse():
     ap.add_argument("--repin-every", type=int, default=64)
     ap.add_argument("--repin-decay", type=float, default=0.9)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "mtp", "stream", "copy", "convert"],
+                    choices=["decode", "prefill", "mtp", "stream", "copy", "convert", "readprobe"],
                     help="decode (headline, with the prefill line), prefill (that line alone), "
                          "mtp (gs64, 8-token verify batches), stream (16 layers from pinned host through an HBM cache), "
                          "copy (plain 1 GiB device copy: bandwidth and counter calibration), "
+                         "readprobe (read-only streaming kernels in the decode GEMVs' access patterns: "
+                         "the practical HBM read ceiling of each), "
                          "convert (FP8 -> int4 conversion of 32 experts)")
     return ap.parse_args()
 
@@ -930,6 +932,60 @@ def run_copy(args, dev):
             "us_per_copy": round(s * 1e6, 2), "n_gpus": 1}
 
 
+def run_readprobe(args, coli, dev):
+    """Read-only streaming kernels (coli_read_probe) over the byte counts of
+    the decode GEMVs, in their access patterns and in plain contiguous chunks.
+    Each pattern: a graph of launches over N_ROTATE copies of its buffer (so
+    the MALL holds none of it between reads), replayed `reps` times, HIP
+    events on the stream; median replay / launches."""
+    import torch
+    gu_bytes = 9 * 2 * 2048 * 3072               # int4 gate and up rows of 9 experts
+    dn_bytes = 9 * 6144 * 1024                   # int4 down rows of 9 experts
+    blob_bytes = 9 * 18915328                    # 9 whole per-row blobs
+    cases = [
+        ("gateup_rows", "rows of 3072 B, 3 waves per row, 32 rows per workgroup (decode gate/up)",
+         gu_bytes, 1, 3072, 32),
+        ("gateup_rows16", "rows of 3072 B, 3 waves per row, 16 rows per workgroup",
+         gu_bytes, 1, 3072, 16),
+        ("gateup_chunks", "contiguous 96 KB per workgroup", gu_bytes, 0, 98304, 0),
+        ("down_rows", "rows of 1024 B, 4 waves x 8 rows per workgroup (decode down)",
+         dn_bytes, 1, 1024, 32),
+        ("down_chunks", "contiguous 32 KB per workgroup", dn_bytes, 0, 32768, 0),
+        ("blobs_chunks", "9 whole blobs, contiguous 96 KB per workgroup", blob_bytes - blob_bytes % 98304 + 98304, 0, 98304, 0),
+    ]
+    stream = torch.cuda.Stream()
+    reps = max(3, min(args.steps, 20))
+    out = {}
+    for name, what, nbytes, pattern, rb, rpw in cases:
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i) for i in range(N_ROTATE)]
+        sink = torch.empty(1 << 20, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(stream):
+            for b in bufs:
+                coli.read_probe(b, pattern, rb, rpw, sink, stream=stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        launches = 4 * N_ROTATE
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(launches):
+                coli.read_probe(bufs[i % N_ROTATE], pattern, rb, rpw, sink, stream=stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ms = time_replays(g, stream, reps)
+        us = float(np.median(ms)) * 1e3 / launches
+        out[name] = {"pattern": what, "bytes": nbytes, "us_per_launch": round(us, 3),
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_of_8TBps": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log(f"readprobe {name}: {us:.2f} us, {out[name]['GBps']} GB/s")
+        del g, bufs
+        torch.cuda.empty_cache()
+    best = max(v["GBps"] for v in out.values())
+    return {"metric": "HBM read ceiling by access pattern (read-only streaming kernels)",
+            "value": best, "unit": "GB/s", "n_gpus": 1, "steps": reps, "higher_is_better": True,
+            "data": "synthetic (constant bytes)", "mall": f"cold ({N_ROTATE} rotating copies)",
+            "patterns": out}
+
+
 def pinned_bytes(nbytes):
     """Exactly `nbytes` of pinned host memory (hipHostMalloc) as a uint8 tensor;
     torch's pinned allocator would round a 77.5 GB request up to a power of two."""
@@ -988,6 +1044,8 @@ def main():
         line = run_mtp(args, coli, dev)
     elif args.workload == "convert":
         line = run_convert(args, coli, dev)
+    elif args.workload == "readprobe":
+        line = run_readprobe(args, coli, dev)
     else:
         line = run_stream(args, coli, dev)
     print(json.dumps(line), flush=True)

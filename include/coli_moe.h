@@ -29,10 +29,14 @@
  * bits 0-3 and 2i+1 in bits 4-7 of byte i; rows are row-major.
  *
  * Expert blob: one contiguous device buffer per expert holding, in order,
- * gate_q [I][H/2], up_q [I][H/2], down_q [H][I/2] (u8), gate_s, up_s
- * ([I] or [I][H/64] f32) and down_s ([H] or [H][I/64] f32); every part starts
- * on a 256-byte boundary (coli_expert_blob_layout gives the offsets). A miss
- * of the expert cache is therefore one copy.
+ * the rows of gate_q and up_q (each [I][H/2] u8) interleaved in blocks of 16
+ * rows (rows 16b..16b+15 of gate, then the same rows of up, for b = 0, 1, ...;
+ * so the gate rows start at the gate_q offset and the up rows 16 rows later,
+ * each with a block stride of 32 rows), then down_q [H][I/2] (u8), gate_s,
+ * up_s ([I] or [I][H/64] f32) and down_s ([H] or [H][I/64] f32); every part
+ * starts on a 256-byte boundary (coli_expert_blob_layout gives the offsets).
+ * A workgroup that reads rows of both matrices reads one contiguous stretch,
+ * and a miss of the expert cache is one copy.
  *
  * int8 experts (shape->wbits 8; the MTP head must be int8 per the int8-MTP
  * page and the practical guide's section 二, and the pages give no int8
@@ -101,7 +105,9 @@ typedef struct coli_moe_shape {
 } coli_moe_shape;
 
 /* Offsets (bytes) of gate_q, up_q, down_q, gate_s, up_s, down_s inside one
- * expert blob, and the blob size. Host-only arithmetic. */
+ * expert blob, and the blob size. Row r of gate is at gate_q + (32 (r / 16) +
+ * r % 16) * row bytes, row r of up at up_q + the same (up_q = gate_q + 16 rows).
+ * Host-only arithmetic. */
 COLI_API coli_status coli_expert_blob_layout(const coli_moe_shape* shape, size_t off[6], size_t* blob_bytes);
 
 /* Quantise d_w [rows][cols] (f32) to d_q [rows][cols/2] (u8) and d_s ([rows]
@@ -408,13 +414,26 @@ COLI_API coli_status coli_profile_summary(const char* name, int64_t* count, doub
  * uncached GEMV-path call (T <= 16, path COLI_PATH_GEMV or AUTO) with the same
  * shape, T, d_blob_table and d_shared_blob. which = 0: the gate/up GEMV (one
  * token: with the routing folded in, which it publishes again into d_ws);
- * 1: the down GEMV (with, for batches, the activation pass before it). The
- * pass reads and writes d_ws only and recomputes what the call computed, so
- * back-to-back launches of one kernel can be captured in a graph and timed.
- * The caller's y and routing outputs are not touched. */
+ * 1: the down GEMV. The pass reads and writes d_ws only and recomputes what
+ * the call computed, so back-to-back launches of one kernel can be captured in
+ * a graph and timed. The caller's y and routing outputs are not touched. */
 COLI_API coli_status coli_profile_rerun(const coli_moe_shape* shape, int32_t T,
                                         const void* const* d_blob_table, const void* d_shared_blob,
                                         int32_t which, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Measurement: a read-only streaming kernel over d_src [bytes] (a multiple of
+ * 16), for the practical HBM read ceiling of an access pattern. pattern 0:
+ * each workgroup of 256 threads reads a contiguous chunk of row_bytes bytes (a
+ * multiple of 4096) with 16-byte loads, up to 16 per thread in flight. pattern
+ * 1: d_src holds rows of row_bytes bytes (row_bytes / 16 threads per row: a
+ * divisor of 256, or 192 for a 3-wave workgroup); each workgroup reads
+ * rows_per_wg consecutive rows (a multiple of the rows its threads cover at
+ * once), one 16-byte load per thread and row, up to 16 in flight; with
+ * row_bytes 3072 and 1024 these are the decode gate/up and down layouts. One 32-bit word per wave goes to d_sink (sink_bytes must hold one
+ * per wave of the launch). Enqueued on `stream`. */
+COLI_API coli_status coli_read_probe(const void* d_src, size_t bytes, int32_t pattern,
+                                     int32_t row_bytes, int32_t rows_per_wg, void* d_sink,
+                                     size_t sink_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ EXPORTED = [
     "coli_expert_cache_reset", "coli_expert_cache_pin", "coli_expert_cache_usage",
     "coli_expert_cache_pin_hot", "coli_expert_cache_repin", "coli_expert_cache_prefetch",
     "coli_moe_lookahead", "coli_debug_fail_copies", "coli_profile_enable", "coli_profile_clear",
-    "coli_profile_summary", "coli_profile_rerun",
+    "coli_profile_summary", "coli_profile_rerun", "coli_read_probe",
 ]
 
 
@@ -121,6 +121,7 @@ def lib():
             L.coli_profile_clear.argtypes = []
             L.coli_profile_summary.argtypes = [ctypes.c_char_p, P(i64), P(ctypes.c_double)]
             L.coli_profile_rerun.argtypes = [P(Shape), i32, vp, vp, i32, vp, sz, vp]
+            L.coli_read_probe.argtypes = [vp, sz, i32, i32, i32, vp, sz, vp]
             _lib = L
     return _lib
 
@@ -434,6 +435,16 @@ def profile_rerun(shape: MoEShape, T: int, table, shared_blob, which: int, ws, s
     GEMV pass of the last layer call made with `ws`."""
     _check(lib().coli_profile_rerun(ctypes.byref(shape.c()), T, _ptr(table), _ptr(shared_blob),
                                     which, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def read_probe(src, pattern: int, row_bytes: int, rows_per_wg: int, sink, stream=None,
+               nbytes: int = None):
+    """coli_read_probe: stream `nbytes` (default all) of the uint8 tensor `src`
+    in a read-only pattern (0: contiguous chunks of row_bytes per workgroup;
+    1: rows of row_bytes, rows_per_wg per workgroup), one word per wave to sink."""
+    n = src.numel() if nbytes is None else nbytes
+    _check(lib().coli_read_probe(_ptr(src), n, pattern, row_bytes, rows_per_wg, _ptr(sink),
+                                 sink.numel() * sink.element_size(), _stream(stream)))
 
 
 class ExpertCache:

@@ -173,9 +173,9 @@ coli_status coli_quantize_expert(const coli_moe_shape* shape, const float* d_gat
     const BlobLayout L = blob_layout(H, I, shape->group, wb);
     uint8_t* b = (uint8_t*)d_blob;
     hipStream_t s = (hipStream_t)stream;
-    st = launch_quantize(d_gate, I, H, shape->group, b + L.gate_q, (float*)(b + L.gate_s), s, wb);
+    st = launch_quantize(d_gate, I, H, shape->group, b + L.gate_q, (float*)(b + L.gate_s), s, wb, true);
     if (st) return st;
-    st = launch_quantize(d_up, I, H, shape->group, b + L.up_q, (float*)(b + L.up_s), s, wb);
+    st = launch_quantize(d_up, I, H, shape->group, b + L.up_q, (float*)(b + L.up_s), s, wb, true);
     if (st) return st;
     return launch_quantize(d_down, H, I, shape->group, b + L.down_q, (float*)(b + L.down_s), s, wb);
     COLI_GUARD_END
@@ -208,10 +208,10 @@ coli_status coli_convert_fp8_expert(const coli_moe_shape* shape, const uint8_t* 
     uint8_t* b = (uint8_t*)d_blob;
     hipStream_t s = (hipStream_t)stream;
     st = launch_convert_fp8(d_gate8, d_gate_scale, I, H, shape->group, b + L.gate_q,
-                            (float*)(b + L.gate_s), s, wb);
+                            (float*)(b + L.gate_s), s, wb, true);
     if (st) return st;
     st = launch_convert_fp8(d_up8, d_up_scale, I, H, shape->group, b + L.up_q,
-                            (float*)(b + L.up_s), s, wb);
+                            (float*)(b + L.up_s), s, wb, true);
     if (st) return st;
     return launch_convert_fp8(d_down8, d_down_scale, H, I, shape->group, b + L.down_q,
                               (float*)(b + L.down_s), s, wb);

@@ -43,6 +43,15 @@ struct BlobLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Gate and up rows of a blob are interleaved in blocks of kGuBlock rows: block
+// b of gate, then block b of up, so that a tile of both matrices' rows is one
+// contiguous stretch. Row r of gate sits at gate_q + gu_row(r) * row bytes, row
+// r of up at up_q + gu_row(r) * row bytes (up_q = gate_q + kGuBlock rows).
+constexpr int kGuBlock = 16;
+__host__ __device__ inline int64_t gu_row(int64_t r) {
+    return (r / kGuBlock) * (2 * kGuBlock) + r % kGuBlock;
+}
+
 inline BlobLayout blob_layout(int64_t H, int64_t I, int32_t group, int32_t wbits = 4) {
     BlobLayout L;
     L.wbits = wbits == 8 ? 8 : 4;
@@ -51,8 +60,9 @@ inline BlobLayout blob_layout(int64_t H, int64_t I, int32_t group, int32_t wbits
     size_t gs = (size_t)I * (size_t)(group ? H / group : 1) * 4;
     size_t ds = (size_t)H * (size_t)(group ? I / group : 1) * 4;
     size_t o = 0;
-    L.gate_q = o; o = align256(o + gq);
-    L.up_q = o;   o = align256(o + gq);
+    L.gate_q = o;                                   // gate and up rows interleaved (gu_row)
+    L.up_q = o + (size_t)kGuBlock * (size_t)(H / div);
+    o = align256(o + 2 * gq);
     L.down_q = o; o = align256(o + dq);
     L.gate_s = o; o = align256(o + gs);
     L.up_s = o;   o = align256(o + gs);
@@ -556,13 +566,15 @@ __device__ __forceinline__ constexpr int transpose_shift() {
 
 // ------------------------------------------------- launch entry points
 // (host functions implemented in the .hip files; all enqueue on `stream`)
+// gu_rows: the q rows of an expert's gate or up matrix, placed at gu_row(r).
 coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t group,
-                            uint8_t* q, float* s, hipStream_t stream, int32_t wbits = 4);
+                            uint8_t* q, float* s, hipStream_t stream, int32_t wbits = 4,
+                            bool gu_rows = false);
 // FP8 e4m3 codes w8 [rows][cols] with scales [ceil(rows/128)][ceil(cols/128)]
 // -> f32 -> int4, through the same quantiser kernels.
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
                                int32_t group, uint8_t* q, float* s, hipStream_t stream,
-                               int32_t wbits = 4);
+                               int32_t wbits = 4, bool gu_rows = false);
 coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int32_t H,
                                  int32_t E, float* logits, hipStream_t stream);
 // Router for small batches (T <= kSmallT): logits (when router_w is given)

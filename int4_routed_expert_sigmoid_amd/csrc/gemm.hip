@@ -77,34 +77,39 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
 
 // ---------------------------------------------------------------- prep
 // x [T][H] f32 -> xb [T][H] bf16 and S_x [T][H/64] (sums of the bf16 values of
-// each 64-column group, left to right). One thread per group.
+// each 64-column group). One thread per 8 columns (two 16-byte loads, lanes
+// reading consecutive bytes); the 8 partial sums of a group sit in 8 adjacent
+// lanes and are added in a fixed tree order (DPP partners 1, 2, then 7).
 __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ x, int T, int H,
                                                    uint16_t* __restrict__ xb,
                                                    float* __restrict__ sx) {
-    const int G = H / 64;
+    const int C8 = H / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)T * G) return;
-    const int64_t t = gid / G;
-    const int g = (int)(gid % G);
-    const float* src = x + t * H + g * 64;
-    uint16_t* dst = xb + t * H + g * 64;
-    float s = 0.f;
-    for (int j = 0; j < 64; j += 8) {
-        const float4 a = *reinterpret_cast<const float4*>(src + j);
-        const float4 b = *reinterpret_cast<const float4*>(src + j + 4);
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        // slot order: positions 0..7 hold columns 0 2 4 6 1 3 5 7
-        uint32_t pk[4];
+    const bool ok = gid < (int64_t)T * C8;
+    const int64_t gc = ok ? gid : (int64_t)T * C8 - 1;
+    const int64_t t = gc / C8;
+    const int c8 = (int)(gc % C8);
+    const float* src = x + t * H + c8 * 8;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    // slot order: positions 0..7 hold columns 0 2 4 6 1 3 5 7
+    uint32_t pk[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c0 = 4 * (i & 1) + (i >> 1), c1 = c0 + 2;     // (0,2) (4,6) (1,3) (5,7)
-            pk[i] = (uint32_t)bf16_bits(v[c0]) | ((uint32_t)bf16_bits(v[c1]) << 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s += bf16_round(v[i]);
-        *reinterpret_cast<uint4*>(dst + j) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    for (int i = 0; i < 4; ++i) {
+        const int c0 = 4 * (i & 1) + (i >> 1), c1 = c0 + 2;     // (0,2) (4,6) (1,3) (5,7)
+        pk[i] = (uint32_t)bf16_bits(v[c0]) | ((uint32_t)bf16_bits(v[c1]) << 16);
     }
-    sx[t * G + g] = s;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += bf16_round(v[i]);
+    s += __int_as_float(lane_xchg<1>(__float_as_int(s)));
+    s += __int_as_float(lane_xchg<2>(__float_as_int(s)));
+    s += __int_as_float(lane_xchg<4>(__float_as_int(s)));       // partner lane ^ 7
+    if (ok) {
+        *reinterpret_cast<uint4*>(xb + t * H + c8 * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        if ((c8 & 7) == 0) sx[t * (H / 64) + c8 / 8] = s;
+    }
 }
 
 // ------------------------------------------------------------ tile list
@@ -412,7 +417,7 @@ __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& i
     const int wrow = rb * 128 + wave * 32;                    // this wave's first weight row
     const bool wlive = wrow < I;                              // false in the last block when I % 128 == 64
     const int irow = min(wrow, I - 32) + ln;                  // this lane's weight row (clamped when dead)
-    const size_t boff = (size_t)irow * (H / 2) + lh * 16;
+    const size_t boff = (size_t)gu_row(irow) * (H / 2) + lh * 16;
     const float* gsc = reinterpret_cast<const float*>(it.blob + L.gate_s);
     const float* usc = reinterpret_cast<const float*>(it.blob + L.up_s);
     const int atok = a.rows_tok[it.begin + min(m0 + (int)(threadIdx.x >> 2), it.count - 1)];
@@ -580,8 +585,7 @@ size_t gemm_tiles_max(int32_t rows, int32_t max_items) {
 coli_status launch_mfma_ffn(const GemmArgs& a, const float* x, int32_t T, int32_t max_tiles,
                             hipStream_t stream) {
     if (a.H % 64 || a.I % 64) return fail(COLI_EUNSUPPORTED, "mfma path: hidden and inter must be multiples of 64");
-    const int G = a.H / 64;
-    const int64_t prep_threads = (int64_t)T * G;
+    const int64_t prep_threads = (int64_t)T * (a.H / 8);
     launch(prep_kernel, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream, x, T,
            a.H, a.xb, a.sx);
     COLI_CHECK_LAUNCH("prep kernel launch");

@@ -94,7 +94,7 @@ __device__ __forceinline__ void gateup_body(
                         // merge at): threads past the row end re-read its last
                         // block, and their products are masked
                         const int ch = min(tid + 64 * W * j, C - 1);
-                        wv[r][mt][j] = load_wblock<W8>(wq[mt] + row * rowbytes, ch);
+                        wv[r][mt][j] = load_wblock<W8>(wq[mt] + gu_row(row) * rowbytes, ch);
                         if (GS) fv[r][mt][j] = ldg_f32(wsc[mt] + (size_t)row * gpr + (ch >> 1));
                     }
             }

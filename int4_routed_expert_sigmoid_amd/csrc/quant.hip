@@ -138,7 +138,8 @@ struct Fp8Src {
 template <typename Src, bool W8>
 __global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t cols,
                                                         uint8_t* __restrict__ q,
-                                                        float* __restrict__ s, int aligned_out) {
+                                                        float* __restrict__ s, int aligned_out,
+                                                        int gu_rows) {
     __shared__ float red[4];
     const int64_t r = blockIdx.x;
     const int64_t words = cols / 8, tail = cols % 8;   // tail is 0, 2, 4 or 6 columns
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t cols,
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float scale = __fdiv_rn(m, W8 ? 127.0f : 7.0f);
     if (threadIdx.x == 0) s[r] = scale;
-    uint8_t* qr = q + r * (W8 ? cols : cols / 2);
+    uint8_t* qr = q + (gu_rows ? gu_row(r) : r) * (W8 ? cols : cols / 2);
     for (int64_t i = threadIdx.x; i < words; i += blockDim.x) {
         float v[8];
         src.load8(r, 8 * i, v);
@@ -176,7 +177,8 @@ __global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t cols,
 template <typename Src, bool W8>
 __global__ __launch_bounds__(256) void quant_g64_kernel(Src src, int64_t rows, int64_t cols,
                                                         uint8_t* __restrict__ q,
-                                                        float* __restrict__ s, int aligned_out) {
+                                                        float* __restrict__ s, int aligned_out,
+                                                        int gu_rows) {
     const int64_t words_per_row = cols / 8;
     const int64_t total = rows * words_per_row;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // word index
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(256) void quant_g64_kernel(Src src, int64_t rows, i
     const float scale = __fdiv_rn(m, W8 ? 127.0f : 7.0f);
     if (i < total) {
         if ((wi & 7) == 0) s[r * (cols / 64) + wi / 8] = scale;
-        store8<W8>(q + r * (W8 ? cols : cols / 2), wi * 8, v, scale, aligned_out);
+        store8<W8>(q + (gu_rows ? gu_row(r) : r) * (W8 ? cols : cols / 2), wi * 8, v, scale, aligned_out);
     }
 }
 
@@ -208,10 +210,11 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(const uint8_t* __restrict
                                                        const float* __restrict__ sc,
                                                        int64_t rows, int64_t cols,
                                                        int64_t sc_cols, uint8_t* __restrict__ q,
-                                                       float* __restrict__ s) {
+                                                       float* __restrict__ s, int gu_rows) {
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;                       // whole waves only
+    uint8_t* qr = q + (gu_rows ? gu_row(r) : r) * (cols >> 1);
     const int64_t units = cols >> 4;
     const uint8_t* row = w8 + r * cols;
     const float* scr = sc + (r >> 7) * sc_cols;
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(const uint8_t* __restrict
                 uint2 out;
                 out.x = pack8(&v[c][0], scale);
                 out.y = pack8(&v[c][8], scale);
-                *reinterpret_cast<uint2*>(q + r * (cols >> 1) + u * 8) = out;
+                *reinterpret_cast<uint2*>(qr + u * 8) = out;
             }
         }
         m = fmaxf(m, mc);
@@ -266,55 +269,55 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(const uint8_t* __restrict
             uint2 out;
             out.x = pack8(&v[c][0], scale);
             out.y = pack8(&v[c][8], scale);
-            *reinterpret_cast<uint2*>(q + r * (cols >> 1) + u * 8) = out;
+            *reinterpret_cast<uint2*>(qr + u * 8) = out;
         }
     }
 }
 
 template <bool G64>
 bool launch_fp8_wave(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
-                     uint8_t* q, float* s, hipStream_t stream) {
+                     uint8_t* q, float* s, int gu_rows, hipStream_t stream) {
     const int64_t nc = (cols / 16 + 63) / 64;
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     const int64_t sc_cols = (cols + 127) / 128;
-    if (nc <= 1) launch(fp8_wave_kernel<1, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s);
-    else if (nc <= 2) launch(fp8_wave_kernel<2, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s);
-    else if (nc <= 4) launch(fp8_wave_kernel<4, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s);
-    else if (nc <= 6) launch(fp8_wave_kernel<6, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s);
-    else if (nc <= 8) launch(fp8_wave_kernel<8, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s);
+    if (nc <= 1) launch(fp8_wave_kernel<1, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
+    else if (nc <= 2) launch(fp8_wave_kernel<2, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
+    else if (nc <= 4) launch(fp8_wave_kernel<4, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
+    else if (nc <= 6) launch(fp8_wave_kernel<6, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
+    else if (nc <= 8) launch(fp8_wave_kernel<8, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
     else return false;
     return true;
 }
 
 template <typename Src, bool W8>
 coli_status launch_quant_t(const Src& src, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
-                           float* s, int aligned_out, hipStream_t stream) {
+                           float* s, int aligned_out, int gu_rows, hipStream_t stream) {
     if (group == 0) {
         if (rows > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: too many rows");
         launch(quant_row_kernel<Src, W8>, dim3((unsigned)rows), dim3(256), 0, stream, src,
-               cols, q, s, aligned_out);
+               cols, q, s, aligned_out, gu_rows);
     } else {
         // the group of 8 lanes must not straddle rows: cols % 64 == 0 is required
         const int64_t total = rows * (cols / 8);
         const int64_t blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: tensor too large");
         launch(quant_g64_kernel<Src, W8>, dim3((unsigned)blocks), dim3(256), 0, stream, src, rows,
-               cols, q, s, aligned_out);
+               cols, q, s, aligned_out, gu_rows);
     }
     return COLI_OK;
 }
 
 template <typename Src>
 coli_status launch_quant(const Src& src, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
-                         float* s, int aligned_out, hipStream_t stream, int32_t wbits) {
+                         float* s, int aligned_out, hipStream_t stream, int32_t wbits, int gu_rows) {
     if (rows == 0) return COLI_OK;
     coli_status st;
     if (wbits == 8) {
         if (cols % kBlock || (uintptr_t)q % 4)
             return fail(COLI_EINVAL, "quantize: int8 rows need cols % 32 == 0 and 4-byte alignment");
-        st = launch_quant_t<Src, true>(src, rows, cols, group, q, s, 1, stream);
+        st = launch_quant_t<Src, true>(src, rows, cols, group, q, s, 1, gu_rows, stream);
     } else {
-        st = launch_quant_t<Src, false>(src, rows, cols, group, q, s, aligned_out, stream);
+        st = launch_quant_t<Src, false>(src, rows, cols, group, q, s, aligned_out, gu_rows, stream);
     }
     if (st) return st;
     COLI_CHECK_LAUNCH("quantize kernel launch");
@@ -324,21 +327,21 @@ coli_status launch_quant(const Src& src, int64_t rows, int64_t cols, int32_t gro
 }  // namespace
 
 coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
-                            float* s, hipStream_t stream, int32_t wbits) {
+                            float* s, hipStream_t stream, int32_t wbits, bool gu_rows) {
     const int aligned = ((uintptr_t)w % 16 == 0) && ((uintptr_t)q % 4 == 0) &&
                         (cols % 8 == 0) ? 1 : 0;
     F32Src src{w, cols, aligned};
-    return launch_quant(src, rows, cols, group, q, s, aligned, stream, wbits);
+    return launch_quant(src, rows, cols, group, q, s, aligned, stream, wbits, gu_rows ? 1 : 0);
 }
 
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
                                int32_t group, uint8_t* q, float* s, hipStream_t stream,
-                               int32_t wbits) {
+                               int32_t wbits, bool gu_rows) {
     if (rows == 0) return COLI_OK;
     if (wbits != 8 && (uintptr_t)w8 % 16 == 0 && (uintptr_t)q % 8 == 0 && cols % 16 == 0 &&
         cols <= 8192 && rows <= 0x1fffffffLL) {
-        const bool ok = group == 0 ? launch_fp8_wave<false>(w8, scale, rows, cols, q, s, stream)
-                                   : launch_fp8_wave<true>(w8, scale, rows, cols, q, s, stream);
+        const bool ok = group == 0 ? launch_fp8_wave<false>(w8, scale, rows, cols, q, s, gu_rows ? 1 : 0, stream)
+                                   : launch_fp8_wave<true>(w8, scale, rows, cols, q, s, gu_rows ? 1 : 0, stream);
         if (ok) {
             COLI_CHECK_LAUNCH("fp8 convert kernel launch");
             return COLI_OK;
@@ -347,7 +350,7 @@ coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t ro
     const int aligned_in = ((uintptr_t)w8 % 8 == 0) && (cols % 8 == 0) ? 1 : 0;
     const int aligned_out = ((uintptr_t)q % 4 == 0) && (cols % 8 == 0) ? 1 : 0;
     Fp8Src src{w8, scale, cols, (cols + 127) / 128, aligned_in};
-    return launch_quant(src, rows, cols, group, q, s, aligned_out, stream, wbits);
+    return launch_quant(src, rows, cols, group, q, s, aligned_out, stream, wbits, gu_rows ? 1 : 0);
 }
 
 }  // namespace coli

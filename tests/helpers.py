@@ -65,3 +65,16 @@ class ExpertSet:
                 qe = zero
             out.append(qe)
         return out
+
+
+def blob_q_rows(blob, off, part: int, rows: int, row_bytes: int):
+    """The weight bytes of blob part `part` (0 gate, 1 up, 2 down) as [rows][row_bytes]
+    in row order. Gate and up rows are interleaved in the blob in blocks of 16 rows
+    (block b of gate, then block b of up, starting at the gate offset); down rows
+    are contiguous."""
+    import numpy as np
+    if part == 2:
+        return blob[off[2]:off[2] + rows * row_bytes].reshape(rows, row_bytes)
+    region = blob[off[0]:off[0] + 2 * rows * row_bytes].reshape(2 * rows, row_bytes)
+    r = np.arange(rows)
+    return region[(r // 16) * 32 + r % 16 + (16 if part == 1 else 0)]

@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(L):
 def test_blob_layout_sizes(L):
     off, nbytes = coli.blob_layout(coli.MoEShape(6144, 2048, 256, 1, 8, 0))
     assert nbytes == 18_915_328
-    assert off == [0, 6291456, 12582912, 18874368, 18882560, 18890752]
+    # gate and up rows interleaved in 16-row blocks: up starts 16 rows of 3072 B after gate
+    assert off == [0, 49152, 12582912, 18874368, 18882560, 18890752]
     off, nbytes = coli.blob_layout(coli.MoEShape(6144, 2048, 256, 1, 8, 64))
     assert nbytes == 21_233_664
     assert all(o % 256 == 0 for o in off)
@@ -92,3 +93,19 @@ def test_argument_errors_before_launch(L):
     # T = 0 is a no-op
     assert L.coli_moe_layer_fwd(ctypes.byref(s), None, 0, vp(1), None, None, vp(1), vp(1), None,
                                 0, None, None, None, 0, None, 0, None) == coli.COLI_OK
+
+
+def test_read_probe_argument_errors(L):
+    vp = ctypes.c_void_p
+    # NULL buffers, sizes that are not whole 16-byte loads
+    assert L.coli_read_probe(None, 1 << 20, 0, 4096, 0, vp(1), 1 << 20, None) == coli.COLI_EINVAL
+    assert L.coli_read_probe(vp(1), 1000, 0, 4096, 0, vp(1), 1 << 20, None) == coli.COLI_EINVAL
+    # chunk not a multiple of 4096; sink too small for one word per wave
+    assert L.coli_read_probe(vp(1), 1 << 20, 0, 3000, 0, vp(1), 1 << 20, None) == coli.COLI_EINVAL
+    assert L.coli_read_probe(vp(1), 1 << 20, 0, 4096, 0, vp(1), 16, None) == coli.COLI_EINVAL
+    # rows: 48 threads per row neither divide 256 nor make a 3-wave row
+    assert L.coli_read_probe(vp(1), 768 * 64, 1, 768, 8, vp(1), 1 << 20, None) == coli.COLI_EINVAL
+    # rows: bytes not a whole number of rows; no rows per workgroup; unknown pattern
+    assert L.coli_read_probe(vp(1), 3072 * 3 + 16, 1, 3072, 16, vp(1), 1 << 20, None) == coli.COLI_EINVAL
+    assert L.coli_read_probe(vp(1), 3072 * 3, 1, 3072, 0, vp(1), 1 << 20, None) == coli.COLI_EINVAL
+    assert L.coli_read_probe(vp(1), 1 << 20, 2, 4096, 0, vp(1), 1 << 20, None) == coli.COLI_EINVAL

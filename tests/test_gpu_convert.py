@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 import synth
+from tests.helpers import blob_q_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +87,7 @@ def test_glm_expert_blob(coli, group):
     b = blob.cpu().numpy()
     for i, ((codes, scale), (r, c)) in enumerate(zip(mats, ((I, H), (I, H), (H, I)))):
         q_ref, s_ref = oracle.convert_fp8_int4(codes, scale, group)
-        q = b[off[i]:off[i] + q_ref.nbytes].reshape(q_ref.shape)
+        q = blob_q_rows(b, off, i, r, q_ref.shape[1]).reshape(q_ref.shape)
         s = b[off[3 + i]:off[3 + i] + s_ref.nbytes].view(np.float32).reshape(s_ref.shape)
         assert np.array_equal(q, q_ref), i
         assert np.array_equal(s, s_ref), i

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from tests.helpers import ExpertSet, rel_l2_rows
+from tests.helpers import blob_q_rows, ExpertSet, rel_l2_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def test_int8_blob_bit_exact(coli, H, I, group):
     b = blob.cpu().numpy()
     for i, (w, r, c) in enumerate(((g, I, H), (u, I, H), (d, H, I))):
         q_ref, s_ref = oracle.quantize_int8(w, group)
-        q = _int8_from_planes(b[off[i]:off[i] + r * c], r, c)
+        q = _int8_from_planes(blob_q_rows(b, off, i, r, c).reshape(-1), r, c)
         s = b[off[3 + i]:off[3 + i] + s_ref.nbytes].view(np.float32).reshape(s_ref.shape)
         assert np.array_equal(q, q_ref), i
         assert np.array_equal(s, s_ref), i
@@ -71,7 +71,7 @@ def test_int8_fp8_conversion(coli):
     b = blob.cpu().numpy()
     for i, ((codes, scale), (r, c)) in enumerate(zip(mats, ((I, H), (I, H), (H, I)))):
         q_ref, s_ref = oracle.quantize_int8(oracle.fp8_block_dequant(codes, scale), 64)
-        assert np.array_equal(_int8_from_planes(b[off[i]:off[i] + r * c], r, c), q_ref), i
+        assert np.array_equal(_int8_from_planes(blob_q_rows(b, off, i, r, c).reshape(-1), r, c), q_ref), i
         s = b[off[3 + i]:off[3 + i] + s_ref.nbytes].view(np.float32).reshape(s_ref.shape)
         assert np.array_equal(s, s_ref), i
 

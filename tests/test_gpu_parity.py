@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from tests.helpers import ExpertSet, rel_l2_rows
+from tests.helpers import blob_q_rows, ExpertSet, rel_l2_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +99,10 @@ def test_quantize_expert_layout(coli):
     qe = oracle.QExpert.quantize(g, u, d, 64)
     parts = qe.parts
     for i, p in enumerate(parts):
-        raw = blob[off[i]:off[i] + p.nbytes]
+        if i < 3:                                    # weight rows (gate and up interleaved)
+            raw = blob_q_rows(blob, off, i, p.shape[0], p.shape[1]).reshape(-1)
+        else:
+            raw = blob[off[i]:off[i] + p.nbytes]
         assert np.array_equal(raw, p.reshape(-1).view(np.uint8)), f"part {i}"
 
 
