@@ -358,7 +358,9 @@ __device__ __forceinline__ float encode_h16_lanes(const float (&v)[NE], int e0,
 #pragma unroll
     for (int p = 0; p < kPlanes; ++p) words[p] = 0u;
     if (m != 0.f) {
-        const float inv = (float)kDigitMax / m;
+        // the hardware reciprocal (1 ulp): X may land one step off the
+        // correctly rounded quotient, and the clamp keeps it in range
+        const float inv = (float)kDigitMax * __builtin_amdgcn_rcpf(m);
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
             uint32_t nib[kPlanes];
@@ -379,7 +381,7 @@ __device__ __forceinline__ float encode_h16_lanes(const float (&v)[NE], int e0,
     xor_or(std::integral_constant<int, 2>{});
     xor_or(std::integral_constant<int, 4>{});
     xor_or(std::integral_constant<int, 8>{});
-    return m == 0.f ? 0.f : m / (float)kDigitMax;
+    return m * (1.0f / (float)kDigitMax);
 }
 
 // ------------------------------------------------------- expert selection

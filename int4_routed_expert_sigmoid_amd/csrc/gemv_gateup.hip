@@ -212,7 +212,7 @@ __device__ __forceinline__ void gateup_body(
             }
             g *= rsg[q];
             u *= rsu[q];
-            g = g / (1.f + expf(-g));                                   // silu(g)
+            g = g * __builtin_amdgcn_rcpf(1.f + __expf(-g));            // silu(g)
             const float hv[1] = {g * u};
             uint32_t words[kPlanes];
             const float sc = encode_h16_lanes<kHBlock, 1, 1>(hv, r % kHBlock, words);
