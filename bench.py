@@ -450,7 +450,10 @@ def run_decode(args, coli, dev):
                      "warm_frac": round(gbps(gu_bytes, gu_warm) / HBM_PEAK_GBPS, 4),
                      "eager_frac": round(gbps(gu_bytes, eager_gu_us) / HBM_PEAK_GBPS, 4),
                      "eager_avg_launch_us": round(eager_gu_us, 3),
-                     "launches_timed": N * reps},
+                     "launches_timed": N * reps,
+                     # the other expert GEMV and the pair (same timing method)
+                     "down_frac": round(gbps(dn_bytes, dn_us) / HBM_PEAK_GBPS, 4),
+                     "both_frac": round(gbps(gu_bytes + dn_bytes, gu_us + dn_us) / HBM_PEAK_GBPS, 4)},
         "expert_gemv": {
             "gateup_us": {"cold": round(gu_cold, 3), "warm": round(gu_warm, 3),
                           "eager": round(eager_gu_us, 3)},
