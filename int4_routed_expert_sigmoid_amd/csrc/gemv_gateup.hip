@@ -235,13 +235,23 @@ __device__ __forceinline__ void gateup_body(
 
 // Work item `item` of a one-token call from the folded routing (FusedRoute).
 // The shared expert's workgroups need no routing and start on their weights
-// at once. Every other wave selects the top-k from the selection codes
-// (select_topk), ranks the kept picks by expert id (the work list order:
-// shared expert first, then the kept experts by id) and takes its own;
-// workgroup (0, first routed item) publishes the routing, the slot-list rows
+// at once. In every other workgroup the first wave selects the top-k from the
+// selection codes (select_topk), ranks the kept picks by expert id (the work
+// list order: shared expert first, then the kept experts by id) and takes the
+// workgroup's own pick, which it hands to the other waves through LDS (they
+// wait at one barrier instead of repeating the selection: all workgroups of a
+// decode launch are resident at once, so a selection per wave would queue
+// about three of them on every SIMD before the first weight load).
+// Workgroup (0, first routed item) publishes the routing, the slot-list rows
 // and the item count, and each (0, item) workgroup its item, for the passes
 // that follow. False: no such item (a slot dropped by top-p).
-__device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkItem& it) {
+struct FusedPick {
+    const uint8_t* blob;
+    int begin, row0, ok;
+};
+
+__device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkItem& it,
+                                           FusedPick* pick) {
     constexpr int EPL = kFusedMaxExperts / 64;
     const int lane = threadIdx.x & 63;
     const int k = fr.k, base = fr.shared ? 1 : 0;
@@ -253,56 +263,67 @@ __device__ __forceinline__ bool fused_item(const FusedRoute& fr, int item, WorkI
         if (blockIdx.x == 0 && threadIdx.x == 0) fr.items[item] = it;
         return true;
     }
-    uint64_t code[EPL];
-    float score[EPL];
-    const void* ptr[EPL];                            // blob pointers, loaded with the codes
+    if (threadIdx.x < 64) {
+        uint64_t code[EPL];
+        float score[EPL];
+        const void* ptr[EPL];                        // blob pointers, loaded with the codes
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = min(lane + 64 * i, fr.E - 1);
-        code[i] = fr.codes[e];
-        score[i] = fr.scores[e];
-        ptr[i] = fr.table[e];
-    }
+        for (int i = 0; i < EPL; ++i) {
+            const int e = min(lane + 64 * i, fr.E - 1);
+            code[i] = fr.codes[e];
+            score[i] = fr.scores[e];
+            ptr[i] = fr.table[e];
+        }
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) code[i] = lane + 64 * i < fr.E ? code[i] : 0;
-    const TopK r = select_topk<EPL>(code, score, k, fr.topp);
-    const int kept = r.kept;
-    const bool mine = lane < kept;
-    int below = 0;                                   // rank of this lane's pick by expert id
-    for (int j = 0; j < kept; ++j) below += __builtin_amdgcn_readlane(r.my_idx, j) < r.my_idx;
-    if (blockIdx.x == 0 && item == base && threadIdx.x < 64) {
-        if (lane < k) {
-            fr.idx[lane] = mine ? r.my_idx : -1;
-            fr.w[lane] = mine ? r.my_w : 0.f;
+        for (int i = 0; i < EPL; ++i) code[i] = lane + 64 * i < fr.E ? code[i] : 0;
+        const TopK r = select_topk<EPL>(code, score, k, fr.topp);
+        const int kept = r.kept;
+        const bool mine = lane < kept;
+        int below = 0;                               // rank of this lane's pick by expert id
+        for (int j = 0; j < kept; ++j) below += __builtin_amdgcn_readlane(r.my_idx, j) < r.my_idx;
+        if (blockIdx.x == 0 && item == base) {
+            if (lane < k) {
+                fr.idx[lane] = mine ? r.my_idx : -1;
+                fr.w[lane] = mine ? r.my_w : 0.f;
+            }
+            if (mine) {
+                fr.rows_tok[below] = 0;
+                fr.rows_out[below] = lane;
+            }
+            if (lane == 0) {
+                fr.rows_tok[k] = 0;
+                fr.rows_out[k] = k;
+                *fr.n_items = base + kept;
+            }
         }
-        if (mine) {
-            fr.rows_tok[below] = 0;
-            fr.rows_out[below] = lane;
-        }
-        if (lane == 0) {
-            fr.rows_tok[k] = 0;
-            fr.rows_out[k] = k;
-            *fr.n_items = base + kept;
-        }
-    }
-    {
         const int rk = item - base;
-        if (rk >= kept) return false;
-        const uint64_t hit = __ballot(mine && below == rk);       // exactly one lane
-        const int src = (int)__builtin_ctzll(hit);
-        const int e = __builtin_amdgcn_readlane(r.my_idx, src);
-        // expert e's pointer sits in lane e % 64, register e / 64 (both uniform)
-        const void* pe = ptr[0];
+        if (rk < kept) {
+            const uint64_t hit = __ballot(mine && below == rk);   // exactly one lane
+            const int src = (int)__builtin_ctzll(hit);
+            const int e = __builtin_amdgcn_readlane(r.my_idx, src);
+            // expert e's pointer sits in lane e % 64, register e / 64 (both uniform)
+            const void* pe = ptr[0];
 #pragma unroll
-        for (int i = 1; i < EPL; ++i) pe = (e >> 6) == i ? ptr[i] : pe;
-        const uint64_t pb = (uint64_t)pe;
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, e & 63);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), e & 63);
-        it.blob = (const uint8_t*)(((uint64_t)hi << 32) | lo);
-        it.begin = rk;
-        it.count = 1;
-        it.row0 = src;
+            for (int i = 1; i < EPL; ++i) pe = (e >> 6) == i ? ptr[i] : pe;
+            const uint64_t pb = (uint64_t)pe;
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, e & 63);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), e & 63);
+            if (lane == 0) {
+                pick->blob = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+                pick->begin = rk;
+                pick->row0 = src;
+                pick->ok = 1;
+            }
+        } else if (lane == 0) {
+            pick->ok = 0;
+        }
     }
+    __syncthreads();
+    if (!pick->ok) return false;
+    it.blob = pick->blob;
+    it.begin = pick->begin;
+    it.count = 1;
+    it.row0 = pick->row0;
     if (blockIdx.x == 0 && threadIdx.x == 0) fr.items[item] = it;
     return true;
 }
@@ -330,10 +351,11 @@ void gateup_kernel(
     uint32_t* __restrict__ hplanes, float* __restrict__ hscale, int H, int I, BlobLayout L,
     FusedRoute fr) {
     __shared__ float red[W * kBlock * (MTK == 1 ? 1 : 2 * 4)];
+    __shared__ FusedPick pick;
     const int item = blockIdx.y;
     WorkItem it;
     if (MTK == 1 && fr.codes) {
-        if (!fused_item(fr, item, it)) return;
+        if (!fused_item(fr, item, it, &pick)) return;
     } else {
         if (item >= *n_items) return;
         it = items[item];
