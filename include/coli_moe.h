@@ -397,6 +397,30 @@ COLI_API coli_status coli_moe_lookahead(const coli_moe_shape* shape, const float
  * Lets the error path of a failed copy be exercised without a faulty device. */
 COLI_API coli_status coli_debug_fail_copies(int32_t n);
 
+/* Testing: log the weight tiles the GEMV kernels stream, so that a test can
+ * check that the batch union reads each unique expert's rows once (lbrq.cn
+ * article "github一周涨11k⭐️！25GB 内存跑 744B GLM-5.2 模型！", section 三
+ * item 4; practical guide section 二). After this call every gate/up and down
+ * GEMV launch (coli_moe_expert_ffn, coli_moe_layer_fwd on the GEMV path) has
+ * thread 0 of each workgroup that streamed a tile atomically add 1 to
+ * *d_count (a device uint32, zeroed by the caller) and, while the old count
+ * is below capacity, write a record of four uint32 to d_records[old count]:
+ *   blob address bits 0..31, bits 32..63,
+ *   pass << 16 | tile   (pass 0: gate/up, a tile being rows [tile * r,
+ *                        (tile + 1) * r) of both matrices; pass 1: down,
+ *                        rows of the down matrix, clamped to hidden),
+ *   r | passes << 16    (r rows per tile: 16 gate/up and 32 down for one
+ *                        token, 32 and 64 for batches; passes: how many
+ *                        times the workgroup walked those rows, once per
+ *                        chunk of up to 4 tokens).
+ * The count goes on past capacity, so an overflow shows. The MFMA path is not
+ * logged. d_count = nullptr turns the log off (the default); both buffers are
+ * the caller's and must outlive the launches that use them. Process-wide, not
+ * thread-safe; launches captured into a graph keep the log set at capture.
+ * Errors: COLI_EINVAL for capacity < 0, or for a capacity > 0 without
+ * d_records. */
+COLI_API coli_status coli_debug_read_log(uint32_t* d_count, void* d_records, int32_t capacity);
+
 /* ---------------------------------------------------------- kernel timing
  * Optional HIP-event timing of the library's main kernels, recorded on the
  * stream each kernel runs on. coli_profile_enable(n) pre-creates n event

@@ -30,7 +30,8 @@ EXPORTED = [
     "coli_expert_cache_release", "coli_expert_cache_table", "coli_expert_cache_stats",
     "coli_expert_cache_reset", "coli_expert_cache_pin", "coli_expert_cache_usage",
     "coli_expert_cache_pin_hot", "coli_expert_cache_repin", "coli_expert_cache_prefetch",
-    "coli_moe_lookahead", "coli_debug_fail_copies", "coli_profile_enable", "coli_profile_clear",
+    "coli_moe_lookahead", "coli_debug_fail_copies", "coli_debug_read_log",
+    "coli_profile_enable", "coli_profile_clear",
     "coli_profile_summary", "coli_profile_rerun", "coli_read_probe",
 ]
 
@@ -117,6 +118,7 @@ def lib():
             L.coli_moe_lookahead.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, i32, P(i32), vp,
                                              sz, vp]
             L.coli_debug_fail_copies.argtypes = [i32]
+            L.coli_debug_read_log.argtypes = [vp, vp, i32]
             L.coli_profile_enable.argtypes = [i32]
             L.coli_profile_clear.argtypes = []
             L.coli_profile_summary.argtypes = [ctypes.c_char_p, P(i64), P(ctypes.c_double)]
@@ -412,6 +414,17 @@ def debug_fail_copies(n: int):
     """coli_debug_fail_copies: the next n expert-cache copies fail (COLI_EHIP)
     before anything is enqueued."""
     _check(lib().coli_debug_fail_copies(n))
+
+
+def debug_read_log(count=None, records=None):
+    """coli_debug_read_log: log the weight tiles the GEMV kernels stream.
+    count: a zeroed 1-element int32/uint32 device tensor; records: an int32
+    device tensor [capacity, 4]. No arguments: log off."""
+    if count is None:
+        _check(lib().coli_debug_read_log(None, None, 0))
+        return
+    cap = 0 if records is None else int(records.shape[0])
+    _check(lib().coli_debug_read_log(_ptr(count), _ptr(records), cap))
 
 
 def profile_enable(max_records: int):

@@ -103,6 +103,32 @@ struct FusedRoute {
 };
 constexpr int kFusedMaxExperts = 256;   // four selection codes per lane
 
+// Optional log of the weight tiles the GEMV kernels stream (switched on by
+// coli_debug_read_log; count == nullptr: off). Thread 0 of every workgroup
+// that streamed a tile appends {blob address low word, high word,
+// pass << 16 | tile, rows per tile | passes over the rows << 16}; pass 0 is
+// the gate/up kernel (a tile: rows of both matrices), 1 the down kernel. The
+// count keeps counting past cap, so an overflow shows.
+struct ReadLog {
+    uint32_t* count;
+    uint4* rec;
+    int32_t cap;
+};
+
+__device__ __forceinline__ void log_read(const ReadLog& rl, const void* blob, int pass, int tile,
+                                         int rows, int passes) {
+    if (rl.count == nullptr || threadIdx.x != 0) return;
+    const uint32_t i = atomicAdd(rl.count, 1u);
+    if (i < (uint32_t)rl.cap) {
+        const uint64_t b = (uint64_t)blob;
+        rl.rec[i] = make_uint4((uint32_t)b, (uint32_t)(b >> 32), ((uint32_t)pass << 16) | (uint32_t)tile,
+                               (uint32_t)rows | ((uint32_t)passes << 16));
+    }
+}
+
+// The log the GEMV launches pass (gemv.hip).
+ReadLog read_log_current();
+
 // ------------------------------------------------------ activation digits
 // The GEMV family multiplies int4 weights by activations held as four planes
 // of signed base-16 digits per 32-element block: x_c ~= scale_b * X_c with

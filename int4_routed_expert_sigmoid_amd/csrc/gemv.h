@@ -12,7 +12,8 @@ namespace coli {
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
                      const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
-                     float* hscale, int H, int I, const BlobLayout& L, const FusedRoute& fr);
+                     float* hscale, int H, int I, const BlobLayout& L, const FusedRoute& fr,
+                     const ReadLog& rl);
 
 // Down-matrix rows per wave (4 waves per workgroup). One-token launches take
 // 8: twice the workgroups for the same 9 x 6 MB read keep more of it in flight
@@ -25,6 +26,7 @@ constexpr int down_rows_per_wave(int mt) { return mt == 1 ? 8 : 16; }
 // the instantiated range.
 bool dispatch_down(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                    const int32_t* n_items, const int32_t* rows_out, const uint32_t* hplanes,
-                   const float* hscale, float* y_rows, int H, int I, const BlobLayout& L);
+                   const float* hscale, float* y_rows, int H, int I, const BlobLayout& L,
+                   const ReadLog& rl);
 
 }  // namespace coli

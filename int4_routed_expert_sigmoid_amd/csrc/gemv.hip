@@ -149,7 +149,7 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
         {
             ProfTag prof("gemv_gateup");
             ok = dispatch_gateup(mt, group, g1, stream, items, n_items, rows_tok, rows_out, xplanes,
-                                 xscale, hplanes, hscale, H, I, L, fr);
+                                 xscale, hplanes, hscale, H, I, L, fr, read_log_current());
         }
         if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: hidden too large (max 16384)");
         COLI_CHECK_LAUNCH("gate/up GEMV launch");
@@ -160,7 +160,7 @@ coli_status launch_gemv_ffn(const WorkItem* items, const int32_t* n_items, int32
     {
         ProfTag prof("gemv_down");
         ok = dispatch_down(mt, group, g2, stream, items, n_items, rows_out, hplanes, hscale, y_rows,
-                           H, I, L);
+                           H, I, L, read_log_current());
     }
     if (!ok) return fail(COLI_EUNSUPPORTED, "gemv: inter too large (max 4096)");
     COLI_CHECK_LAUNCH("down GEMV launch");
@@ -178,4 +178,24 @@ coli_status launch_combine(const float* y_rows, const float* w, const int32_t* i
     return COLI_OK;
 }
 
+// The weight-tile read log (coli_debug_read_log); off unless a caller sets it.
+static ReadLog g_read_log = {nullptr, nullptr, 0};
+
+ReadLog read_log_current() { return g_read_log; }
+
 }  // namespace coli
+
+using namespace coli;
+
+extern "C" {
+
+COLI_API coli_status coli_debug_read_log(uint32_t* d_count, void* d_records, int32_t capacity) {
+    if (capacity < 0) return fail(COLI_EINVAL, "debug_read_log: capacity must be >= 0");
+    if (d_count && capacity > 0 && !d_records)
+        return fail(COLI_EINVAL, "debug_read_log: records buffer missing");
+    g_read_log = d_count ? ReadLog{d_count, static_cast<uint4*>(d_records), capacity}
+                         : ReadLog{nullptr, nullptr, 0};
+    return COLI_OK;
+}
+
+}  // extern "C"

@@ -159,13 +159,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W8 ? (NCH =
 void down_kernel(
     const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items,
     const int32_t* __restrict__ rows_out, const uint32_t* __restrict__ hplanes,
-    const float* __restrict__ hscale, float* __restrict__ y_rows, int H, int I, BlobLayout L) {
+    const float* __restrict__ hscale, float* __restrict__ y_rows, int H, int I, BlobLayout L,
+    ReadLog rl) {
     const int item = blockIdx.y;
     if (item >= *n_items) return;
     const WorkItem it = items[item];
     if constexpr (MTK == 1) {
         down_body<NCH, 1, GS, true, W8>(it, rows_out, hplanes, hscale, y_rows, H, I, L);
+        log_read(rl, it.blob, 1, blockIdx.x, 4 * down_rows_per_wave(1), 1);
     } else {
+        log_read(rl, it.blob, 1, blockIdx.x, 4 * down_rows_per_wave(4),
+                 it.count <= 2 ? 1 : (it.count + 3) / 4);
         if (it.count == 1) down_body<NCH, 1, GS, false, W8>(it, rows_out, hplanes, hscale, y_rows, H, I, L);
         else if (it.count == 2) down_body<NCH, 2, GS, false, W8>(it, rows_out, hplanes, hscale, y_rows, H, I, L);
         else down_body<NCH, 4, GS, false, W8>(it, rows_out, hplanes, hscale, y_rows, H, I, L);
@@ -175,30 +179,31 @@ void down_kernel(
 template <int NCH, int MT, bool GS>
 void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
               const int32_t* rows_out, const uint32_t* hp, const float* hs, float* y, int H,
-              int I, const BlobLayout& L) {
+              int I, const BlobLayout& L, const ReadLog& rl) {
     if (L.wbits == 8)
         launch((down_kernel<NCH, MT, GS, true>), grid, dim3(256), 0, s, items, n_items, rows_out,
-               hp, hs, y, H, I, L);
+               hp, hs, y, H, I, L, rl);
     else
         launch((down_kernel<NCH, MT, GS, false>), grid, dim3(256), 0, s, items, n_items, rows_out,
-               hp, hs, y, H, I, L);
+               hp, hs, y, H, I, L, rl);
 }
 
 template <int NCH, bool GS>
 void by_mt(int mt, dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
            const int32_t* rows_out, const uint32_t* hp, const float* hs, float* y, int H, int I,
-           const BlobLayout& L) {
-    if (mt == 1) launch_t<NCH, 1, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L);
-    else launch_t<NCH, 4, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L);
+           const BlobLayout& L, const ReadLog& rl) {
+    if (mt == 1) launch_t<NCH, 1, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L, rl);
+    else launch_t<NCH, 4, GS>(grid, s, items, n_items, rows_out, hp, hs, y, H, I, L, rl);
 }
 
 template <bool GS>
 bool by_width(int CI, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
               const int32_t* n_items, const int32_t* rows_out, const uint32_t* hp,
-              const float* hs, float* y, int H, int I, const BlobLayout& L) {
+              const float* hs, float* y, int H, int I, const BlobLayout& L,
+              const ReadLog& rl) {
     const int nch = (CI + 63) / 64;
-    if (nch == 1) by_mt<1, GS>(mt, grid, s, items, n_items, rows_out, hp, hs, y, H, I, L);
-    else if (nch == 2) by_mt<2, GS>(mt, grid, s, items, n_items, rows_out, hp, hs, y, H, I, L);
+    if (nch == 1) by_mt<1, GS>(mt, grid, s, items, n_items, rows_out, hp, hs, y, H, I, L, rl);
+    else if (nch == 2) by_mt<2, GS>(mt, grid, s, items, n_items, rows_out, hp, hs, y, H, I, L, rl);
     else return false;
     return true;
 }
@@ -207,12 +212,13 @@ bool by_width(int CI, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
 
 bool dispatch_down(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                    const int32_t* n_items, const int32_t* rows_out, const uint32_t* hplanes,
-                   const float* hscale, float* y_rows, int H, int I, const BlobLayout& L) {
+                   const float* hscale, float* y_rows, int H, int I, const BlobLayout& L,
+                   const ReadLog& rl) {
     const int CI = I / kBlock;
     return group ? by_width<true>(CI, mt, grid, s, items, n_items, rows_out, hplanes, hscale,
-                                  y_rows, H, I, L)
+                                  y_rows, H, I, L, rl)
                  : by_width<false>(CI, mt, grid, s, items, n_items, rows_out, hplanes, hscale,
-                                   y_rows, H, I, L);
+                                   y_rows, H, I, L, rl);
 }
 
 }  // namespace coli

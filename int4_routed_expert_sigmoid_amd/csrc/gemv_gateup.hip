@@ -349,7 +349,7 @@ void gateup_kernel(
     const int32_t* __restrict__ rows_tok, const int32_t* __restrict__ rows_out,
     const uint32_t* __restrict__ xplanes, const float* __restrict__ xscale,
     uint32_t* __restrict__ hplanes, float* __restrict__ hscale, int H, int I, BlobLayout L,
-    FusedRoute fr) {
+    FusedRoute fr, ReadLog rl) {
     __shared__ float red[W * kBlock * (MTK == 1 ? 1 : 2 * 4)];
     __shared__ FusedPick pick;
     const int item = blockIdx.y;
@@ -363,7 +363,9 @@ void gateup_kernel(
     const int t = blockIdx.x;
     if constexpr (MTK == 1) {
         gateup_body<W, NCH, 1, GS, true, W8>(it, t, rows_tok, rows_out, xplanes, xscale, hplanes, hscale, H, I, L, red);
+        log_read(rl, it.blob, 0, t, 16, 1);
     } else {
+        log_read(rl, it.blob, 0, t, 32, it.count <= 2 ? 1 : (it.count + 3) / 4);
         if (it.count == 1)
             gateup_body<W, NCH, 1, GS, false, W8>(it, t, rows_tok, rows_out, xplanes, xscale, hplanes, hscale, H, I, L, red);
         else if (it.count == 2)
@@ -377,34 +379,35 @@ template <int W, int NCH, int MTK, bool GS>
 void launch_t(dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
               const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp,
               const float* xs, uint32_t* hp, float* hs, int H, int I, const BlobLayout& L,
-              const FusedRoute& fr) {
+              const FusedRoute& fr, const ReadLog& rl) {
     if (L.wbits == 8) {
         launch((gateup_kernel<W, NCH, MTK, GS, true>), grid, dim3(64 * W), 0, s, items, n_items,
-               rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+               rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
         return;
     }
     launch((gateup_kernel<W, NCH, MTK, GS, false>), grid, dim3(64 * W), 0, s, items, n_items,
-                       rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+                       rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
 }
 
 template <int W, int NCH, bool GS>
 void by_mt(int mt, dim3 grid, hipStream_t s, const WorkItem* items, const int32_t* n_items,
            const int32_t* rows_tok, const int32_t* rows_out, const uint32_t* xp, const float* xs,
-           uint32_t* hp, float* hs, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
-    if (mt == 1) launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
-    else launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+           uint32_t* hp, float* hs, int H, int I, const BlobLayout& L, const FusedRoute& fr,
+           const ReadLog& rl) {
+    if (mt == 1) launch_t<W, NCH, 1, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
+    else launch_t<W, NCH, 4, GS>(grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
 }
 
 template <bool GS>
 bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
               const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
               const uint32_t* xp, const float* xs, uint32_t* hp, float* hs, int H, int I,
-              const BlobLayout& L, const FusedRoute& fr) {
-    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
-    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
-    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
-    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
-    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr);
+              const BlobLayout& L, const FusedRoute& fr, const ReadLog& rl) {
+    if (C <= 64) by_mt<1, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
+    else if (C <= 128) by_mt<2, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
+    else if (C <= 192) by_mt<3, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
+    else if (C <= 256) by_mt<4, 1, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
+    else if (C <= 512) by_mt<4, 2, GS>(mt, grid, s, items, n_items, rows_tok, rows_out, xp, xs, hp, hs, H, I, L, fr, rl);
     else return false;
     return true;
 }
@@ -414,12 +417,13 @@ bool by_width(int C, int mt, dim3 grid, hipStream_t s, const WorkItem* items,
 bool dispatch_gateup(int mt, int group, dim3 grid, hipStream_t s, const WorkItem* items,
                      const int32_t* n_items, const int32_t* rows_tok, const int32_t* rows_out,
                      const uint32_t* xplanes, const float* xscale, uint32_t* hplanes,
-                     float* hscale, int H, int I, const BlobLayout& L, const FusedRoute& fr) {
+                     float* hscale, int H, int I, const BlobLayout& L, const FusedRoute& fr,
+                     const ReadLog& rl) {
     const int C = H / kBlock;
     return group ? by_width<true>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                  xscale, hplanes, hscale, H, I, L, fr)
+                                  xscale, hplanes, hscale, H, I, L, fr, rl)
                  : by_width<false>(C, mt, grid, s, items, n_items, rows_tok, rows_out, xplanes,
-                                   xscale, hplanes, hscale, H, I, L, fr);
+                                   xscale, hplanes, hscale, H, I, L, fr, rl);
 }
 
 }  // namespace coli

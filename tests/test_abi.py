@@ -109,3 +109,17 @@ def test_read_probe_argument_errors(L):
     assert L.coli_read_probe(vp(1), 3072 * 3 + 16, 1, 3072, 16, vp(1), 1 << 20, None) == coli.COLI_EINVAL
     assert L.coli_read_probe(vp(1), 3072 * 3, 1, 3072, 0, vp(1), 1 << 20, None) == coli.COLI_EINVAL
     assert L.coli_read_probe(vp(1), 1 << 20, 2, 4096, 0, vp(1), 1 << 20, None) == coli.COLI_EINVAL
+
+
+def test_read_log_argument_errors(L):
+    vp = ctypes.c_void_p
+    try:
+        # negative capacity; a capacity without a records buffer
+        assert L.coli_debug_read_log(vp(16), vp(32), -1) == coli.COLI_EINVAL
+        assert L.coli_debug_read_log(vp(16), None, 4) == coli.COLI_EINVAL
+        # a count with no capacity (counts only) is accepted: this only records the
+        # pointers, nothing runs here
+        assert L.coli_debug_read_log(vp(16), None, 0) == coli.COLI_OK
+    finally:
+        # never leave a stand-in address behind for a later launch in this process
+        assert L.coli_debug_read_log(None, None, 0) == coli.COLI_OK
