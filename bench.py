@@ -904,7 +904,7 @@ def run_convert(args, coli, dev):
         "data": "synthetic checkpoint-style FP8 (N(0, 0.02) weights, block max / 448 scales)",
         "config": {"workload": f"FP8 -> int4 conversion of {n_exp} GLM-5.2-shaped experts per step",
                    "hidden": H, "inter": I, "experts_per_step": n_exp},
-        "roofline": {"bound": "hbm", "kernel": "fp8_wave_kernel (3 launches per expert)",
+        "roofline": {"bound": "hbm", "kernel": "fp8_wave_kernel (2 launches per expert: gate and up together, then down)",
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_expert": per_expert},

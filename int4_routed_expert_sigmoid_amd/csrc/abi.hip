@@ -207,11 +207,9 @@ coli_status coli_convert_fp8_expert(const coli_moe_shape* shape, const uint8_t* 
     const BlobLayout L = blob_layout(H, I, shape->group, wb);
     uint8_t* b = (uint8_t*)d_blob;
     hipStream_t s = (hipStream_t)stream;
-    st = launch_convert_fp8(d_gate8, d_gate_scale, I, H, shape->group, b + L.gate_q,
-                            (float*)(b + L.gate_s), s, wb, true);
-    if (st) return st;
-    st = launch_convert_fp8(d_up8, d_up_scale, I, H, shape->group, b + L.up_q,
-                            (float*)(b + L.up_s), s, wb, true);
+    st = launch_convert_fp8_pair(d_gate8, d_gate_scale, b + L.gate_q, (float*)(b + L.gate_s),
+                                 d_up8, d_up_scale, b + L.up_q, (float*)(b + L.up_s), I, H,
+                                 shape->group, s, wb, true);
     if (st) return st;
     return launch_convert_fp8(d_down8, d_down_scale, H, I, shape->group, b + L.down_q,
                               (float*)(b + L.down_s), s, wb);

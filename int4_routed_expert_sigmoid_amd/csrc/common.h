@@ -603,6 +603,13 @@ coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t 
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
                                int32_t group, uint8_t* q, float* s, hipStream_t stream,
                                int32_t wbits = 4, bool gu_rows = false);
+// Two matrices of the same shape (an expert's gate and up) in one launch when
+// both fit the one-wave-per-row kernel, else one after the other.
+coli_status launch_convert_fp8_pair(const uint8_t* w8a, const float* scale_a, uint8_t* qa,
+                                    float* sa, const uint8_t* w8b, const float* scale_b,
+                                    uint8_t* qb, float* sb, int64_t rows, int64_t cols,
+                                    int32_t group, hipStream_t stream, int32_t wbits,
+                                    bool gu_rows);
 coli_status launch_router_logits(const float* wr, const float* x, int32_t T, int32_t H,
                                  int32_t E, float* logits, hipStream_t stream);
 // Router for small batches (T <= kSmallT): logits (when router_w is given)

@@ -29,13 +29,33 @@ __device__ __forceinline__ int quant_q(float v, float scale, float inv) {
     return (int)fminf(fmaxf(r, (float)QLO), (float)QHI);
 }
 
-// int4: 8 nibbles of one output word.
+// rint(t) of quant_q without its division, clamped, and whether the word
+// needs the division: |t - rint(t)| within the window of a half-integer, or t
+// not finite (the comparison fails for NaN). Same window and same rounding as
+// quant_q, so a word built from these equals one built from quant_q whenever
+// no element is flagged.
+template <int QLO, int QHI>
+__device__ __forceinline__ int quant_fast(float v, float inv, bool& near) {
+    const float t = v * inv;
+    const float r = rintf(t);
+    near |= !(fabsf(t - r) < 0.5f - 0x1p-14f);
+    return (int)__builtin_amdgcn_fmed3f(r, (float)QLO, (float)QHI);
+}
+
+// int4: 8 nibbles of one output word. The division is taken once per word,
+// and only for words with an element near a half-integer quotient.
 __device__ __forceinline__ uint32_t pack8(const float v[8], float scale) {
-    uint32_t word = 0;
     if (scale == 0.f) return 0;
     const float inv = __fdiv_rn(1.0f, scale);
+    uint32_t word = 0;
+    bool near = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_q<-8, 7>(v[i], scale, inv) & 15) << (4 * i);
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_fast<-8, 7>(v[i], inv, near) & 15) << (4 * i);
+    if (near) {
+        word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= (uint32_t)(quant_q<-8, 7>(v[i], scale, inv) & 15) << (4 * i);
+    }
     return word;
 }
 
@@ -47,11 +67,18 @@ __device__ __forceinline__ void pack8_w8(const float v[8], float scale, uint32_t
     if (scale == 0.f) return;
     lo = 0;
     const float inv = __fdiv_rn(1.0f, scale);
+    bool near = false;
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quant_fast<-128, 127>(v[i], inv, near);
+    if (near) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = quant_q<-128, 127>(v[i], scale, inv);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int q = quant_q<-128, 127>(v[i], scale, inv);
-        hi |= (uint32_t)((q >> 4) & 15) << (4 * i);
-        lo |= (uint32_t)((q & 15) ^ 8) << (4 * i);
+        hi |= (uint32_t)((q[i] >> 4) & 15) << (4 * i);
+        lo |= (uint32_t)((q[i] & 15) ^ 8) << (4 * i);
     }
 }
 
@@ -199,6 +226,15 @@ __global__ __launch_bounds__(256) void quant_g64_kernel(Src src, int64_t rows, i
     }
 }
 
+// Up to two FP8 matrices of the same shape converted by one launch (an
+// expert's gate and up): matrix blockIdx.y.
+struct Fp8Pair {
+    const uint8_t* w8[2];
+    const float* sc[2];
+    uint8_t* q[2];
+    float* s[2];
+};
+
 // FP8 rows of up to 8192 columns, 16-byte aligned, cols % 16 == 0: one wave
 // per row. Lane l holds units of 16 columns (one 16-byte load each) at
 // columns 16 (64 c + l) for c < NC, so every load instruction of the wave
@@ -206,14 +242,16 @@ __global__ __launch_bounds__(256) void quant_g64_kernel(Src src, int64_t rows, i
 // and the packing. gs64: the four lanes of a 64-column group share its max
 // through two shuffles.
 template <int NC, bool G64>
-__global__ __launch_bounds__(256) void fp8_wave_kernel(const uint8_t* __restrict__ w8,
-                                                       const float* __restrict__ sc,
-                                                       int64_t rows, int64_t cols,
-                                                       int64_t sc_cols, uint8_t* __restrict__ q,
-                                                       float* __restrict__ s, int gu_rows) {
+__global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t rows, int64_t cols,
+                                                       int64_t sc_cols, int gu_rows) {
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;                       // whole waves only
+    const int mi = blockIdx.y;
+    const uint8_t* __restrict__ w8 = mats.w8[mi];
+    const float* __restrict__ sc = mats.sc[mi];
+    uint8_t* __restrict__ q = mats.q[mi];
+    float* __restrict__ s = mats.s[mi];
     uint8_t* qr = q + (gu_rows ? gu_row(r) : r) * (cols >> 1);
     const int64_t units = cols >> 4;
     const uint8_t* row = w8 + r * cols;
@@ -275,18 +313,26 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(const uint8_t* __restrict
 }
 
 template <bool G64>
-bool launch_fp8_wave(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
-                     uint8_t* q, float* s, int gu_rows, hipStream_t stream) {
+bool launch_fp8_wave(const Fp8Pair& mats, int n_mats, int64_t rows, int64_t cols, int gu_rows,
+                     hipStream_t stream) {
     const int64_t nc = (cols / 16 + 63) / 64;
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)n_mats), block(256);
     const int64_t sc_cols = (cols + 127) / 128;
-    if (nc <= 1) launch(fp8_wave_kernel<1, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
-    else if (nc <= 2) launch(fp8_wave_kernel<2, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
-    else if (nc <= 4) launch(fp8_wave_kernel<4, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
-    else if (nc <= 6) launch(fp8_wave_kernel<6, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
-    else if (nc <= 8) launch(fp8_wave_kernel<8, G64>, grid, block, 0, stream, w8, scale, rows, cols, sc_cols, q, s, gu_rows);
+    if (nc <= 1) launch(fp8_wave_kernel<1, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+    else if (nc <= 2) launch(fp8_wave_kernel<2, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+    else if (nc <= 4) launch(fp8_wave_kernel<4, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+    else if (nc <= 6) launch(fp8_wave_kernel<6, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+    else if (nc <= 8) launch(fp8_wave_kernel<8, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
     else return false;
     return true;
+}
+
+// The one-wave-per-row kernel takes rows of 16-byte aligned codes, whole
+// 16-column units, at most 8192 columns, and 8-byte aligned int4 rows.
+bool fp8_wave_fits(const uint8_t* w8, const uint8_t* q, int64_t rows, int64_t cols,
+                   int32_t wbits) {
+    return wbits != 8 && (uintptr_t)w8 % 16 == 0 && (uintptr_t)q % 8 == 0 && cols % 16 == 0 &&
+           cols <= 8192 && rows <= 0x1fffffffLL;
 }
 
 template <typename Src, bool W8>
@@ -338,10 +384,10 @@ coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t ro
                                int32_t group, uint8_t* q, float* s, hipStream_t stream,
                                int32_t wbits, bool gu_rows) {
     if (rows == 0) return COLI_OK;
-    if (wbits != 8 && (uintptr_t)w8 % 16 == 0 && (uintptr_t)q % 8 == 0 && cols % 16 == 0 &&
-        cols <= 8192 && rows <= 0x1fffffffLL) {
-        const bool ok = group == 0 ? launch_fp8_wave<false>(w8, scale, rows, cols, q, s, gu_rows ? 1 : 0, stream)
-                                   : launch_fp8_wave<true>(w8, scale, rows, cols, q, s, gu_rows ? 1 : 0, stream);
+    if (fp8_wave_fits(w8, q, rows, cols, wbits)) {
+        const Fp8Pair one{{w8, w8}, {scale, scale}, {q, q}, {s, s}};
+        const bool ok = group == 0 ? launch_fp8_wave<false>(one, 1, rows, cols, gu_rows ? 1 : 0, stream)
+                                   : launch_fp8_wave<true>(one, 1, rows, cols, gu_rows ? 1 : 0, stream);
         if (ok) {
             COLI_CHECK_LAUNCH("fp8 convert kernel launch");
             return COLI_OK;
@@ -351,6 +397,26 @@ coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t ro
     const int aligned_out = ((uintptr_t)q % 4 == 0) && (cols % 8 == 0) ? 1 : 0;
     Fp8Src src{w8, scale, cols, (cols + 127) / 128, aligned_in};
     return launch_quant(src, rows, cols, group, q, s, aligned_out, stream, wbits, gu_rows ? 1 : 0);
+}
+
+coli_status launch_convert_fp8_pair(const uint8_t* w8a, const float* scale_a, uint8_t* qa,
+                                    float* sa, const uint8_t* w8b, const float* scale_b,
+                                    uint8_t* qb, float* sb, int64_t rows, int64_t cols,
+                                    int32_t group, hipStream_t stream, int32_t wbits,
+                                    bool gu_rows) {
+    if (rows == 0) return COLI_OK;
+    if (fp8_wave_fits(w8a, qa, rows, cols, wbits) && fp8_wave_fits(w8b, qb, rows, cols, wbits)) {
+        const Fp8Pair two{{w8a, w8b}, {scale_a, scale_b}, {qa, qb}, {sa, sb}};
+        const bool ok = group == 0 ? launch_fp8_wave<false>(two, 2, rows, cols, gu_rows ? 1 : 0, stream)
+                                   : launch_fp8_wave<true>(two, 2, rows, cols, gu_rows ? 1 : 0, stream);
+        if (ok) {
+            COLI_CHECK_LAUNCH("fp8 convert kernel launch");
+            return COLI_OK;
+        }
+    }
+    coli_status st = launch_convert_fp8(w8a, scale_a, rows, cols, group, qa, sa, stream, wbits, gu_rows);
+    if (st) return st;
+    return launch_convert_fp8(w8b, scale_b, rows, cols, group, qb, sb, stream, wbits, gu_rows);
 }
 
 }  // namespace coli
