@@ -50,7 +50,8 @@
  * Conventions for every call:
  *  - d_* pointers are device memory, h_* pointers host memory. The caller owns
  *    all of them; the library keeps none after a call returns (the expert
- *    cache handle aside).
+ *    cache handle's pools and arena, and the buffers of the testing read log,
+ *    coli_debug_read_log, aside).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls only enqueue work on it and return, unless stated otherwise.
  *  - Return value: COLI_OK, or a negative code with a message readable via
