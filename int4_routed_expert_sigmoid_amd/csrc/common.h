@@ -598,6 +598,11 @@ __device__ __forceinline__ constexpr int transpose_shift() {
 coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t group,
                             uint8_t* q, float* s, hipStream_t stream, int32_t wbits = 4,
                             bool gu_rows = false);
+// Two f32 matrices of the same shape (an expert's gate and up): one launch
+// with per-row scales when both have the same alignment, else two.
+coli_status launch_quantize_pair(const float* wa, uint8_t* qa, float* sa, const float* wb,
+                                 uint8_t* qb, float* sb, int64_t rows, int64_t cols,
+                                 int32_t group, hipStream_t stream, int32_t wbits, bool gu_rows);
 // FP8 e4m3 codes w8 [rows][cols] with scales [ceil(rows/128)][ceil(cols/128)]
 // -> f32 -> int4, through the same quantiser kernels.
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,

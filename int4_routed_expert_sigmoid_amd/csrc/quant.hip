@@ -161,21 +161,51 @@ struct Fp8Src {
     }
 };
 
-// One workgroup per row: block-wide max, then quantise and pack.
-template <typename Src, bool W8>
-__global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t cols,
-                                                        uint8_t* __restrict__ q,
-                                                        float* __restrict__ s, int aligned_out,
-                                                        int gu_rows) {
+// One workgroup per row: block-wide max, then quantise and pack. The first
+// NW words of each thread (8 columns each, thread t holding words t + 256 j)
+// stay in registers between the max and the packing, so a row of up to
+// 2048 NW columns is read once; words beyond are read again (from L2 at best:
+// with thousands of rows in flight, a second pass over the whole matrix goes
+// back to memory). Loads past the row end are clamped to its last word and
+// their values ignored, so every load of the first pass is issued at once.
+// Grid row y (blockIdx.y) converts matrix y of the pair: an expert's gate and
+// up matrices go through one launch.
+template <typename Src>
+struct QuantPair {
+    Src src[2];
+    uint8_t* q[2];
+    float* s[2];
+};
+
+template <typename Src, bool W8, int NW>
+__global__ __launch_bounds__(256) void quant_row_kernel(QuantPair<Src> mats, int64_t cols,
+                                                        int aligned_out, int gu_rows) {
     __shared__ float red[4];
     const int64_t r = blockIdx.x;
+    const int mi = blockIdx.y;
+    const Src src = mats.src[mi];
+    uint8_t* __restrict__ q = mats.q[mi];
+    float* __restrict__ s = mats.s[mi];
     const int64_t words = cols / 8, tail = cols % 8;   // tail is 0, 2, 4 or 6 columns
+    float v[NW][8] = {};
     float m = 0.f;
-    for (int64_t i = threadIdx.x; i < words; i += blockDim.x) {
-        float v[8];
-        src.load8(r, 8 * i, v);
+    if (words > 0) {                                   // rows of fewer than 8 columns: tail only
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+        for (int j = 0; j < NW; ++j) {
+            const int64_t i = threadIdx.x + (int64_t)j * 256;
+            src.load8(r, 8 * (i < words ? i : words - 1), v[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+        if (threadIdx.x + (int64_t)j * 256 < words)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[j][k]));
+    for (int64_t i = threadIdx.x + (int64_t)NW * 256; i < words; i += 256) {
+        float t[8];
+        src.load8(r, 8 * i, t);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(t[k]));
     }
     if (threadIdx.x == 0)
         for (int64_t c = words * 8; c < cols; ++c) m = fmaxf(m, fabsf(src.load1(r, c)));
@@ -187,15 +217,20 @@ __global__ __launch_bounds__(256) void quant_row_kernel(Src src, int64_t cols,
     const float scale = __fdiv_rn(m, W8 ? 127.0f : 7.0f);
     if (threadIdx.x == 0) s[r] = scale;
     uint8_t* qr = q + (gu_rows ? gu_row(r) : r) * (W8 ? cols : cols / 2);
-    for (int64_t i = threadIdx.x; i < words; i += blockDim.x) {
-        float v[8];
-        src.load8(r, 8 * i, v);
-        store8<W8>(qr, 8 * i, v, scale, aligned_out);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        const int64_t i = threadIdx.x + (int64_t)j * 256;
+        if (i < words) store8<W8>(qr, 8 * i, v[j], scale, aligned_out);
+    }
+    for (int64_t i = threadIdx.x + (int64_t)NW * 256; i < words; i += 256) {
+        float t[8];
+        src.load8(r, 8 * i, t);
+        store8<W8>(qr, 8 * i, t, scale, aligned_out);
     }
     if (!W8 && threadIdx.x == 0 && tail) {           // int8 rows are whole blocks
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int64_t c = 0; c < tail; ++c) v[c] = src.load1(r, words * 8 + c);
-        uint32_t word = pack8(v, scale);
+        float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int64_t c = 0; c < tail; ++c) t[c] = src.load1(r, words * 8 + c);
+        uint32_t word = pack8(t, scale);
         for (int64_t b = 0; b < tail / 2; ++b) qr[4 * words + b] = (uint8_t)(word >> (8 * b));
     }
 }
@@ -335,13 +370,23 @@ bool fp8_wave_fits(const uint8_t* w8, const uint8_t* q, int64_t rows, int64_t co
            cols <= 8192 && rows <= 0x1fffffffLL;
 }
 
+// Per-row scales: one launch for matrix a, or for a and the same-shaped b
+// (b_src non-null; same aligned_out). gs64: matrix a only.
 template <typename Src, bool W8>
 coli_status launch_quant_t(const Src& src, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
-                           float* s, int aligned_out, int gu_rows, hipStream_t stream) {
+                           float* s, int aligned_out, int gu_rows, hipStream_t stream,
+                           const Src* b_src = nullptr, uint8_t* b_q = nullptr,
+                           float* b_s = nullptr) {
     if (group == 0) {
         if (rows > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: too many rows");
-        launch(quant_row_kernel<Src, W8>, dim3((unsigned)rows), dim3(256), 0, stream, src,
-               cols, q, s, aligned_out, gu_rows);
+        const QuantPair<Src> mats{{src, b_src ? *b_src : src}, {q, b_src ? b_q : q},
+                                  {s, b_src ? b_s : s}};
+        // words of 8 columns per thread kept in registers: the row's, up to 4
+        const int64_t nw = (cols / 8 + 255) / 256;
+        const dim3 grid((unsigned)rows, b_src ? 2u : 1u), block(256);
+        if (nw <= 1) launch(quant_row_kernel<Src, W8, 1>, grid, block, 0, stream, mats, cols, aligned_out, gu_rows);
+        else if (nw <= 2) launch(quant_row_kernel<Src, W8, 2>, grid, block, 0, stream, mats, cols, aligned_out, gu_rows);
+        else launch(quant_row_kernel<Src, W8, 4>, grid, block, 0, stream, mats, cols, aligned_out, gu_rows);
     } else {
         // the group of 8 lanes must not straddle rows: cols % 64 == 0 is required
         const int64_t total = rows * (cols / 8);
@@ -355,15 +400,17 @@ coli_status launch_quant_t(const Src& src, int64_t rows, int64_t cols, int32_t g
 
 template <typename Src>
 coli_status launch_quant(const Src& src, int64_t rows, int64_t cols, int32_t group, uint8_t* q,
-                         float* s, int aligned_out, hipStream_t stream, int32_t wbits, int gu_rows) {
+                         float* s, int aligned_out, hipStream_t stream, int32_t wbits, int gu_rows,
+                         const Src* b_src = nullptr, uint8_t* b_q = nullptr, float* b_s = nullptr) {
     if (rows == 0) return COLI_OK;
     coli_status st;
     if (wbits == 8) {
-        if (cols % kBlock || (uintptr_t)q % 4)
+        if (cols % kBlock || (uintptr_t)q % 4 || (b_src && (uintptr_t)b_q % 4))
             return fail(COLI_EINVAL, "quantize: int8 rows need cols % 32 == 0 and 4-byte alignment");
-        st = launch_quant_t<Src, true>(src, rows, cols, group, q, s, 1, gu_rows, stream);
+        st = launch_quant_t<Src, true>(src, rows, cols, group, q, s, 1, gu_rows, stream, b_src, b_q, b_s);
     } else {
-        st = launch_quant_t<Src, false>(src, rows, cols, group, q, s, aligned_out, gu_rows, stream);
+        st = launch_quant_t<Src, false>(src, rows, cols, group, q, s, aligned_out, gu_rows, stream,
+                                        b_src, b_q, b_s);
     }
     if (st) return st;
     COLI_CHECK_LAUNCH("quantize kernel launch");
@@ -378,6 +425,20 @@ coli_status launch_quantize(const float* w, int64_t rows, int64_t cols, int32_t 
                         (cols % 8 == 0) ? 1 : 0;
     F32Src src{w, cols, aligned};
     return launch_quant(src, rows, cols, group, q, s, aligned, stream, wbits, gu_rows ? 1 : 0);
+}
+
+coli_status launch_quantize_pair(const float* wa, uint8_t* qa, float* sa, const float* wb,
+                                 uint8_t* qb, float* sb, int64_t rows, int64_t cols,
+                                 int32_t group, hipStream_t stream, int32_t wbits, bool gu_rows) {
+    const int al_a = ((uintptr_t)wa % 16 == 0) && ((uintptr_t)qa % 4 == 0) && (cols % 8 == 0) ? 1 : 0;
+    const int al_b = ((uintptr_t)wb % 16 == 0) && ((uintptr_t)qb % 4 == 0) && (cols % 8 == 0) ? 1 : 0;
+    if (group != 0 || al_a != al_b) {
+        coli_status st = launch_quantize(wa, rows, cols, group, qa, sa, stream, wbits, gu_rows);
+        if (st) return st;
+        return launch_quantize(wb, rows, cols, group, qb, sb, stream, wbits, gu_rows);
+    }
+    const F32Src a{wa, cols, al_a}, b{wb, cols, al_b};
+    return launch_quant(a, rows, cols, group, qa, sa, al_a, stream, wbits, gu_rows ? 1 : 0, &b, qb, sb);
 }
 
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
