@@ -208,10 +208,12 @@ __device__ __forceinline__ bool unit_of(int n_tiles, int n_rb, int& tile, int& r
 // of down) and the tile's token halves (the second only when TWO). The 64 x 64
 // activation block of each k step is staged once per workgroup in LDS (double
 // buffered, one barrier per k step) and shared by the 4 waves. Weight nibbles
-// pass through the wave's own LDS region in whole cache lines. With GS, every
-// k step is one 64-column scale group: its sums start from the -136 * S
-// correction (the C operand of the step's first MFMA, read from LDS) and are
-// folded into `out` with the group's scale; otherwise `out` holds the raw sums.
+// pass through the wave's own LDS region in whole cache lines (half lines
+// with gs64). With GS, every k step is one 64-column scale group, and `out`
+// counts in units of the current group's scale: at each group the sums so far
+// are rescaled by (previous scale / this scale) and take the group's -136 * S
+// correction (read from LDS), and at the end they are multiplied by the last
+// scale; otherwise `out` holds the raw sums.
 constexpr int kLdsRow = 72;          // bf16 per LDS activation row (64 + 8 pad: conflict-free 16-B reads)
 constexpr int kSB = 4 * 2 * 32 * 128;  // bytes of the per-wave weight-line regions of a workgroup
 
@@ -234,11 +236,11 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     const int lane = threadIdx.x & 63, ln = lane & 31, lh = lane >> 5;
     const int ar = threadIdx.x >> 2, aq = threadIdx.x & 3;     // staging: row, 16-column quarter
     const bool aload = TWO || ar < 32;                         // wave-uniform
-    // per-row scales: accumulate straight into `out`; gs64: per-group sums in `part`
-    f32x16 part[2][2];
-    f32x16 (&acc)[2][2] = GS ? part : out;
+    // the sums accumulate straight into `out`: with per-row scales as raw sums,
+    // with gs64 in units of the current group's scale (rescaled at each group)
+    f32x16 (&acc)[2][2] = out;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = out[b][0] = out[b][1] = f32x16{};
+    for (int b = 0; b < 2; ++b) out[b][0] = out[b][1] = f32x16{};
     // activation rows run kA k steps ahead (2 with per-row scales, 1 with
     // gs64): register set k % kA holds k step k between its load and its
     // store to LDS at the end of step k - 1
@@ -263,7 +265,7 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
         F[0] = gs0[kb];
         F[1] = gs1[kb];
     };
-    auto mma = [&](int buf, const uint4 (&P)[2], const f32x16 (&C)[2]) {
+    auto mma = [&](int buf, const uint4 (&P)[2]) {
         const uint4* r0 = reinterpret_cast<const uint4*>(&sA[buf][ln][lh * 32]);
         const uint4* r1 = reinterpret_cast<const uint4*>(&sA[buf][32 + ln][lh * 32]);
 #pragma unroll
@@ -275,26 +277,33 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
             for (int b = 0; b < 2; ++b) {
                 const uint32_t w = s == 0 ? P[b].x : s == 1 ? P[b].y : s == 2 ? P[b].z : P[b].w;
                 const bf16x8 bb = nib8_to_bf16(w);
-                const bool first = GS && s == 0;             // gs64: the group starts from C
-                acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bb, first ? C[0] : acc[b][0], 0, 0, 0);
-                if (TWO) acc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bb, first ? C[1] : acc[b][1], 0, 0, 0);
+                acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bb, acc[b][0], 0, 0, 0);
+                if (TWO) acc[b][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bb, acc[b][1], 0, 0, 0);
             }
         }
     };
-    auto ldC = [&](int kb, f32x16 (&C)[2]) {                  // gs64: -136 * S of the k step's group
+    // gs64: the group of k step kb starts from the sums so far in units of its
+    // own scale, acc * (previous scale / this scale), plus its -136 * S
+    // correction (staged in LDS); an all-zero group (scale 0) keeps the
+    // previous unit. Then out = sum_g scale_g * P_g = acc * (last scale).
+    float unit[2] = {0.f, 0.f};                                // the scale acc is counted in, per row
+    auto regroup = [&](int kb, const float (&f)[2]) {
         const float* cs_k = s_cs + kb % kCsChunk;
+        float ratio[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const float fe = f[b] != 0.f ? f[b] : unit[b];
+            ratio[b] = (kb == 0 || fe == 0.f) ? 0.f : unit[b] * __builtin_amdgcn_rcpf(fe);
+            unit[b] = fe;
+        }
 #pragma unroll
         for (int mb = 0; mb < (TWO ? 2 : 1); ++mb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) C[mb][j] = cs_k[(mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)) * kCsChunk];
-    };
-    auto fold = [&](const float (&f)[2]) {
+            for (int j = 0; j < 16; ++j) {
+                const float cs = cs_k[(mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3)) * kCsChunk];
 #pragma unroll
-        for (int mb = 0; mb < (TWO ? 2 : 1); ++mb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) out[b][mb][j] = fmaf(f[b], acc[b][mb][j], out[b][mb][j]);
+                for (int b = 0; b < 2; ++b) acc[b][mb][j] = fmaf(acc[b][mb][j], ratio[b], cs);
+            }
     };
     const int last = nk - 1;
     ldA(0, 0);
@@ -306,8 +315,8 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
         for (int j = 0; j < kF; ++j) ldF(F[j], min(j, last));
     }
     // Weight rows go through the wave's own LDS region in whole (per-row
-    // scales) or half (gs64, whose group sums and folds leave fewer registers)
-    // cache lines. Every GL k steps the wave requests the next GL steps of its
+    // scales) or half (gs64, whose rescaling leaves fewer registers) cache
+    // lines. Every GL k steps the wave requests the next GL steps of its
     // 64 rows (gate and up, or two column blocks of down): a load of RPI rows
     // x GL * 32 bytes touches RPI lines and uses GL * 32 bytes of each, where
     // the MFMA operand layout would touch 32 lines and use 32 bytes of each.
@@ -359,26 +368,24 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     const int ng = (nk + GL - 1) / GL, last_g = ng - 1;
     // one k step (k & 1 == d & 1 == the LDS activation buffer): request the
     // activation block kA steps ahead, multiply the current one with the
-    // step's weights; gs64: fold the group sums with their scales and request
-    // the scales kF steps ahead; store the next activation block
+    // step's weights (gs64: after rescaling the sums to the step's group and
+    // requesting the scales kF steps ahead); store the next activation block
     auto kstep = [&](int k, int d, bool group_end, int g) {
         if (GS && k % kCsChunk == 0) stage_group_sums(s_cs, sums, rows, it, m0, nk, k);
         ldA(k % kA, min(k + kA, last));
         if (kA >= 2) asm volatile("" ::: "memory");
-        f32x16 C[2];
-        if constexpr (GS) ldC(k, C);
-        uint4 Pk[2];
-        ldP(d, Pk);
-        // gs64 (two waves per SIMD, VALU folds between the MFMA blocks): the
-        // wave with MFMAs to issue goes first (measured 2% faster; with per-row
-        // scales it measured slower)
-        if constexpr (GS) __builtin_amdgcn_s_setprio(1);
-        mma(d & 1, Pk, C);
-        if constexpr (GS) __builtin_amdgcn_s_setprio(0);
         if constexpr (GS) {
-            fold(F[d % kF]);
+            regroup(k, F[d % kF]);
             ldF(F[d % kF], min(k + kF, last));
         }
+        uint4 Pk[2];
+        ldP(d, Pk);
+        // gs64 (VALU regrouping between the MFMA blocks): the wave with MFMAs
+        // to issue goes first (measured 2% faster; with per-row scales it
+        // measured slower)
+        if constexpr (GS) __builtin_amdgcn_s_setprio(1);
+        mma(d & 1, Pk);
+        if constexpr (GS) __builtin_amdgcn_s_setprio(0);
         stA((d & 1) ^ 1, (k + 1) % kA);
         if (group_end) {
             stG();
@@ -398,6 +405,14 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
 #pragma unroll
     for (int d = 0; d < GL; ++d)
         if (g * GL + d < nk) kstep(g * GL + d, d, false, g);
+    if constexpr (GS) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int mb = 0; mb < (TWO ? 2 : 1); ++mb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) out[b][mb][j] *= unit[b];
+    }
 }
 
 // ----------------------------------------------------------------- gate/up
@@ -469,13 +484,12 @@ __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& i
     }
 }
 
-// Three resident waves per SIMD with per-row scales (three workgroups per
-// CU also fit the LDS), two with gs64 (its group sums in registers).
+// Three resident waves per SIMD (three workgroups per CU also fit the LDS).
 template <bool GS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GS ? 2 : 3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void gemm_gateup_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
-    __shared__ __align__(16) uint8_t sB[kSB];    // the waves' weight-line regions
+    __shared__ __align__(16) uint8_t sB[GS ? kSB / 2 : kSB];    // the waves' weight-line regions (half lines with gs64)
     __shared__ float s_part[4][kTileM];          // per-wave token sums of bf16(h)
     __shared__ float s_tot[kTileM];              // per-token sum of the bf16 x row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
@@ -543,10 +557,10 @@ __device__ __forceinline__ void down_tile(const GemmArgs& a, const WorkItem& it,
 }
 
 template <bool GS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GS ? 2 : 3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void gemm_down_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
-    __shared__ __align__(16) uint8_t sB[kSB];    // the waves' weight-line regions
+    __shared__ __align__(16) uint8_t sB[GS ? kSB / 2 : kSB];    // the waves' weight-line regions (half lines with gs64)
     __shared__ float s_tot[kTileM];              // per-row sum of the bf16 h row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
     __shared__ float s_cs[GS ? kTileM * kCsChunk : 1];   // gs64: -136 * group sums, [row][group]
