@@ -225,7 +225,7 @@ __device__ __forceinline__ const uint8_t* shfl_ptr(const uint8_t* p, int src) {
     return (const uint8_t*)(((uint64_t)hi << 32) | lo);
 }
 
-template <bool GS, bool TWO>
+template <bool GS, bool TWO, int GL>
 __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int nk,
                                          const uint8_t* __restrict__ b0, const uint8_t* __restrict__ b1,
                                          const float* __restrict__ gs0, const float* __restrict__ gs1,
@@ -241,10 +241,10 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     f32x16 (&acc)[2][2] = out;
 #pragma unroll
     for (int b = 0; b < 2; ++b) out[b][0] = out[b][1] = f32x16{};
-    // activation rows run kA k steps ahead (2 with per-row scales, 1 with
-    // gs64): register set k % kA holds k step k between its load and its
+    // activation rows run kA k steps ahead (2; 1 with gs64 half lines, for
+    // registers): register set k % kA holds k step k between its load and its
     // store to LDS at the end of step k - 1
-    constexpr int kA = GS ? 1 : 2;
+    constexpr int kA = (GS && GL == 2) ? 1 : 2;
     // gs64: the group scales of the weight rows run kF k steps ahead
     constexpr int kF = 2;
     uint4 Ar[kA][2] = {};
@@ -314,10 +314,10 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
 #pragma unroll
         for (int j = 0; j < kF; ++j) ldF(F[j], min(j, last));
     }
-    // Weight rows go through the wave's own LDS region in whole (per-row
-    // scales) or half (gs64, whose rescaling leaves fewer registers) cache
-    // lines. Every GL k steps the wave requests the next GL steps of its
-    // 64 rows (gate and up, or two column blocks of down): a load of RPI rows
+    // Weight rows go through the wave's own LDS region in whole (GL = 4) or
+    // half (GL = 2) cache lines. Every GL k steps the wave requests the next
+    // GL steps of its 64 rows (gate and up, or two column blocks of down): a
+    // load of RPI rows
     // x GL * 32 bytes touches RPI lines and uses GL * 32 bytes of each, where
     // the MFMA operand layout would touch 32 lines and use 32 bytes of each.
     // At the end of a group the wave stores the next group into its region
@@ -325,7 +325,7 @@ __device__ __forceinline__ void mainloop(const uint16_t* __restrict__ arow, int 
     // on distinct banks for the operand reads below) and each k step reads its
     // operands from there. Only the wave itself reads its region, and one
     // wave's LDS operations execute in order, so no barrier is needed.
-    constexpr int GL = GS ? 2 : 4;                             // k steps per load group
+    static_assert(GL == 2 || GL == 4, "k steps per load group");
     constexpr int NG = 2 * GL;                                 // 16-byte chunks per row and group
     constexpr int RPI = 64 / NG;                               // rows per load
     constexpr int NI = 32 / RPI;                               // loads per matrix and group
@@ -442,7 +442,7 @@ __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& i
     // load would make every store wait for the stores before it
     const float fg = GS ? 1.f : gsc[irow], fu = GS ? 1.f : usc[irow];
     f32x16 out[2][2];
-    mainloop<GS, TWO>(arow, G, it.blob + L.gate_q + boff, it.blob + L.up_q + boff,
+    mainloop<GS, TWO, 4>(arow, G, it.blob + L.gate_q + boff, it.blob + L.up_q + boff,
                       gsc + (size_t)irow * G, usc + (size_t)irow * G, a.sx, a.rows_tok, it, m0,
                       sA, s_cs, sB, out);
 
@@ -484,12 +484,16 @@ __device__ __forceinline__ void gateup_tile(const GemmArgs& a, const WorkItem& i
     }
 }
 
-// Three resident waves per SIMD (three workgroups per CU also fit the LDS).
+// Three resident waves per SIMD with per-row scales (three workgroups per CU
+// also fit the LDS), two with gs64: its whole-line weight staging needs more
+// registers than three allow, and half lines (three waves) were fetched twice
+// from memory, the line evicted between its two halves (11.2 GB of L2 misses
+// per call against 5.6), which cost more than the lower occupancy.
 template <bool GS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GS ? 2 : 3)))
 void gemm_gateup_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t sA[2][kTileM][kLdsRow];
-    __shared__ __align__(16) uint8_t sB[GS ? kSB / 2 : kSB];    // the waves' weight-line regions (half lines with gs64)
+    __shared__ __align__(16) uint8_t sB[kSB];    // the waves' weight-line regions
     __shared__ float s_part[4][kTileM];          // per-wave token sums of bf16(h)
     __shared__ float s_tot[kTileM];              // per-token sum of the bf16 x row
     __shared__ int s_out[kTileM];                // output row of each tile row, -1 past the item
@@ -535,7 +539,7 @@ __device__ __forceinline__ void down_tile(const GemmArgs& a, const WorkItem& it,
 
     const float f[2] = {GS ? 1.f : dsc[cc0], GS ? 1.f : dsc[cc1]};   // before the loop, as in gate/up
     f32x16 out[2][2];
-    mainloop<GS, TWO>(arow, GI, dq + (size_t)cc0 * (I / 2) + lh * 16, dq + (size_t)cc1 * (I / 2) + lh * 16,
+    mainloop<GS, TWO, GS ? 2 : 4>(arow, GI, dq + (size_t)cc0 * (I / 2) + lh * 16, dq + (size_t)cc1 * (I / 2) + lh * 16,
                       dsc + (size_t)cc0 * GI, dsc + (size_t)cc1 * GI, a.sh, a.rows_out, it, m0,
                       sA, s_cs, sB, out);
 
@@ -556,6 +560,9 @@ __device__ __forceinline__ void down_tile(const GemmArgs& a, const WorkItem& it,
         }
 }
 
+// Three resident waves per SIMD; with gs64 the weights go in half lines (the
+// whole-line staging's registers would leave two waves, which measured slower
+// here than the lines fetched twice).
 template <bool GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void gemm_down_kernel(GemmArgs a) {
