@@ -64,7 +64,7 @@ WsLayout ws_layout(const coli_moe_shape* s, int32_t T, int32_t path) {
     W.n_unique = take(4);
     W.n_items = take(4);
     W.union_ws = take(union_ws_bytes(T, (int32_t)k, (int32_t)E));
-    W.items = take((E + 1) * sizeof(WorkItem));
+    W.items = take((size_t)std::max<int64_t>(E + 1, split_items_bound(E, T, k, true)) * sizeof(WorkItem));
     W.rows_tok = take(R * 4);
     W.rows_out = take(R * 4);
     W.xplanes = take((size_t)T * (H / kBlock) * kWordsPerBlock * 4);

@@ -174,6 +174,7 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
         ra.topp = s->topp;
         ra.codes = fold ? at<uint64_t>(ws, W.codes) : nullptr;
         ra.scores = fold ? at<float>(ws, W.scores) : nullptr;
+        ra.split = !mfma ? 1 : 0;
         st = launch_router_small(ra, stream);
         if (st) return st;
         encoded = true;
@@ -199,7 +200,12 @@ coli_status run_layer(const coli_moe_shape* s, const float* x, int32_t T, const 
             if (st) return st;
         }
     }
-    const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
+    // small batches on the GEMV path split their experts into items of at most
+    // kItemTokens tokens (one token: every item has one)
+    const bool split_items = T > 1 && T <= kSmallT && !cache && !mfma;
+    const int32_t max_items = split_items
+        ? (int32_t)split_items_bound(E, T, k, shared_blob != nullptr)
+        : (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
     if (!cache) {
         st = run_ffn(s, mfma, x, T, max_items, at<float>(ws, W.y_rows), ws, W, encoded, stream,
                      fold ? &fr : nullptr, kPassBoth, split);
@@ -244,7 +250,10 @@ coli_status run_rerun(const coli_moe_shape* s, int32_t T, const void* const* tab
     coli_status st = pick_mfma(s, T, COLI_PATH_GEMV, &mfma);
     if (st) return st;
     const int32_t E = s->n_routed, k = s->top_k;
-    const int32_t max_items = (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
+    // the work list the layer call left: split items for small batches
+    const int32_t max_items = T > 1 && T <= kSmallT
+        ? (int32_t)split_items_bound(E, T, k, shared_blob != nullptr)
+        : (int32_t)std::min<int64_t>(E, (int64_t)T * k) + (shared_blob ? 1 : 0);
     // the routing the gate/up pass republishes goes to the workspace's own copy
     const bool fold = folds_routing(s, T, false, false);
     const FusedRoute fr = fold ? fused_route(s, table, shared_blob, at<int32_t>(ws, W.idx),

@@ -218,6 +218,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
         route_token<EPL>(lg + (int64_t)t * E, a.bias, E, k, a.topp, a.idx + (int64_t)t * k,
                          a.w + (int64_t)t * k, s_idx + t * k);
     const int base = a.shared_blob ? 1 : 0;
+    // the shared expert's items (its T tokens, split like the routed experts')
+    const int sbase = !a.shared_blob ? 0 : a.split ? (T + kItemTokens - 1) / kItemTokens : 1;
     if (T == 1 && a.phase_mask == nullptr) {
         // one token: the k picks are distinct, so the union is their order by
         // expert id; every count is 0 or 1 and each offset is the number of
@@ -292,18 +294,19 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
     __syncthreads();
     // offsets, the unique list and the kept work items in one scan: thread
     // tid owns experts tid*EPT .. tid*EPT+3 and scans the packed triple
-    // (assignments << 22 | unique << 11 | kept); the fields cannot carry
-    // (assignments <= 512, experts <= 1024)
+    // (assignments << 22 | unique << 11 | work items); the fields cannot carry
+    // (assignments and items <= 512, experts <= 1024)
     int c[EPT];
     uint32_t packed = 0;
-    bool keep[EPT];
+    int nit[EPT];                           // work items of the expert (0: not kept)
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
         c[i] = e < E ? s_cnt[e] : 0;
-        keep[i] = with_items && c[i] > 0 &&
-                  (a.phase_mask == nullptr || a.phase_mask[e] == a.phase);
-        packed += ((uint32_t)c[i] << 22) + ((uint32_t)(c[i] > 0) << 11) + (uint32_t)keep[i];
+        const bool keep = with_items && c[i] > 0 &&
+                          (a.phase_mask == nullptr || a.phase_mask[e] == a.phase);
+        nit[i] = !keep ? 0 : a.split ? (c[i] + kItemTokens - 1) / kItemTokens : 1;
+        packed += ((uint32_t)c[i] << 22) + ((uint32_t)(c[i] > 0) << 11) + (uint32_t)nit[i];
     }
     uint32_t total = 0;
     const uint32_t pre = block_excl_scan(packed, s_scan, &total);
@@ -316,13 +319,14 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
             a.offsets[e] = off;
             s_off[e] = off;
             if (c[i] > 0) a.unique[upos++] = e;
-            if (keep[i]) {
+            for (int p = 0; p < nit[i]; ++p) {
+                const int first = a.split ? p * kItemTokens : 0;
                 WorkItem it;
                 it.blob = (const uint8_t*)tptr[i];
-                it.begin = off;
-                it.count = c[i];
+                it.begin = off + first;
+                it.count = a.split ? min(kItemTokens, c[i] - first) : c[i];
                 it.row0 = s_first[e];
-                a.items[base + kpos++] = it;
+                a.items[sbase + kpos++] = it;
             }
             off += c[i];
         }
@@ -333,14 +337,17 @@ __global__ __launch_bounds__(kRouterThreads) void router_plan_kernel(SmallRouter
         // work items: the shared expert first, then the kept unique experts;
         // without a table (cached calls) the items are formed later
         if (with_items && a.shared_blob) {
-            WorkItem it;
-            it.blob = (const uint8_t*)a.shared_blob;
-            it.begin = n;
-            it.count = T;
-            it.row0 = n;
-            a.items[0] = it;
+            for (int p = 0; p < sbase; ++p) {
+                const int first = a.split ? p * kItemTokens : 0;
+                WorkItem it;
+                it.blob = (const uint8_t*)a.shared_blob;
+                it.begin = n + first;
+                it.count = a.split ? min(kItemTokens, T - first) : T;
+                it.row0 = n + first;
+                a.items[p] = it;
+            }
         }
-        *a.n_items = with_items ? base + (int)(total & 0x7FF) : 0;
+        *a.n_items = with_items ? sbase + (int)(total & 0x7FF) : 0;
     }
     __syncthreads();
     // stable positions: rank of assignment i among earlier equal experts

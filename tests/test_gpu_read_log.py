@@ -6,8 +6,12 @@ With the GEMV read log on (coli_debug_read_log), every workgroup that streams
 a tile of an expert's weight rows records (blob, pass, tile). The oracle's
 routing of the same inputs decides which experts must appear: every expert of
 the union, and the shared one, has each gate/up tile and each down tile
-exactly once; no other expert appears (the experts outside the union all
-point at one zero blob, so a read of any of them shows as that blob)."""
+streamed once per work item, and no other expert appears (the experts outside
+the union all point at one zero blob, so a read of any of them shows as that
+blob). One token: one item per expert. Small batches: an expert that c of the
+tokens selected is ceil(c / 4) items of consecutive tokens, whose workgroups
+for one tile run side by side (so that the rows cross HBM once; the MTP
+counter profile checks the bytes), each walking its rows once."""
 from collections import Counter
 
 import numpy as np
@@ -84,15 +88,15 @@ def _check_union_read_once(shape, T, recs, idx_ref, ex):
     one = T == 1
     rows_gu, rows_dn = (16, 32) if one else (32, 64)
     n_gu, n_dn = I // rows_gu, -(-H // rows_dn)
+    items_of = lambda cnt: 1 if one else -(-cnt // 4)
     seen = Counter(zip(blob.tolist(), pas.tolist(), tile.tolist()))
-    assert max(seen.values()) == 1, "a tile was streamed by two workgroups"
     want = {(bb, p, t) for bb in expect for p, nt in ((0, n_gu), (1, n_dn)) for t in range(nt)}
     assert set(seen) == want
+    for (bb, p, t), times in seen.items():
+        assert times == items_of(expect[bb]), "a tile was streamed more often than its items"
     assert np.all(rows[pas == 0] == rows_gu) and np.all(rows[pas == 1] == rows_dn)
-    # each workgroup walks its rows once per chunk of up to 4 of the expert's tokens
-    for bb, cnt in expect.items():
-        w = walks[blob == bb]
-        assert np.all(w == (1 if cnt <= 2 else -(-cnt // 4))), (cnt, np.unique(w))
+    # every workgroup walks its rows once (its item has at most 4 tokens)
+    assert np.all(walks == 1), np.unique(walks)
     return len(expect)
 
 
@@ -111,14 +115,17 @@ def test_mtp_verify_batch_reads_each_unique_expert_once(coli):
     recs, n, idx_ref, ex = _logged_layer(coli, shape, 8, 22, "zipf")
     u = _check_union_read_once(shape, 8, recs, idx_ref, ex)
     assert u - 1 == len(np.unique(idx_ref)) < 64          # tokens do share experts
-    assert n == u * (2048 // 32 + 6144 // 64)
+    _, cnt = np.unique(idx_ref, return_counts=True)
+    items = int(sum(-(-c // 4) for c in cnt)) + 2         # the shared expert: 8 tokens, 2 items
+    assert (cnt > 4).any() and n == items * (2048 // 32 + 6144 // 64)
 
 
 @pytest.mark.parametrize("T,E,k,n_shared,seed", [(3, 16, 4, 0, 23), (13, 32, 4, 1, 24),
                                                  (2, 8, 8, 1, 25)])
 def test_small_batches_read_union_once(coli, T, E, k, n_shared, seed):
-    """Batches of a small layer: no shared expert, a token count with chunks of
-    4 and a remainder, and every expert selected by both tokens."""
+    """Batches of a small layer: no shared expert, a token count that splits
+    experts into items of 4 tokens and a remainder, and every expert selected
+    by both tokens."""
     shape = coli.MoEShape(512, 256, E, n_shared, k, 0)
     recs, _, idx_ref, ex = _logged_layer(coli, shape, T, seed, "zipf")
     _check_union_read_once(shape, T, recs, idx_ref, ex)
