@@ -71,10 +71,10 @@ inline BlobLayout blob_layout(int64_t H, int64_t I, int32_t group, int32_t wbits
     return L;
 }
 
-// One unit of GEMV/GEMM work: an expert blob applied to `count` rows of the
-// slot list starting at `begin`.
-// One expert's share of a work list: its blob, its rows begin .. begin+count-1
-// of the slot list (rows_tok / rows_out), and rows_out[begin] (row0).
+// One unit of GEMV/GEMM work: an expert blob applied to rows begin ..
+// begin+count-1 of the slot list (rows_tok / rows_out). row0 is rows_out[begin]
+// where one-token passes read it (one-token work lists); items of a batch keep
+// their expert's first assignment there, unread.
 struct WorkItem {
     const uint8_t* blob;
     int32_t begin;
