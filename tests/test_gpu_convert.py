@@ -91,3 +91,63 @@ def test_glm_expert_blob(coli, group):
         s = b[off[3 + i]:off[3 + i] + s_ref.nbytes].view(np.float32).reshape(s_ref.shape)
         assert np.array_equal(q, q_ref), i
         assert np.array_equal(s, s_ref), i
+
+
+def _offset_view(a, off, dtype):
+    """A contiguous device view of array a that starts `off` elements into a
+    larger buffer (off = 0: an ordinary aligned tensor)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    buf = torch.zeros(a.size + off, dtype=dtype, device="cuda")
+    buf[off:].copy_(torch.from_numpy(a.reshape(-1)))
+    return buf[off:].view(a.shape)
+
+
+@pytest.mark.parametrize("group", [0, 64])
+@pytest.mark.parametrize("offs", [(1, 0, 0), (8, 8, 3), (0, 1, 16)])
+def test_expert_blob_from_unaligned_matrices(coli, group, offs):
+    """Gate and up are converted together when both take the wave path; a
+    gate or up matrix that starts off a 16-byte boundary sends the pair to
+    separate launches (one of them the byte-wise path). Every blob part still
+    equals the oracle's conversion bit for bit."""
+    import torch
+    H, I = 256, 128
+    shape = coli.MoEShape(H, I, 8, 1, 2, group)
+    dims = ((I, H), (I, H), (H, I))
+    mats = [synth.fp8_block_matrix(10, 0, 12, m, r, c)
+            for m, (r, c) in zip((synth.MAT_GATE, synth.MAT_UP, synth.MAT_DOWN), dims)]
+    args = []
+    for (codes, scale), o in zip(mats, offs):
+        args += [_offset_view(codes, o, torch.uint8), _dev(scale)]
+    blob = coli.convert_fp8_expert(shape, *args)
+    torch.cuda.synchronize()
+    off, _ = coli.blob_layout(shape)
+    b = blob.cpu().numpy()
+    for i, ((codes, scale), (r, c)) in enumerate(zip(mats, dims)):
+        q_ref, s_ref = oracle.convert_fp8_int4(codes, scale, group)
+        q = blob_q_rows(b, off, i, r, q_ref.shape[1]).reshape(q_ref.shape)
+        s = b[off[3 + i]:off[3 + i] + s_ref.nbytes].view(np.float32).reshape(s_ref.shape)
+        assert np.array_equal(q, q_ref), i
+        assert np.array_equal(s, s_ref), i
+
+
+@pytest.mark.parametrize("group", [0, 64])
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 1), (1, 1, 0)])
+def test_quantize_expert_unaligned_matrices(coli, group, offs):
+    """f32 gate / up matrices off a 16-byte boundary: one unaligned sends the
+    per-row pair launch to two launches, both unaligned keep the pair launch on
+    its element-wise loads. Bit-exact against the oracle's quantizer."""
+    import torch
+    H, I = 256, 128
+    shape = coli.MoEShape(H, I, 8, 1, 2, group)
+    g, u, d = synth.expert_weights(4, 0, 1, H, I)
+    views = [_offset_view(a, o, torch.float32) for a, o in zip((g, u, d), offs)]
+    blob = coli.quantize_expert(shape, *views).cpu().numpy()
+    qe = oracle.QExpert.quantize(g, u, d, group)
+    off, _ = coli.blob_layout(shape)
+    for i, p in enumerate(qe.parts):
+        if i < 3:
+            raw = blob_q_rows(blob, off, i, p.shape[0], p.shape[1]).reshape(-1)
+        else:
+            raw = blob[off[i]:off[i] + p.nbytes]
+        assert np.array_equal(raw, p.reshape(-1).view(np.uint8)), f"part {i}"
