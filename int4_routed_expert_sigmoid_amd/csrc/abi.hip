@@ -9,6 +9,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "layer.h"
+#include "quant.h"
 
 namespace coli {
 
@@ -173,10 +174,9 @@ coli_status coli_quantize_expert(const coli_moe_shape* shape, const float* d_gat
     const BlobLayout L = blob_layout(H, I, shape->group, wb);
     uint8_t* b = (uint8_t*)d_blob;
     hipStream_t s = (hipStream_t)stream;
-    st = launch_quantize_pair(d_gate, b + L.gate_q, (float*)(b + L.gate_s), d_up, b + L.up_q,
-                              (float*)(b + L.up_s), I, H, shape->group, s, wb, true);
-    if (st) return st;
-    return launch_quantize(d_down, H, I, shape->group, b + L.down_q, (float*)(b + L.down_s), s, wb);
+    return launch_quantize_expert(d_gate, b + L.gate_q, (float*)(b + L.gate_s), d_up, b + L.up_q,
+                                  (float*)(b + L.up_s), d_down, b + L.down_q, (float*)(b + L.down_s),
+                                  H, I, shape->group, s, wb);
     COLI_GUARD_END
 }
 

@@ -9,6 +9,7 @@
 // scale 0 gives q = 0. Each thread owns 8 consecutive columns, i.e. one
 // 32-bit word of packed output.
 #include "common.h"
+#include "quant.h"
 
 namespace coli {
 namespace {
@@ -168,30 +169,46 @@ struct Fp8Src {
 // with thousands of rows in flight, a second pass over the whole matrix goes
 // back to memory). Loads past the row end are clamped to its last word and
 // their values ignored, so every load of the first pass is issued at once.
-// Grid row y (blockIdx.y) converts matrix y of the pair: an expert's gate and
-// up matrices go through one launch.
+// One launch covers up to three matrices (an expert's gate, up and down, each
+// with its own shape): rows are numbered across them in order, and workgroup
+// b takes row b, so the short rows of the last matrix fill the tail of the
+// long ones.
 template <typename Src>
-struct QuantPair {
-    Src src[2];
-    uint8_t* q[2];
-    float* s[2];
+struct QuantSet {
+    Src src[3];
+    uint8_t* q[3];
+    float* s[3];
+    int64_t rows[3];     // 0 for an absent matrix
+    int gu_rows[3];      // rows placed at gu_row(r) (an expert's gate or up)
 };
 
 template <typename Src, bool W8, int NW>
-__global__ __launch_bounds__(256) void quant_row_kernel(QuantPair<Src> mats, int64_t cols,
-                                                        int aligned_out, int gu_rows) {
+__global__ __launch_bounds__(256) void quant_row_kernel(QuantSet<Src> mats, int aligned_out) {
     __shared__ float red[4];
-    const int64_t r = blockIdx.x;
-    const int mi = blockIdx.y;
-    const Src src = mats.src[mi];
-    uint8_t* __restrict__ q = mats.q[mi];
-    float* __restrict__ s = mats.s[mi];
+    // the matrix of this row (uniform selects: no indexed copy of the argument)
+    int64_t r = blockIdx.x;
+    int mi = 0;
+    if (r >= mats.rows[0]) {
+        r -= mats.rows[0];
+        mi = 1;
+        if (r >= mats.rows[1]) {
+            r -= mats.rows[1];
+            mi = 2;
+        }
+    }
+    const Src src = mi == 0 ? mats.src[0] : mi == 1 ? mats.src[1] : mats.src[2];
+    uint8_t* __restrict__ q = mi == 0 ? mats.q[0] : mi == 1 ? mats.q[1] : mats.q[2];
+    float* __restrict__ s = mi == 0 ? mats.s[0] : mi == 1 ? mats.s[1] : mats.s[2];
+    const int gu_rows = mi == 0 ? mats.gu_rows[0] : mi == 1 ? mats.gu_rows[1] : mats.gu_rows[2];
+    const int64_t cols = src.cols;
     const int64_t words = cols / 8, tail = cols % 8;   // tail is 0, 2, 4 or 6 columns
     float v[NW][8] = {};
     float m = 0.f;
-    if (words > 0) {                                   // rows of fewer than 8 columns: tail only
 #pragma unroll
-        for (int j = 0; j < NW; ++j) {
+    for (int j = 0; j < NW; ++j) {
+        // register words wholly past a short row's end are not loaded (the
+        // condition is the same for the whole workgroup)
+        if ((int64_t)j * 256 < words) {
             const int64_t i = threadIdx.x + (int64_t)j * 256;
             src.load8(r, 8 * (i < words ? i : words - 1), v[j]);
         }
@@ -370,6 +387,24 @@ bool fp8_wave_fits(const uint8_t* w8, const uint8_t* q, int64_t rows, int64_t co
            cols <= 8192 && rows <= 0x1fffffffLL;
 }
 
+// Per-row scales for the matrices of a set in one launch; max_cols is the
+// widest row (it sets the words each thread keeps in registers).
+template <typename Src, bool W8>
+coli_status launch_quant_set(const QuantSet<Src>& mats, int64_t max_cols, int aligned_out,
+                             hipStream_t stream) {
+    const int64_t total = mats.rows[0] + mats.rows[1] + mats.rows[2];
+    if (total > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: too many rows");
+    if (total == 0) return COLI_OK;
+    // words of 8 columns per thread kept in registers: the widest row's, up to 4
+    const int64_t nw = (max_cols / 8 + 255) / 256;
+    const dim3 grid((unsigned)total), block(256);
+    if (nw <= 1) launch(quant_row_kernel<Src, W8, 1>, grid, block, 0, stream, mats, aligned_out);
+    else if (nw <= 2) launch(quant_row_kernel<Src, W8, 2>, grid, block, 0, stream, mats, aligned_out);
+    else if (nw <= 3) launch(quant_row_kernel<Src, W8, 3>, grid, block, 0, stream, mats, aligned_out);
+    else launch(quant_row_kernel<Src, W8, 4>, grid, block, 0, stream, mats, aligned_out);
+    return COLI_OK;
+}
+
 // Per-row scales: one launch for matrix a, or for a and the same-shaped b
 // (b_src non-null; same aligned_out). gs64: matrix a only.
 template <typename Src, bool W8>
@@ -379,14 +414,19 @@ coli_status launch_quant_t(const Src& src, int64_t rows, int64_t cols, int32_t g
                            float* b_s = nullptr) {
     if (group == 0) {
         if (rows > 0x7fffffffLL) return fail(COLI_EUNSUPPORTED, "quantize: too many rows");
-        const QuantPair<Src> mats{{src, b_src ? *b_src : src}, {q, b_src ? b_q : q},
-                                  {s, b_src ? b_s : s}};
-        // words of 8 columns per thread kept in registers: the row's, up to 4
-        const int64_t nw = (cols / 8 + 255) / 256;
-        const dim3 grid((unsigned)rows, b_src ? 2u : 1u), block(256);
-        if (nw <= 1) launch(quant_row_kernel<Src, W8, 1>, grid, block, 0, stream, mats, cols, aligned_out, gu_rows);
-        else if (nw <= 2) launch(quant_row_kernel<Src, W8, 2>, grid, block, 0, stream, mats, cols, aligned_out, gu_rows);
-        else launch(quant_row_kernel<Src, W8, 4>, grid, block, 0, stream, mats, cols, aligned_out, gu_rows);
+        QuantSet<Src> mats{};
+        mats.src[0] = mats.src[1] = mats.src[2] = src;
+        mats.q[0] = mats.q[1] = mats.q[2] = q;
+        mats.s[0] = mats.s[1] = mats.s[2] = s;
+        mats.rows[0] = rows;
+        mats.gu_rows[0] = mats.gu_rows[1] = gu_rows;
+        if (b_src) {
+            mats.src[1] = *b_src;
+            mats.q[1] = b_q;
+            mats.s[1] = b_s;
+            mats.rows[1] = rows;
+        }
+        return launch_quant_set<Src, W8>(mats, cols, aligned_out, stream);
     } else {
         // the group of 8 lanes must not straddle rows: cols % 64 == 0 is required
         const int64_t total = rows * (cols / 8);
@@ -439,6 +479,42 @@ coli_status launch_quantize_pair(const float* wa, uint8_t* qa, float* sa, const 
     }
     const F32Src a{wa, cols, al_a}, b{wb, cols, al_b};
     return launch_quant(a, rows, cols, group, qa, sa, al_a, stream, wbits, gu_rows ? 1 : 0, &b, qb, sb);
+}
+
+coli_status launch_quantize_expert(const float* wg, uint8_t* qg, float* sg, const float* wu,
+                                   uint8_t* qu, float* su, const float* wd, uint8_t* qd, float* sd,
+                                   int64_t H, int64_t I, int32_t group, hipStream_t stream,
+                                   int32_t wbits) {
+    auto al = [](const float* w, const uint8_t* q, int64_t cols) {
+        return ((uintptr_t)w % 16 == 0) && ((uintptr_t)q % 4 == 0) && (cols % 8 == 0) ? 1 : 0;
+    };
+    const int ag = al(wg, qg, H), au = al(wu, qu, H), ad = al(wd, qd, I);
+    const bool w8_ok = wbits != 8 || (H % kBlock == 0 && I % kBlock == 0 && (uintptr_t)qg % 4 == 0 &&
+                                      (uintptr_t)qu % 4 == 0 && (uintptr_t)qd % 4 == 0);
+    if (group != 0 || ag != au || ag != ad || !w8_ok || I == 0 || H == 0) {
+        coli_status st = launch_quantize_pair(wg, qg, sg, wu, qu, su, I, H, group, stream, wbits, true);
+        if (st) return st;
+        return launch_quantize(wd, H, I, group, qd, sd, stream, wbits, false);
+    }
+    QuantSet<F32Src> mats{};
+    mats.src[0] = F32Src{wg, H, ag};
+    mats.src[1] = F32Src{wu, H, au};
+    mats.src[2] = F32Src{wd, I, ad};
+    mats.q[0] = qg;
+    mats.q[1] = qu;
+    mats.q[2] = qd;
+    mats.s[0] = sg;
+    mats.s[1] = su;
+    mats.s[2] = sd;
+    mats.rows[0] = mats.rows[1] = I;
+    mats.rows[2] = H;
+    mats.gu_rows[0] = mats.gu_rows[1] = 1;
+    const int64_t wide = H > I ? H : I;
+    const coli_status st = wbits == 8 ? launch_quant_set<F32Src, true>(mats, wide, 1, stream)
+                                      : launch_quant_set<F32Src, false>(mats, wide, ag, stream);
+    if (st) return st;
+    COLI_CHECK_LAUNCH("quantize kernel launch");
+    return COLI_OK;
 }
 
 coli_status launch_convert_fp8(const uint8_t* w8, const float* scale, int64_t rows, int64_t cols,
