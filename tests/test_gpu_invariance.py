@@ -5,8 +5,9 @@
   both must compute the same function). Per token, the integer block sums are
   exact and the float reductions run in the same order for any batch, so the
   outputs must be bit-identical.
-- Reuse: the same workspace serves consecutive calls (its counters return to
-  zero), and repeated calls give identical bits.
+- Reuse: the same workspace serves consecutive calls without being cleared
+  (every call writes each region it reads), and repeated calls give identical
+  bits.
 """
 import numpy as np
 import pytest
