@@ -132,11 +132,13 @@ def test_expert_blob_from_unaligned_matrices(coli, group, offs):
 
 
 @pytest.mark.parametrize("group", [0, 64])
-@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 1), (1, 1, 0)])
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 1), (1, 1, 0), (1, 1, 1)])
 def test_quantize_expert_unaligned_matrices(coli, group, offs):
-    """f32 gate / up matrices off a 16-byte boundary: one unaligned sends the
-    per-row pair launch to two launches, both unaligned keep the pair launch on
-    its element-wise loads. Bit-exact against the oracle's quantizer."""
+    """f32 expert matrices off a 16-byte boundary. Per-row scales: the three
+    matrices share one launch only when all three are aligned alike (all
+    unaligned: element-wise loads and byte stores); otherwise gate and up go
+    through the pair launch (itself split when only one of them is unaligned)
+    and down through its own. Bit-exact against the oracle's quantizer."""
     import torch
     H, I = 256, 128
     shape = coli.MoEShape(H, I, 8, 1, 2, group)
