@@ -44,8 +44,12 @@ __device__ __forceinline__ int quant_fast(float v, float inv, bool& near) {
 }
 
 // int4: 8 nibbles of one output word. The division is taken once per word,
-// and only for words with an element near a half-integer quotient. The fast
-// path needs no clamp: every caller's scale is the maximum |v| of the values
+// and only for words with an element near a half-integer quotient: with
+// |v / scale| <= 7 (1 + 2^-24), t is within 2^-20 of the exact quotient and
+// the correctly rounded quotient within 2^-22 of it, so a t farther than
+// 2^-19 from every half-integer rounds like the correctly rounded quotient;
+// the fast path flags a window of 2^-18 (quant_q's wider one then picks the
+// elements it divides). The fast path needs no clamp: every caller's scale is the maximum |v| of the values
 // it packs divided by 7, so a finite t = v * inv stays within 7 (1 + 2^-22) and
 // rounds to -7..7 (non-finite t takes the division). Adding 1.5 * 2^23 to the
 // rounded value puts it, in two's complement, in the low bits of the sum, so
@@ -60,7 +64,7 @@ __device__ __forceinline__ uint32_t pack8(const float v[8], float scale) {
     for (int i = 0; i < 8; ++i) {
         const float t = v[i] * inv;
         const float r = rintf(t);
-        near |= !(fabsf(t - r) < 0.5f - 0x1p-14f);
+        near |= !(fabsf(t - r) < 0.5f - 0x1p-18f);
         b[i] = __float_as_uint(r + 0x1.8p23f);
     }
     uint32_t p[4];
@@ -242,8 +246,10 @@ __global__ __launch_bounds__(256) void quant_row_kernel(QuantSet<Src> mats, int 
     }
     if (threadIdx.x == 0)
         for (int64_t c = words * 8; c < cols; ++c) m = fmaxf(m, fabsf(src.load1(r, c)));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    // non-negative and never NaN (fmaxf drops NaN operands): the bits order
+    // like the values, so the wave maximum is an integer one over DPP /
+    // permlane partners
+    m = __uint_as_float(wave_umax(__float_as_uint(m)));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -284,9 +290,10 @@ __global__ __launch_bounds__(256) void quant_g64_kernel(Src src, int64_t rows, i
     float m = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
+    // the group's 8 lanes: DPP partners lane^1, lane^2, lane^7
+    m = fmaxf(m, __int_as_float(lane_xchg<1>(__float_as_int(m))));
+    m = fmaxf(m, __int_as_float(lane_xchg<2>(__float_as_int(m))));
+    m = fmaxf(m, __int_as_float(lane_xchg<4>(__float_as_int(m))));
     const float scale = __fdiv_rn(m, W8 ? 127.0f : 7.0f);
     if (i < total) {
         if ((wi & 7) == 0) s[r * (cols / 64) + wi / 8] = scale;
@@ -343,14 +350,22 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t row
         e4m3x4_to_f32(raw[c].z, &v[c][8]);
         e4m3x4_to_f32(raw[c].w, &v[c][12]);
         float mc = 0.f;
+        if ((int64_t)(c + 1) * 64 <= units) {        // the whole wave inside the row: no mask
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            v[c][i] = ok ? v[c][i] * f[c] : 0.f;
-            mc = fmaxf(mc, fabsf(v[c][i]));
+            for (int i = 0; i < 16; ++i) {
+                v[c][i] *= f[c];
+                mc = fmaxf(mc, fabsf(v[c][i]));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                v[c][i] = ok ? v[c][i] * f[c] : 0.f;
+                mc = fmaxf(mc, fabsf(v[c][i]));
+            }
         }
         if (G64) {
-            mc = fmaxf(mc, __shfl_xor(mc, 1));
-            mc = fmaxf(mc, __shfl_xor(mc, 2));
+            mc = fmaxf(mc, __int_as_float(lane_xchg<1>(__float_as_int(mc))));
+            mc = fmaxf(mc, __int_as_float(lane_xchg<2>(__float_as_int(mc))));
             const float scale = __fdiv_rn(mc, 7.0f);
             if (ok) {
                 const int64_t u = (int64_t)c * 64 + lane;
@@ -364,8 +379,10 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t row
         m = fmaxf(m, mc);
     }
     if (G64) return;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    // the row maximum: m is a non-negative float (never NaN: fmaxf drops NaN
+    // operands), so its bits order like its value and the wave's largest is
+    // an integer maximum over DPP / permlane partners
+    m = __uint_as_float(wave_umax(__float_as_uint(m)));
     const float scale = __fdiv_rn(m, 7.0f);
     if (lane == 0) s[r] = scale;
 #pragma unroll
