@@ -316,26 +316,32 @@ struct Fp8Pair {
 // reads 1 KB of one row; the decoded row stays in registers between the max
 // and the packing. gs64: the four lanes of a 64-column group share its max
 // through two shuffles.
-template <int NC, bool G64>
+template <int NC, bool G64, int SPLIT>
 __global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t rows, int64_t cols,
                                                        int64_t sc_cols, int gu_rows) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= rows) return;                       // whole waves only
+    // SPLIT waves of one workgroup share a row: wave part p takes the units
+    // [p NC 64, (p + 1) NC 64) and the row maximum is exchanged through LDS
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, part = wave % SPLIT;
+    const int64_t r = (int64_t)blockIdx.x * (4 / SPLIT) + wave / SPLIT;
+    const bool live = r < rows;                  // the same for the waves of a row
+    if (SPLIT == 1 && !live) return;             // whole waves only
     const int mi = blockIdx.y;
     const uint8_t* __restrict__ w8 = mats.w8[mi];
     const float* __restrict__ sc = mats.sc[mi];
     uint8_t* __restrict__ q = mats.q[mi];
     float* __restrict__ s = mats.s[mi];
-    uint8_t* qr = q + (gu_rows ? gu_row(r) : r) * (cols >> 1);
+    const int64_t rr = live ? r : rows - 1;      // dead rows re-read the last one, convert nothing
+    uint8_t* qr = q + (gu_rows ? gu_row(rr) : rr) * (cols >> 1);
     const int64_t units = cols >> 4;
-    const uint8_t* row = w8 + r * cols;
-    const float* scr = sc + (r >> 7) * sc_cols;
+    const int64_t ubase = (int64_t)part * NC * 64;
+    const uint8_t* row = w8 + rr * cols;
+    const float* scr = sc + (rr >> 7) * sc_cols;
     uint4 raw[NC];
     float f[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int64_t u = (int64_t)c * 64 + lane;
+        const int64_t u = ubase + (int64_t)c * 64 + lane;
         const int64_t uc = u < units ? u : 0;    // clamped: every load is in bounds
         raw[c] = *reinterpret_cast<const uint4*>(row + uc * 16);
         f[c] = scr[(uc * 16) >> 7];
@@ -344,13 +350,14 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t row
     float m = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const bool ok = (int64_t)c * 64 + lane < units;
+        const int64_t u = ubase + (int64_t)c * 64 + lane;
+        const bool ok = u < units;
         e4m3x4_to_f32(raw[c].x, &v[c][0]);
         e4m3x4_to_f32(raw[c].y, &v[c][4]);
         e4m3x4_to_f32(raw[c].z, &v[c][8]);
         e4m3x4_to_f32(raw[c].w, &v[c][12]);
         float mc = 0.f;
-        if ((int64_t)(c + 1) * 64 <= units) {        // the whole wave inside the row: no mask
+        if (ubase + (int64_t)(c + 1) * 64 <= units) {   // the whole wave inside the row: no mask
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 v[c][i] *= f[c];
@@ -367,9 +374,8 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t row
             mc = fmaxf(mc, __int_as_float(lane_xchg<1>(__float_as_int(mc))));
             mc = fmaxf(mc, __int_as_float(lane_xchg<2>(__float_as_int(mc))));
             const float scale = __fdiv_rn(mc, 7.0f);
-            if (ok) {
-                const int64_t u = (int64_t)c * 64 + lane;
-                if ((lane & 3) == 0) s[r * (cols >> 6) + (u >> 2)] = scale;
+            if (ok && live) {
+                if ((lane & 3) == 0) s[rr * (cols >> 6) + (u >> 2)] = scale;
                 uint2 out;
                 out.x = pack8(&v[c][0], scale);
                 out.y = pack8(&v[c][8], scale);
@@ -383,11 +389,18 @@ __global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t row
     // operands), so its bits order like its value and the wave's largest is
     // an integer maximum over DPP / permlane partners
     m = __uint_as_float(wave_umax(__float_as_uint(m)));
+    if constexpr (SPLIT > 1) {
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < SPLIT; ++p) m = fmaxf(m, red[wave - part + p]);
+    }
+    if (!live) return;
     const float scale = __fdiv_rn(m, 7.0f);
-    if (lane == 0) s[r] = scale;
+    if (lane == 0 && part == 0) s[rr] = scale;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int64_t u = (int64_t)c * 64 + lane;
+        const int64_t u = ubase + (int64_t)c * 64 + lane;
         if (u < units) {
             uint2 out;
             out.x = pack8(&v[c][0], scale);
@@ -401,13 +414,20 @@ template <bool G64>
 bool launch_fp8_wave(const Fp8Pair& mats, int n_mats, int64_t rows, int64_t cols, int gu_rows,
                      hipStream_t stream) {
     const int64_t nc = (cols / 16 + 63) / 64;
-    const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)n_mats), block(256);
     const int64_t sc_cols = (cols + 127) / 128;
-    if (nc <= 1) launch(fp8_wave_kernel<1, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
-    else if (nc <= 2) launch(fp8_wave_kernel<2, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
-    else if (nc <= 4) launch(fp8_wave_kernel<4, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
-    else if (nc <= 6) launch(fp8_wave_kernel<6, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
-    else if (nc <= 8) launch(fp8_wave_kernel<8, G64>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+    const dim3 block(256);
+    // rows of 3 to 6 units per lane go to two waves each (twice the waves in
+    // flight); other widths take one wave per row
+    if (nc > 2 && nc <= 6) {
+        const dim3 grid((unsigned)((rows + 1) / 2), (unsigned)n_mats);
+        if (nc <= 4) launch(fp8_wave_kernel<2, G64, 2>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+        else launch(fp8_wave_kernel<3, G64, 2>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+        return true;
+    }
+    const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)n_mats);
+    if (nc <= 1) launch(fp8_wave_kernel<1, G64, 1>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+    else if (nc <= 2) launch(fp8_wave_kernel<2, G64, 1>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
+    else if (nc <= 8) launch(fp8_wave_kernel<8, G64, 1>, grid, block, 0, stream, mats, rows, cols, sc_cols, gu_rows);
     else return false;
     return true;
 }
