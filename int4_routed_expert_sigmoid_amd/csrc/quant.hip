@@ -49,12 +49,13 @@ __device__ __forceinline__ int quant_fast(float v, float inv, bool& near) {
 // the correctly rounded quotient within 2^-22 of it, so a t farther than
 // 2^-19 from every half-integer rounds like the correctly rounded quotient;
 // the fast path flags a window of 2^-18 (quant_q's wider one then picks the
-// elements it divides). The fast path needs no clamp: every caller's scale is the maximum |v| of the values
-// it packs divided by 7, so a finite t = v * inv stays within 7 (1 + 2^-22) and
-// rounds to -7..7 (non-finite t takes the division). Adding 1.5 * 2^23 to the
-// rounded value puts it, in two's complement, in the low bits of the sum, so
-// the code is the sum's low nibble; nibble pairs are joined in the low byte of
-// a word and the four bytes gathered with two byte permutes.
+// elements it divides). The fast path needs no clamp: every caller's scale is
+// the maximum |v| of the values it packs divided by 7, so a finite
+// t = v * inv stays within 7 (1 + 2^-22) and rounds to -7..7 (non-finite t
+// takes the division). Adding 1.5 * 2^23 to the rounded value puts it, in
+// two's complement, in the low bits of the sum, so the code is the sum's low
+// nibble; nibble pairs are joined in the low byte of a word and the four
+// bytes gathered with two byte permutes.
 __device__ __forceinline__ uint32_t pack8(const float v[8], float scale) {
     if (scale == 0.f) return 0;
     const float inv = __fdiv_rn(1.0f, scale);
@@ -310,12 +311,13 @@ struct Fp8Pair {
     float* s[2];
 };
 
-// FP8 rows of up to 8192 columns, 16-byte aligned, cols % 16 == 0: one wave
-// per row. Lane l holds units of 16 columns (one 16-byte load each) at
-// columns 16 (64 c + l) for c < NC, so every load instruction of the wave
-// reads 1 KB of one row; the decoded row stays in registers between the max
-// and the packing. gs64: the four lanes of a 64-column group share its max
-// through two shuffles.
+// FP8 rows of up to 8192 columns, 16-byte aligned, cols % 16 == 0, each
+// converted by SPLIT waves of one workgroup (two for rows of 2049 to 6144
+// codes, one otherwise). Lane l of wave part p holds units of 16 columns (one
+// 16-byte load each) at columns 16 (64 (p NC + c) + l) for c < NC, so every
+// load instruction of a wave reads 1 KB of one row; the decoded values stay in
+// registers between the row maximum and the packing. gs64: the four lanes of a
+// 64-column group share its max through two DPP exchanges.
 template <int NC, bool G64, int SPLIT>
 __global__ __launch_bounds__(256) void fp8_wave_kernel(Fp8Pair mats, int64_t rows, int64_t cols,
                                                        int64_t sc_cols, int gu_rows) {
